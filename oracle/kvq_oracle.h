@@ -1,0 +1,105 @@
+/*
+ * kvq_oracle.h -- plain, slow CPU oracle for the compressed-KV decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links or calls
+ * this code; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no source with the GPU path.
+ *
+ * What it computes (sources: the pages listed in the functions below):
+ *   - historical K/V of one (layer, KV head) stored per token; tokens inside
+ *     the sequence's visual span are stored as b-bit codes (b in {2,4,8}) with
+ *     one (fp16 scale, fp16 min) pair per group of g values along the head
+ *     dimension; text tokens and protected heads (b = 16) keep bfloat16
+ *     (nuiw.github.io "VLM_KV_Quantization" sections 1-2: only the historical
+ *     cache is compressed, Visual/Text and K/V handled separately; HeadGuard
+ *     briefing: ~1/8 of physical KV heads keep image K and optionally V in
+ *     bf16);
+ *   - dequantisation x^ = code * scale + min, exact in double;
+ *   - single-query softmax attention over the dequantised rows, in double,
+ *     and the KL divergence between two attention distributions
+ *     (VLM_KV_Quantization section 3, D_KL(P_FP16 || P_Q)).
+ *
+ * Arithmetic is IEEE-754 binary32 where the quantiser fixes it (built with
+ * -ffp-contract=off, no fast-math) and binary64 elsewhere.  The fp16/bf16
+ * conversions are written from the IEEE-754 encoding definitions.
+ */
+#ifndef KVQ_ORACLE_H
+#define KVQ_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t num_layers, batch, num_q_heads, num_kv_heads, head_dim, group_size;
+  const int32_t *capacity;  /* [batch] rows reserved per sequence */
+  const int32_t *vis_begin; /* [batch] visual span [vis_begin, vis_end) */
+  const int32_t *vis_end;
+  const uint8_t *k_bits; /* [num_layers*num_kv_heads] in {2,4,8,16} */
+  const uint8_t *v_bits;
+} orc_config;
+
+typedef struct {
+  uint64_t total_bytes, payload_bytes, code_bytes, meta_bytes;
+  uint64_t bf16_visual_bytes, bf16_text_bytes, quantized_values, stored_values;
+} orc_cache_info;
+
+/* ---- IEEE-754 conversions -------------------------------------------- */
+uint16_t orc_f16_round_down(float x); /* largest binary16 <= x; zero -> +0 */
+uint16_t orc_f16_round_up(float x);   /* smallest binary16 >= x; zero -> +0 */
+double orc_f16_value(uint16_t h);
+uint16_t orc_bf16_round_nearest_even(float x);
+double orc_bf16_value(uint16_t b);
+
+/* ---- quantiser ---------------------------------------------------------- */
+/* One group of g values -> g codes plus fp16 (scale, min) bit patterns. */
+void orc_quantize_group(const float *x, int g, int bits, uint8_t *codes,
+                        uint16_t *scale16, uint16_t *min16);
+/* Round half to even, from the definition (no libm call). */
+double orc_round_half_even(double v);
+
+/* ---- layout --------------------------------------------------------------- */
+int orc_validate(const orc_config *c);
+int orc_cache_bytes(const orc_config *c, orc_cache_info *info);
+/* Byte offsets of the three planes of (layer, head, X), X = 0 for K, 1 for V.
+ * A plane that has no rows gets its offset anyway (size 0). */
+int orc_plane_offsets(const orc_config *c, int layer, int head, int X,
+                      uint64_t *vis, uint64_t *meta, uint64_t *txt);
+/* Where the row of position t of sequence s lives: plane 0 = VIS, 2 = TXT;
+ * row index within that plane. */
+int orc_row_of(const orc_config *c, int seq, int t, int *plane, int64_t *row);
+
+/* ---- store / load ---------------------------------------------------------- */
+/* Store rows t0..t1-1 of (layer, seq, head, X) from float32 src [(t1-t0), D]. */
+int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
+                   int head, int X, int t0, int t1, const float *src);
+/* Dequantised row of position t as exact doubles [D]. */
+int orc_load_row(const orc_config *c, const uint8_t *cache, int layer, int seq,
+                 int head, int X, int t, double *out);
+
+/* ---- attention ------------------------------------------------------------- */
+/* out[D] = softmax(scale * K q) V over T rows (row-major [T, D]); lse gets
+ * log(sum exp(scale * K q)) in natural log.  All double. */
+void orc_attention(const double *q, const double *K, const double *V, int T,
+                   int D, double scale, double *out, double *lse);
+/* Full decode for one (layer, seq, q-head): dequantise rows [0, len) of the
+ * KV head this query head reads, then attention. q_bf16 is the query's bf16
+ * bits [D]. scores (optional, [len]) receive the scaled logits. */
+int orc_decode_one(const orc_config *c, const uint8_t *cache, int layer,
+                   int seq, int qhead, int len, const uint16_t *q_bf16,
+                   float sm_scale, double *out, double *lse, double *scores);
+/* All (layer in [l0, l0+nl), seq, q-head): q/out laid out [nl, batch, Hq, D].
+ * lens [batch].  Returns 0 on success. */
+int orc_decode_all(const orc_config *c, const uint8_t *cache, int l0, int nl,
+                   const int32_t *lens, const uint16_t *q_bf16, float sm_scale,
+                   double *out);
+/* KL(P || Q) for two logit vectors of length T (natural log). */
+double orc_kl_logits(const double *s_p, const double *s_q, int T);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
