@@ -1,0 +1,396 @@
+"""Decode-step benchmark of libkvq on one MI355X.
+
+One step = the hot path of one decode step over a whole model:
+  1. kvq_quantize stores the new token's K/V for every layer (one launch,
+     positions [T, T+1): a generated token, so a bf16 row), then
+  2. kvq_decode_attention attends over [0, T+1) for every layer, KV head and
+     query head (split-K over token chunks + log-sum-exp merge).
+The cache is rotated over several replicas (>= 512 MB in total) so each step
+reads HBM, not the 256 MB Infinity Cache.  Inputs are resident in HBM before
+the timed region.
+
+Printed: one JSON line (rank 0).  `value` is effective HBM GB/s of the whole
+step (algorithmic bytes / step time); `roofline` refers to the decode
+attention launch, timed with HIP events on the stream it runs on.
+`cpu_baseline` times the CPU oracle (single thread) on a bounded sample of the
+same workload, scaled to one step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="headguard_step",
+                    choices=["headguard_step", "long_gqa", "llava_layer", "ragged_serving"])
+    ap.add_argument("--chunk", type=int, default=0, help="split chunk in tokens (0 = library)")
+    ap.add_argument("--replica-mb", type=int, default=512)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the bf16 reference, quantize block and copy measurements")
+    return ap.parse_args()
+
+
+def workload(name):
+    from quantized_decode_attention_quantize_amd import synth
+    if name == "headguard_step":
+        return synth.headguard_step(extra_capacity=1)
+    if name == "long_gqa":
+        w = synth.long_gqa()
+    elif name == "llava_layer":
+        w = synth.llava_layer(kbits=4, vbits=2)
+    else:
+        w = synth.ragged_serving()
+    w.capacity = [c + 1 for c in w.capacity]
+    return w
+
+
+def describe(w):
+    return {
+        "headguard_step": "LLaVA-OneVision-7B-shaped full decode step: 28 layers x 4 KV heads "
+                          "(28 query heads, D=128), 14 text + 6273 visual + 1 appended token; "
+                          "14 seeded protected heads bf16, others K INT4 / V INT2, group 64",
+        "long_gqa": "B=4 x 32768 tokens, 32 query / 8 KV heads, D=128, K INT4 / V INT2 g64",
+        "llava_layer": "one LLaVA-shaped layer, 6287+1 tokens, K INT4 / V INT2 g64",
+        "ragged_serving": "B=64 ragged 1024..16384 tokens, 28/4 heads, K INT8 / V INT4 g64",
+    }[w.name]
+
+
+def stored_row_bytes(w, l, h, X, t, s):
+    D, g = w.head_dim, w.group_size
+    b = int((w.v_bits if X else w.k_bits)[l * w.num_kv_heads + h])
+    visual = w.vis_begin[s] <= t < w.vis_end[s]
+    if visual and b < 16:
+        return D * b // 8 + (D // g) * 4
+    return 2 * D
+
+
+def algorithmic_bytes(w, lens):
+    """Stored K/V bytes every attended position costs, plus q and out."""
+    D, g = w.head_dim, w.group_size
+    total = 0
+    for l in range(w.num_layers):
+        for h in range(w.num_kv_heads):
+            for X in (0, 1):
+                b = int((w.v_bits if X else w.k_bits)[l * w.num_kv_heads + h])
+                for s in range(w.batch):
+                    n = lens[s]
+                    nv = max(0, min(n, w.vis_end[s]) - w.vis_begin[s])
+                    nt = n - nv
+                    vis_row = (D * b // 8 + (D // g) * 4) if b < 16 else 2 * D
+                    total += nv * vis_row + nt * 2 * D
+    total += 2 * w.num_layers * w.batch * w.num_q_heads * D * 2  # q in, out
+    return total
+
+
+class Events:
+    def __init__(self, torch, n):
+        self.s = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.e = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def times_ms(self):
+        return np.array([a.elapsed_time(b) for a, b in zip(self.s, self.e)])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+              "multi-GPU path: the decode kernel runs on one GPU's share and sharding is "
+              "described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from quantized_decode_attention_quantize_amd import kvq, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvq.lib()
+    stream = torch.cuda.current_stream()
+
+    w = workload(args.workload)
+    T = [c - 1 for c in w.capacity]          # history length before the step
+    lens = [t + 1 for t in T]                # attended after appending
+    cfg = kvq.Config.from_workload(w)
+    info = kvq.kvq_cache_bytes(cfg)
+    nbytes = info["total_bytes"]
+    R = max(2, math.ceil(args.replica_mb * 2 ** 20 / nbytes))
+    log(f"workload {w.name}: cache {nbytes / 1e6:.1f} MB x {R} replicas")
+
+    ref_cfg = None
+    if not args.no_extras:
+        rw = workload(args.workload)
+        rw.k_bits[:] = 16
+        rw.v_bits[:] = 16
+        ref_cfg = kvq.Config.from_workload(rw)
+        ref_bytes = kvq.kvq_cache_bytes(ref_cfg)["total_bytes"]
+        R_ref = max(2, math.ceil(args.replica_mb * 2 ** 20 / ref_bytes))
+
+    # ---- fill caches (untimed) ------------------------------------------
+    t_gen = time.time()
+    cache0 = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    ref0 = torch.zeros(ref_bytes, dtype=torch.uint8, device=dev) if ref_cfg else None
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    for l in range(w.num_layers):
+        for s in range(w.batch):
+            k = to_dev(w.sources(l, [s], 0, T[s], "k")[None])
+            v = to_dev(w.sources(l, [s], 0, T[s], "v")[None])
+            kvq.kvq_quantize(cfg, cache0, l, 1, [s], 0, T[s], k, v)
+            if ref0 is not None:
+                kvq.kvq_quantize(ref_cfg, ref0, l, 1, [s], 0, T[s], k, v)
+        if l % 7 == 0:
+            log(f"stored layer {l}")
+    torch.cuda.synchronize()
+    caches = [cache0] + [cache0.clone() for _ in range(R - 1)]
+    refs = ([ref0] + [ref0.clone() for _ in range(R_ref - 1)]) if ref0 is not None else []
+    log(f"caches ready in {time.time() - t_gen:.1f} s")
+
+    # new token's K/V (bf16) for all layers: [L, B, Hkv, 1, D]
+    from quantized_decode_attention_quantize_amd.synth import TAG_APPEND_K, TAG_APPEND_V
+    kn = np.stack([np.stack([np.stack([w.k_rows(l, s, h, T[s], T[s] + 1, TAG_APPEND_K)
+                                        for h in range(w.num_kv_heads)])
+                              for s in range(w.batch)]) for l in range(w.num_layers)])
+    vn = np.stack([np.stack([np.stack([w.v_rows(l, s, h, T[s], T[s] + 1, TAG_APPEND_V)
+                                        for h in range(w.num_kv_heads)])
+                              for s in range(w.batch)]) for l in range(w.num_layers)])
+    k_new, v_new = to_dev(kn), to_dev(vn)
+    q_bits = np.stack([w.q_bits(l) for l in range(w.num_layers)])
+    q = to_dev(q_bits)
+    out = torch.empty_like(q)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
+    seq_ids = list(range(w.batch))
+    ws = torch.empty(kvq.workspace_bytes(cfg, w.num_layers, args.chunk), dtype=torch.uint8,
+                     device=dev)
+    same_T = len(set(T)) == 1
+
+    def step(i, ev=None, j=None):
+        c = caches[i % R]
+        if same_T:
+            kvq.kvq_quantize(cfg, c, 0, w.num_layers, seq_ids, T[0], T[0] + 1, k_new, v_new)
+        else:
+            for s in range(w.batch):
+                kvq.kvq_quantize(cfg, c, 0, w.num_layers, [s], T[s], T[s] + 1,
+                                 k_new[:, s:s + 1].contiguous(), v_new[:, s:s + 1].contiguous())
+        if ev is not None:
+            ev.s[j].record(stream)
+        kvq.kvq_decode_attention(cfg, c, 0, w.num_layers, lens_d, q, out, w.sm_scale,
+                                 args.chunk, ws)
+        if ev is not None:
+            ev.e[j].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = Events(torch, args.steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, ev, i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    dec_ms = ev.times_ms()
+    dec_avg, dec_med = float(dec_ms.mean()), float(np.median(dec_ms))
+
+    alg = algorithmic_bytes(w, lens)
+    append_bytes = 2 * w.num_layers * w.batch * w.num_kv_heads * w.head_dim * 2 * 2
+    step_bytes = alg + append_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_gbs = alg / (dec_avg * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us "
+        f"(median {dec_med * 1e3:.1f}), {dec_gbs:.0f} GB/s")
+
+    extras = {}
+    if not args.no_extras:
+        # bf16 reference: same shapes, every row bf16 (bandwidth reference)
+        ref_alg = algorithmic_bytes(_bf16_like(w), lens)
+        wsr = torch.empty(kvq.workspace_bytes(ref_cfg, w.num_layers, args.chunk),
+                          dtype=torch.uint8, device=dev)
+        for i in range(args.warmup):
+            kvq.kvq_decode_attention(ref_cfg, refs[i % R_ref], 0, w.num_layers, lens_d, q, out,
+                                     w.sm_scale, args.chunk, wsr)
+        er = Events(torch, args.steps)
+        for i in range(args.steps):
+            er.s[i].record(stream)
+            kvq.kvq_decode_attention(ref_cfg, refs[i % R_ref], 0, w.num_layers, lens_d, q, out,
+                                     w.sm_scale, args.chunk, wsr)
+            er.e[i].record(stream)
+        torch.cuda.synchronize()
+        r_ms = float(er.times_ms().mean())
+        extras["bf16_reference_decode"] = {
+            "us": round(r_ms * 1e3, 2), "algorithmic_bytes": ref_alg,
+            "gbps": round(ref_alg / (r_ms * 1e-3) / 1e9, 1),
+            "speedup_of_quantized": round(r_ms / dec_avg, 3)}
+        extras["quantize_block"] = quantize_block(torch, kvq, synth, dev, stream, args)
+        extras["copy_ceiling"] = copy_ceiling(torch, dev, stream)
+        del refs, wsr
+
+    cpu = None if args.no_cpu else cpu_baseline(w, lens, q_bits, alg)
+
+    line = {
+        "metric": "decode-attn µs/step + effective HBM GB/s (% of MI355X peak), INT4/INT2 KV",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(w), "name": w.name, "layers": w.num_layers,
+                   "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "group": w.group_size, "tokens": lens,
+                   "cache_replicas": R, "chunk_tokens": args.chunk,
+                   "step_bytes": step_bytes} if w.batch <= 4 else
+                  {"workload": describe(w), "name": w.name, "cache_replicas": R,
+                   "step_bytes": step_bytes},
+        "decode": {"us_avg": round(dec_avg * 1e3, 2), "us_median": round(dec_med * 1e3, 2),
+                   "algorithmic_bytes": alg, "gbps": round(dec_gbs, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "kvq_decode_attention (split + merge launches)"},
+        "cpu_baseline": cpu,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+def _bf16_like(w):
+    import copy
+    r = copy.deepcopy(w)
+    r.k_bits[:] = 16
+    r.v_bits[:] = 16
+    return r
+
+
+def quantize_block(torch, kvq, synth, dev, stream, args):
+    """Quantize path: a fresh 6273-token visual block (bf16 in) for 8
+    sequences, K INT8 / V INT4 group 64 -> packed codes + meta."""
+    w = synth.visual_block()
+    cfg = kvq.Config.from_workload(w)
+    cache = torch.zeros(kvq.kvq_cache_bytes(cfg)["total_bytes"], dtype=torch.uint8, device=dev)
+    vb, ve = w.vis_begin[0], w.vis_end[0]
+    seqs = list(range(w.batch))
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k = to_dev(np.stack([w.sources(0, [s], vb, ve, "k")[0] for s in seqs])[None])
+    v = to_dev(np.stack([w.sources(0, [s], vb, ve, "v")[0] for s in seqs])[None])
+    R = 4
+    ks = [k] + [k.clone() for _ in range(R - 1)]
+    vs = [v] + [v.clone() for _ in range(R - 1)]
+    n = ve - vb
+    rd = 2 * w.batch * w.num_kv_heads * n * w.head_dim * 2
+    wr = w.batch * w.num_kv_heads * n * (w.head_dim * 8 // 8 + w.head_dim * 4 // 8 + 2 * 8)
+    for i in range(10):
+        kvq.kvq_quantize(cfg, cache, 0, 1, seqs, vb, ve, ks[i % R], vs[i % R])
+    ev = Events(torch, 50)
+    for i in range(50):
+        ev.s[i].record(stream)
+        kvq.kvq_quantize(cfg, cache, 0, 1, seqs, vb, ve, ks[i % R], vs[i % R])
+        ev.e[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(ev.times_ms().mean())
+    return {"workload": "8 seqs x 6273 visual tokens x 4 KV heads, bf16 in, K INT8 / V INT4 g64",
+            "us": round(ms * 1e3, 2), "read_bytes": rd, "write_bytes": wr,
+            "gbps": round((rd + wr) / (ms * 1e-3) / 1e9, 1)}
+
+
+def copy_ceiling(torch, dev, stream):
+    """A plain device-to-device copy of 1 GiB: the practical HBM ceiling."""
+    n = 2 ** 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    ev = Events(torch, 10)
+    for i in range(10):
+        ev.s[i].record(stream)
+        b.copy_(a)
+        ev.e[i].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median(ev.times_ms()))
+    return {"bytes_moved": 2 * n, "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
+def cpu_baseline(w, lens, q_bits, alg_bytes):
+    """Time the CPU oracle (one thread) decoding a bounded sample of the step:
+    every query head of a few layers over the full history, then scale to the
+    whole step."""
+    import oracle
+    cfg = oracle.Config.from_workload(w)
+    cache = oracle.new_cache(cfg)
+    n_layers = min(2, w.num_layers)
+    layers = list(range(n_layers))
+    seqs = list(range(min(w.batch, 2)))
+    for l in layers:
+        for s in seqs:
+            for h in range(w.num_kv_heads):
+                T = lens[s] - 1
+                oracle.store_rows(cfg, cache, l, s, h, 0, 0, T,
+                                  _f32(w.k_rows(l, s, h, 0, T)))
+                oracle.store_rows(cfg, cache, l, s, h, 1, 0, T,
+                                  _f32(w.v_rows(l, s, h, 0, T)))
+                oracle.store_rows(cfg, cache, l, s, h, 0, T, T + 1, np.zeros((1, w.head_dim),
+                                                                             np.float32))
+                oracle.store_rows(cfg, cache, l, s, h, 1, T, T + 1, np.zeros((1, w.head_dim),
+                                                                             np.float32))
+    t0 = time.perf_counter()
+    n_heads = 0
+    for l in layers:
+        for s in seqs:
+            for i in range(w.num_q_heads):
+                oracle.decode_one(cfg, cache, l, s, i, lens[s], q_bits[l, s, i], w.sm_scale)
+                n_heads += 1
+    dt = time.perf_counter() - t0
+    total_heads = w.num_layers * w.batch * w.num_q_heads
+    step_s = dt * total_heads / n_heads
+    return {"value": round(alg_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds_per_step": round(step_s, 3),
+            "sample": f"{n_heads} (layer, seq, query-head) decodes over the full history "
+                      f"({n_layers} layers x {len(seqs)} seqs x {w.num_q_heads} heads), "
+                      f"{dt:.2f} s, scaled x{total_heads / n_heads:.1f} to one step"}
+
+
+def _f32(a):
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return a.astype(np.float32)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * kvq.h -- C ABI of libkvq: decode-step attention over a compressed VLM KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * A vision-language model's historical K/V cache, per layer [B, H_kv, T, D],
+ * is stored compressed: inside each sequence's visual span the rows are
+ * group-wise INT8/INT4/INT2 codes, everything else (system text, question
+ * and generated tokens) stays at full precision, and K and V may use
+ * different widths.  Sources: nuiw.github.io "VLM_KV_Quantization"
+ * (section 1: the same historical cache at FP16/INT8/INT4/INT2 with the
+ * Visual/Text and K/V axes separated; section 2: prompt = [system text]
+ * [visual tokens] [question], cache [1, 4, T, 128] per layer with GQA 28:4;
+ * section 4: K and V differ in sensitivity).  Selected physical KV heads can
+ * keep their visual K, and optionally V, in bf16 on top of the low-bit
+ * quantiser (jiinsi.com HeadGuard briefing, core bullets).  Decoding reads
+ * the compressed rows and reconstructs them on chip inside a split-K
+ * flash-decoding kernel, never writing reconstructed K/V back to memory
+ * (gist.science 2604.02570, section 2-D: fused kernel, on-chip
+ * reconstruction, no intermediate tensors in VRAM).
+ *
+ * Quantiser (one group of g values along D of one token, b bits, n = 2^b-1):
+ *   mn16 = largest binary16 <= min(x)           (a zero is stored as +0)
+ *   r    = fl32(max(x) - mn16)
+ *   sc16 = 0 if r == 0, else smallest binary16 >= fl32(r / n)
+ *   code = clamp(rint_half_even(fl32(fl32(x - mn16) / sc16)), 0, n)
+ *          (0 when sc16 == 0); reconstruction x^ = code * sc16 + mn16.
+ * Every fl32 is one IEEE binary32 operation, rounded to nearest even.
+ * Rows stored at full precision are bf16 (round to nearest even).
+ *
+ * Cache layout (all integers little-endian)
+ * -----------------------------------------
+ * For every layer l, KV head h and X in (K, V), in that nesting order, three
+ * planes, each starting on a 256-byte boundary of the cache buffer:
+ *   VIS  rows for every visual position: D*b/8 bytes of codes, element d at
+ *        bit d*b of the row (byte d*b/8, bit (d*b)%8); or 2*D bf16 bytes when
+ *        b == 16.
+ *   META rows for every visual position when b < 16: for group j = 0..D/g-1
+ *        the fp16 scale then the fp16 min (4 bytes per group).
+ *   TXT  one bf16 row (2*D bytes) per non-visual position.
+ * Inside each plane the sequences follow each other in batch order; sequence
+ * s owns vis_end[s]-vis_begin[s] VIS/META rows and capacity[s] minus that
+ * many TXT rows.  Position t of sequence s is visual when
+ * vis_begin[s] <= t < vis_end[s]; a text position t maps to TXT row t if
+ * t < vis_begin[s], else t - (vis_end[s] - vis_begin[s]).  Padding bytes
+ * between planes are unspecified.
+ *
+ * Ownership, streams, errors
+ * --------------------------
+ * Every device pointer is owned by the caller (typically torch tensors);
+ * libkvq never allocates, frees or retains device memory and keeps no
+ * mutable global state.  Host arrays are read only during the call.
+ * kvq_quantize and kvq_decode_attention only enqueue work on `stream`
+ * (a hipStream_t; NULL = the default stream) and never synchronise; faults
+ * inside kernels surface at the caller's next synchronisation.  Every entry
+ * point validates all arguments on the host before any HIP call: when it
+ * returns an error nothing has been launched.  No C++ exception crosses the
+ * ABI.  Calls are re-entrant for distinct buffers.
+ *
+ * Supported shapes: head_dim D in {64, 128}; group_size g in {32, 64, 128}
+ * with g dividing D; bits in {2, 4, 8, 16}; num_q_heads a multiple of
+ * num_kv_heads.  Values whose stored fp16 scale/min would overflow binary16
+ * (|x| > 65504) are outside the supported range.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  KVQ_ERR_SHAPE = 2,       /* inconsistent sizes or spans                      */
+  KVQ_ERR_UNSUPPORTED = 3, /* well-formed but outside the supported shapes     */
+  KVQ_ERR_RANGE = 4,       /* layer / sequence / position index out of range   */
+  KVQ_ERR_WORKSPACE = 5,   /* workspace smaller than required                  */
+  KVQ_ERR_ALIGN = 6,       /* device pointer misaligned                        */
+  KVQ_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed       */
+  KVQ_ERR_INTERNAL = 8     /* unexpected internal failure                      */
+} kvq_status;
+
+typedef enum { KVQ_SRC_F32 = 0, KVQ_SRC_BF16 = 1 } kvq_src_dtype;
+
+/* Describes one cache.  All pointers are HOST arrays. */
+typedef struct {
+  int32_t num_layers;   /* L  >= 1                                             */
+  int32_t batch;        /* B  >= 1 sequences                                   */
+  int32_t num_q_heads;  /* Hq >= 1, multiple of num_kv_heads                   */
+  int32_t num_kv_heads; /* Hkv >= 1                                            */
+  int32_t head_dim;     /* D                                                   */
+  int32_t group_size;   /* g, quantisation group along D                       */
+  const int32_t *capacity;  /* [B] rows reserved per sequence (>= 1)          */
+  const int32_t *vis_begin; /* [B] 0 <= vis_begin <= vis_end <= capacity      */
+  const int32_t *vis_end;   /* [B]                                              */
+  const uint8_t *k_bits;    /* [L*Hkv] K width per (layer, KV head), 16 = bf16 */
+  const uint8_t *v_bits;    /* [L*Hkv] V width per (layer, KV head)            */
+} kvq_config;
+
+typedef struct {
+  uint64_t total_bytes;       /* bytes to allocate: payload + plane padding    */
+  uint64_t payload_bytes;     /* exact stored bytes, no padding                */
+  uint64_t code_bytes;        /* packed codes of visual rows                   */
+  uint64_t meta_bytes;        /* fp16 (scale, min) pairs                       */
+  uint64_t bf16_visual_bytes; /* visual rows of 16-bit (protected) heads       */
+  uint64_t bf16_text_bytes;   /* text rows (every head, K and V)               */
+  uint64_t quantized_values;  /* K/V scalars stored as codes                   */
+  uint64_t stored_values;     /* all K/V scalars: 2*L*Hkv*D*sum(capacity)      */
+} kvq_cache_info;
+
+/* Storage size of the cache `cfg` describes.  Host only, pure, synchronous.
+ * Errors: KVQ_ERR_NULL (cfg/info/arrays), KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_cache_bytes(const kvq_config *cfg, kvq_cache_info *info);
+
+/* Store positions [tok_begin, tok_end) of the sequences seq_ids[0..num_seqs)
+ * for layers [layer_begin, layer_begin + num_layers) into `cache`.
+ *
+ * Each row's format follows from its position and head: a visual position in
+ * a head whose width is < 16 is quantised (codes + meta); every other row
+ * (text, question, generated tokens; protected heads) is stored as bf16.
+ * Prefill of a whole sequence is one call over [0, capacity); appending a
+ * decoded token is a call over [T, T+1).
+ *
+ *   cache   device, kvq_cache_info.total_bytes, 256-byte aligned, written
+ *   seq_ids HOST [num_seqs], distinct, each in [0, batch)
+ *   k_src,
+ *   v_src   device, 16-byte aligned, contiguous
+ *           [num_layers, num_seqs, num_kv_heads, tok_end - tok_begin, D]
+ *           of float32 (KVQ_SRC_F32) or bf16 (KVQ_SRC_BF16)
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN,
+ * KVQ_ERR_RANGE (layer range, seq id, or a position outside [0, capacity)),
+ * KVQ_ERR_HIP.  An empty token range is a no-op returning KVQ_OK. */
+kvq_status kvq_quantize(const kvq_config *cfg, void *cache, int32_t layer_begin,
+                        int32_t num_layers, int32_t num_seqs, const int32_t *seq_ids,
+                        int32_t tok_begin, int32_t tok_end, const void *k_src,
+                        const void *v_src, kvq_src_dtype src_dtype, void *stream);
+
+/* One decode step of attention for layers [layer_begin, layer_begin +
+ * num_layers): for every layer l, sequence s and query head i,
+ *   out[l,s,i,:] = softmax(sm_scale * K^ q) V^   over positions [0, seq_lens[s])
+ * of KV head floor(i * Hkv / Hq), with K^, V^ the stored rows reconstructed
+ * on chip (codes * scale + min, or bf16).  Split-K over token chunks with a
+ * log-sum-exp merge; fp32 accumulation; out rounded to bf16 (nearest even).
+ *
+ *   cache      device, as written by kvq_quantize (read only)
+ *   seq_lens   DEVICE int32 [batch], 1 <= seq_lens[s] <= capacity[s]
+ *              (values outside that range are clamped into it)
+ *   q          device bf16 [num_layers, batch, Hq, D], 16-byte aligned
+ *   out        device bf16 [num_layers, batch, Hq, D], 16-byte aligned; must
+ *              not alias q, cache or workspace
+ *   sm_scale   softmax scale applied to q.k (e.g. 1/sqrt(D)), fp32
+ *   chunk_tokens  tokens per split-K chunk, 0 = library choice; otherwise a
+ *              positive multiple of 32
+ *   workspace  device scratch for split partials, 256-byte aligned.  If
+ *              workspace == NULL the call only writes the required size to
+ *              *workspace_bytes and launches nothing.  Otherwise
+ *              *workspace_bytes is the size provided.  The required size
+ *              depends on cfg, the layer count and chunk_tokens only.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN,
+ * KVQ_ERR_RANGE (layer range), KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
+kvq_status kvq_decode_attention(const kvq_config *cfg, const void *cache,
+                                int32_t layer_begin, int32_t num_layers,
+                                const int32_t *seq_lens, const void *q, void *out,
+                                float sm_scale, int32_t chunk_tokens, void *workspace,
+                                size_t *workspace_bytes, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *kvq_status_string(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

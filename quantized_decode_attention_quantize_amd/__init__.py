@@ -5,14 +5,12 @@ The compute path is a C-ABI shared library of hand-written HIP kernels
 (``csrc/``, declared in ``include/kvq.h``); ``kvq`` is a thin ctypes binding
 with the same call names.  ``synth`` draws the seeded synthetic workloads.
 """
+import importlib
+
 __all__ = ["kvq", "synth"]
 
 
 def __getattr__(name):
-    if name == "kvq":
-        from . import kvq as _kvq
-        return _kvq
-    if name == "synth":
-        from . import synth as _synth
-        return _synth
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,195 @@
+// kvq_quantize.hip -- store K/V rows into the compressed cache (gfx950).
+//
+// Visual rows of heads narrower than 16 bits become group-wise asymmetric
+// min-max codes with an fp16 (scale, min) pair per group; every other row is
+// stored as bf16 (nuiw.github.io "VLM_KV_Quantization" sections 1-2: only
+// the historical cache is compressed, Visual/Text and K/V separated;
+// HeadGuard briefing: protected heads keep bf16).  The quantiser's exact
+// arithmetic is spelled out in include/kvq.h.
+//
+// Mapping: one row (token) of D values is handled by D/8 consecutive lanes,
+// 8 values per lane (one 16-byte bf16 load or two for fp32).  A quantisation
+// group of g values spans g/8 lanes; its min/max is a butterfly over those
+// lanes.  Codes of one lane are contiguous in the packed row (8*b bits, b
+// bytes), so each lane issues one store of b bytes; the first lane of a group
+// writes the group's 4-byte (scale, min) pair.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+__device__ inline uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+__device__ inline float f16_float(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// One binary16 step toward -inf / +inf from a finite or infinite pattern.
+__device__ inline uint16_t f16_step_down(uint16_t h) {
+  if ((h & 0x7FFFu) == 0) return 0x8001u;          // +-0 -> -min subnormal
+  return (h & 0x8000u) ? uint16_t(h + 1u) : uint16_t(h - 1u);
+}
+__device__ inline uint16_t f16_step_up(uint16_t h) {
+  if ((h & 0x7FFFu) == 0) return 0x0001u;
+  return (h & 0x8000u) ? uint16_t(h - 1u) : uint16_t(h + 1u);
+}
+
+// Largest binary16 <= x: convert with round-to-nearest-even (v_cvt_f16_f32,
+// default MODE), step down once if that landed above x.  Zero -> +0.
+__device__ inline uint16_t f16_round_down(float x) {
+  uint16_t h = f16_bits((_Float16)x);
+  if (f16_float(h) > x) h = f16_step_down(h);
+  return (h & 0x7FFFu) ? h : uint16_t(0);
+}
+// Smallest binary16 >= x.
+__device__ inline uint16_t f16_round_up(float x) {
+  uint16_t h = f16_bits((_Float16)x);
+  if (f16_float(h) < x) h = f16_step_up(h);
+  return (h & 0x7FFFu) ? h : uint16_t(0);
+}
+
+__device__ inline uint16_t bf16_rne(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+__device__ inline float bf16_float(uint16_t b) {
+  return __builtin_bit_cast(float, uint32_t(b) << 16);
+}
+
+template <int LANES>  // butterfly over aligned groups of LANES lanes
+__device__ inline float group_min(float v) {
+#pragma unroll
+  for (int o = 1; o < LANES; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+template <int LANES>
+__device__ inline float group_max(float v) {
+#pragma unroll
+  for (int o = 1; o < LANES; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Quantise this lane's 8 values (part of a group spanning GL lanes) and
+// return the packed codes (8*bits bits).  Writes (scale | min << 16) to meta.
+template <int GL>
+__device__ inline uint64_t quantize8(const float (&x)[8], int bits, uint32_t& meta) {
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
+  }
+  lo = group_min<GL>(lo);
+  hi = group_max<GL>(hi);
+  const uint16_t mn16 = f16_round_down(lo);
+  const float mn = f16_float(mn16);
+  const float n = float((1 << bits) - 1);
+  const float range = hi - mn;
+  uint16_t sc16 = 0;
+  uint64_t packed = 0;
+  if (range != 0.0f) {
+    sc16 = f16_round_up(range / n);
+    const float sc = f16_float(sc16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float c = __builtin_rintf((x[i] - mn) / sc);
+      c = fminf(fmaxf(c, 0.0f), n);
+      packed |= uint64_t(uint32_t(c)) << (i * bits);
+    }
+  }
+  meta = uint32_t(sc16) | (uint32_t(mn16) << 16);
+  return packed;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
+  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int RPB = 256 / LPR;         // rows per block
+  const int lane_in_row = threadIdx.x % LPR;
+  const int row_in_block = threadIdx.x / LPR;
+  const int z = blockIdx.z;              // (lh, X)
+  const int lh = z >> 1, X = z & 1;
+  const int sl = blockIdx.y;             // sequence within this launch
+  const int r = blockIdx.x * RPB + row_in_block;  // token within [0, n_tok)
+  const bool active = r < a.n_tok;
+  const int rr = active ? r : a.n_tok - 1;  // keep inactive lanes in bounds
+  const int t = a.tok_begin + rr;
+
+  // source element offset: [nl, num_seqs, Hkv, n_tok, D]
+  const int glh = a.lh_off + lh;         // layer-local * Hkv + head
+  const int l_local = glh / a.Hkv, h = glh % a.Hkv;
+  const int64_t src_row =
+      ((int64_t(l_local) * a.num_seqs_total + (a.seq_off + sl)) * a.Hkv + h) * a.n_tok + rr;
+  const void* src = X ? a.v_src : a.k_src;
+  float x[8];
+  if (a.src_bf16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(src) + src_row * D + lane_in_row * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) +
+                                                      src_row * D + lane_in_row * 8);
+    const float4 u = p[0], v = p[1];
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  }
+
+  const int bits = a.bits[lh][X];
+  const int vb = a.vb[sl], ve = a.ve[sl];
+  const bool visual = t >= vb && t < ve;
+  uint8_t* vis = a.cache + uint64_t(a.base256[lh][X]) * 256u;
+
+  // Every lane of a row takes the same branch; groups never straddle rows.
+  if (visual && bits < 16) {
+    uint32_t meta;
+    uint64_t packed;
+    if (a.g == 32) packed = quantize8<4>(x, bits, meta);
+    else if (a.g == 64) packed = quantize8<8>(x, bits, meta);
+    else packed = quantize8<16>(x, bits, meta);
+    if (!active) return;
+    const int64_t row = a.vrow0[sl] + (t - vb);
+    uint8_t* rowp = vis + row * (D * bits / 8) + lane_in_row * bits;
+    if (bits == 2) *reinterpret_cast<uint16_t*>(rowp) = uint16_t(packed);
+    else if (bits == 4) *reinterpret_cast<uint32_t*>(rowp) = uint32_t(packed);
+    else *reinterpret_cast<uint2*>(rowp) = make_uint2(uint32_t(packed), uint32_t(packed >> 32));
+    const int gl = a.g / 8;
+    if (lane_in_row % gl == 0) {
+      uint8_t* metap = vis + meta_plane_offset(a.Rvis, D, bits) + row * ((D / a.g) * 4);
+      *reinterpret_cast<uint32_t*>(metap + (lane_in_row / gl) * 4) = meta;
+    }
+  } else {
+    if (!active) return;
+    uint8_t* rowp;
+    if (visual) {  // 16-bit (protected) head: visual row kept bf16 in VIS
+      rowp = vis + (a.vrow0[sl] + (t - vb)) * int64_t(2 * D);
+    } else {
+      const int64_t trow = a.trow0[sl] + (t < vb ? t : t - (ve - vb));
+      rowp = vis + txt_plane_offset(a.Rvis, D, a.g, bits) + trow * int64_t(2 * D);
+    }
+    uint4 o;
+    o.x = uint32_t(bf16_rne(x[0])) | (uint32_t(bf16_rne(x[1])) << 16);
+    o.y = uint32_t(bf16_rne(x[2])) | (uint32_t(bf16_rne(x[3])) << 16);
+    o.z = uint32_t(bf16_rne(x[4])) | (uint32_t(bf16_rne(x[5])) << 16);
+    o.w = uint32_t(bf16_rne(x[6])) | (uint32_t(bf16_rne(x[7])) << 16);
+    *reinterpret_cast<uint4*>(rowp + lane_in_row * 16) = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
+                           hipStream_t stream) {
+  const int rpb = 256 / (a.D / 8);
+  dim3 grid((a.n_tok + rpb - 1) / rpb, n_seq_launch, n_lh_launch * 2);
+  if (a.D == 128)
+    hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,186 @@
+"""ctypes binding of libkvq (include/kvq.h), same call names as the C ABI.
+
+Argument marshalling only: torch tensors become device pointers, the current
+torch stream becomes the HIP stream, host arrays become C arrays.  Every step
+of the computation runs in libkvq's HIP kernels; there is no fallback path.
+If ``libkvq.so`` has not been built the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK = 0
+KVQ_ERR_NULL = 1
+KVQ_ERR_SHAPE = 2
+KVQ_ERR_UNSUPPORTED = 3
+KVQ_ERR_RANGE = 4
+KVQ_ERR_WORKSPACE = 5
+KVQ_ERR_ALIGN = 6
+KVQ_ERR_HIP = 7
+KVQ_ERR_INTERNAL = 8
+KVQ_SRC_F32 = 0
+KVQ_SRC_BF16 = 1
+
+EXPORTS = ("kvq_cache_bytes", "kvq_quantize", "kvq_decode_attention", "kvq_status_string")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class _Cfg(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("batch", C.c_int32),
+                ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("group_size", C.c_int32),
+                ("capacity", C.POINTER(C.c_int32)), ("vis_begin", C.POINTER(C.c_int32)),
+                ("vis_end", C.POINTER(C.c_int32)), ("k_bits", C.POINTER(C.c_uint8)),
+                ("v_bits", C.POINTER(C.c_uint8))]
+
+
+class _Info(C.Structure):
+    _fields_ = [(n, C.c_uint64) for n in (
+        "total_bytes", "payload_bytes", "code_bytes", "meta_bytes",
+        "bf16_visual_bytes", "bf16_text_bytes", "quantized_values", "stored_values")]
+
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load libkvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"libkvq.so not found at {path}; build it with "
+                               "`python -m quantized_decode_attention_quantize_amd.build`")
+        L = C.CDLL(path)
+        P = C.c_void_p
+        L.kvq_cache_bytes.restype = C.c_int
+        L.kvq_cache_bytes.argtypes = [C.POINTER(_Cfg), C.POINTER(_Info)]
+        L.kvq_quantize.restype = C.c_int
+        L.kvq_quantize.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, C.c_int32,
+                                   C.POINTER(C.c_int32), C.c_int32, C.c_int32, P, P,
+                                   C.c_int, P]
+        L.kvq_decode_attention.restype = C.c_int
+        L.kvq_decode_attention.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, P, P, P,
+                                           C.c_float, C.c_int32, P, C.POINTER(C.c_size_t), P]
+        L.kvq_status_string.restype = C.c_char_p
+        L.kvq_status_string.argtypes = [C.c_int]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kvq_status_string(int(status)).decode()
+
+
+class Config:
+    """A kvq_config plus the host arrays it points into."""
+
+    def __init__(self, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, group_size: int, capacity, vis_begin, vis_end, k_bits, v_bits):
+        self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
+        self.vis_begin = np.ascontiguousarray(vis_begin, dtype=np.int32)
+        self.vis_end = np.ascontiguousarray(vis_end, dtype=np.int32)
+        self.k_bits = np.ascontiguousarray(k_bits, dtype=np.uint8)
+        self.v_bits = np.ascontiguousarray(v_bits, dtype=np.uint8)
+        self.num_layers, self.batch = num_layers, batch
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.head_dim, self.group_size = head_dim, group_size
+        self.c = _Cfg(num_layers, batch, num_q_heads, num_kv_heads, head_dim, group_size,
+                      self.capacity.ctypes.data_as(C.POINTER(C.c_int32)),
+                      self.vis_begin.ctypes.data_as(C.POINTER(C.c_int32)),
+                      self.vis_end.ctypes.data_as(C.POINTER(C.c_int32)),
+                      self.k_bits.ctypes.data_as(C.POINTER(C.c_uint8)),
+                      self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)))
+
+    @classmethod
+    def from_workload(cls, w) -> "Config":
+        a = w.config_arrays()
+        return cls(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                   w.group_size, a["capacity"], a["vis_begin"], a["vis_end"],
+                   a["k_bits"], a["v_bits"])
+
+    @property
+    def ref(self):
+        return C.byref(self.c)
+
+
+def _check(status: int, where: str) -> None:
+    if status != KVQ_OK:
+        raise KvqError(status, where)
+
+
+def _dev_ptr(t, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> Optional[C.c_void_p]:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def kvq_cache_bytes(cfg: Config) -> Dict[str, int]:
+    info = _Info()
+    _check(lib().kvq_cache_bytes(cfg.ref, C.byref(info)), "kvq_cache_bytes")
+    return {n: int(getattr(info, n)) for n, _ in _Info._fields_}
+
+
+def kvq_quantize(cfg: Config, cache, layer_begin: int, num_layers: int,
+                 seq_ids: Sequence[int], tok_begin: int, tok_end: int, k_src, v_src,
+                 stream=None) -> None:
+    """k_src/v_src: device float32 or bfloat16 [num_layers, len(seq_ids), Hkv, n_tok, D]."""
+    import torch
+    if k_src.dtype != v_src.dtype:
+        raise ValueError("k_src and v_src must share a dtype")
+    if k_src.dtype == torch.bfloat16:
+        dt = KVQ_SRC_BF16
+    elif k_src.dtype == torch.float32:
+        dt = KVQ_SRC_F32
+    else:
+        raise ValueError("sources must be float32 or bfloat16")
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+    _check(lib().kvq_quantize(cfg.ref, _dev_ptr(cache, "cache"), layer_begin, num_layers,
+                              len(ids), ids.ctypes.data_as(C.POINTER(C.c_int32)),
+                              tok_begin, tok_end, _dev_ptr(k_src, "k_src"),
+                              _dev_ptr(v_src, "v_src"), dt, _stream(stream)), "kvq_quantize")
+
+
+def workspace_bytes(cfg: Config, num_layers: int, chunk_tokens: int = 0) -> int:
+    n = C.c_size_t(0)
+    _check(lib().kvq_decode_attention(cfg.ref, None, 0, num_layers, None, None, None, 1.0,
+                                      chunk_tokens, None, C.byref(n), None),
+           "kvq_decode_attention(size query)")
+    return int(n.value)
+
+
+def kvq_decode_attention(cfg: Config, cache, layer_begin: int, num_layers: int, seq_lens,
+                         q, out, sm_scale: float, chunk_tokens: int = 0, workspace=None,
+                         stream=None) -> None:
+    """seq_lens: device int32 [batch]; q/out: device bf16 [num_layers, batch, Hq, D].
+    workspace: device uint8 tensor of at least workspace_bytes(...) bytes."""
+    if workspace is None:
+        raise ValueError("workspace tensor required (see workspace_bytes)")
+    n = C.c_size_t(workspace.numel() * workspace.element_size())
+    _check(lib().kvq_decode_attention(cfg.ref, _dev_ptr(cache, "cache"), layer_begin,
+                                      num_layers, _dev_ptr(seq_lens, "seq_lens"),
+                                      _dev_ptr(q, "q"), _dev_ptr(out, "out"), float(sm_scale),
+                                      chunk_tokens, _dev_ptr(workspace, "workspace"),
+                                      C.byref(n), _stream(stream)), "kvq_decode_attention")

@@ -1,0 +1,198 @@
+"""GPU parity of libkvq against the CPU oracle (MI355X).
+
+Stored bytes must be identical to the oracle's (codes, fp16 scale/min, bf16
+rows; padding between planes excluded).  Attention outputs (bf16) must be
+within max-abs 5e-3 and relative L2 2e-3 of the oracle's fp64 result on the
+same stored cache.  Every case prints its name before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from quantized_decode_attention_quantize_amd import kvq, synth
+
+from kvq_testlib import Pair, assert_close, errors
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvq.lib()
+    yield
+
+
+# --------------------------------------------------------------------------
+# quantize: bit-exact
+
+
+def test_quantize_tiny_bitexact():
+    _say("quantize tiny fp32 source")
+    p = Pair(synth.tiny())
+    p.store()
+    assert p.mismatches() == 0
+
+
+def test_quantize_llava_layer_bitexact():
+    _say("quantize llava layer bf16 source")
+    p = Pair(synth.llava_layer())
+    p.store()
+    assert p.mismatches() == 0
+
+
+@pytest.mark.parametrize("kb,vb", [(8, 2), (2, 8), (16, 4), (4, 16), (8, 8)])
+def test_quantize_widths_bitexact(kb, vb):
+    _say("quantize widths", kb, vb)
+    w = synth.llava_layer(seed=11, kbits=kb, vbits=vb)
+    w.capacity = [700]
+    w.vis_end = [650]
+    w.seq_lens = [700]
+    p = Pair(w)
+    p.store()
+    assert p.mismatches() == 0
+
+
+def test_quantize_headguard_sampled_layers_bitexact():
+    _say("quantize headguard 28 layers, compare sampled layers")
+    w = synth.headguard_step()
+    prot_layers = sorted({int(i) // 4 for i in w.protected})
+    layers = sorted({0, 27, prot_layers[0], prot_layers[-1]})
+    p = Pair(w)
+    p.store(oracle_too=False)
+    p.store(layers=layers)  # overwrite sampled layers on both sides (same bytes on GPU)
+    assert p.mismatches(layers=layers) == 0
+
+
+def test_quantize_appending_matches_full_store():
+    """Storing one position at a time (decode-time appends) writes the same
+    bytes as storing the whole range at once."""
+    _say("quantize append vs full")
+    w = synth.tiny(seed=5)
+    w.capacity = [300]
+    w.vis_begin = [20]
+    w.vis_end = [260]
+    p = Pair(w)
+    p.store(t0=0, t1=250)
+    for t in range(250, 300):
+        p.store(t0=t, t1=t + 1)
+    assert p.mismatches() == 0
+
+
+def test_quantize_d64_d128_groups():
+    for D, g in [(64, 32), (64, 64), (128, 32), (128, 128)]:
+        _say("quantize D/g", D, g)
+        kb = np.array([4, 2], dtype=np.uint8)
+        vb = np.array([8, 16], dtype=np.uint8)
+        w = synth.Workload(f"dg{D}_{g}", 1, 2, 4, 2, D, g, [90, 130], [5, 0], [85, 100],
+                           [90, 130], kb, vb, seed=D + g)
+        p = Pair(w)
+        p.store()
+        assert p.mismatches() == 0
+
+
+# --------------------------------------------------------------------------
+# decode: within tolerance of the oracle
+
+
+def _check_decode(p: Pair, lens, layers=None, chunk=0, what=""):
+    w = p.w
+    out, q = p.decode(lens, chunk=chunk)
+    layers = range(w.num_layers) if layers is None else layers
+    got, ref = [], []
+    for l in layers:
+        for s in range(w.batch):
+            for i in range(w.num_q_heads):
+                ref.append(p.oracle_decode(l, s, i, lens[s], q[l, s, i]))
+                got.append(out[l, s, i])
+    return assert_close(np.array(got), np.array(ref), what)
+
+
+def test_decode_tiny():
+    _say("decode tiny")
+    p = Pair(synth.tiny())
+    p.store()
+    _check_decode(p, [256], what="tiny")
+
+
+def test_decode_llava_layer():
+    _say("decode llava layer")
+    p = Pair(synth.llava_layer())
+    p.store()
+    _check_decode(p, [6287], what="llava")
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 224, 1024, 8192])
+def test_decode_split_invariance(chunk):
+    _say("decode split chunk", chunk)
+    w = synth.llava_layer(seed=7, kbits=4, vbits=2)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [6287], chunk=chunk, what=f"chunk {chunk}")
+
+
+@pytest.mark.parametrize("length", [1, 2, 13, 14, 15, 47, 3000, 6286, 6287])
+def test_decode_lengths(length):
+    """len < vis_begin (text only), inside the visual span, full."""
+    _say("decode length", length)
+    w = synth.llava_layer(seed=3, kbits=8, vbits=4)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [length], what=f"len {length}")
+
+
+def test_decode_headguard_step():
+    _say("decode headguard 28 layers (sampled layers vs oracle)")
+    w = synth.headguard_step()
+    prot_layers = sorted({int(i) // 4 for i in w.protected})
+    layers = sorted({0, 27, prot_layers[0]})
+    p = Pair(w)
+    p.store(oracle_too=False)
+    p.store(layers=layers)
+    _check_decode(p, [6287], layers=layers, what="headguard")
+
+
+def test_decode_bf16_reference_config():
+    _say("decode all-bf16 cache")
+    w = synth.llava_layer(seed=9, kbits=16, vbits=16)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [6287], what="bf16")
+
+
+def test_decode_mixed_formats_and_d64():
+    for D, g, kb, vb in [(64, 32, 4, 2), (64, 64, 16, 2), (128, 32, 2, 16), (128, 128, 8, 8)]:
+        _say("decode D/g/kb/vb", D, g, kb, vb)
+        w = synth.Workload(f"m{D}", 2, 2, 8, 2, D, g, [300, 170], [10, 0], [290, 170],
+                           [300, 170], np.full(4, kb, np.uint8), np.full(4, vb, np.uint8),
+                           seed=D + kb)
+        p = Pair(w)
+        p.store()
+        _check_decode(p, [300, 101], what=f"D{D} g{g} k{kb} v{vb}")
+
+
+def test_decode_empty_visual_span_and_all_visual():
+    _say("decode no visual rows / all visual rows")
+    kb = np.array([2], np.uint8)
+    w = synth.Workload("edge", 1, 3, 4, 1, 128, 64, [100, 90, 64], [40, 0, 0], [40, 90, 64],
+                       [100, 90, 64], kb, kb, seed=77)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [100, 90, 64], what="edge spans")
+
+
+def test_decode_deterministic():
+    _say("decode determinism")
+    p = Pair(synth.tiny(seed=8))
+    p.store(oracle_too=False)
+    a, _ = p.decode([256])
+    b, _ = p.decode([256])
+    assert np.array_equal(a, b)
