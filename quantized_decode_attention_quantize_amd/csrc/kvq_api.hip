@@ -247,7 +247,10 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
     if (chunk_tokens < 0 || chunk_tokens % 32) return KVQ_ERR_SHAPE;
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
-    const int chunk = chunk_tokens ? chunk_tokens : default_chunk(cfg, num_layers, 256, 1024);
+    const bool use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
+    const int chunk = chunk_tokens ? chunk_tokens
+                                   : use_mfma ? default_chunk(cfg, num_layers, 128, 1024)
+                                              : default_chunk(cfg, num_layers, 256, 1024);
     const DecodePlan plan = plan_decode(cfg, num_layers, chunk);
     if (!workspace) {
       *workspace_bytes = plan.total;
@@ -316,9 +319,14 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
           }
           a.lh_glob[i] = uint16_t(glh);
         }
-        if (launch_decode_simple(a, ns_l, hs) != hipSuccess) return KVQ_ERR_HIP;
+        const hipError_t e = use_mfma ? launch_decode_mfma(a, ns_l, hs)
+                                      : launch_decode_simple(a, ns_l, hs);
+        if (e != hipSuccess) return KVQ_ERR_HIP;
       }
-      if (launch_decode_merge(a, num_layers, ns_l, hs) != hipSuccess) return KVQ_ERR_HIP;
+      // the matrix-core kernel finishes single-chunk calls itself
+      if (!(use_mfma && plan.max_chunks == 1) &&
+          launch_decode_merge(a, num_layers, ns_l, hs) != hipSuccess)
+        return KVQ_ERR_HIP;
     }
     return KVQ_OK;
   } catch (...) {

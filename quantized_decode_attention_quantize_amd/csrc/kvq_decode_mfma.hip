@@ -1,0 +1,530 @@
+// kvq_decode_mfma.hip -- split-K decode attention on the CDNA4 matrix cores.
+//
+// Same contract as the general split kernel (kvq_decode.hip): one workgroup
+// per token chunk of one (layer, sequence, KV head); stored rows are
+// reconstructed on chip and never written back (gist.science 2604.02570,
+// section 2-D: reconstruction fused into flash decoding); K/V widths per
+// head and the Visual/Text split follow nuiw.github.io "VLM_KV_Quantization"
+// (sections 1-2) and the HeadGuard briefing (bf16 protected heads).
+//
+// Work of one wave: 32 tokens per step, all contractions on
+// v_mfma_f32_16x16x32_{f16,bf16} (wave64, 16x16 tile, K = 32):
+//
+//   q.k   S^T[token][c] = sum_k A[token][k] B[k][c] over two 16-token tiles.
+//         A = stored K row data of the tile, B = Q' (built once per segment).
+//         Column c = (head h, group j) = h * NG + j: Q' holds head h's query
+//         restricted to the d of group j, so each column accumulates one
+//         group's partial dot product and the group's fp16 scale/min apply
+//         after the product: score = sum_j sc_j * acc_j + mn_j * sum_{d in j} q_d.
+//         Integer codes enter the MFMA as exact binary16 SUBNORMALS: the code
+//         bits are masked into place (value code * w * 2^-24 for a power of two
+//         w set by the bit position); Q' carries 1/w, and 2^24 goes into the
+//         scale.  bf16 rows enter the bf16 MFMA directly.
+//   p.v   O[c][d] = sum_t A[c][t] B[t][d], eight (D=128) 16-column blocks.
+//         The q.k result already sits in the A-operand layout (lane = column
+//         c, registers = tokens), so no transpose is needed.  Row c of A holds
+//         p * scale_V(token, group of c) in f16 (or p as a bf16 hi/lo pair for
+//         bf16 V); B holds V codes as subnormals (or bf16 values).  Output
+//         column d keeps row (h, group(d)); the min term sum_t p * min_V is an
+//         fp32 side sum per row.
+//
+// Lane layout of v_mfma_f32_16x16x32 (checked on gfx950): A: lane l holds row
+// l%16, k = 8(l/16)..+7; B: lane l holds column l%16, same k; C: lane l holds
+// column l%16, rows 4(l/16)..+3.
+//
+// Online softmax in log2 units with a lazy running max: the wave rescales
+// only when a column's max grows by more than kLazy, so p <= 2^kLazy.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr float kLazy = 6.0f;  // p <= 2^6 between rescales
+
+__device__ inline f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ inline float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, uint16_t(w)); }
+__device__ inline float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, uint16_t(w >> 16)); }
+__device__ inline float bf16f(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+__device__ inline uint32_t pack_f16(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)lo)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (_Float16)hi)) << 16);
+}
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+}
+__device__ inline float dpp_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
+                                                            0xF, 0xF, false));
+}
+__device__ inline float dpp_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
+                                                            0xF, 0xF, false));
+}
+
+// ---------------------------------------------------------------------------
+// Per-format row geometry.  D elements per row; a K row is split into 4 lane
+// quarters of D/4 elements; a V row into 16 lane columns of D/16 elements.
+template <int D, int B>
+struct Fmt {
+  static constexpr int kRowBytes = B == 16 ? 2 * D : D * B / 8;
+  static constexpr int kKDwords = kRowBytes / 16;   // per lane quarter
+  static constexpr int kVBytes = kRowBytes / 16;    // per lane column
+};
+
+// Slot map of the q.k A operand: k-step s, lane quarter jq, slot e (0..7) ->
+// head-dim index d and the power-of-two weight w of the stored code bits
+// (operand value = code * w * 2^-24).  Must mirror k_operand() below.
+template <int D, int B>
+__device__ inline void kslot(int s, int jq, int e, int& d, float& w) {
+  const int c0 = jq * (D / 4);
+  const int kp = e >> 1, hf = e & 1;
+  if (B == 16) {
+    d = c0 + 8 * s + e;
+    w = 1.0f;
+  } else if (B == 8) {
+    const int di = 2 * s + (kp >> 1);
+    d = c0 + 4 * di + (kp & 1) + 2 * hf;
+    w = 1.0f;
+  } else if (B == 4) {
+    d = c0 + 8 * s + kp + 4 * hf;
+    w = (kp & 1) ? 16.0f : 1.0f;
+  } else {  // B == 2
+    const int odd = s & 1;
+    d = c0 + 16 * (s >> 1) + (odd ? 4 : 0) + kp + 8 * hf;
+    w = (!odd || kp) ? float(1 << (2 * kp)) : 256.0f;
+  }
+}
+
+// A operand (4 dwords) of k-step s from this lane's raw K dwords.
+template <int D, int B>
+__device__ inline u32x4 k_operand(const uint32_t* w, int s) {
+  u32x4 a;
+  if (B == 16) {
+    a[0] = w[4 * s]; a[1] = w[4 * s + 1]; a[2] = w[4 * s + 2]; a[3] = w[4 * s + 3];
+  } else if (B == 8) {
+    const uint32_t x = w[2 * s], y = w[2 * s + 1];
+    a[0] = x & 0x00FF00FFu; a[1] = (x >> 8) & 0x00FF00FFu;
+    a[2] = y & 0x00FF00FFu; a[3] = (y >> 8) & 0x00FF00FFu;
+  } else if (B == 4) {
+    const uint32_t x = w[s], t = x >> 8;
+    a[0] = x & 0x000F000Fu; a[1] = x & 0x00F000F0u;
+    a[2] = t & 0x000F000Fu; a[3] = t & 0x00F000F0u;
+  } else {
+    const uint32_t x = w[s >> 1];
+    if ((s & 1) == 0) {
+      a[0] = x & 0x00030003u; a[1] = x & 0x000C000Cu;
+      a[2] = x & 0x00300030u; a[3] = x & 0x00C000C0u;
+    } else {
+      const uint32_t t = x >> 8;
+      a[0] = x & 0x03000300u; a[1] = t & 0x000C000Cu;
+      a[2] = t & 0x00300030u; a[3] = t & 0x00C000C0u;
+    }
+  }
+  return a;
+}
+
+// p.v B operand of block mb from the V data of two tokens (a: lo half, b: hi
+// half).  Value = code * wv(mb) * 2^-24, or the bf16 element itself.
+template <int D, int B>
+__device__ inline uint32_t v_pair(const uint32_t* a, const uint32_t* b, int mb) {
+  if (B == 16) {
+    return __builtin_amdgcn_perm(b[mb >> 1], a[mb >> 1], (mb & 1) ? 0x07060302u : 0x05040100u);
+  } else if (B == 8) {
+    const uint32_t sel = 0x0C000C00u | (uint32_t(4 + (mb & 3)) << 16) | uint32_t(mb & 3);
+    return __builtin_amdgcn_perm(b[mb >> 2], a[mb >> 2], sel);
+  } else if (B == 4) {
+    const uint32_t x = __builtin_amdgcn_perm(b[0], a[0], (mb & 4) ? 0x07060302u : 0x05040100u);
+    const uint32_t t = (mb & 2) ? (x >> 8) : x;
+    return t & ((mb & 1) ? 0x00F000F0u : 0x000F000Fu);
+  } else {
+    const uint32_t x = (a[0] & 0xFFFFu) | (b[0] << 16);
+    if (D == 128 && mb >= 5) return (x >> 8) & (0x00030003u << (2 * (mb - 4)));
+    return x & (0x00030003u << (2 * mb));
+  }
+}
+template <int D, int B>
+__device__ constexpr float v_weight(int mb) {
+  return B == 16 ? 1.0f
+       : B == 8  ? 1.0f
+       : B == 4  ? ((mb & 1) ? 16.0f : 1.0f)
+       : (D == 128 && mb >= 5) ? float(1 << (2 * (mb - 4))) : float(1 << (2 * mb));
+}
+// Factor by which p.v MFMA outputs of block mb exceed the true value.
+template <int D, int B>
+__device__ constexpr float v_inflation(int mb) {
+  return B == 16 ? 1.0f : v_weight<D, B>(mb) * 5.9604644775390625e-08f;  // * 2^-24
+}
+
+template <int D>
+struct WaveState {
+  static constexpr int NB = D / 16;
+  f32x4 o[NB];      // p.v accumulators, scaled per the current V format
+  float m;          // running max (log2 units) of this lane's column
+  float l;          // partial sum of p over this lane's tokens
+  float mt;         // partial sum of p * min_V over this lane's tokens
+};
+
+struct Ctx {
+  const uint8_t* kvis;  // K planes of this (layer, head)
+  const uint8_t* kmeta;
+  const uint8_t* ktxt;
+  const uint8_t* vvis;
+  const uint8_t* vmeta;
+  const uint8_t* vtxt;
+  const uint16_t* q_lds;  // [G][D] bf16 bits of this workgroup's queries
+  float qscale;
+  int G, NG;
+  int lane, n, jq;        // lane, column (l % 16), quarter (l / 16)
+};
+
+// Build Q' for k format KB: per k-step, 8 slots of this lane's column.
+template <int D, int KB>
+__device__ inline void build_q(const Ctx& c, int g, u32x4 (&qop)[D / 32], float& qsum_scaled) {
+  const int h = c.n / c.NG, gj = c.n % c.NG;
+  const bool live = c.n < c.G * c.NG;
+  float qs = 0.0f;
+  for (int s = 0; s < D / 32; ++s) {
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      float v2[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        int d;
+        float w;
+        kslot<D, KB>(s, c.jq, 2 * e2 + hf, d, w);
+        const float qv = bf16f(c.q_lds[(live ? h : 0) * D + d]);
+        v2[hf] = (live && d / g == gj) ? qv / w : 0.0f;
+      }
+      qop[s][e2] = KB == 16 ? pack_bf16(v2[0], v2[1]) : pack_f16(v2[0], v2[1]);
+    }
+  }
+  if (live) {
+    for (int d = gj * g; d < gj * g + g; ++d) qs += bf16f(c.q_lds[h * D + d]);
+  }
+  qsum_scaled = qs * c.qscale;
+}
+
+template <typename T>
+__device__ inline void load_bytes(const uint8_t* p, uint32_t* out, int nbytes) {
+  // nbytes in {1, 2, 4, 8, 16, 32, 64}; p aligned to min(nbytes, 16)
+  if (nbytes >= 16) {
+    for (int i = 0; i < nbytes / 16; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+    }
+  } else if (nbytes == 8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    out[0] = v.x; out[1] = v.y;
+  } else if (nbytes == 4) {
+    out[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if (nbytes == 2) {
+    out[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else {
+    out[0] = *p;
+  }
+}
+
+// One segment [x0, x1) of rows of one format, rows starting at plane row
+// row0 (K and V share row numbering).  KB/VB: stored widths (16 = bf16).
+template <int D, int KB, int VB>
+__device__ void run_segment(const Ctx& c, WaveState<D>& st, int g, int x0, int x1,
+                            int64_t row0, bool visual) {
+  constexpr int KS = D / 32;
+  constexpr int NB = D / 16;
+  using KF = Fmt<D, KB>;
+  using VF = Fmt<D, VB>;
+  const uint8_t* kbase = visual ? c.kvis : c.ktxt;
+  const uint8_t* vbase = visual ? c.vvis : c.vtxt;
+  const int NG = c.NG, gj = c.n % NG;
+
+  u32x4 qop[KS];
+  float qs;
+  build_q<D, KB>(c, g, qop, qs);
+  const float c24 = c.qscale * 16777216.0f;  // 2^24 * qscale
+
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) st.o[mb] *= v_inflation<D, VB>(mb);
+
+  for (int base = x0; base < x1; base += 32) {
+    // ---- loads ------------------------------------------------------------
+    uint32_t kraw[2][KF::kKDwords > 0 ? KF::kKDwords : 1];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int t = min(base + 16 * tau + c.n, x1 - 1);
+      const uint8_t* p = kbase + (row0 + (t - x0)) * KF::kRowBytes + c.jq * (KF::kRowBytes / 4);
+      load_bytes<uint32_t>(p, kraw[tau], KF::kRowBytes / 4);
+    }
+    uint32_t kmeta[8], vmeta[8];
+    uint32_t vraw[8][(VF::kVBytes + 3) / 4];
+    int valid_mask = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = base + 16 * (e >> 2) + 4 * c.jq + (e & 3);
+      valid_mask |= (t < x1) << e;
+      const int64_t r = row0 + (min(t, x1 - 1) - x0);
+      if (KB < 16) kmeta[e] = *reinterpret_cast<const uint32_t*>(c.kmeta + r * (NG * 4) + gj * 4);
+      if (VB < 16) vmeta[e] = *reinterpret_cast<const uint32_t*>(c.vmeta + r * (NG * 4) + gj * 4);
+      load_bytes<uint32_t>(vbase + r * VF::kRowBytes + c.n * VF::kVBytes, vraw[e], VF::kVBytes);
+    }
+
+    // ---- q.k ----------------------------------------------------------------
+    f32x4 acc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      acc[tau] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 a = k_operand<D, KB>(kraw[tau], s);
+        acc[tau] = KB == 16 ? mfma_bf16(a, qop[s], acc[tau]) : mfma_f16(a, qop[s], acc[tau]);
+      }
+    }
+    float sc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float a = acc[e >> 2][e & 3];
+      float part;
+      if (KB < 16) part = a * (f16lo(kmeta[e]) * c24) + f16hi(kmeta[e]) * qs;
+      else part = a * c.qscale;
+      if (NG >= 2) part += dpp_xor1(part);
+      if (NG >= 4) part += dpp_xor2(part);
+      sc[e] = ((valid_mask >> e) & 1) ? part : -INFINITY;
+    }
+
+    // ---- online softmax (lazy rescale) -------------------------------------
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(st.m, mx);
+    if (__builtin_amdgcn_ballot_w64(mnew > st.m + kLazy) != 0) {
+      const float alpha = exp2f(st.m - mnew);  // 0 on the first step (m = -inf)
+      st.l *= alpha;
+      st.mt *= alpha;
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * c.jq + i);
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[mb][i] *= ar[i];
+      st.m = mnew;
+    }
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = exp2f(sc[e] - st.m);
+      st.l += p[e];
+    }
+
+    // ---- p.v ------------------------------------------------------------------
+    u32x4 pa, pb;  // A operand (and the bf16 low part for bf16 V)
+    if (VB < 16) {
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
+        pa[e2] = pack_f16(p0 * f16lo(vmeta[2 * e2]), p1 * f16lo(vmeta[2 * e2 + 1]));
+        st.mt += p0 * f16hi(vmeta[2 * e2]) + p1 * f16hi(vmeta[2 * e2 + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
+        pa[e2] = pack_bf16(p0, p1);
+        pb[e2] = pack_bf16(p0 - bf16f(pa[e2] & 0xFFFFu), p1 - bf16f(pa[e2] >> 16));
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+      u32x4 b;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) b[e2] = v_pair<D, VB>(vraw[2 * e2], vraw[2 * e2 + 1], mb);
+      if (VB == 16) {
+        st.o[mb] = mfma_bf16(pa, b, st.o[mb]);
+        st.o[mb] = mfma_bf16(pb, b, st.o[mb]);
+      } else {
+        st.o[mb] = mfma_f16(pa, b, st.o[mb]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) st.o[mb] *= 1.0f / v_inflation<D, VB>(mb);
+}
+
+template <int D, int KB, int VB>
+__device__ inline void run_visual(const Ctx& c, WaveState<D>& st, int g, int x0, int x1,
+                                  int64_t row0) {
+  run_segment<D, KB, VB>(c, st, g, x0, x1, row0, true);
+}
+
+template <int D>
+__device__ void dispatch_visual(int kb, int vb, const Ctx& c, WaveState<D>& st, int g, int x0,
+                                int x1, int64_t row0) {
+#define KVQ_VIS(K, V) \
+  if (kb == K && vb == V) { run_visual<D, K, V>(c, st, g, x0, x1, row0); return; }
+  KVQ_VIS(2, 2) KVQ_VIS(2, 4) KVQ_VIS(2, 8) KVQ_VIS(2, 16)
+  KVQ_VIS(4, 2) KVQ_VIS(4, 4) KVQ_VIS(4, 8) KVQ_VIS(4, 16)
+  KVQ_VIS(8, 2) KVQ_VIS(8, 4) KVQ_VIS(8, 8) KVQ_VIS(8, 16)
+  KVQ_VIS(16, 2) KVQ_VIS(16, 4) KVQ_VIS(16, 8) KVQ_VIS(16, 16)
+#undef KVQ_VIS
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int NB = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = blockIdx.y;
+  const int lh = a.lh_glob[slot];
+  const int l_local = lh / a.Hkv, h = lh % a.Hkv;
+  const int sl = blockIdx.z, s = a.seq_off + sl;
+  const int cap = a.cap[sl];
+  int len = a.seq_lens[s];
+  len = len < 1 ? 1 : (len > cap ? cap : len);
+  const int t0 = blockIdx.x * a.chunk;
+  if (t0 >= len) return;
+  const int t1 = min(t0 + a.chunk, len);
+  const int G = a.G, g = a.g;
+  const int NG = D / g;
+
+  __shared__ uint16_t q_lds[kMaxGroupRatio * D];
+  __shared__ float o_lds[kWaves][kMaxGroupRatio][D];
+  __shared__ float ml_lds[kWaves][kMaxGroupRatio][2];
+
+  const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+  for (int i = threadIdx.x; i < G * D; i += 256) q_lds[i] = qp[i];
+  __syncthreads();
+
+  Ctx c;
+  {
+    const int kb = a.bits[slot][0], vb = a.bits[slot][1];
+    c.kvis = a.cache + uint64_t(a.base256[slot][0]) * 256u;
+    c.kmeta = c.kvis + meta_plane_offset(a.Rvis, D, kb);
+    c.ktxt = c.kvis + txt_plane_offset(a.Rvis, D, g, kb);
+    c.vvis = a.cache + uint64_t(a.base256[slot][1]) * 256u;
+    c.vmeta = c.vvis + meta_plane_offset(a.Rvis, D, vb);
+    c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
+  }
+  c.q_lds = q_lds;
+  c.qscale = a.qscale;
+  c.G = G;
+  c.NG = NG;
+  c.lane = lane;
+  c.n = lane & 15;
+  c.jq = lane >> 4;
+
+  WaveState<D> st;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) st.o[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.mt = 0.0f;
+
+  // this wave's share of the chunk, in whole 32-token steps
+  const int per_wave = a.chunk / kWaves;
+  const int wa = t0 + wave * per_wave;
+  const int wb = min(wa + per_wave, t1);
+  if (wa < wb) {
+    const int vb = a.vb[sl], ve = a.ve[sl];
+    const int64_t vrow0 = a.vrow0[sl], trow0 = a.trow0[sl];
+    const int kb = a.bits[slot][0], vbits = a.bits[slot][1];
+    // text prefix [0, vb), visual [vb, ve), text suffix [ve, cap)
+    int x0 = wa, x1 = min(wb, vb);
+    if (x0 < x1) run_segment<D, 16, 16>(c, st, g, x0, x1, trow0 + x0, false);
+    x0 = max(wa, vb);
+    x1 = min(wb, ve);
+    if (x0 < x1) dispatch_visual<D>(kb, vbits, c, st, g, x0, x1, vrow0 + (x0 - vb));
+    x0 = max(wa, ve);
+    x1 = wb;
+    if (x0 < x1) run_segment<D, 16, 16>(c, st, g, x0, x1, trow0 + (x0 - (ve - vb)), false);
+  }
+
+  // ---- wave result -> LDS: per head m, l and unnormalised o[d] ---------------
+  float l_col = st.l + __shfl_xor(st.l, 16);
+  l_col += __shfl_xor(l_col, 32);
+  float mt_col = st.mt + __shfl_xor(st.mt, 16);
+  mt_col += __shfl_xor(mt_col, 32);
+  const int n = lane & 15, jq = lane >> 4;
+  if (jq == 0 && n < G * NG && n % NG == 0) {
+    ml_lds[wave][n / NG][0] = st.m;
+    ml_lds[wave][n / NG][1] = l_col;
+  }
+  float mt_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mt_row[i] = __shfl(mt_col, 4 * jq + i);
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    const int d = NB * n + mb;
+    const int gd = d / g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * jq + i;
+      if (r < G * NG && r % NG == gd) o_lds[wave][r / NG][d] = st.o[mb][i] + mt_row[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- combine waves; write the chunk's partial (or the final output) --------
+  const bool single = a.max_chunks == 1;
+  const int64_t pidx = partial_index(l_local, s, h, blockIdx.x, a.B, a.Hkv, a.max_chunks);
+  for (int i = threadIdx.x; i < G * D; i += 256) {
+    const int j = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (ml_lds[w][j][1] > 0.0f) M = fmaxf(M, ml_lds[w][j][0]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (ml_lds[w][j][1] > 0.0f) {
+        const float f = exp2f(ml_lds[w][j][0] - M);
+        L += ml_lds[w][j][1] * f;
+        acc += o_lds[w][j][d] * f;
+      }
+    }
+    if (single) {
+      a.out[((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G + j) * D + d] =
+          __builtin_bit_cast(uint16_t, (__bf16)(acc / L));
+    } else {
+      a.ws_o[(pidx * G + j) * D + d] = acc / L;
+      if (d == 0) {
+        a.ws_ml[(pidx * G + j) * 2 + 0] = M;
+        a.ws_ml[(pidx * G + j) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool mfma_supported(int D, int g, int G) {
+  return (D == 64 || D == 128) && G * (D / g) <= 16;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int n_seq_launch, hipStream_t stream) {
+  dim3 grid(a.max_chunks, a.n_lh, n_seq_launch);
+  if (a.D == 128)
+    hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

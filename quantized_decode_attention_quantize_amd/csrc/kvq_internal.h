@@ -73,6 +73,10 @@ __host__ __device__ inline int64_t partial_index(int l, int s, int h, int x, int
 hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
                            hipStream_t stream);
 hipError_t launch_decode_simple(const DecodeArgs& a, int n_seq_launch, hipStream_t stream);
+// Matrix-core split kernel: needs (D / g) * G <= 16 (one 16-row MFMA tile of
+// (head, group) columns); writes the final output itself when max_chunks == 1.
+bool mfma_supported(int D, int g, int G);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int n_seq_launch, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int nl, int n_seq_launch,
                                hipStream_t stream);
 

@@ -179,6 +179,20 @@ def test_decode_mixed_formats_and_d64():
         _check_decode(p, [300, 101], what=f"D{D} g{g} k{kb} v{vb}")
 
 
+@pytest.mark.parametrize("hq,hkv,g", [(28, 4, 32), (16, 1, 64), (8, 8, 128)])
+def test_decode_general_kernel_shapes(hq, hkv, g):
+    """(head, group) columns beyond one 16-wide tile go to the general kernel;
+    G = 1 (no GQA) goes to the matrix-core kernel."""
+    _say("decode heads/group", hq, hkv, g)
+    kb = np.full(hkv, 4, np.uint8)
+    vb = np.full(hkv, 2, np.uint8)
+    w = synth.Workload(f"gen{hq}", 1, 1, hq, hkv, 128, g, [700], [14], [700], [700], kb, vb,
+                       seed=hq + g)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [700], what=f"Hq{hq} Hkv{hkv} g{g}")
+
+
 def test_decode_empty_visual_span_and_all_visual():
     _say("decode no visual rows / all visual rows")
     kb = np.array([2], np.uint8)
