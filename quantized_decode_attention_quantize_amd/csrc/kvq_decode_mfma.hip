@@ -140,23 +140,50 @@ __device__ inline u32x4 k_operand(const uint32_t* w, int s) {
   return a;
 }
 
-// p.v B operand of block mb from the V data of two tokens (a: lo half, b: hi
-// half).  Value = code * wv(mb) * 2^-24, or the bf16 element itself.
+// p.v B operand: for a pair of tokens (a: lo half, b: hi half) the lane's V
+// slices are first merged into pair words (vpair_words), then each 16-column
+// block mb takes one masked word (v_block).  Value = code * wv(mb) * 2^-24,
+// or the bf16 element itself.
 template <int D, int B>
-__device__ inline uint32_t v_pair(const uint32_t* a, const uint32_t* b, int mb) {
-  if (B == 16) {
+struct VPair {
+  static constexpr int N = B == 16 ? D / 32 : B == 8 ? D / 64 : 2;
+  uint32_t w[N];
+};
+template <int D, int B>
+__device__ inline VPair<D, B> vpair_words(const uint32_t* a, const uint32_t* b) {
+  VPair<D, B> r;
+  if constexpr (B == 16) {  // bf16 elements 2i, 2i+1 of each token
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      r.w[i] = a[i];          // kept raw; v_block permutes
+    }
+  } else if constexpr (B == 8) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) r.w[i] = a[i];
+  } else if constexpr (B == 4) {
+    r.w[0] = __builtin_amdgcn_perm(b[0], a[0], 0x05040100u);  // nibbles 0..3 of a | b
+    r.w[1] = __builtin_amdgcn_perm(b[0], a[0], 0x07060302u);  // nibbles 4..7
+  } else {
+    r.w[0] = (a[0] & 0xFFFFu) | (b[0] << 16);
+    r.w[1] = r.w[0] >> 8;
+  }
+  return r;
+}
+template <int D, int B>
+__device__ inline uint32_t v_block(const VPair<D, B>& pw, const uint32_t* a, const uint32_t* b,
+                                   int mb) {
+  if constexpr (B == 16) {
     return __builtin_amdgcn_perm(b[mb >> 1], a[mb >> 1], (mb & 1) ? 0x07060302u : 0x05040100u);
-  } else if (B == 8) {
+  } else if constexpr (B == 8) {
     const uint32_t sel = 0x0C000C00u | (uint32_t(4 + (mb & 3)) << 16) | uint32_t(mb & 3);
     return __builtin_amdgcn_perm(b[mb >> 2], a[mb >> 2], sel);
-  } else if (B == 4) {
-    const uint32_t x = __builtin_amdgcn_perm(b[0], a[0], (mb & 4) ? 0x07060302u : 0x05040100u);
+  } else if constexpr (B == 4) {
+    const uint32_t x = pw.w[(mb >> 2) & 1];
     const uint32_t t = (mb & 2) ? (x >> 8) : x;
     return t & ((mb & 1) ? 0x00F000F0u : 0x000F000Fu);
   } else {
-    const uint32_t x = (a[0] & 0xFFFFu) | (b[0] << 16);
-    if (D == 128 && mb >= 5) return (x >> 8) & (0x00030003u << (2 * (mb - 4)));
-    return x & (0x00030003u << (2 * mb));
+    if (D == 128 && mb >= 5) return pw.w[1] & (0x00030003u << (2 * (mb - 4)));
+    return pw.w[0] & (0x00030003u << (2 * mb));
   }
 }
 template <int D, int B>
@@ -188,18 +215,20 @@ struct Ctx {
   const uint8_t* vvis;
   const uint8_t* vmeta;
   const uint8_t* vtxt;
-  const uint16_t* q_lds;  // [G][D] bf16 bits of this workgroup's queries
+  const uint16_t* q_lds;   // [G][D] bf16 bits of this workgroup's queries
+  const float* qsum_lds;   // [G * NG] sum of q over each (head, group), times qscale
   float qscale;
-  int G, NG;
-  int lane, n, jq;        // lane, column (l % 16), quarter (l / 16)
+  int G;
+  int lane, n, jq;         // lane, column (l % 16), quarter (l / 16)
 };
 
 // Build Q' for k format KB: per k-step, 8 slots of this lane's column.
-template <int D, int KB>
-__device__ inline void build_q(const Ctx& c, int g, u32x4 (&qop)[D / 32], float& qsum_scaled) {
-  const int h = c.n / c.NG, gj = c.n % c.NG;
-  const bool live = c.n < c.G * c.NG;
-  float qs = 0.0f;
+template <int D, int NG, int KB>
+__device__ inline void build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
+  constexpr int g = D / NG;
+  const int h = c.n / NG, gj = c.n % NG;
+  const bool live = c.n < c.G * NG;
+#pragma unroll
   for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -210,176 +239,261 @@ __device__ inline void build_q(const Ctx& c, int g, u32x4 (&qop)[D / 32], float&
         float w;
         kslot<D, KB>(s, c.jq, 2 * e2 + hf, d, w);
         const float qv = bf16f(c.q_lds[(live ? h : 0) * D + d]);
-        v2[hf] = (live && d / g == gj) ? qv / w : 0.0f;
+        v2[hf] = (live && d / g == gj) ? qv * (1.0f / w) : 0.0f;  // w: power of two
       }
       qop[s][e2] = KB == 16 ? pack_bf16(v2[0], v2[1]) : pack_f16(v2[0], v2[1]);
     }
   }
-  if (live) {
-    for (int d = gj * g; d < gj * g + g; ++d) qs += bf16f(c.q_lds[h * D + d]);
-  }
-  qsum_scaled = qs * c.qscale;
 }
 
-template <typename T>
-__device__ inline void load_bytes(const uint8_t* p, uint32_t* out, int nbytes) {
-  // nbytes in {1, 2, 4, 8, 16, 32, 64}; p aligned to min(nbytes, 16)
-  if (nbytes >= 16) {
-    for (int i = 0; i < nbytes / 16; ++i) {
+template <int NBYTES>
+__device__ inline void load_bytes(const uint8_t* p, uint32_t* out) {
+  if constexpr (NBYTES >= 16) {
+#pragma unroll
+    for (int i = 0; i < NBYTES / 16; ++i) {
       const uint4 v = reinterpret_cast<const uint4*>(p)[i];
       out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
     }
-  } else if (nbytes == 8) {
+  } else if constexpr (NBYTES == 8) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     out[0] = v.x; out[1] = v.y;
-  } else if (nbytes == 4) {
+  } else if constexpr (NBYTES == 4) {
     out[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if (nbytes == 2) {
+  } else if constexpr (NBYTES == 2) {
     out[0] = *reinterpret_cast<const uint16_t*>(p);
   } else {
     out[0] = *p;
   }
 }
 
-// One segment [x0, x1) of rows of one format, rows starting at plane row
-// row0 (K and V share row numbering).  KB/VB: stored widths (16 = bf16).
+// Raw data one lane needs for one 32-token step.
 template <int D, int KB, int VB>
-__device__ void run_segment(const Ctx& c, WaveState<D>& st, int g, int x0, int x1,
-                            int64_t row0, bool visual) {
+struct Step {
+  static constexpr int KDW = Fmt<D, KB>::kRowBytes / 16;          // dwords per K quarter-row
+  static constexpr int VDW = (Fmt<D, VB>::kVBytes + 3) / 4;       // dwords per V lane slice
+  uint32_t k[2][KDW];
+  uint32_t km[KB < 16 ? 8 : 1];
+  uint32_t vm[VB < 16 ? 8 : 1];
+  uint32_t v[8][VDW];
+};
+
+// Lane byte offsets of one step, relative to the step's first row.  In full
+// steps the per-slot parts are compile-time constants added to three base
+// offsets; the tail step clamps every slot's row to the segment end.
+template <int D, int NG, int KB, int VB>
+struct Offs {
+  static constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
+  uint32_t k0, m0, v0;   // tile-0 / slot-0 base offsets
+  uint32_t k[2], m[8], v[8];  // clamped offsets (tail step only)
+  __device__ inline void full(const Ctx& c) {
+    k0 = uint32_t(c.n * KR + c.jq * (KR / 4));
+    m0 = uint32_t(4 * c.jq * MR + (c.n % NG) * 4);
+    v0 = uint32_t(4 * c.jq * VR + c.n * Fmt<D, VB>::kVBytes);
+  }
+  __device__ inline void clamped(const Ctx& c, int rows_left) {
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int r = min(16 * tau + c.n, rows_left - 1);
+      k[tau] = uint32_t(r * KR + c.jq * (KR / 4));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = min(16 * (e >> 2) + 4 * c.jq + (e & 3), rows_left - 1);
+      m[e] = uint32_t(r * MR + (c.n % NG) * 4);
+      v[e] = uint32_t(r * VR + c.n * Fmt<D, VB>::kVBytes);
+    }
+  }
+  static constexpr uint32_t kslot_off(int tau) { return uint32_t(16 * tau * KR); }
+  static constexpr uint32_t mslot_off(int e) { return uint32_t((16 * (e >> 2) + (e & 3)) * MR); }
+  static constexpr uint32_t vslot_off(int e) { return uint32_t((16 * (e >> 2) + (e & 3)) * VR); }
+};
+
+template <int D, int NG, int KB, int VB, bool CLAMPED>
+__device__ inline void load_step(const uint8_t* kp, const uint8_t* kmp, const uint8_t* vp,
+                                 const uint8_t* vmp, const Offs<D, NG, KB, VB>& o,
+                                 Step<D, KB, VB>& st) {
+  using O = Offs<D, NG, KB, VB>;
+  constexpr int KQ = Fmt<D, KB>::kRowBytes / 4;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+    load_bytes<KQ>(kp + (CLAMPED ? o.k[tau] : o.k0 + O::kslot_off(tau)), st.k[tau]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t mo = CLAMPED ? o.m[e] : o.m0 + O::mslot_off(e);
+    const uint32_t vo = CLAMPED ? o.v[e] : o.v0 + O::vslot_off(e);
+    if constexpr (KB < 16) st.km[e] = *reinterpret_cast<const uint32_t*>(kmp + mo);
+    if constexpr (VB < 16) st.vm[e] = *reinterpret_cast<const uint32_t*>(vmp + mo);
+    load_bytes<Fmt<D, VB>::kVBytes>(vp + vo, st.v[e]);
+  }
+}
+
+// q.k, softmax and p.v of one 32-token step.  MASKED: the step may run past
+// the segment end (rows_left < 32).
+template <int D, int NG, int KB, int VB, bool MASKED>
+__device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D, KB, VB>& st,
+                                    const u32x4 (&qop)[D / 32], float qs, float c24,
+                                    int rows_left) {
   constexpr int KS = D / 32;
   constexpr int NB = D / 16;
-  using KF = Fmt<D, KB>;
-  using VF = Fmt<D, VB>;
-  const uint8_t* kbase = visual ? c.kvis : c.ktxt;
-  const uint8_t* vbase = visual ? c.vvis : c.vtxt;
-  const int NG = c.NG, gj = c.n % NG;
+  f32x4 acc[2];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    acc[tau] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 a = k_operand<D, KB>(st.k[tau], s);
+      acc[tau] = KB == 16 ? mfma_bf16(a, qop[s], acc[tau]) : mfma_f16(a, qop[s], acc[tau]);
+    }
+  }
+  float sc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a = acc[e >> 2][e & 3];
+    float part;
+    if constexpr (KB < 16) part = a * (f16lo(st.km[e]) * c24) + f16hi(st.km[e]) * qs;
+    else part = a * c.qscale;
+    if constexpr (NG >= 2) part += dpp_xor1(part);
+    if constexpr (NG >= 4) part += dpp_xor2(part);
+    if constexpr (MASKED) {
+      const int r = 16 * (e >> 2) + 4 * c.jq + (e & 3);
+      part = r < rows_left ? part : -INFINITY;
+    }
+    sc[e] = part;
+  }
 
-  u32x4 qop[KS];
-  float qs;
-  build_q<D, KB>(c, g, qop, qs);
+  // online softmax with a lazy running max
+  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mnew = fmaxf(ws.m, mx);
+  if (__builtin_amdgcn_ballot_w64(mnew > ws.m + kLazy) != 0) {
+    const float alpha = __builtin_amdgcn_exp2f(ws.m - mnew);  // 0 on the first step
+    ws.l *= alpha;
+    ws.mt *= alpha;
+    float ar[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * c.jq + i);
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ws.o[mb][i] *= ar[i];
+    ws.m = mnew;
+  }
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(sc[e] - ws.m);
+    ws.l += p[e];
+  }
+
+  u32x4 pa, pb;  // A operand (and the bf16 low part for bf16 V)
+  if constexpr (VB < 16) {
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
+      pa[e2] = pack_f16(p0 * f16lo(st.vm[2 * e2]), p1 * f16lo(st.vm[2 * e2 + 1]));
+      ws.mt += p0 * f16hi(st.vm[2 * e2]) + p1 * f16hi(st.vm[2 * e2 + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
+      pa[e2] = pack_bf16(p0, p1);
+      pb[e2] = pack_bf16(p0 - bf16f(pa[e2] & 0xFFFFu), p1 - bf16f(pa[e2] >> 16));
+    }
+  }
+  VPair<D, VB> pw[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) pw[e2] = vpair_words<D, VB>(st.v[2 * e2], st.v[2 * e2 + 1]);
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    u32x4 b;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) b[e2] = v_block<D, VB>(pw[e2], st.v[2 * e2], st.v[2 * e2 + 1], mb);
+    if constexpr (VB == 16) {
+      ws.o[mb] = mfma_bf16(pa, b, ws.o[mb]);
+      ws.o[mb] = mfma_bf16(pb, b, ws.o[mb]);
+    } else {
+      ws.o[mb] = mfma_f16(pa, b, ws.o[mb]);
+    }
+  }
+}
+
+// One segment [x0, x1) of rows of one format, rows starting at plane row
+// row0 (K and V share row numbering).  KB/VB: stored widths (16 = bf16).
+template <int D, int NG, int KB, int VB>
+__device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int64_t row0,
+                            bool visual) {
+  constexpr int NB = D / 16;
+  constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
+  const uint8_t* kp = (visual ? c.kvis : c.ktxt) + row0 * KR;
+  const uint8_t* vp = (visual ? c.vvis : c.vtxt) + row0 * VR;
+  const uint8_t* kmp = c.kmeta + row0 * MR;
+  const uint8_t* vmp = c.vmeta + row0 * MR;
+
+  u32x4 qop[D / 32];
+  build_q<D, NG, KB>(c, qop);
+  const float qs = c.n < c.G * NG ? c.qsum_lds[c.n] : 0.0f;
   const float c24 = c.qscale * 16777216.0f;  // 2^24 * qscale
 
 #pragma unroll
-  for (int mb = 0; mb < NB; ++mb) st.o[mb] *= v_inflation<D, VB>(mb);
+  for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= v_inflation<D, VB>(mb);
 
-  for (int base = x0; base < x1; base += 32) {
-    // ---- loads ------------------------------------------------------------
-    uint32_t kraw[2][KF::kKDwords > 0 ? KF::kKDwords : 1];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int t = min(base + 16 * tau + c.n, x1 - 1);
-      const uint8_t* p = kbase + (row0 + (t - x0)) * KF::kRowBytes + c.jq * (KF::kRowBytes / 4);
-      load_bytes<uint32_t>(p, kraw[tau], KF::kRowBytes / 4);
-    }
-    uint32_t kmeta[8], vmeta[8];
-    uint32_t vraw[8][(VF::kVBytes + 3) / 4];
-    int valid_mask = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = base + 16 * (e >> 2) + 4 * c.jq + (e & 3);
-      valid_mask |= (t < x1) << e;
-      const int64_t r = row0 + (min(t, x1 - 1) - x0);
-      if (KB < 16) kmeta[e] = *reinterpret_cast<const uint32_t*>(c.kmeta + r * (NG * 4) + gj * 4);
-      if (VB < 16) vmeta[e] = *reinterpret_cast<const uint32_t*>(c.vmeta + r * (NG * 4) + gj * 4);
-      load_bytes<uint32_t>(vbase + r * VF::kRowBytes + c.n * VF::kVBytes, vraw[e], VF::kVBytes);
-    }
-
-    // ---- q.k ----------------------------------------------------------------
-    f32x4 acc[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      acc[tau] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 a = k_operand<D, KB>(kraw[tau], s);
-        acc[tau] = KB == 16 ? mfma_bf16(a, qop[s], acc[tau]) : mfma_f16(a, qop[s], acc[tau]);
+  const int rows = x1 - x0;
+  const int nfull = rows / 32;
+  Offs<D, NG, KB, VB> of;
+  of.full(c);
+  // Quantised steps are small (~32 VGPRs of raw data): double-buffer them so
+  // the loads of step i+1 fly while step i computes.  bf16 steps carry 64
+  // VGPRs of data and run single-buffered.
+  constexpr bool kPrefetch = KB < 16 && VB < 16;
+  Step<D, KB, VB> sa;
+  int i = 0;
+  if constexpr (kPrefetch) {
+    Step<D, KB, VB> sb;
+    if (nfull > 0) load_step<D, NG, KB, VB, false>(kp, kmp, vp, vmp, of, sa);
+    for (; i + 2 <= nfull; i += 2) {
+      const int64_t o1 = int64_t(i + 1) * 32;
+      load_step<D, NG, KB, VB, false>(kp + o1 * KR, kmp + o1 * MR, vp + o1 * VR, vmp + o1 * MR,
+                                      of, sb);
+      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+      if (i + 2 < nfull) {
+        const int64_t o2 = int64_t(i + 2) * 32;
+        load_step<D, NG, KB, VB, false>(kp + o2 * KR, kmp + o2 * MR, vp + o2 * VR,
+                                        vmp + o2 * MR, of, sa);
       }
+      compute_step<D, NG, KB, VB, false>(c, ws, sb, qop, qs, c24, 32);
     }
-    float sc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float a = acc[e >> 2][e & 3];
-      float part;
-      if (KB < 16) part = a * (f16lo(kmeta[e]) * c24) + f16hi(kmeta[e]) * qs;
-      else part = a * c.qscale;
-      if (NG >= 2) part += dpp_xor1(part);
-      if (NG >= 4) part += dpp_xor2(part);
-      sc[e] = ((valid_mask >> e) & 1) ? part : -INFINITY;
+    if (i < nfull) {  // one full step left, already loaded into sa
+      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+      ++i;
     }
-
-    // ---- online softmax (lazy rescale) -------------------------------------
-    float mx = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(st.m, mx);
-    if (__builtin_amdgcn_ballot_w64(mnew > st.m + kLazy) != 0) {
-      const float alpha = exp2f(st.m - mnew);  // 0 on the first step (m = -inf)
-      st.l *= alpha;
-      st.mt *= alpha;
-      float ar[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * c.jq + i);
-#pragma unroll
-      for (int mb = 0; mb < NB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.o[mb][i] *= ar[i];
-      st.m = mnew;
+  } else {
+    for (; i < nfull; ++i) {
+      const int64_t o = int64_t(i) * 32;
+      load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of,
+                                      sa);
+      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
     }
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(sc[e] - st.m);
-      st.l += p[e];
-    }
-
-    // ---- p.v ------------------------------------------------------------------
-    u32x4 pa, pb;  // A operand (and the bf16 low part for bf16 V)
-    if (VB < 16) {
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
-        pa[e2] = pack_f16(p0 * f16lo(vmeta[2 * e2]), p1 * f16lo(vmeta[2 * e2 + 1]));
-        st.mt += p0 * f16hi(vmeta[2 * e2]) + p1 * f16hi(vmeta[2 * e2 + 1]);
-      }
-    } else {
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
-        pa[e2] = pack_bf16(p0, p1);
-        pb[e2] = pack_bf16(p0 - bf16f(pa[e2] & 0xFFFFu), p1 - bf16f(pa[e2] >> 16));
-      }
-    }
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-      u32x4 b;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) b[e2] = v_pair<D, VB>(vraw[2 * e2], vraw[2 * e2 + 1], mb);
-      if (VB == 16) {
-        st.o[mb] = mfma_bf16(pa, b, st.o[mb]);
-        st.o[mb] = mfma_bf16(pb, b, st.o[mb]);
-      } else {
-        st.o[mb] = mfma_f16(pa, b, st.o[mb]);
-      }
-    }
+  }
+  const int tail = rows - 32 * nfull;
+  if (tail > 0) {
+    const int64_t o = int64_t(nfull) * 32;
+    of.clamped(c, tail);
+    load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of, sa);
+    compute_step<D, NG, KB, VB, true>(c, ws, sa, qop, qs, c24, tail);
   }
 
 #pragma unroll
-  for (int mb = 0; mb < NB; ++mb) st.o[mb] *= 1.0f / v_inflation<D, VB>(mb);
+  for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= 1.0f / v_inflation<D, VB>(mb);
 }
 
-template <int D, int KB, int VB>
-__device__ inline void run_visual(const Ctx& c, WaveState<D>& st, int g, int x0, int x1,
-                                  int64_t row0) {
-  run_segment<D, KB, VB>(c, st, g, x0, x1, row0, true);
-}
-
-template <int D>
-__device__ void dispatch_visual(int kb, int vb, const Ctx& c, WaveState<D>& st, int g, int x0,
-                                int x1, int64_t row0) {
+template <int D, int NG>
+__device__ void dispatch_visual(int kb, int vb, const Ctx& c, WaveState<D>& st, int x0, int x1,
+                                int64_t row0) {
 #define KVQ_VIS(K, V) \
-  if (kb == K && vb == V) { run_visual<D, K, V>(c, st, g, x0, x1, row0); return; }
+  if (kb == K && vb == V) { run_segment<D, NG, K, V>(c, st, x0, x1, row0, true); return; }
   KVQ_VIS(2, 2) KVQ_VIS(2, 4) KVQ_VIS(2, 8) KVQ_VIS(2, 16)
   KVQ_VIS(4, 2) KVQ_VIS(4, 4) KVQ_VIS(4, 8) KVQ_VIS(4, 16)
   KVQ_VIS(8, 2) KVQ_VIS(8, 4) KVQ_VIS(8, 8) KVQ_VIS(8, 16)
@@ -387,10 +501,12 @@ __device__ void dispatch_visual(int kb, int vb, const Ctx& c, WaveState<D>& st, 
 #undef KVQ_VIS
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+template <int D, int NG>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NB = D / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int g = D / NG;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int slot = blockIdx.y;
   const int lh = a.lh_glob[slot];
   const int l_local = lh / a.Hkv, h = lh % a.Hkv;
@@ -401,15 +517,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int t0 = blockIdx.x * a.chunk;
   if (t0 >= len) return;
   const int t1 = min(t0 + a.chunk, len);
-  const int G = a.G, g = a.g;
-  const int NG = D / g;
+  const int G = a.G;
 
   __shared__ uint16_t q_lds[kMaxGroupRatio * D];
+  __shared__ float qsum_lds[16];
   __shared__ float o_lds[kWaves][kMaxGroupRatio][D];
   __shared__ float ml_lds[kWaves][kMaxGroupRatio][2];
 
   const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
   for (int i = threadIdx.x; i < G * D; i += 256) q_lds[i] = qp[i];
+  __syncthreads();
+  if (threadIdx.x < G * NG) {  // sum of q over each (head, group), times qscale
+    const int hh = threadIdx.x / NG, gg = threadIdx.x % NG;
+    float acc = 0.0f;
+    for (int d = gg * g; d < gg * g + g; ++d) acc += bf16f(q_lds[hh * D + d]);
+    qsum_lds[threadIdx.x] = acc * a.qscale;
+  }
   __syncthreads();
 
   Ctx c;
@@ -423,9 +546,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
   }
   c.q_lds = q_lds;
+  c.qsum_lds = qsum_lds;
   c.qscale = a.qscale;
   c.G = G;
-  c.NG = NG;
   c.lane = lane;
   c.n = lane & 15;
   c.jq = lane >> 4;
@@ -447,13 +570,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int kb = a.bits[slot][0], vbits = a.bits[slot][1];
     // text prefix [0, vb), visual [vb, ve), text suffix [ve, cap)
     int x0 = wa, x1 = min(wb, vb);
-    if (x0 < x1) run_segment<D, 16, 16>(c, st, g, x0, x1, trow0 + x0, false);
+    if (x0 < x1) run_segment<D, NG, 16, 16>(c, st, x0, x1, trow0 + x0, false);
     x0 = max(wa, vb);
     x1 = min(wb, ve);
-    if (x0 < x1) dispatch_visual<D>(kb, vbits, c, st, g, x0, x1, vrow0 + (x0 - vb));
+    if (x0 < x1) dispatch_visual<D, NG>(kb, vbits, c, st, x0, x1, vrow0 + (x0 - vb));
     x0 = max(wa, ve);
     x1 = wb;
-    if (x0 < x1) run_segment<D, 16, 16>(c, st, g, x0, x1, trow0 + (x0 - (ve - vb)), false);
+    if (x0 < x1) run_segment<D, NG, 16, 16>(c, st, x0, x1, trow0 + (x0 - (ve - vb)), false);
   }
 
   // ---- wave result -> LDS: per head m, l and unnormalised o[d] ---------------
@@ -520,11 +643,15 @@ bool mfma_supported(int D, int g, int G) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int n_seq_launch, hipStream_t stream) {
   dim3 grid(a.max_chunks, a.n_lh, n_seq_launch);
-  if (a.D == 128)
-    hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  const int NG = a.D / a.g;
+#define KVQ_LAUNCH(DD, NN)                                                           \
+  if (a.D == DD && NG == NN) {                                                       \
+    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN>), grid, dim3(256), 0, stream, a); \
+    return hipGetLastError();                                                        \
+  }
+  KVQ_LAUNCH(128, 1) KVQ_LAUNCH(128, 2) KVQ_LAUNCH(128, 4) KVQ_LAUNCH(64, 1) KVQ_LAUNCH(64, 2)
+#undef KVQ_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq
