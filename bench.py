@@ -48,13 +48,17 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the bf16 reference, quantize block and copy measurements")
+    ap.add_argument("--protected", type=int, default=14,
+                    help="HeadGuard protected (bf16) heads of the 28-layer step")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
 
 
-def workload(name):
+def workload(name, protected=14):
     from quantized_decode_attention_quantize_amd import synth
     if name == "headguard_step":
-        return synth.headguard_step(extra_capacity=1)
+        return synth.headguard_step(num_protected=protected, extra_capacity=1)
     if name == "long_gqa":
         w = synth.long_gqa()
     elif name == "llava_layer":
@@ -125,10 +129,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_only:
+        print(json.dumps({"copy_ceiling": copy_ceiling(torch, dev, torch.cuda.current_stream())}))
+        return
     kvq.lib()
     stream = torch.cuda.current_stream()
 
-    w = workload(args.workload)
+    w = workload(args.workload, args.protected)
     T = [c - 1 for c in w.capacity]          # history length before the step
     lens = [t + 1 for t in T]                # attended after appending
     cfg = kvq.Config.from_workload(w)
@@ -139,7 +146,7 @@ def main():
 
     ref_cfg = None
     if not args.no_extras:
-        rw = workload(args.workload)
+        rw = workload(args.workload, args.protected)
         rw.k_bits[:] = 16
         rw.v_bits[:] = 16
         ref_cfg = kvq.Config.from_workload(rw)

@@ -156,13 +156,18 @@ kvq_status kvq_quantize(const kvq_config *cfg, void *cache, int32_t layer_begin,
  *   out        device bf16 [num_layers, batch, Hq, D], 16-byte aligned; must
  *              not alias q, cache or workspace
  *   sm_scale   softmax scale applied to q.k (e.g. 1/sqrt(D)), fp32
- *   chunk_tokens  tokens per split-K chunk, 0 = library choice; otherwise a
- *              positive multiple of 32
+ *   chunk_tokens  0 = library choice: each (layer, seq, KV head) is split into
+ *              workgroups in proportion to its capacity and per-token cost so
+ *              that all waves of the call fit the device at once; otherwise
+ *              a positive multiple of 32 = tokens per split-K workgroup
  *   workspace  device scratch for split partials, 256-byte aligned.  If
  *              workspace == NULL the call only writes the required size to
  *              *workspace_bytes and launches nothing.  Otherwise
  *              *workspace_bytes is the size provided.  The required size
- *              depends on cfg, the layer count and chunk_tokens only.
+ *              depends on cfg, the layer range and chunk_tokens (and, for
+ *              chunk_tokens == 0, on the current device's compute-unit count).
+ *              Its contents need no initialisation; concurrent calls must use
+ *              distinct workspaces.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN,
  * KVQ_ERR_RANGE (layer range), KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
 kvq_status kvq_decode_attention(const kvq_config *cfg, const void *cache,

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -107,23 +108,91 @@ int default_chunk(const kvq_config* c, int nl, int quantum, int64_t target) {
   return int(std::max<int64_t>(ch, quantum));
 }
 
+// Compute units of the current device (256 on MI355X); 256 when no device
+// can be queried (host-only use such as workspace size queries in tests).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1)
+    return 256;
+  return n;
+}
+
+static_assert(sizeof(DecodeArgs) <= 4096, "decode kernel arguments exceed 4 KB");
+static_assert(sizeof(QuantizeArgs) <= 4096, "quantize kernel arguments exceed 4 KB");
+
 struct DecodePlan {
-  int chunk, max_chunks;
+  int chunk;                  // tokens per workgroup; 0 = balanced split
+  std::vector<int> nx;        // [batch] workgroups per (layer, head) before mult
+  std::vector<uint8_t> mult;  // [num_layers * Hkv] of the call: heavy-head multiplier
+  int max_chunks;
   int64_t entries;
-  size_t o_bytes, ml_bytes, total;
+  size_t o_bytes, ml_bytes, cnt_bytes, total;
 };
 
-DecodePlan plan_decode(const kvq_config* c, int nl, int chunk) {
+// Split planning.  With chunk_tokens > 0 (or on the general kernel) every
+// workgroup takes a fixed token chunk.  Otherwise (matrix-core kernel) the
+// split is balanced: each (layer, seq, head) gets workgroups in proportion to
+// its capacity and cost so that all waves fit the device in one round
+// (8 waves per CU: the kernel runs at two waves per SIMD); all-bf16 heads move
+// ~4.6x the bytes per token of INT4/INT2 heads and take about twice as long
+// per step, so they get twice the workgroups.
+DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_tokens,
+                       bool use_mfma) {
   DecodePlan p;
-  int max_cap = 0;
-  for (int s = 0; s < c->batch; ++s) max_cap = std::max(max_cap, c->capacity[s]);
-  p.chunk = chunk;
-  p.max_chunks = (max_cap + chunk - 1) / chunk;
+  const int B = c->batch, Hkv = c->num_kv_heads;
+  p.nx.assign(B, 1);
+  p.mult.assign(size_t(nl) * Hkv, 1);
+  if (chunk_tokens > 0 || !use_mfma) {
+    p.chunk = chunk_tokens > 0 ? chunk_tokens : default_chunk(c, nl, 256, 1024);
+    for (int s = 0; s < B; ++s) p.nx[s] = (c->capacity[s] + p.chunk - 1) / p.chunk;
+  } else {
+    p.chunk = 0;
+    int64_t msum = 0;
+    for (int i = 0; i < nl * Hkv; ++i) {
+      const int l = layer_begin + i / Hkv, h = i % Hkv;
+      p.mult[i] = (bits_of(c, l, h, 0) == 16 && bits_of(c, l, h, 1) == 16) ? 2 : 1;
+      msum += p.mult[i];
+    }
+    int64_t caps = 0;
+    for (int s = 0; s < B; ++s) caps += c->capacity[s];
+    // Budget: two 4-wave workgroups per CU (the kernel runs two waves per
+    // SIMD), so every CU carries the same load and all waves run in one round.
+    const int64_t budget = int64_t(device_cus()) * 2;
+    constexpr int kMinWaveTokens = 128;  // keep >= 4 steps per wave
+    std::vector<double> frac(B);
+    int64_t used = 0;
+    for (int s = 0; s < B; ++s) {
+      const double want = double(budget) * double(c->capacity[s]) / double(caps * msum);
+      const int nmax = (c->capacity[s] + kMfmaWaves * kMinWaveTokens - 1) /
+                       (kMfmaWaves * kMinWaveTokens);
+      p.nx[s] = std::max(1, std::min(int(want), nmax));
+      frac[s] = p.nx[s] < nmax ? want - std::floor(want) : -1.0;
+      used += int64_t(p.nx[s]) * msum;
+    }
+    // largest remainders take what is left of the budget
+    while (used + msum <= budget) {
+      int best = -1;
+      for (int s = 0; s < B; ++s)
+        if (frac[s] > 0.0 && (best < 0 || frac[s] > frac[best])) best = s;
+      if (best < 0) break;
+      ++p.nx[best];
+      frac[best] = -1.0;
+      used += msum;
+    }
+  }
+  int mx = 1;
+  for (int s = 0; s < B; ++s) mx = std::max(mx, p.nx[s]);
+  int mm = 1;
+  for (uint8_t m : p.mult) mm = std::max<int>(mm, m);
+  p.max_chunks = mx * mm;
   const int G = c->num_q_heads / c->num_kv_heads;
-  p.entries = int64_t(nl) * c->batch * c->num_kv_heads * p.max_chunks;
+  p.entries = int64_t(nl) * B * Hkv * p.max_chunks;
   p.o_bytes = size_t(align256(p.entries * G * c->head_dim * 4));
   p.ml_bytes = size_t(align256(p.entries * G * 2 * 4));
-  p.total = p.o_bytes + p.ml_bytes;
+  p.cnt_bytes = size_t(align256(int64_t(nl) * B * Hkv * 4));
+  p.total = p.o_bytes + p.ml_bytes + p.cnt_bytes;
   return p;
 }
 
@@ -248,10 +317,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
     const bool use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
-    const int chunk = chunk_tokens ? chunk_tokens
-                                   : use_mfma ? default_chunk(cfg, num_layers, 128, 1024)
-                                              : default_chunk(cfg, num_layers, 256, 1024);
-    const DecodePlan plan = plan_decode(cfg, num_layers, chunk);
+    const DecodePlan plan = plan_decode(cfg, layer_begin, num_layers, chunk_tokens, use_mfma);
     if (!workspace) {
       *workspace_bytes = plan.total;
       return KVQ_OK;
@@ -288,6 +354,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
       a.out = static_cast<uint16_t*>(out);
       a.ws_o = reinterpret_cast<float*>(ws);
       a.ws_ml = reinterpret_cast<float*>(ws + plan.o_bytes);
+      a.ws_cnt = reinterpret_cast<int32_t*>(ws + plan.o_bytes + plan.ml_bytes);
       a.qscale = sm_scale * 1.4426950408889634f;
       a.Rvis = lay.Rvis;
       a.D = lay.D;
@@ -306,7 +373,10 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
         a.cap[i] = cfg->capacity[s];
         a.vrow0[i] = int32_t(lay.vrow0[s]);
         a.trow0[i] = int32_t(lay.trow0[s]);
+        a.nx[i] = plan.nx[s];
+        a.nxcum[i + 1] = a.nxcum[i] + plan.nx[s];
       }
+      a.n_seq = ns_l;
       for (int lh0 = 0; lh0 < nlh; lh0 += kMaxLH) {
         const int nlh_l = std::min(kMaxLH, nlh - lh0);
         a.n_lh = nlh_l;
@@ -318,13 +388,15 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
             a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
           }
           a.lh_glob[i] = uint16_t(glh);
+          a.mult[i] = plan.mult[glh];
+          a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
         }
         const hipError_t e = use_mfma ? launch_decode_mfma(a, ns_l, hs)
                                       : launch_decode_simple(a, ns_l, hs);
         if (e != hipSuccess) return KVQ_ERR_HIP;
       }
-      // the matrix-core kernel finishes single-chunk calls itself
-      if (!(use_mfma && plan.max_chunks == 1) &&
+      // with one workgroup per (layer, seq, head) the split kernel wrote the output
+      if (plan.max_chunks > 1 &&
           launch_decode_merge(a, num_layers, ns_l, hs) != hipSuccess)
         return KVQ_ERR_HIP;
     }

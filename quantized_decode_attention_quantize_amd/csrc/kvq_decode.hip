@@ -89,11 +89,12 @@ __global__ __launch_bounds__(256) void decode_simple_kernel(DecodeArgs a) {
   const int lh = a.lh_glob[slot];
   const int l_local = lh / a.Hkv, h = lh % a.Hkv;
   const int sl = blockIdx.z, s = a.seq_off + sl;
+  const int nxs = a.nx[sl];  // workgroups of this (layer, seq, head); chunk mode
+  if (int(blockIdx.x) >= nxs) return;
   const int cap = a.cap[sl];
   int len = a.seq_lens[s];
   len = len < 1 ? 1 : (len > cap ? cap : len);
-  const int t0 = blockIdx.x * a.chunk;
-  if (t0 >= len) return;
+  const int t0 = min(int(blockIdx.x) * a.chunk, len);  // empty when past len
   const int t1 = min(t0 + a.chunk, len);
   const int G = a.G;
   const int vb = a.vb[sl], ve = a.ve[sl];
@@ -182,10 +183,13 @@ __global__ __launch_bounds__(256) void decode_simple_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int64_t pidx = partial_index(l_local, s, h, blockIdx.x, a.B, a.Hkv, a.max_chunks);
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    a.ws_cnt[(int64_t(l_local) * a.B + s) * a.Hkv + h] = nxs;
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int j = i / D, d = i % D;
     float M = -INFINITY;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_ml[w][j][0]);
+    for (int w = 0; w < NW; ++w)
+      if (red_ml[w][j][1] > 0.0f) M = fmaxf(M, red_ml[w][j][0]);
     float L = 0.0f, acc = 0.0f;
     for (int w = 0; w < NW; ++w) {
       if (red_ml[w][j][1] > 0.0f) {
@@ -194,10 +198,16 @@ __global__ __launch_bounds__(256) void decode_simple_kernel(DecodeArgs a) {
         acc += red_o[w][j][d] * sc;
       }
     }
-    a.ws_o[(pidx * G + j) * D + d] = acc / L;
-    if (d == 0) {
-      a.ws_ml[(pidx * G + j) * 2 + 0] = M;
-      a.ws_ml[(pidx * G + j) * 2 + 1] = L;
+    const float o = L > 0.0f ? acc / L : 0.0f;  // L == 0: no token in this workgroup
+    if (nxs == 1) {
+      a.out[((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G + j) * D + d] =
+          __builtin_bit_cast(uint16_t, (__bf16)o);
+    } else {
+      a.ws_o[(pidx * G + j) * D + d] = o;
+      if (d == 0) {
+        a.ws_ml[(pidx * G + j) * 2 + 0] = M;
+        a.ws_ml[(pidx * G + j) * 2 + 1] = L;
+      }
     }
   }
 }
@@ -211,18 +221,20 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int l_local = blockIdx.z;
   const int lane = threadIdx.x;
   const int G = a.G, h = i / G, j = i % G;
-  const int cap = a.cap[sl];
-  int len = a.seq_lens[s];
-  len = len < 1 ? 1 : (len > cap ? cap : len);
-  const int nc = (len + a.chunk - 1) / a.chunk;
+  const int nc = a.ws_cnt[(int64_t(l_local) * a.B + s) * a.Hkv + h];
+  if (nc <= 1) return;  // one workgroup: the split kernel wrote the output
   const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.ws_ml[((p0 + c) * G + j) * 2]);
+  for (int c = 0; c < nc; ++c) {
+    const float* ml = a.ws_ml + ((p0 + c) * G + j) * 2;
+    if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
+  }
   float W = 0.0f, acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
   for (int c = 0; c < nc; ++c) {
     const float* ml = a.ws_ml + ((p0 + c) * G + j) * 2;
+    if (!(ml[1] > 0.0f)) continue;  // empty workgroup
     const float w = ml[1] * exp2f(ml[0] - M);
     W += w;
     const float* op = a.ws_o + ((p0 + c) * G + j) * D + lane * DPL;

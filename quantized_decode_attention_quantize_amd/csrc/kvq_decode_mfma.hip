@@ -216,18 +216,22 @@ struct Ctx {
   const uint8_t* vmeta;
   const uint8_t* vtxt;
   const uint16_t* q_lds;   // [G][D] bf16 bits of this workgroup's queries
-  const float* qsum_lds;   // [G * NG] sum of q over each (head, group), times qscale
+  uint8_t* stage;          // this wave's LDS stage (kStageBytes)
   float qscale;
   int G;
   int lane, n, jq;         // lane, column (l % 16), quarter (l / 16)
 };
 
 // Build Q' for k format KB: per k-step, 8 slots of this lane's column.
+// Returns the sum of q over the column's (head, group), times qscale: each
+// lane's slots cover its quarter of the head dim exactly once, so a sum over
+// the four quarters completes it.
 template <int D, int NG, int KB>
-__device__ inline void build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
+__device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
   constexpr int g = D / NG;
   const int h = c.n / NG, gj = c.n % NG;
   const bool live = c.n < c.G * NG;
+  float qs = 0.0f;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
 #pragma unroll
@@ -239,11 +243,16 @@ __device__ inline void build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
         float w;
         kslot<D, KB>(s, c.jq, 2 * e2 + hf, d, w);
         const float qv = bf16f(c.q_lds[(live ? h : 0) * D + d]);
-        v2[hf] = (live && d / g == gj) ? qv * (1.0f / w) : 0.0f;  // w: power of two
+        const bool in = live && d / g == gj;
+        qs += in ? qv : 0.0f;
+        v2[hf] = in ? qv * (1.0f / w) : 0.0f;  // w: power of two
       }
       qop[s][e2] = KB == 16 ? pack_bf16(v2[0], v2[1]) : pack_f16(v2[0], v2[1]);
     }
   }
+  qs += __shfl_xor(qs, 16);
+  qs += __shfl_xor(qs, 32);
+  return qs * c.qscale;
 }
 
 template <int NBYTES>
@@ -420,6 +429,96 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
   }
 }
 
+// ---------------------------------------------------------------------------
+// Cooperative staging of quantised steps through wave-private LDS.
+//
+// The 32 rows of a step form contiguous tiles in each plane (K codes, K meta,
+// V codes, V meta).  Lane l loads bytes [l * RB/2, (l + 1) * RB/2) of a tile
+// of row size RB -- row l/2, half l%2 -- with the widest loads the piece
+// allows, writes the piece to the same offset of the wave's LDS stage, and
+// the operands are then read back in the MFMA layouts.  Versus loading the
+// operand layouts straight from memory this issues ~5 wide loads per step
+// instead of ~26 narrow ones and keeps ~14 VGPRs per step in flight instead
+// of ~32, so two steps stay in flight per wave.
+template <int NBYTES>
+__device__ inline void store_bytes(uint8_t* p, const uint32_t* in) {
+  if constexpr (NBYTES >= 16) {
+#pragma unroll
+    for (int i = 0; i < NBYTES / 16; ++i)
+      reinterpret_cast<uint4*>(p)[i] = make_uint4(in[4 * i], in[4 * i + 1], in[4 * i + 2],
+                                                  in[4 * i + 3]);
+  } else if constexpr (NBYTES == 8) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(in[0], in[1]);
+  } else if constexpr (NBYTES == 4) {
+    *reinterpret_cast<uint32_t*>(p) = in[0];
+  } else {
+    *reinterpret_cast<uint16_t*>(p) = uint16_t(in[0]);
+  }
+}
+
+template <int D, int NG, int KB, int VB>
+struct Stage {
+  static constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
+  static constexpr int KP = KR / 2, VP = VR / 2, MP = MR / 2;  // bytes per lane per tile
+  static constexpr int kOffKM = 32 * KR, kOffV = kOffKM + 32 * MR, kOffVM = kOffV + 32 * VR;
+  static constexpr int kBytes = kOffVM + 32 * MR;
+  uint32_t k[KP / 4];
+  uint32_t km[(MP + 3) / 4];
+  uint32_t v[VP / 4];
+  uint32_t vm[(MP + 3) / 4];
+};
+
+// Wave-private LDS stage large enough for every quantised format.
+constexpr int kStageBytes = 2 * (32 * 128 + 32 * 16);  // INT8 K and V at D=128, NG=4
+
+// Lane piece of tile rows [0, 32) of step `step`; rows at or past rows_total
+// are clamped to the segment's last row (those lanes re-read cached bytes).
+template <int D, int NG, int KB, int VB>
+__device__ inline void stage_load(const uint8_t* kp, const uint8_t* kmp, const uint8_t* vp,
+                                  const uint8_t* vmp, int step, int rows_total, int lane,
+                                  Stage<D, NG, KB, VB>& st) {
+  using S = Stage<D, NG, KB, VB>;
+  const int row = min(step * 32 + (lane >> 1), rows_total - 1);
+  const int half = lane & 1;
+  load_bytes<S::KP>(kp + row * S::KR + half * S::KP, st.k);
+  load_bytes<S::MP>(kmp + row * S::MR + half * S::MP, st.km);
+  load_bytes<S::VP>(vp + row * S::VR + half * S::VP, st.v);
+  load_bytes<S::MP>(vmp + row * S::MR + half * S::MP, st.vm);
+}
+
+// Lanes exchange data through the stage, so the compiler must not move one
+// lane's LDS accesses across another's: wave barriers order the previous
+// step's reads before these writes, and these writes before the next reads
+// (LDS executes one wave's instructions in order).
+template <int D, int NG, int KB, int VB>
+__device__ inline void stage_put(uint8_t* lds, int lane, const Stage<D, NG, KB, VB>& st) {
+  using S = Stage<D, NG, KB, VB>;
+  __builtin_amdgcn_wave_barrier();
+  store_bytes<S::KP>(lds + lane * S::KP, st.k);
+  store_bytes<S::MP>(lds + S::kOffKM + lane * S::MP, st.km);
+  store_bytes<S::VP>(lds + S::kOffV + lane * S::VP, st.v);
+  store_bytes<S::MP>(lds + S::kOffVM + lane * S::MP, st.vm);
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Operand gather from the LDS stage into the layout compute_step expects.
+template <int D, int NG, int KB, int VB>
+__device__ inline void stage_get(const uint8_t* lds, const Ctx& c, Step<D, KB, VB>& st) {
+  using S = Stage<D, NG, KB, VB>;
+  constexpr int KQ = S::KR / 4, VBY = Fmt<D, VB>::kVBytes;
+  const int gj = c.n % NG;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+    load_bytes<KQ>(lds + (16 * tau + c.n) * S::KR + c.jq * KQ, st.k[tau]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = 16 * (e >> 2) + 4 * c.jq + (e & 3);
+    st.km[e] = *reinterpret_cast<const uint32_t*>(lds + S::kOffKM + r * S::MR + gj * 4);
+    st.vm[e] = *reinterpret_cast<const uint32_t*>(lds + S::kOffVM + r * S::MR + gj * 4);
+    load_bytes<VBY>(lds + S::kOffV + r * S::VR + c.n * VBY, st.v[e]);
+  }
+}
+
 // One segment [x0, x1) of rows of one format, rows starting at plane row
 // row0 (K and V share row numbering).  KB/VB: stored widths (16 = bf16).
 template <int D, int NG, int KB, int VB>
@@ -433,8 +532,7 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   const uint8_t* vmp = c.vmeta + row0 * MR;
 
   u32x4 qop[D / 32];
-  build_q<D, NG, KB>(c, qop);
-  const float qs = c.n < c.G * NG ? c.qsum_lds[c.n] : 0.0f;
+  const float qs = build_q<D, NG, KB>(c, qop);
   const float c24 = c.qscale * 16777216.0f;  // 2^24 * qscale
 
 #pragma unroll
@@ -447,27 +545,32 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   // Quantised steps are small (~32 VGPRs of raw data): double-buffer them so
   // the loads of step i+1 fly while step i computes.  bf16 steps carry 64
   // VGPRs of data and run single-buffered.
-  constexpr bool kPrefetch = KB < 16 && VB < 16;
+  constexpr bool kStaged = KB < 16 && VB < 16;
   Step<D, KB, VB> sa;
   int i = 0;
-  if constexpr (kPrefetch) {
-    Step<D, KB, VB> sb;
-    if (nfull > 0) load_step<D, NG, KB, VB, false>(kp, kmp, vp, vmp, of, sa);
-    for (; i + 2 <= nfull; i += 2) {
-      const int64_t o1 = int64_t(i + 1) * 32;
-      load_step<D, NG, KB, VB, false>(kp + o1 * KR, kmp + o1 * MR, vp + o1 * VR, vmp + o1 * MR,
-                                      of, sb);
-      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
-      if (i + 2 < nfull) {
-        const int64_t o2 = int64_t(i + 2) * 32;
-        load_step<D, NG, KB, VB, false>(kp + o2 * KR, kmp + o2 * MR, vp + o2 * VR,
-                                        vmp + o2 * MR, of, sa);
+  if constexpr (kStaged) {
+    // Two register stages in flight; loads inside the loop are unconditional
+    // (clamped to the last full step) so the wait counts stay exact.
+    if (nfull > 0) {
+      Stage<D, NG, KB, VB> ga, gb;
+      stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, 0, 32 * nfull, c.lane, ga);
+      stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, min(1, nfull - 1), 32 * nfull, c.lane, gb);
+      for (; i + 1 < nfull; i += 2) {
+        stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
+        stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, min(i + 2, nfull - 1), 32 * nfull, c.lane, ga);
+        stage_get<D, NG, KB, VB>(c.stage, c, sa);
+        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+        stage_put<D, NG, KB, VB>(c.stage, c.lane, gb);
+        stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, min(i + 3, nfull - 1), 32 * nfull, c.lane, gb);
+        stage_get<D, NG, KB, VB>(c.stage, c, sa);
+        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
       }
-      compute_step<D, NG, KB, VB, false>(c, ws, sb, qop, qs, c24, 32);
-    }
-    if (i < nfull) {  // one full step left, already loaded into sa
-      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
-      ++i;
+      if (i < nfull) {  // odd step count: the last full step sits in ga
+        stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
+        stage_get<D, NG, KB, VB>(c.stage, c, sa);
+        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+        ++i;
+      }
     }
   } else {
     for (; i < nfull; ++i) {
@@ -507,32 +610,27 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int g = D / NG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int slot = blockIdx.y;
+  int slot, sl, x;
+  decode_block(a, blockIdx.x, a.n_seq, slot, sl, x);
   const int lh = a.lh_glob[slot];
   const int l_local = lh / a.Hkv, h = lh % a.Hkv;
-  const int sl = blockIdx.z, s = a.seq_off + sl;
+  const int s = a.seq_off + sl;
+  const int nxs = a.nx[sl] * a.mult[slot];  // workgroups of this (layer, seq, head)
   const int cap = a.cap[sl];
   int len = a.seq_lens[s];
   len = len < 1 ? 1 : (len > cap ? cap : len);
-  const int t0 = blockIdx.x * a.chunk;
-  if (t0 >= len) return;
-  const int t1 = min(t0 + a.chunk, len);
   const int G = a.G;
 
   __shared__ uint16_t q_lds[kMaxGroupRatio * D];
-  __shared__ float qsum_lds[16];
-  __shared__ float o_lds[kWaves][kMaxGroupRatio][D];
   __shared__ float ml_lds[kWaves][kMaxGroupRatio][2];
+  // wave stages during the loop; per-wave outputs for the final combine after it
+  constexpr int kOBytes = kWaves * kMaxGroupRatio * D * 4;
+  constexpr int kUnion = kOBytes > kWaves * kStageBytes ? kOBytes : kWaves * kStageBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnion];
+  float(*o_lds)[kMaxGroupRatio][D] = reinterpret_cast<float(*)[kMaxGroupRatio][D]>(big_lds);
 
   const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
   for (int i = threadIdx.x; i < G * D; i += 256) q_lds[i] = qp[i];
-  __syncthreads();
-  if (threadIdx.x < G * NG) {  // sum of q over each (head, group), times qscale
-    const int hh = threadIdx.x / NG, gg = threadIdx.x % NG;
-    float acc = 0.0f;
-    for (int d = gg * g; d < gg * g + g; ++d) acc += bf16f(q_lds[hh * D + d]);
-    qsum_lds[threadIdx.x] = acc * a.qscale;
-  }
   __syncthreads();
 
   Ctx c;
@@ -546,7 +644,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
   }
   c.q_lds = q_lds;
-  c.qsum_lds = qsum_lds;
+  c.stage = big_lds + wave * kStageBytes;
   c.qscale = a.qscale;
   c.G = G;
   c.lane = lane;
@@ -560,10 +658,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   st.l = 0.0f;
   st.mt = 0.0f;
 
-  // this wave's share of the chunk, in whole 32-token steps
-  const int per_wave = a.chunk / kWaves;
-  const int wa = t0 + wave * per_wave;
-  const int wb = min(wa + per_wave, t1);
+  int wa, wb;
+  wave_range(x, wave, nxs, len, a.chunk, kWaves, wa, wb);
   if (wa < wb) {
     const int vb = a.vb[sl], ve = a.ve[sl];
     const int64_t vrow0 = a.vrow0[sl], trow0 = a.trow0[sl];
@@ -580,6 +676,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // ---- wave result -> LDS: per head m, l and unnormalised o[d] ---------------
+  __syncthreads();  // stages are reused as o_lds below
   float l_col = st.l + __shfl_xor(st.l, 16);
   l_col += __shfl_xor(l_col, 32);
   float mt_col = st.mt + __shfl_xor(st.mt, 16);
@@ -604,9 +701,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- combine waves; write the chunk's partial (or the final output) --------
-  const bool single = a.max_chunks == 1;
-  const int64_t pidx = partial_index(l_local, s, h, blockIdx.x, a.B, a.Hkv, a.max_chunks);
+  // ---- combine waves; write the workgroup's partial (or the final output) ----
+  const bool single = nxs == 1;
+  const int64_t pidx = partial_index(l_local, s, h, x, a.B, a.Hkv, a.max_chunks);
+  if (x == 0 && threadIdx.x == 0)
+    a.ws_cnt[(int64_t(l_local) * a.B + s) * a.Hkv + h] = nxs;
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int j = i / D, d = i % D;
     float M = -INFINITY;
@@ -617,16 +716,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       if (ml_lds[w][j][1] > 0.0f) {
-        const float f = exp2f(ml_lds[w][j][0] - M);
+        const float f = __builtin_amdgcn_exp2f(ml_lds[w][j][0] - M);
         L += ml_lds[w][j][1] * f;
         acc += o_lds[w][j][d] * f;
       }
     }
+    const float o = L > 0.0f ? acc / L : 0.0f;  // L == 0: no token in this workgroup
     if (single) {
       a.out[((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G + j) * D + d] =
-          __builtin_bit_cast(uint16_t, (__bf16)(acc / L));
+          __builtin_bit_cast(uint16_t, (__bf16)o);
     } else {
-      a.ws_o[(pidx * G + j) * D + d] = acc / L;
+      a.ws_o[(pidx * G + j) * D + d] = o;
       if (d == 0) {
         a.ws_ml[(pidx * G + j) * 2 + 0] = M;
         a.ws_ml[(pidx * G + j) * 2 + 1] = L;
@@ -642,7 +742,8 @@ bool mfma_supported(int D, int g, int G) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int n_seq_launch, hipStream_t stream) {
-  dim3 grid(a.max_chunks, a.n_lh, n_seq_launch);
+  (void)n_seq_launch;  // a.n_seq
+  const dim3 grid(a.nxcum[a.n_seq] * a.mcum[a.n_lh], 1, 1);  // compact block list
   const int NG = a.D / a.g;
 #define KVQ_LAUNCH(DD, NN)                                                           \
   if (a.D == DD && NG == NN) {                                                       \

@@ -52,17 +52,71 @@ struct DecodeArgs {
   uint16_t* out;            // bf16 [nl, B, Hq, D]
   float* ws_o;              // [entries][G][D] normalised partial outputs
   float* ws_ml;             // [entries][G][2] (running max m in log2 units, sum l)
+  int32_t* ws_cnt;          // [nl * B * Hkv] partial count of each (layer, seq, head)
   float qscale;             // sm_scale * log2(e)
   int64_t Rvis;
   int D, g, G, Hkv, Hq, B;
-  int chunk, max_chunks;
+  int chunk;                // tokens per workgroup; 0 = balanced split (see nx)
+  int max_chunks;           // partial slots per (layer, seq, head)
   int seq_off;              // first global sequence of this launch
   int n_lh;                 // (layer-local, head) pairs in this launch
+  int n_seq;                // sequences in this launch
   uint16_t lh_glob[kMaxLH];  // grid.y slot -> layer_local * Hkv + head
   uint32_t base256[kMaxLH][2];  // per slot: VIS plane offset / 256 of K and V
   uint8_t bits[kMaxLH][2];
+  uint8_t mult[kMaxLH];     // per slot: workgroup multiplier of heavy (bf16) heads
+  uint16_t mcum[kMaxLH + 1];  // per slot: sum of mult over earlier slots (compact grid)
   int32_t vb[kMaxSeq], ve[kMaxSeq], cap[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
+  int32_t nx[kMaxSeq];      // per sequence: workgroups per (layer, head) before mult
+  int32_t nxcum[kMaxSeq + 1];  // per sequence: sum of nx over earlier sequences
 };
+
+// Compact 1-D grid of the split kernels: block b enumerates, slot-major, every
+// (slot, sequence, x < nx[seq] * mult[slot]) with no idle blocks, so the
+// round-robin dealing of blocks to the XCDs stays even.  Returns slot, the
+// sequence index within the launch and x.
+__device__ inline void decode_block(const DecodeArgs& a, int b, int n_seq, int& slot, int& sl,
+                                    int& x) {
+  const int per_mult = a.nxcum[n_seq];  // workgroups of one slot with mult 1
+  int lo = 0, hi = a.n_lh - 1;          // last slot with per_mult * mcum[slot] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (per_mult * int(a.mcum[mid]) <= b) lo = mid; else hi = mid - 1;
+  }
+  slot = lo;
+  const int m = a.mult[slot];
+  const int r = b - per_mult * int(a.mcum[slot]);
+  lo = 0;
+  hi = n_seq - 1;                       // last sequence with m * nxcum[seq] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (m * a.nxcum[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  sl = lo;
+  x = r - m * a.nxcum[sl];
+}
+
+// Token range of wave `w` of workgroup `x` out of `nxs` workgroups of one
+// (layer, seq, head) with `len` attended tokens.  chunk > 0: workgroup x takes
+// [x * chunk, (x + 1) * chunk) and its waves split that evenly.  chunk == 0
+// (balanced): the len tokens form ceil(len / 32) steps dealt into 4 * nxs
+// nearly equal wave units.
+__host__ __device__ inline void wave_range(int x, int w, int nxs, int len, int chunk,
+                                           int waves, int& a, int& b) {
+  if (chunk > 0) {
+    const int per = chunk / waves;
+    a = x * chunk + w * per;
+    b = a + per;
+    const int e = x * chunk + chunk;
+    if (b > e) b = e;
+  } else {
+    const int64_t nblk = (len + 31) / 32, U = int64_t(waves) * nxs, u = int64_t(x) * waves + w;
+    a = int(32 * (u * nblk / U));
+    b = int(32 * ((u + 1) * nblk / U));
+  }
+  if (a > len) a = len;
+  if (b > len) b = len;
+}
 
 // Index of a split partial: (layer-local l, global seq s, head h, chunk x).
 __host__ __device__ inline int64_t partial_index(int l, int s, int h, int x, int B, int Hkv,
@@ -79,5 +133,7 @@ bool mfma_supported(int D, int g, int G);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int n_seq_launch, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int nl, int n_seq_launch,
                                hipStream_t stream);
+constexpr int kMfmaWaves = 4;      // waves per workgroup of the matrix-core kernel
+constexpr int kSimpleWaves = 4;    // waves per workgroup of the general kernel
 
 }  // namespace kvq
