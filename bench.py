@@ -191,7 +191,7 @@ def main():
     out = torch.empty_like(q)
     lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
     seq_ids = list(range(w.batch))
-    ws = torch.empty(kvq.workspace_bytes(cfg, w.num_layers, args.chunk), dtype=torch.uint8,
+    ws = torch.zeros(kvq.workspace_bytes(cfg, w.num_layers, args.chunk), dtype=torch.uint8,
                      device=dev)
     same_T = len(set(T)) == 1
 
@@ -238,7 +238,7 @@ def main():
     if not args.no_extras:
         # bf16 reference: same shapes, every row bf16 (bandwidth reference)
         ref_alg = algorithmic_bytes(_bf16_like(w), lens)
-        wsr = torch.empty(kvq.workspace_bytes(ref_cfg, w.num_layers, args.chunk),
+        wsr = torch.zeros(kvq.workspace_bytes(ref_cfg, w.num_layers, args.chunk),
                           dtype=torch.uint8, device=dev)
         for i in range(args.warmup):
             kvq.kvq_decode_attention(ref_cfg, refs[i % R_ref], 0, w.num_layers, lens_d, q, out,

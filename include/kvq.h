@@ -49,8 +49,8 @@
  * Ownership, streams, errors
  * --------------------------
  * Every device pointer is owned by the caller (typically torch tensors);
- * libkvq never allocates, frees or retains device memory and keeps no
- * mutable global state.  Host arrays are read only during the call.
+ * libkvq never allocates, frees or retains device memory; its only global
+ * state is a per-device cache of the compute-unit count.  Host arrays are read only during the call.
  * kvq_quantize and kvq_decode_attention only enqueue work on `stream`
  * (a hipStream_t; NULL = the default stream) and never synchronise; faults
  * inside kernels surface at the caller's next synchronisation.  Every entry
@@ -160,14 +160,16 @@ kvq_status kvq_quantize(const kvq_config *cfg, void *cache, int32_t layer_begin,
  *              workgroups in proportion to its capacity and per-token cost so
  *              that all waves of the call fit the device at once; otherwise
  *              a positive multiple of 32 = tokens per split-K workgroup
- *   workspace  device scratch for split partials, 256-byte aligned.  If
- *              workspace == NULL the call only writes the required size to
- *              *workspace_bytes and launches nothing.  Otherwise
- *              *workspace_bytes is the size provided.  The required size
- *              depends on cfg, the layer range and chunk_tokens (and, for
- *              chunk_tokens == 0, on the current device's compute-unit count).
- *              Its contents need no initialisation; concurrent calls must use
- *              distinct workspaces.
+ *   workspace  device scratch for split partials and the merge's arrival
+ *              counters, 256-byte aligned.  If workspace == NULL the call only
+ *              writes the required size to *workspace_bytes and launches
+ *              nothing.  Otherwise *workspace_bytes is the size provided.  The
+ *              required size depends on cfg, the layer range and chunk_tokens
+ *              (and, for chunk_tokens == 0, on the current device's
+ *              compute-unit count).  The workspace must be zero-filled before
+ *              its first use; every call leaves it ready for the next one, so a
+ *              workspace can be reused across calls of any shape that fits it.
+ *              Calls that may overlap in time must use distinct workspaces.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN,
  * KVQ_ERR_RANGE (layer range), KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */
 kvq_status kvq_decode_attention(const kvq_config *cfg, const void *cache,

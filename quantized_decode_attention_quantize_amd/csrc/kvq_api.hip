@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -110,12 +111,18 @@ int default_chunk(const kvq_config* c, int nl, int quantum, int64_t target) {
 
 // Compute units of the current device (256 on MI355X); 256 when no device
 // can be queried (host-only use such as workspace size queries in tests).
+// The count is read once per device and cached.
 int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices && (n = cached[dev].load(std::memory_order_relaxed)) > 0)
+    return n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n < 1)
     return 256;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -128,7 +135,7 @@ struct DecodePlan {
   std::vector<uint8_t> mult;  // [num_layers * Hkv] of the call: heavy-head multiplier
   int max_chunks;
   int64_t entries;
-  size_t o_bytes, ml_bytes, cnt_bytes, total;
+  size_t o_bytes, ml_bytes, cnt_bytes, arrive_bytes, total;
 };
 
 // Split planning.  With chunk_tokens > 0 (or on the general kernel) every
@@ -192,7 +199,8 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
   p.o_bytes = size_t(align256(p.entries * G * c->head_dim * 4));
   p.ml_bytes = size_t(align256(p.entries * G * 2 * 4));
   p.cnt_bytes = size_t(align256(int64_t(nl) * B * Hkv * 4));
-  p.total = p.o_bytes + p.ml_bytes + p.cnt_bytes;
+  p.arrive_bytes = size_t(align256(int64_t(nl) * B * Hkv * 4));
+  p.total = p.o_bytes + p.ml_bytes + p.cnt_bytes + p.arrive_bytes;
   return p;
 }
 
@@ -342,8 +350,25 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
       return bx > by;
     });
 
+    // Matrix-core launches are per visual format: each launch takes the pairs
+    // whose visual K/V widths are one (kb, vb) combination, and the all-bf16
+    // (protected) pairs ride along with the first such group.
+    std::vector<int> fkey(nlh);
+    std::vector<int> groups;  // distinct keys kb * 32 + vb, in slot order
+    for (int i = 0; i < nlh; ++i) {
+      const int glh = order[i], l = layer_begin + glh / Hkv, h = glh % Hkv;
+      fkey[i] = bits_of(cfg, l, h, 0) * 32 + bits_of(cfg, l, h, 1);
+    }
+    for (int i = 0; i < nlh; ++i)
+      if (fkey[i] != 16 * 32 + 16 && std::find(groups.begin(), groups.end(), fkey[i]) == groups.end())
+        groups.push_back(fkey[i]);
+    if (groups.empty()) groups.push_back(16 * 32 + 16);
+    if (!use_mfma) groups.assign(1, -1);  // the general kernel takes every format
+
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const hipStream_t hs = static_cast<hipStream_t>(stream);
+    std::vector<int> sel;
+    sel.reserve(nlh);
     for (int s0 = 0; s0 < cfg->batch; s0 += kMaxSeq) {
       const int ns_l = std::min(kMaxSeq, cfg->batch - s0);
       DecodeArgs a;
@@ -355,6 +380,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
       a.ws_o = reinterpret_cast<float*>(ws);
       a.ws_ml = reinterpret_cast<float*>(ws + plan.o_bytes);
       a.ws_cnt = reinterpret_cast<int32_t*>(ws + plan.o_bytes + plan.ml_bytes);
+      a.ws_arrive = reinterpret_cast<int32_t*>(ws + plan.o_bytes + plan.ml_bytes + plan.cnt_bytes);
       a.qscale = sm_scale * 1.4426950408889634f;
       a.Rvis = lay.Rvis;
       a.D = lay.D;
@@ -377,26 +403,33 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
         a.nxcum[i + 1] = a.nxcum[i] + plan.nx[s];
       }
       a.n_seq = ns_l;
-      for (int lh0 = 0; lh0 < nlh; lh0 += kMaxLH) {
-        const int nlh_l = std::min(kMaxLH, nlh - lh0);
-        a.n_lh = nlh_l;
-        for (int i = 0; i < nlh_l; ++i) {
-          const int glh = order[lh0 + i];  // layer-local * Hkv + head
-          const int l = layer_begin + glh / Hkv, h = glh % Hkv;
-          for (int X = 0; X < 2; ++X) {
-            a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * Hkv + h) * 2 + X] / 256);
-            a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
+      for (size_t gi = 0; gi < groups.size(); ++gi) {
+        const int key = groups[gi];
+        sel.clear();
+        for (int i = 0; i < nlh; ++i)
+          if (key < 0 || fkey[i] == key || (gi == 0 && fkey[i] == 16 * 32 + 16)) sel.push_back(i);
+        for (size_t k0 = 0; k0 < sel.size(); k0 += kMaxLH) {
+          const int nlh_l = int(std::min<size_t>(kMaxLH, sel.size() - k0));
+          a.n_lh = nlh_l;
+          for (int i = 0; i < nlh_l; ++i) {
+            const int glh = order[sel[k0 + i]];  // layer-local * Hkv + head
+            const int l = layer_begin + glh / Hkv, h = glh % Hkv;
+            for (int X = 0; X < 2; ++X) {
+              a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * Hkv + h) * 2 + X] / 256);
+              a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
+            }
+            a.lh_glob[i] = uint16_t(glh);
+            a.mult[i] = plan.mult[glh];
+            a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
           }
-          a.lh_glob[i] = uint16_t(glh);
-          a.mult[i] = plan.mult[glh];
-          a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
+          const hipError_t e = use_mfma ? launch_decode_mfma(a, key / 32, key % 32, hs)
+                                        : launch_decode_simple(a, ns_l, hs);
+          if (e != hipSuccess) return KVQ_ERR_HIP;
         }
-        const hipError_t e = use_mfma ? launch_decode_mfma(a, ns_l, hs)
-                                      : launch_decode_simple(a, ns_l, hs);
-        if (e != hipSuccess) return KVQ_ERR_HIP;
       }
-      // with one workgroup per (layer, seq, head) the split kernel wrote the output
-      if (plan.max_chunks > 1 &&
+      // the general kernel leaves split partials for a separate merge; the
+      // matrix-core kernel merges them itself
+      if (!use_mfma && plan.max_chunks > 1 &&
           launch_decode_merge(a, num_layers, ns_l, hs) != hipSuccess)
         return KVQ_ERR_HIP;
     }

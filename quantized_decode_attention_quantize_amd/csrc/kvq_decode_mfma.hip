@@ -69,13 +69,36 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
   return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) |
          (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
 }
+// Lane l's value from lane l^1 / l^2 (quad permutes; no lane is out of
+// bounds, bound_ctrl lets the move fold into the consuming add).
 __device__ inline float dpp_xor1(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
-                                                            0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1,
+                                                               0xF, 0xF, true));
 }
 __device__ inline float dpp_xor2(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
-                                                            0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E,
+                                                               0xF, 0xF, true));
+}
+// Max over lanes {l, l^16, l^32, l^48} (the four row quarters of one MFMA
+// column) with the gfx950 cross-row swaps instead of LDS permutes.
+__device__ inline float max_over_quarters(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m = fmaxf(__builtin_bit_cast(float, unsigned(r32[0])),
+                        __builtin_bit_cast(float, unsigned(r32[1])));
+  const unsigned w = __builtin_bit_cast(unsigned, m);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__builtin_bit_cast(float, unsigned(r16[0])), __builtin_bit_cast(float, unsigned(r16[1])));
+}
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// f16 pair (round to nearest even) of lo * slo, hi * shi.  Written as fmas
+// with a zero addend so each half is one mixed-precision fma into its half
+// of the result register.
+__device__ inline uint32_t pack_f16_mul(float lo, float slo, float hi, float shi) {
+  f16x2 r;
+  r.x = (_Float16)__builtin_fmaf(lo, slo, 0.0f);
+  r.y = (_Float16)__builtin_fmaf(hi, shi, 0.0f);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -149,8 +172,22 @@ struct VPair {
   static constexpr int N = B == 16 ? D / 32 : B == 8 ? D / 64 : 2;
   uint32_t w[N];
 };
+// Bytes per lane per token of a V row (one of 16 lane columns).
 template <int D, int B>
-__device__ inline VPair<D, B> vpair_words(const uint32_t* a, const uint32_t* b) {
+__device__ constexpr int v_lane_bytes() { return (B == 16 ? 2 * D : D * B / 8) / 16; }
+// Byte selector that merges this lane's V slice of two tokens (a low, b
+// high) into one pair word when the slice is 1 or 2 bytes wide and sits at
+// byte offset o of the dword it was read in (o = 0 when loaded on its own).
+template <int D, int B>
+__device__ inline uint32_t v_pair_selector(int o) {
+  constexpr int VBY = v_lane_bytes<D, B>();
+  if constexpr (VBY == 2)
+    return uint32_t(o) | uint32_t(o + 1) << 8 | uint32_t(o + 4) << 16 | uint32_t(o + 5) << 24;
+  else
+    return uint32_t(o) | 0x0Cu << 8 | uint32_t(o + 4) << 16 | 0x0Cu << 24;  // 0x0C: zero byte
+}
+template <int D, int B>
+__device__ inline VPair<D, B> vpair_words(const uint32_t* a, const uint32_t* b, uint32_t vsel) {
   VPair<D, B> r;
   if constexpr (B == 16) {  // bf16 elements 2i, 2i+1 of each token
 #pragma unroll
@@ -160,11 +197,11 @@ __device__ inline VPair<D, B> vpair_words(const uint32_t* a, const uint32_t* b) 
   } else if constexpr (B == 8) {
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) r.w[i] = a[i];
-  } else if constexpr (B == 4) {
+  } else if constexpr (B == 4 && v_lane_bytes<D, B>() == 4) {
     r.w[0] = __builtin_amdgcn_perm(b[0], a[0], 0x05040100u);  // nibbles 0..3 of a | b
     r.w[1] = __builtin_amdgcn_perm(b[0], a[0], 0x07060302u);  // nibbles 4..7
-  } else {
-    r.w[0] = (a[0] & 0xFFFFu) | (b[0] << 16);
+  } else {  // 1- or 2-byte slices: one selector merge
+    r.w[0] = __builtin_amdgcn_perm(b[0], a[0], vsel);
     r.w[1] = r.w[0] >> 8;
   }
   return r;
@@ -223,9 +260,9 @@ struct Ctx {
 };
 
 // Build Q' for k format KB: per k-step, 8 slots of this lane's column.
-// Returns the sum of q over the column's (head, group), times qscale: each
-// lane's slots cover its quarter of the head dim exactly once, so a sum over
-// the four quarters completes it.
+// Returns the sum of q over the column's (head, group), times 2^-24 (the unit
+// of the code products): each lane's slots cover its quarter of the head dim
+// exactly once, so a sum over the four quarters completes it.
 template <int D, int NG, int KB>
 __device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
   constexpr int g = D / NG;
@@ -252,7 +289,7 @@ __device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
   }
   qs += __shfl_xor(qs, 16);
   qs += __shfl_xor(qs, 32);
-  return qs * c.qscale;
+  return qs * 5.9604644775390625e-08f;  // * 2^-24, exact
 }
 
 template <int NBYTES>
@@ -336,12 +373,60 @@ __device__ inline void load_step(const uint8_t* kp, const uint8_t* kmp, const ui
   }
 }
 
+// exp, P operand and p.v of one step, given the scaled scores and the
+// (possibly just raised) running max.
+template <int D, int NG, int KB, int VB>
+__device__ inline void finish_step(WaveState<D>& ws, const Step<D, KB, VB>& st,
+                                   const float (&sc)[8], float cs, uint32_t vsel) {
+  constexpr int NB = D / 16;
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], cs, -ws.m));
+    ws.l += p[e];
+  }
+
+  u32x4 pa, pb;  // A operand (and the bf16 low part for bf16 V)
+  if constexpr (VB < 16) {
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
+      pa[e2] = pack_f16_mul(p0, f16lo(st.vm[2 * e2]), p1, f16lo(st.vm[2 * e2 + 1]));
+      ws.mt = __builtin_fmaf(p0, f16hi(st.vm[2 * e2]), ws.mt);
+      ws.mt = __builtin_fmaf(p1, f16hi(st.vm[2 * e2 + 1]), ws.mt);
+    }
+  } else {
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
+      pa[e2] = pack_bf16(p0, p1);
+      pb[e2] = pack_bf16(p0 - bf16f(pa[e2] & 0xFFFFu), p1 - bf16f(pa[e2] >> 16));
+    }
+  }
+  VPair<D, VB> pw[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2)
+    pw[e2] = vpair_words<D, VB>(st.v[2 * e2], st.v[2 * e2 + 1], vsel);
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) {
+    u32x4 b;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) b[e2] = v_block<D, VB>(pw[e2], st.v[2 * e2], st.v[2 * e2 + 1], mb);
+    if constexpr (VB == 16) {
+      ws.o[mb] = mfma_bf16(pa, b, ws.o[mb]);
+      ws.o[mb] = mfma_bf16(pb, b, ws.o[mb]);
+    } else {
+      ws.o[mb] = mfma_f16(pa, b, ws.o[mb]);
+    }
+  }
+}
+
 // q.k, softmax and p.v of one 32-token step.  MASKED: the step may run past
-// the segment end (rows_left < 32).
+// the segment end (rows_left < 32).  vsel: see v_pair_selector.
 template <int D, int NG, int KB, int VB, bool MASKED>
 __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D, KB, VB>& st,
-                                    const u32x4 (&qop)[D / 32], float qs, float c24,
-                                    int rows_left) {
+                                    const u32x4 (&qop)[D / 32], float qsr, float c24,
+                                    int rows_left, uint32_t vsel) {
   constexpr int KS = D / 32;
   constexpr int NB = D / 16;
   f32x4 acc[2];
@@ -354,13 +439,17 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
       acc[tau] = KB == 16 ? mfma_bf16(a, qop[s], acc[tau]) : mfma_f16(a, qop[s], acc[tau]);
     }
   }
+  // scaled scores v: score (log2 units) = v * cs.  Quantised K: v = sc * acc +
+  // mn * qsr with acc in units of 2^-24 (see build_q), so cs = 2^24 * qscale
+  // and qsr = 2^-24 * sum(q over the group); bf16 K: v = acc, cs = qscale.
+  const float cs = KB < 16 ? c24 : c.qscale;
   float sc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float a = acc[e >> 2][e & 3];
     float part;
-    if constexpr (KB < 16) part = a * (f16lo(st.km[e]) * c24) + f16hi(st.km[e]) * qs;
-    else part = a * c.qscale;
+    if constexpr (KB < 16) part = __builtin_fmaf(f16lo(st.km[e]), a, f16hi(st.km[e]) * qsr);
+    else part = a;
     if constexpr (NG >= 2) part += dpp_xor1(part);
     if constexpr (NG >= 4) part += dpp_xor2(part);
     if constexpr (MASKED) {
@@ -370,11 +459,13 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
     sc[e] = part;
   }
 
-  // online softmax with a lazy running max
+  // online softmax with a lazy running max: the accumulators are rescaled
+  // only when a column's max grows by more than kLazy, so p <= 2^kLazy.  The
+  // rare rescaling path carries its own copy of the p.v tail, which keeps the
+  // accumulators in place on the common path.
   float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                    fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_over_quarters(mx) * cs;
   const float mnew = fmaxf(ws.m, mx);
   if (__builtin_amdgcn_ballot_w64(mnew > ws.m + kLazy) != 0) {
     const float alpha = __builtin_amdgcn_exp2f(ws.m - mnew);  // 0 on the first step
@@ -389,44 +480,7 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
       for (int i = 0; i < 4; ++i) ws.o[mb][i] *= ar[i];
     ws.m = mnew;
   }
-  float p[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    p[e] = __builtin_amdgcn_exp2f(sc[e] - ws.m);
-    ws.l += p[e];
-  }
-
-  u32x4 pa, pb;  // A operand (and the bf16 low part for bf16 V)
-  if constexpr (VB < 16) {
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
-      pa[e2] = pack_f16(p0 * f16lo(st.vm[2 * e2]), p1 * f16lo(st.vm[2 * e2 + 1]));
-      ws.mt += p0 * f16hi(st.vm[2 * e2]) + p1 * f16hi(st.vm[2 * e2 + 1]);
-    }
-  } else {
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float p0 = p[2 * e2], p1 = p[2 * e2 + 1];
-      pa[e2] = pack_bf16(p0, p1);
-      pb[e2] = pack_bf16(p0 - bf16f(pa[e2] & 0xFFFFu), p1 - bf16f(pa[e2] >> 16));
-    }
-  }
-  VPair<D, VB> pw[4];
-#pragma unroll
-  for (int e2 = 0; e2 < 4; ++e2) pw[e2] = vpair_words<D, VB>(st.v[2 * e2], st.v[2 * e2 + 1]);
-#pragma unroll
-  for (int mb = 0; mb < NB; ++mb) {
-    u32x4 b;
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) b[e2] = v_block<D, VB>(pw[e2], st.v[2 * e2], st.v[2 * e2 + 1], mb);
-    if constexpr (VB == 16) {
-      ws.o[mb] = mfma_bf16(pa, b, ws.o[mb]);
-      ws.o[mb] = mfma_bf16(pb, b, ws.o[mb]);
-    } else {
-      ws.o[mb] = mfma_f16(pa, b, ws.o[mb]);
-    }
-  }
+  finish_step<D, NG, KB, VB>(ws, st, sc, cs, vsel);
 }
 
 // ---------------------------------------------------------------------------
@@ -471,19 +525,50 @@ struct Stage {
 // Wave-private LDS stage large enough for every quantised format.
 constexpr int kStageBytes = 2 * (32 * 128 + 32 * 16);  // INT8 K and V at D=128, NG=4
 
-// Lane piece of tile rows [0, 32) of step `step`; rows at or past rows_total
-// are clamped to the segment's last row (those lanes re-read cached bytes).
+// Buffer resource over `bytes` bytes from `base` (raw, unswizzled): loads
+// through it take a per-lane 32-bit offset plus a wave-uniform offset, so a
+// step's loads need no per-lane address arithmetic.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           int(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
+                                           0x00020000);
+}
+template <int NBYTES>
+__device__ inline void buf_load(Rsrc r, uint32_t voff, uint32_t soff, uint32_t* out) {
+  if constexpr (NBYTES >= 16) {
+#pragma unroll
+    for (int i = 0; i < NBYTES / 16; ++i) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, 0);
+      out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
+    }
+  } else if constexpr (NBYTES == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    out[0] = v[0]; out[1] = v[1];
+  } else if constexpr (NBYTES == 4) {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  } else {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  }
+}
+
+// The four planes of one segment (K codes, K meta, V codes, V meta).
+struct SegPlanes {
+  Rsrc k, km, v, vm;
+};
+
+// Lane piece of tile rows [0, 32) of full step `step` (wave-uniform): row
+// l/2, half l%2 of every plane's tile.
 template <int D, int NG, int KB, int VB>
-__device__ inline void stage_load(const uint8_t* kp, const uint8_t* kmp, const uint8_t* vp,
-                                  const uint8_t* vmp, int step, int rows_total, int lane,
+__device__ inline void stage_load(const SegPlanes& pl, int step, int lane,
                                   Stage<D, NG, KB, VB>& st) {
   using S = Stage<D, NG, KB, VB>;
-  const int row = min(step * 32 + (lane >> 1), rows_total - 1);
-  const int half = lane & 1;
-  load_bytes<S::KP>(kp + row * S::KR + half * S::KP, st.k);
-  load_bytes<S::MP>(kmp + row * S::MR + half * S::MP, st.km);
-  load_bytes<S::VP>(vp + row * S::VR + half * S::VP, st.v);
-  load_bytes<S::MP>(vmp + row * S::MR + half * S::MP, st.vm);
+  const uint32_t row = uint32_t(lane >> 1), half = uint32_t(lane & 1);
+  const uint32_t r0 = uint32_t(step) * 32u;
+  buf_load<S::KP>(pl.k, row * S::KR + half * S::KP, r0 * S::KR, st.k);
+  buf_load<S::MP>(pl.km, row * S::MR + half * S::MP, r0 * S::MR, st.km);
+  buf_load<S::VP>(pl.v, row * S::VR + half * S::VP, r0 * S::VR, st.v);
+  buf_load<S::MP>(pl.vm, row * S::MR + half * S::MP, r0 * S::MR, st.vm);
 }
 
 // Lanes exchange data through the stage, so the compiler must not move one
@@ -515,7 +600,11 @@ __device__ inline void stage_get(const uint8_t* lds, const Ctx& c, Step<D, KB, V
     const int r = 16 * (e >> 2) + 4 * c.jq + (e & 3);
     st.km[e] = *reinterpret_cast<const uint32_t*>(lds + S::kOffKM + r * S::MR + gj * 4);
     st.vm[e] = *reinterpret_cast<const uint32_t*>(lds + S::kOffVM + r * S::MR + gj * 4);
-    load_bytes<VBY>(lds + S::kOffV + r * S::VR + c.n * VBY, st.v[e]);
+    if constexpr (VBY <= 2)  // the aligned dword holding the slice; see v_pair_selector
+      st.v[e][0] = *reinterpret_cast<const uint32_t*>(lds + S::kOffV + r * S::VR +
+                                                     ((c.n * VBY) & ~3));
+    else
+      load_bytes<VBY>(lds + S::kOffV + r * S::VR + c.n * VBY, st.v[e]);
   }
 }
 
@@ -531,44 +620,68 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   const uint8_t* kmp = c.kmeta + row0 * MR;
   const uint8_t* vmp = c.vmeta + row0 * MR;
 
+  const int rows = x1 - x0;
+  const int nfull = rows / 32;
+  constexpr int VBY = Fmt<D, VB>::kVBytes;
+  // Quantised steps are small (~14 VGPRs per lane): two of them fly through
+  // registers into the wave's LDS stage while earlier ones compute; their
+  // first loads are issued before Q' is built so the latencies overlap.
+  // bf16 steps carry 64 VGPRs of data and load straight into operands.
+  constexpr bool kStaged = KB < 16 && VB < 16;
+  using S = Stage<D, NG, KB, VB>;
+  // steps in flight per wave: two, unless a step's lane piece is large (INT8)
+  constexpr int kDepth = S::KP + S::VP <= 48 ? 2 : 1;
+  S ga, gb;
+  SegPlanes pl;
+  if constexpr (kStaged) {
+    pl.k = make_rsrc(kp, int64_t(rows) * KR);
+    pl.km = make_rsrc(kmp, int64_t(rows) * MR);
+    pl.v = make_rsrc(vp, int64_t(rows) * VR);
+    pl.vm = make_rsrc(vmp, int64_t(rows) * MR);
+    if (nfull > 0) {
+      stage_load<D, NG, KB, VB>(pl, 0, c.lane, ga);
+      if constexpr (kDepth == 2) stage_load<D, NG, KB, VB>(pl, min(1, nfull - 1), c.lane, gb);
+    }
+  }
+
   u32x4 qop[D / 32];
-  const float qs = build_q<D, NG, KB>(c, qop);
+  const float qsr = build_q<D, NG, KB>(c, qop);
   const float c24 = c.qscale * 16777216.0f;  // 2^24 * qscale
 
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= v_inflation<D, VB>(mb);
 
-  const int rows = x1 - x0;
-  const int nfull = rows / 32;
   Offs<D, NG, KB, VB> of;
   of.full(c);
-  // Quantised steps are small (~32 VGPRs of raw data): double-buffer them so
-  // the loads of step i+1 fly while step i computes.  bf16 steps carry 64
-  // VGPRs of data and run single-buffered.
-  constexpr bool kStaged = KB < 16 && VB < 16;
   Step<D, KB, VB> sa;
+  const uint32_t vsel_mem = v_pair_selector<D, VB>(0);
   int i = 0;
   if constexpr (kStaged) {
-    // Two register stages in flight; loads inside the loop are unconditional
-    // (clamped to the last full step) so the wait counts stay exact.
-    if (nfull > 0) {
-      Stage<D, NG, KB, VB> ga, gb;
-      stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, 0, 32 * nfull, c.lane, ga);
-      stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, min(1, nfull - 1), 32 * nfull, c.lane, gb);
+    const uint32_t vsel = v_pair_selector<D, VB>((c.n * VBY) & 3);
+    // loads inside the loop are unconditional (clamped to the last full step)
+    // so the wait counts stay exact
+    if (kDepth == 1) {
+      for (; i < nfull; ++i) {
+        stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
+        stage_load<D, NG, KB, VB>(pl, min(i + 1, nfull - 1), c.lane, ga);
+        stage_get<D, NG, KB, VB>(c.stage, c, sa);
+        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
+      }
+    } else if (nfull > 0) {
       for (; i + 1 < nfull; i += 2) {
         stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
-        stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, min(i + 2, nfull - 1), 32 * nfull, c.lane, ga);
+        stage_load<D, NG, KB, VB>(pl, min(i + 2, nfull - 1), c.lane, ga);
         stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
         stage_put<D, NG, KB, VB>(c.stage, c.lane, gb);
-        stage_load<D, NG, KB, VB>(kp, kmp, vp, vmp, min(i + 3, nfull - 1), 32 * nfull, c.lane, gb);
+        stage_load<D, NG, KB, VB>(pl, min(i + 3, nfull - 1), c.lane, gb);
         stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
       }
       if (i < nfull) {  // odd step count: the last full step sits in ga
         stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
         stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
         ++i;
       }
     }
@@ -577,7 +690,7 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
       const int64_t o = int64_t(i) * 32;
       load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of,
                                       sa);
-      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qs, c24, 32);
+      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel_mem);
     }
   }
   const int tail = rows - 32 * nfull;
@@ -585,43 +698,51 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     const int64_t o = int64_t(nfull) * 32;
     of.clamped(c, tail);
     load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of, sa);
-    compute_step<D, NG, KB, VB, true>(c, ws, sa, qop, qs, c24, tail);
+    compute_step<D, NG, KB, VB, true>(c, ws, sa, qop, qsr, c24, tail, vsel_mem);
   }
 
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= 1.0f / v_inflation<D, VB>(mb);
 }
 
-template <int D, int NG>
-__device__ void dispatch_visual(int kb, int vb, const Ctx& c, WaveState<D>& st, int x0, int x1,
-                                int64_t row0) {
-#define KVQ_VIS(K, V) \
-  if (kb == K && vb == V) { run_segment<D, NG, K, V>(c, st, x0, x1, row0, true); return; }
-  KVQ_VIS(2, 2) KVQ_VIS(2, 4) KVQ_VIS(2, 8) KVQ_VIS(2, 16)
-  KVQ_VIS(4, 2) KVQ_VIS(4, 4) KVQ_VIS(4, 8) KVQ_VIS(4, 16)
-  KVQ_VIS(8, 2) KVQ_VIS(8, 4) KVQ_VIS(8, 8) KVQ_VIS(8, 16)
-  KVQ_VIS(16, 2) KVQ_VIS(16, 4) KVQ_VIS(16, 8) KVQ_VIS(16, 16)
-#undef KVQ_VIS
-}
-
-template <int D, int NG>
+// One instance per (D, groups per row, visual K/V widths): a launch holds
+// only (layer, head) pairs whose visual rows have widths (KB, VB) or are bf16
+// (protected heads), so each instance carries two row paths -- the quantised
+// one and the bf16 one that text rows use anyway -- and nothing else.
+template <int D, int NG, int KB, int VB>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NB = D / 16;
   constexpr int g = D / NG;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+
+  // The per-slot / per-sequence tables are indexed by values computed here, so
+  // reading them from the argument segment would chain a dozen dependent
+  // memory round trips.  One cooperative 16-byte copy puts the whole argument
+  // block in LDS; every table lookup below is then an LDS read.
+  static_assert(sizeof(DecodeArgs) % 16 == 0, "argument block copied in 16-byte pieces");
+  constexpr int kArgVec = int(sizeof(DecodeArgs) / 16);
+  __shared__ uint4 args_lds[kArgVec];
+  {
+    const uint4* src = (const uint4*)(__builtin_amdgcn_kernarg_segment_ptr());
+    for (int i = threadIdx.x; i < kArgVec; i += 256) args_lds[i] = src[i];
+  }
+  __syncthreads();
+  const DecodeArgs& t = *reinterpret_cast<const DecodeArgs*>(args_lds);
+
   int slot, sl, x;
-  decode_block(a, blockIdx.x, a.n_seq, slot, sl, x);
-  const int lh = a.lh_glob[slot];
+  decode_block(t, blockIdx.x, a.n_seq, slot, sl, x);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  sl = __builtin_amdgcn_readfirstlane(sl);
+  x = __builtin_amdgcn_readfirstlane(x);
+  const int lh = __builtin_amdgcn_readfirstlane(int(t.lh_glob[slot]));
   const int l_local = lh / a.Hkv, h = lh % a.Hkv;
   const int s = a.seq_off + sl;
-  const int nxs = a.nx[sl] * a.mult[slot];  // workgroups of this (layer, seq, head)
-  const int cap = a.cap[sl];
-  int len = a.seq_lens[s];
-  len = len < 1 ? 1 : (len > cap ? cap : len);
+  const int nxs = __builtin_amdgcn_readfirstlane(t.nx[sl] * int(t.mult[slot]));
+  const int cap = __builtin_amdgcn_readfirstlane(t.cap[sl]);
   const int G = a.G;
 
-  __shared__ uint16_t q_lds[kMaxGroupRatio * D];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kMaxGroupRatio * D];
   __shared__ float ml_lds[kWaves][kMaxGroupRatio][2];
   // wave stages during the loop; per-wave outputs for the final combine after it
   constexpr int kOBytes = kWaves * kMaxGroupRatio * D * 4;
@@ -629,17 +750,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnion];
   float(*o_lds)[kMaxGroupRatio][D] = reinterpret_cast<float(*)[kMaxGroupRatio][D]>(big_lds);
 
+  // the G query rows of this KV head: G * D bf16, 16 bytes per thread
+  // (G * D / 8 <= 256 threads; rows start 16-byte aligned since D * 2 >= 128)
   const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += 256) q_lds[i] = qp[i];
+  if (int(threadIdx.x) < G * D / 8)
+    reinterpret_cast<uint4*>(q_lds)[threadIdx.x] = reinterpret_cast<const uint4*>(qp)[threadIdx.x];
+  int len = a.seq_lens[s];
+  len = len < 1 ? 1 : (len > cap ? cap : len);
   __syncthreads();
 
+  const int kbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][0]));
+  const int vbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][1]));
   Ctx c;
   {
-    const int kb = a.bits[slot][0], vb = a.bits[slot][1];
-    c.kvis = a.cache + uint64_t(a.base256[slot][0]) * 256u;
+    const int kb = kbits, vb = vbits;
+    c.kvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][0])) * 256u;
     c.kmeta = c.kvis + meta_plane_offset(a.Rvis, D, kb);
     c.ktxt = c.kvis + txt_plane_offset(a.Rvis, D, g, kb);
-    c.vvis = a.cache + uint64_t(a.base256[slot][1]) * 256u;
+    c.vvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][1])) * 256u;
     c.vmeta = c.vvis + meta_plane_offset(a.Rvis, D, vb);
     c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
   }
@@ -661,15 +789,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   int wa, wb;
   wave_range(x, wave, nxs, len, a.chunk, kWaves, wa, wb);
   if (wa < wb) {
-    const int vb = a.vb[sl], ve = a.ve[sl];
-    const int64_t vrow0 = a.vrow0[sl], trow0 = a.trow0[sl];
-    const int kb = a.bits[slot][0], vbits = a.bits[slot][1];
+    const int vb = __builtin_amdgcn_readfirstlane(t.vb[sl]);
+    const int ve = __builtin_amdgcn_readfirstlane(t.ve[sl]);
+    const int64_t vrow0 = __builtin_amdgcn_readfirstlane(t.vrow0[sl]);
+    const int64_t trow0 = __builtin_amdgcn_readfirstlane(t.trow0[sl]);
     // text prefix [0, vb), visual [vb, ve), text suffix [ve, cap)
     int x0 = wa, x1 = min(wb, vb);
     if (x0 < x1) run_segment<D, NG, 16, 16>(c, st, x0, x1, trow0 + x0, false);
     x0 = max(wa, vb);
     x1 = min(wb, ve);
-    if (x0 < x1) dispatch_visual<D, NG>(kb, vbits, c, st, x0, x1, vrow0 + (x0 - vb));
+    if (x0 < x1) {
+      if (KB == 16 && VB == 16) {
+        run_segment<D, NG, 16, 16>(c, st, x0, x1, vrow0 + (x0 - vb), true);
+      } else if (kbits == KB && vbits == VB) {
+        run_segment<D, NG, KB, VB>(c, st, x0, x1, vrow0 + (x0 - vb), true);
+      } else {  // bf16 visual rows of a protected head
+        run_segment<D, NG, 16, 16>(c, st, x0, x1, vrow0 + (x0 - vb), true);
+      }
+    }
     x0 = max(wa, ve);
     x1 = wb;
     if (x0 < x1) run_segment<D, NG, 16, 16>(c, st, x0, x1, trow0 + (x0 - (ve - vb)), false);
@@ -703,9 +840,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 
   // ---- combine waves; write the workgroup's partial (or the final output) ----
   const bool single = nxs == 1;
+  const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
   const int64_t pidx = partial_index(l_local, s, h, x, a.B, a.Hkv, a.max_chunks);
-  if (x == 0 && threadIdx.x == 0)
-    a.ws_cnt[(int64_t(l_local) * a.B + s) * a.Hkv + h] = nxs;
+  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int j = i / D, d = i % D;
     float M = -INFINITY;
@@ -723,36 +860,125 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     }
     const float o = L > 0.0f ? acc / L : 0.0f;  // L == 0: no token in this workgroup
     if (single) {
-      a.out[((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G + j) * D + d] =
-          __builtin_bit_cast(uint16_t, (__bf16)o);
+      outp[i] = __builtin_bit_cast(uint16_t, (__bf16)o);
     } else {
-      a.ws_o[(pidx * G + j) * D + d] = o;
+      // write-through (system-coherent) stores: the merging workgroup may sit
+      // on another XCD and reads them past its own caches
+      __hip_atomic_store(&a.ws_o[(pidx * G + j) * D + d], o, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
       if (d == 0) {
-        a.ws_ml[(pidx * G + j) * 2 + 0] = M;
-        a.ws_ml[(pidx * G + j) * 2 + 1] = L;
+        __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], M, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 1], L, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
+  if (single) return;
+
+  // ---- split-K merge by the last workgroup of this (layer, seq, head) -------
+  // Each workgroup waits until its partial has reached memory, then counts
+  // itself in; the one that completes the count merges all partials with the
+  // log-sum-exp rule (reading them past the caches) and resets the counter to
+  // zero for the next call.  No cache write-back or invalidation is needed.
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(&a.ws_arrive[entry], 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_SYSTEM) == nxs - 1;
+  __syncthreads();
+  if (!is_last) return;
+  const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
+  // (m, l) of every partial and head, staged in LDS (the o_lds storage) when
+  // they fit, else read from memory each time
+  const float* gml = a.ws_ml + p0 * G * 2;
+  float* pml = &o_lds[0][0][0];
+  const bool staged = nxs * G * 2 <= kOBytes / 4;
+  if (staged) {
+    for (int i = threadIdx.x; i < nxs * G * 2; i += 256)
+      pml[i] = __hip_atomic_load(&gml[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+  }
+  auto ml_at = [&](int k) {
+    return staged ? pml[k] : __hip_atomic_load(&gml[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  };
+  for (int i = threadIdx.x; i < G * D; i += 256) {
+    const int j = i / D, d = i % D;
+    float M = -INFINITY;
+    for (int cx = 0; cx < nxs; ++cx)
+      if (ml_at((cx * G + j) * 2 + 1) > 0.0f) M = fmaxf(M, ml_at((cx * G + j) * 2));
+    float W = 0.0f, acc = 0.0f;
+    for (int cx = 0; cx < nxs; ++cx) {
+      const float lx = ml_at((cx * G + j) * 2 + 1);
+      if (!(lx > 0.0f)) continue;  // a workgroup without tokens
+      const float wgt = lx * __builtin_amdgcn_exp2f(ml_at((cx * G + j) * 2) - M);
+      W += wgt;
+      acc += wgt * __hip_atomic_load(&a.ws_o[((p0 + cx) * G + j) * D + d], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    outp[i] = __builtin_bit_cast(uint16_t, (__bf16)(acc / W));
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&a.ws_arrive[entry], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace
 
+#if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 0
 bool mfma_supported(int D, int g, int G) {
   return (D == 64 || D == 128) && G * (D / g) <= 16;
 }
+#endif
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int n_seq_launch, hipStream_t stream) {
-  (void)n_seq_launch;  // a.n_seq
-  const dim3 grid(a.nxcum[a.n_seq] * a.mcum[a.n_lh], 1, 1);  // compact block list
-  const int NG = a.D / a.g;
-#define KVQ_LAUNCH(DD, NN)                                                           \
-  if (a.D == DD && NG == NN) {                                                       \
-    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN>), grid, dim3(256), 0, stream, a); \
-    return hipGetLastError();                                                        \
+// The instances are spread over parts so a build can compile them in
+// parallel (-DKVQ_MFMA_PART=0..4, one object each); without the macro one
+// object holds every part.
+#define KVQ_LAUNCH(DD, NN, K, V)                                                           \
+  if (kb == K && vb == V) {                                                                \
+    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN, K, V>), grid, dim3(256), 0, stream, a); \
+    return hipGetLastError();                                                              \
   }
-  KVQ_LAUNCH(128, 1) KVQ_LAUNCH(128, 2) KVQ_LAUNCH(128, 4) KVQ_LAUNCH(64, 1) KVQ_LAUNCH(64, 2)
+#define KVQ_PART_FN(DD, NN)                                                                 \
+  hipError_t launch_decode_mfma_##DD##_##NN(const DecodeArgs& a, int kb, int vb,           \
+                                            hipStream_t stream) {                           \
+    const dim3 grid(a.nxcum[a.n_seq] * a.mcum[a.n_lh], 1, 1); /* compact block list */    \
+    KVQ_LAUNCH(DD, NN, 2, 2) KVQ_LAUNCH(DD, NN, 2, 4) KVQ_LAUNCH(DD, NN, 2, 8)              \
+    KVQ_LAUNCH(DD, NN, 2, 16) KVQ_LAUNCH(DD, NN, 4, 2) KVQ_LAUNCH(DD, NN, 4, 4)             \
+    KVQ_LAUNCH(DD, NN, 4, 8) KVQ_LAUNCH(DD, NN, 4, 16) KVQ_LAUNCH(DD, NN, 8, 2)             \
+    KVQ_LAUNCH(DD, NN, 8, 4) KVQ_LAUNCH(DD, NN, 8, 8) KVQ_LAUNCH(DD, NN, 8, 16)             \
+    KVQ_LAUNCH(DD, NN, 16, 2) KVQ_LAUNCH(DD, NN, 16, 4) KVQ_LAUNCH(DD, NN, 16, 8)           \
+    KVQ_LAUNCH(DD, NN, 16, 16)                                                              \
+    return hipErrorInvalidValue;                                                            \
+  }
+#if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 0
+KVQ_PART_FN(128, 1)
+#endif
+#if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 1
+KVQ_PART_FN(128, 2)
+#endif
+#if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 2
+KVQ_PART_FN(128, 4)
+#endif
+#if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 3
+KVQ_PART_FN(64, 1)
+#endif
+#if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 4
+KVQ_PART_FN(64, 2)
+#endif
+#undef KVQ_PART_FN
 #undef KVQ_LAUNCH
+
+#if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 0
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kb, int vb, hipStream_t stream) {
+  const int NG = a.D / a.g;
+  if (a.D == 128 && NG == 1) return launch_decode_mfma_128_1(a, kb, vb, stream);
+  if (a.D == 128 && NG == 2) return launch_decode_mfma_128_2(a, kb, vb, stream);
+  if (a.D == 128 && NG == 4) return launch_decode_mfma_128_4(a, kb, vb, stream);
+  if (a.D == 64 && NG == 1) return launch_decode_mfma_64_1(a, kb, vb, stream);
+  if (a.D == 64 && NG == 2) return launch_decode_mfma_64_2(a, kb, vb, stream);
   return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace kvq

@@ -53,6 +53,8 @@ struct DecodeArgs {
   float* ws_o;              // [entries][G][D] normalised partial outputs
   float* ws_ml;             // [entries][G][2] (running max m in log2 units, sum l)
   int32_t* ws_cnt;          // [nl * B * Hkv] partial count of each (layer, seq, head)
+  int32_t* ws_arrive;       // [nl * B * Hkv] arrival counters of the fused merge; zero
+                            // between calls (the last arriving workgroup resets them)
   float qscale;             // sm_scale * log2(e)
   int64_t Rvis;
   int D, g, G, Hkv, Hq, B;
@@ -69,7 +71,10 @@ struct DecodeArgs {
   int32_t vb[kMaxSeq], ve[kMaxSeq], cap[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
   int32_t nx[kMaxSeq];      // per sequence: workgroups per (layer, head) before mult
   int32_t nxcum[kMaxSeq + 1];  // per sequence: sum of nx over earlier sequences
+  int32_t pad_[2];          // the split kernels copy this block in 16-byte pieces
 };
+static_assert(sizeof(DecodeArgs) % 16 == 0, "DecodeArgs is copied in 16-byte pieces");
+static_assert(sizeof(DecodeArgs) <= 4096, "DecodeArgs must fit the kernel argument limit");
 
 // Compact 1-D grid of the split kernels: block b enumerates, slot-major, every
 // (slot, sequence, x < nx[seq] * mult[slot]) with no idle blocks, so the
@@ -130,7 +135,13 @@ hipError_t launch_decode_simple(const DecodeArgs& a, int n_seq_launch, hipStream
 // Matrix-core split kernel: needs (D / g) * G <= 16 (one 16-row MFMA tile of
 // (head, group) columns); writes the final output itself when max_chunks == 1.
 bool mfma_supported(int D, int g, int G);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int n_seq_launch, hipStream_t stream);
+// kb, vb: the visual widths every non-bf16 (layer, head) pair of the launch has.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
+hipError_t launch_decode_mfma_128_1(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
+hipError_t launch_decode_mfma_128_2(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
+hipError_t launch_decode_mfma_128_4(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
+hipError_t launch_decode_mfma_64_1(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
+hipError_t launch_decode_mfma_64_2(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int nl, int n_seq_launch,
                                hipStream_t stream);
 constexpr int kMfmaWaves = 4;      // waves per workgroup of the matrix-core kernel

@@ -175,7 +175,8 @@ def kvq_decode_attention(cfg: Config, cache, layer_begin: int, num_layers: int, 
                          q, out, sm_scale: float, chunk_tokens: int = 0, workspace=None,
                          stream=None) -> None:
     """seq_lens: device int32 [batch]; q/out: device bf16 [num_layers, batch, Hq, D].
-    workspace: device uint8 tensor of at least workspace_bytes(...) bytes."""
+    workspace: device uint8 tensor of at least workspace_bytes(...) bytes, zero-filled
+    before its first use (e.g. torch.zeros); each call leaves it ready for reuse."""
     if workspace is None:
         raise ValueError("workspace tensor required (see workspace_bytes)")
     n = C.c_size_t(workspace.numel() * workspace.element_size())

@@ -134,7 +134,7 @@ class Pair:
         q = bf16_device(q_bits, self.device)
         out = t.empty_like(q)
         lens_d = t.tensor(np.asarray(lens, dtype=np.int32), device=self.device)
-        ws = t.empty(kvq.workspace_bytes(self.cfg, nl, chunk), dtype=t.uint8, device=self.device)
+        ws = t.zeros(kvq.workspace_bytes(self.cfg, nl, chunk), dtype=t.uint8, device=self.device)
         kvq.kvq_decode_attention(self.cfg, self.cache, layer_begin, nl, lens_d, q, out,
                                  w.sm_scale, chunk, ws)
         t.cuda.synchronize()

@@ -210,3 +210,41 @@ def test_decode_deterministic():
     a, _ = p.decode([256])
     b, _ = p.decode([256])
     assert np.array_equal(a, b)
+
+
+def test_decode_per_head_formats_in_one_call():
+    """(layer, head) pairs of one call with different visual widths: the call is
+    split into one launch per width combination, bf16 heads join the first."""
+    _say("decode per-head formats")
+    kb = np.array([4, 16, 16, 8, 2, 4, 16, 8], np.uint8)
+    vb = np.array([2, 16, 2, 4, 2, 2, 16, 8], np.uint8)
+    w = synth.Workload("perhead", 2, 2, 16, 4, 128, 64, [400, 333], [14, 5], [390, 333],
+                       [400, 333], kb, vb, seed=21)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [400, 300], what="per-head formats")
+    _check_decode(p, [397, 333], chunk=64, what="per-head formats chunk 64")
+
+
+def test_decode_workspace_reuse_across_shapes():
+    """The merge's arrival counters return to zero after every call, so one
+    workspace serves consecutive calls with other lengths, layer ranges and
+    split sizes."""
+    _say("decode workspace reuse")
+    import torch
+    from kvq_testlib import bf16_device, bf16_to_f64
+    w = synth.llava_layer(seed=13, kbits=4, vbits=2)
+    p = Pair(w)
+    p.store()
+    ws = torch.zeros(max(kvq.workspace_bytes(p.cfg, 1, c) for c in (0, 64, 1024)),
+                     dtype=torch.uint8, device="cuda")
+    q_bits = w.q_bits(0)[None]
+    q = bf16_device(q_bits)
+    for n, chunk in [(6287, 0), (1000, 64), (6287, 1024), (37, 0), (6287, 0)]:
+        out = torch.empty_like(q)
+        lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+        kvq.kvq_decode_attention(p.cfg, p.cache, 0, 1, lens, q, out, w.sm_scale, chunk, ws)
+        torch.cuda.synchronize()
+        got = bf16_to_f64(out)[0, 0]
+        ref = np.stack([p.oracle_decode(0, 0, i, n, q_bits[0, 0, i]) for i in range(w.num_q_heads)])
+        assert_close(got, ref, f"reuse len {n} chunk {chunk}")
