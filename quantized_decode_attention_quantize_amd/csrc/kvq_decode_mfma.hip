@@ -48,6 +48,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr float kLazy = 6.0f;  // p <= 2^6 between rescales
+#ifndef KVQ_RING_DEPTH
+#define KVQ_RING_DEPTH 2  // quantised steps in flight per wave
+#endif
 
 __device__ inline f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -421,9 +424,9 @@ __device__ inline void finish_step(WaveState<D>& ws, const Step<D, KB, VB>& st,
   }
 }
 
-// q.k, softmax and p.v of one 32-token step.  MASKED: the step may run past
-// the segment end (rows_left < 32).  vsel: see v_pair_selector.
-template <int D, int NG, int KB, int VB, bool MASKED>
+// q.k, softmax and p.v of one 32-token step of which the first rows_left
+// (1..32, wave-uniform) rows are real.  vsel: see v_pair_selector.
+template <int D, int NG, int KB, int VB>
 __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D, KB, VB>& st,
                                     const u32x4 (&qop)[D / 32], float qsr, float c24,
                                     int rows_left, uint32_t vsel) {
@@ -452,17 +455,16 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
     else part = a;
     if constexpr (NG >= 2) part += dpp_xor1(part);
     if constexpr (NG >= 4) part += dpp_xor2(part);
-    if constexpr (MASKED) {
-      const int r = 16 * (e >> 2) + 4 * c.jq + (e & 3);
-      part = r < rows_left ? part : -INFINITY;
-    }
     sc[e] = part;
+  }
+  if (rows_left < 32) {  // a segment's last step: rows past its end do not count
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (16 * (e >> 2) + 4 * c.jq + (e & 3) >= rows_left) sc[e] = -INFINITY;
   }
 
   // online softmax with a lazy running max: the accumulators are rescaled
-  // only when a column's max grows by more than kLazy, so p <= 2^kLazy.  The
-  // rare rescaling path carries its own copy of the p.v tail, which keeps the
-  // accumulators in place on the common path.
+  // only when a column's max grows by more than kLazy, so p <= 2^kLazy.
   float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                    fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
   mx = max_over_quarters(mx) * cs;
@@ -529,6 +531,9 @@ constexpr int kStageBytes = 2 * (32 * 128 + 32 * 16);  // INT8 K and V at D=128,
 // through it take a per-lane 32-bit offset plus a wave-uniform offset, so a
 // step's loads need no per-lane address arithmetic.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+// Cache-policy operand of buffer loads: sc0 | sc1, i.e. system-coherent (the
+// load is served past this XCD's caches).
+constexpr int kCoherent = 1 | 16;
 __device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            int(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
@@ -557,13 +562,14 @@ struct SegPlanes {
   Rsrc k, km, v, vm;
 };
 
-// Lane piece of tile rows [0, 32) of full step `step` (wave-uniform): row
-// l/2, half l%2 of every plane's tile.
+// Lane piece of tile rows [0, 32) of step `step` (wave-uniform): row l/2,
+// half l%2 of every plane's tile.  Only the first `rows` (1..32) rows exist;
+// lanes of the others re-read the step's last row.
 template <int D, int NG, int KB, int VB>
-__device__ inline void stage_load(const SegPlanes& pl, int step, int lane,
+__device__ inline void stage_load(const SegPlanes& pl, int step, int rows, int lane,
                                   Stage<D, NG, KB, VB>& st) {
   using S = Stage<D, NG, KB, VB>;
-  const uint32_t row = uint32_t(lane >> 1), half = uint32_t(lane & 1);
+  const uint32_t row = min(uint32_t(lane >> 1), uint32_t(rows - 1)), half = uint32_t(lane & 1);
   const uint32_t r0 = uint32_t(step) * 32u;
   buf_load<S::KP>(pl.k, row * S::KR + half * S::KP, r0 * S::KR, st.k);
   buf_load<S::MP>(pl.km, row * S::MR + half * S::MP, r0 * S::MR, st.km);
@@ -621,26 +627,28 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   const uint8_t* vmp = c.vmeta + row0 * MR;
 
   const int rows = x1 - x0;
-  const int nfull = rows / 32;
+  const int nsteps = (rows + 31) / 32;
+  auto rows_in = [&](int st) { return min(32, rows - 32 * st); };
   constexpr int VBY = Fmt<D, VB>::kVBytes;
-  // Quantised steps are small (~14 VGPRs per lane): two of them fly through
-  // registers into the wave's LDS stage while earlier ones compute; their
-  // first loads are issued before Q' is built so the latencies overlap.
-  // bf16 steps carry 64 VGPRs of data and load straight into operands.
+  // Quantised steps are small (~14 VGPRs per lane for INT4/INT2): kDepth of
+  // them are in flight from memory into registers while earlier ones go
+  // through the wave's LDS stage and compute; the first loads are issued
+  // before Q' is built so the latencies overlap.  bf16 steps carry 64 VGPRs
+  // of data and load straight into operands.
   constexpr bool kStaged = KB < 16 && VB < 16;
   using S = Stage<D, NG, KB, VB>;
-  // steps in flight per wave: two, unless a step's lane piece is large (INT8)
-  constexpr int kDepth = S::KP + S::VP <= 48 ? 2 : 1;
-  S ga, gb;
+  constexpr int kDepth = S::KP + S::VP <= 48 ? KVQ_RING_DEPTH : 2;
+  S g[kDepth];
   SegPlanes pl;
   if constexpr (kStaged) {
     pl.k = make_rsrc(kp, int64_t(rows) * KR);
     pl.km = make_rsrc(kmp, int64_t(rows) * MR);
     pl.v = make_rsrc(vp, int64_t(rows) * VR);
     pl.vm = make_rsrc(vmp, int64_t(rows) * MR);
-    if (nfull > 0) {
-      stage_load<D, NG, KB, VB>(pl, 0, c.lane, ga);
-      if constexpr (kDepth == 2) stage_load<D, NG, KB, VB>(pl, min(1, nfull - 1), c.lane, gb);
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int st = min(k, nsteps - 1);
+      stage_load<D, NG, KB, VB>(pl, st, rows_in(st), c.lane, g[k]);
     }
   }
 
@@ -651,54 +659,42 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= v_inflation<D, VB>(mb);
 
-  Offs<D, NG, KB, VB> of;
-  of.full(c);
   Step<D, KB, VB> sa;
-  const uint32_t vsel_mem = v_pair_selector<D, VB>(0);
-  int i = 0;
   if constexpr (kStaged) {
     const uint32_t vsel = v_pair_selector<D, VB>((c.n * VBY) & 3);
-    // loads inside the loop are unconditional (clamped to the last full step)
-    // so the wait counts stay exact
-    if (kDepth == 1) {
-      for (; i < nfull; ++i) {
-        stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
-        stage_load<D, NG, KB, VB>(pl, min(i + 1, nfull - 1), c.lane, ga);
+    // The ring is unrolled kDepth steps deep.  Loads are unconditional (past
+    // the last step they re-read it) so the compiler's wait counts stay
+    // exact; only the compute of steps past the end is skipped.
+    for (int i = 0; i < nsteps; i += kDepth) {
+#pragma unroll
+      for (int k = 0; k < kDepth; ++k) {
+        const int st = i + k;
+        const int nxt = min(st + kDepth, nsteps - 1);
+        stage_put<D, NG, KB, VB>(c.stage, c.lane, g[k]);
+        stage_load<D, NG, KB, VB>(pl, nxt, rows_in(nxt), c.lane, g[k]);
         stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
-      }
-    } else if (nfull > 0) {
-      for (; i + 1 < nfull; i += 2) {
-        stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
-        stage_load<D, NG, KB, VB>(pl, min(i + 2, nfull - 1), c.lane, ga);
-        stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
-        stage_put<D, NG, KB, VB>(c.stage, c.lane, gb);
-        stage_load<D, NG, KB, VB>(pl, min(i + 3, nfull - 1), c.lane, gb);
-        stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
-      }
-      if (i < nfull) {  // odd step count: the last full step sits in ga
-        stage_put<D, NG, KB, VB>(c.stage, c.lane, ga);
-        stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel);
-        ++i;
+        if (st < nsteps) compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(st), vsel);
       }
     }
   } else {
-    for (; i < nfull; ++i) {
+    const uint32_t vsel_mem = v_pair_selector<D, VB>(0);
+    Offs<D, NG, KB, VB> of;
+    of.full(c);
+    const int nfull = rows / 32;
+    for (int i = 0; i < nfull; ++i) {
       const int64_t o = int64_t(i) * 32;
       load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of,
                                       sa);
-      compute_step<D, NG, KB, VB, false>(c, ws, sa, qop, qsr, c24, 32, vsel_mem);
+      compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, 32, vsel_mem);
     }
-  }
-  const int tail = rows - 32 * nfull;
-  if (tail > 0) {
-    const int64_t o = int64_t(nfull) * 32;
-    of.clamped(c, tail);
-    load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of, sa);
-    compute_step<D, NG, KB, VB, true>(c, ws, sa, qop, qsr, c24, tail, vsel_mem);
+    const int tail = rows - 32 * nfull;
+    if (tail > 0) {
+      const int64_t o = int64_t(nfull) * 32;
+      of.clamped(c, tail);
+      load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of,
+                                     sa);
+      compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, tail, vsel_mem);
+    }
   }
 
 #pragma unroll
@@ -743,12 +739,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   const int G = a.G;
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[kMaxGroupRatio * D];
-  __shared__ float ml_lds[kWaves][kMaxGroupRatio][2];
+  __shared__ float ml_lds[kWaves][16][2];
   // wave stages during the loop; per-wave outputs for the final combine after it
   constexpr int kOBytes = kWaves * kMaxGroupRatio * D * 4;
   constexpr int kUnion = kOBytes > kWaves * kStageBytes ? kOBytes : kWaves * kStageBytes;
   __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnion];
-  float(*o_lds)[kMaxGroupRatio][D] = reinterpret_cast<float(*)[kMaxGroupRatio][D]>(big_lds);
 
   // the G query rows of this KV head: G * D bf16, 16 bytes per thread
   // (G * D / 8 <= 256 threads; rows start 16-byte aligned since D * 2 >= 128)
@@ -793,70 +788,68 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int ve = __builtin_amdgcn_readfirstlane(t.ve[sl]);
     const int64_t vrow0 = __builtin_amdgcn_readfirstlane(t.vrow0[sl]);
     const int64_t trow0 = __builtin_amdgcn_readfirstlane(t.trow0[sl]);
-    // text prefix [0, vb), visual [vb, ve), text suffix [ve, cap)
-    int x0 = wa, x1 = min(wb, vb);
-    if (x0 < x1) run_segment<D, NG, 16, 16>(c, st, x0, x1, trow0 + x0, false);
-    x0 = max(wa, vb);
-    x1 = min(wb, ve);
-    if (x0 < x1) {
-      if (KB == 16 && VB == 16) {
-        run_segment<D, NG, 16, 16>(c, st, x0, x1, vrow0 + (x0 - vb), true);
-      } else if (kbits == KB && vbits == VB) {
-        run_segment<D, NG, KB, VB>(c, st, x0, x1, vrow0 + (x0 - vb), true);
-      } else {  // bf16 visual rows of a protected head
-        run_segment<D, NG, 16, 16>(c, st, x0, x1, vrow0 + (x0 - vb), true);
-      }
+    const bool quant_vis = !(KB == 16 && VB == 16) && kbits == KB && vbits == VB;
+    // text prefix [0, vb), visual [vb, ve), text suffix [ve, cap) in order;
+    // kept as a loop so each row path is emitted once
+#pragma clang loop unroll(disable)
+    for (int seg = 0; seg < 3; ++seg) {
+      const int x0 = seg == 0 ? wa : seg == 1 ? max(wa, vb) : max(wa, ve);
+      const int x1 = seg == 0 ? min(wb, vb) : seg == 1 ? min(wb, ve) : wb;
+      if (x0 >= x1) continue;
+      const int64_t row0 = seg == 1 ? vrow0 + (x0 - vb)
+                                    : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
+      if (seg == 1 && quant_vis)
+        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true);
+      else  // text rows, or bf16 visual rows of a protected head
+        run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, seg == 1);
     }
-    x0 = max(wa, ve);
-    x1 = wb;
-    if (x0 < x1) run_segment<D, NG, 16, 16>(c, st, x0, x1, trow0 + (x0 - (ve - vb)), false);
   }
 
-  // ---- wave result -> LDS: per head m, l and unnormalised o[d] ---------------
-  __syncthreads();  // stages are reused as o_lds below
+  // ---- wave results -> LDS ---------------------------------------------------
+  // Row c of every wave's p.v accumulator (column (head, group) c of S) goes
+  // to o_all[wave][c][d] with the V-min term added; (m, l) per column to
+  // ml_all.  Rows of dead columns and the other groups' d are written too
+  // and simply never read.
+  __syncthreads();  // the stages are reused as o_all below
   float l_col = st.l + __shfl_xor(st.l, 16);
   l_col += __shfl_xor(l_col, 32);
   float mt_col = st.mt + __shfl_xor(st.mt, 16);
   mt_col += __shfl_xor(mt_col, 32);
   const int n = lane & 15, jq = lane >> 4;
-  if (jq == 0 && n < G * NG && n % NG == 0) {
-    ml_lds[wave][n / NG][0] = st.m;
-    ml_lds[wave][n / NG][1] = l_col;
+  float(*o_all)[16][D] = reinterpret_cast<float(*)[16][D]>(big_lds);
+  if (jq == 0) {
+    ml_lds[wave][n][0] = st.m;
+    ml_lds[wave][n][1] = l_col;
   }
-  float mt_row[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) mt_row[i] = __shfl(mt_col, 4 * jq + i);
+  for (int i = 0; i < 4; ++i) {
+    const float mt_r = __shfl(mt_col, 4 * jq + i);
+    f32x4 v[NB / 4];
 #pragma unroll
-  for (int mb = 0; mb < NB; ++mb) {
-    const int d = NB * n + mb;
-    const int gd = d / g;
+    for (int mb = 0; mb < NB; ++mb) v[mb / 4][mb % 4] = st.o[mb][i] + mt_r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * jq + i;
-      if (r < G * NG && r % NG == gd) o_lds[wave][r / NG][d] = st.o[mb][i] + mt_row[i];
-    }
+    for (int k = 0; k < NB / 4; ++k)
+      reinterpret_cast<f32x4*>(&o_all[wave][4 * jq + i][NB * n])[k] = v[k];
   }
   __syncthreads();
 
   // ---- combine waves; write the workgroup's partial (or the final output) ----
+  // head j's value at d lives in row c = j * NG + (d / g)
   const bool single = nxs == 1;
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
   const int64_t pidx = partial_index(l_local, s, h, x, a.B, a.Hkv, a.max_chunks);
   uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
   for (int i = threadIdx.x; i < G * D; i += 256) {
-    const int j = i / D, d = i % D;
+    const int j = i / D, d = i % D, cr = j * NG + d / g;
     float M = -INFINITY;
-#pragma unroll
     for (int w = 0; w < kWaves; ++w)
-      if (ml_lds[w][j][1] > 0.0f) M = fmaxf(M, ml_lds[w][j][0]);
+      if (ml_lds[w][cr][1] > 0.0f) M = fmaxf(M, ml_lds[w][cr][0]);
     float L = 0.0f, acc = 0.0f;
-#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (ml_lds[w][j][1] > 0.0f) {
-        const float f = __builtin_amdgcn_exp2f(ml_lds[w][j][0] - M);
-        L += ml_lds[w][j][1] * f;
-        acc += o_lds[w][j][d] * f;
-      }
+      const float lw = ml_lds[w][cr][1];
+      const float f = lw > 0.0f ? __builtin_amdgcn_exp2f(ml_lds[w][cr][0] - M) : 0.0f;
+      L += lw * f;
+      acc += o_all[w][cr][d] * f;
     }
     const float o = L > 0.0f ? acc / L : 0.0f;  // L == 0: no token in this workgroup
     if (single) {
@@ -864,7 +857,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     } else {
       // write-through (system-coherent) stores: the merging workgroup may sit
       // on another XCD and reads them past its own caches
-      __hip_atomic_store(&a.ws_o[(pidx * G + j) * D + d], o, __ATOMIC_RELAXED,
+      __hip_atomic_store(&a.ws_o[pidx * G * D + i], o, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);
       if (d == 0) {
         __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], M, __ATOMIC_RELAXED,
@@ -889,35 +882,57 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                                      __HIP_MEMORY_SCOPE_SYSTEM) == nxs - 1;
   __syncthreads();
   if (!is_last) return;
+  // Partials go through LDS (the o_all storage) in batches of kBatch: per
+  // batch every partial row and (m, l) pair is pulled in with independent
+  // 16-byte loads that bypass the caches, then folded into a running
+  // log-sum-exp per output element.
   const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
-  // (m, l) of every partial and head, staged in LDS (the o_lds storage) when
-  // they fit, else read from memory each time
-  const float* gml = a.ws_ml + p0 * G * 2;
-  float* pml = &o_lds[0][0][0];
-  const bool staged = nxs * G * 2 <= kOBytes / 4;
-  if (staged) {
-    for (int i = threadIdx.x; i < nxs * G * 2; i += 256)
-      pml[i] = __hip_atomic_load(&gml[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const int kBatch = (kOBytes / 4) / (G * (D + 2));  // partials per LDS batch (>= 1)
+  float* po = &o_all[0][0][0];
+  float Mr[(kMaxGroupRatio * D + 255) / 256], Wr[(kMaxGroupRatio * D + 255) / 256],
+      Ar[(kMaxGroupRatio * D + 255) / 256];
+#pragma unroll
+  for (int k = 0; k < (kMaxGroupRatio * D + 255) / 256; ++k) {
+    Mr[k] = -INFINITY;
+    Wr[k] = 0.0f;
+    Ar[k] = 0.0f;
+  }
+  for (int c0 = 0; c0 < nxs; c0 += kBatch) {
+    const int nb = min(kBatch, nxs - c0);
+    const int n_o = nb * G * D, n_ml = nb * G * 2;
+    float* pml = po + n_o;
+    const Rsrc ro = make_rsrc(a.ws_o + (p0 + c0) * G * D, int64_t(n_o) * 4);
+    const Rsrc rm = make_rsrc(a.ws_ml + (p0 + c0) * G * 2, int64_t(n_ml) * 4);
+    for (int v = threadIdx.x; v < n_o / 4; v += 256)
+      reinterpret_cast<u32x4*>(po)[v] =
+          __builtin_amdgcn_raw_buffer_load_b128(ro, uint32_t(v) * 16u, 0, kCoherent);
+    for (int k = threadIdx.x; k < n_ml; k += 256)
+      pml[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rm, uint32_t(k) * 4u, 0, kCoherent));
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < (kMaxGroupRatio * D + 255) / 256; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      if (i >= G * D) break;
+      const int j = i / D;
+      for (int cx = 0; cx < nb; ++cx) {
+        const float lx = pml[(cx * G + j) * 2 + 1];
+        if (!(lx > 0.0f)) continue;  // a workgroup without tokens
+        const float mx = pml[(cx * G + j) * 2];
+        const float mnew = fmaxf(Mr[k], mx);
+        const float r = __builtin_amdgcn_exp2f(Mr[k] - mnew);  // 0 while Mr is -inf
+        const float wx = lx * __builtin_amdgcn_exp2f(mx - mnew);
+        Wr[k] = Wr[k] * r + wx;
+        Ar[k] = Ar[k] * r + wx * po[cx * G * D + i];
+        Mr[k] = mnew;
+      }
+    }
     __syncthreads();
   }
-  auto ml_at = [&](int k) {
-    return staged ? pml[k] : __hip_atomic_load(&gml[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  };
-  for (int i = threadIdx.x; i < G * D; i += 256) {
-    const int j = i / D, d = i % D;
-    float M = -INFINITY;
-    for (int cx = 0; cx < nxs; ++cx)
-      if (ml_at((cx * G + j) * 2 + 1) > 0.0f) M = fmaxf(M, ml_at((cx * G + j) * 2));
-    float W = 0.0f, acc = 0.0f;
-    for (int cx = 0; cx < nxs; ++cx) {
-      const float lx = ml_at((cx * G + j) * 2 + 1);
-      if (!(lx > 0.0f)) continue;  // a workgroup without tokens
-      const float wgt = lx * __builtin_amdgcn_exp2f(ml_at((cx * G + j) * 2) - M);
-      W += wgt;
-      acc += wgt * __hip_atomic_load(&a.ws_o[((p0 + cx) * G + j) * D + d], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    outp[i] = __builtin_bit_cast(uint16_t, (__bf16)(acc / W));
+#pragma unroll
+  for (int k = 0; k < (kMaxGroupRatio * D + 255) / 256; ++k) {
+    const int i = threadIdx.x + 256 * k;
+    if (i < G * D) outp[i] = __builtin_bit_cast(uint16_t, (__bf16)(Ar[k] / Wr[k]));
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.ws_arrive[entry], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
