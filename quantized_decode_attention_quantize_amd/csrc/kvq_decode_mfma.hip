@@ -834,24 +834,42 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   __syncthreads();
 
   // ---- combine waves; write the workgroup's partial (or the final output) ----
-  // head j's value at d lives in row c = j * NG + (d / g)
+  // Per row c, one thread turns the waves' (m, l) into combine weights
+  // f_w = 2^(m_w - M) (0 for a wave without tokens) and L = sum l_w f_w;
+  // every output element is then a branch-free weighted sum over the waves.
+  // Head j's value at d lives in row c = j * NG + (d / g).
+  __shared__ __attribute__((aligned(16))) float wts[16][kWaves];
+  __shared__ float rowL[16], rowM[16];
+  if (threadIdx.x < 16) {
+    const int cr = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      M = ml_lds[w][cr][1] > 0.0f ? fmaxf(M, ml_lds[w][cr][0]) : M;
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float lw = ml_lds[w][cr][1];
+      const float f = lw > 0.0f ? __builtin_amdgcn_exp2f(ml_lds[w][cr][0] - M) : 0.0f;
+      wts[cr][w] = f;
+      L += lw * f;
+    }
+    rowL[cr] = L;
+    rowM[cr] = M;
+  }
+  __syncthreads();
   const bool single = nxs == 1;
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
   const int64_t pidx = partial_index(l_local, s, h, x, a.B, a.Hkv, a.max_chunks);
   uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int j = i / D, d = i % D, cr = j * NG + d / g;
-    float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w)
-      if (ml_lds[w][cr][1] > 0.0f) M = fmaxf(M, ml_lds[w][cr][0]);
-    float L = 0.0f, acc = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float lw = ml_lds[w][cr][1];
-      const float f = lw > 0.0f ? __builtin_amdgcn_exp2f(ml_lds[w][cr][0] - M) : 0.0f;
-      L += lw * f;
-      acc += o_all[w][cr][d] * f;
-    }
-    const float o = L > 0.0f ? acc / L : 0.0f;  // L == 0: no token in this workgroup
+    const f32x4 f = *reinterpret_cast<const f32x4*>(wts[cr]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc += o_all[w][cr][d] * f[w];
+    const float L = rowL[cr];
+    const float o = L > 0.0f ? acc * __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
     if (single) {
       outp[i] = __builtin_bit_cast(uint16_t, (__bf16)o);
     } else {
@@ -860,7 +878,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       __hip_atomic_store(&a.ws_o[pidx * G * D + i], o, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);
       if (d == 0) {
-        __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], M, __ATOMIC_RELAXED,
+        __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], rowM[cr], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
         __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 1], L, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
@@ -882,57 +900,101 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                                      __HIP_MEMORY_SCOPE_SYSTEM) == nxs - 1;
   __syncthreads();
   if (!is_last) return;
-  // Partials go through LDS (the o_all storage) in batches of kBatch: per
-  // batch every partial row and (m, l) pair is pulled in with independent
-  // 16-byte loads that bypass the caches, then folded into a running
-  // log-sum-exp per output element.
+  // Merge in LDS (the o_all storage): the (m, l) pairs of all partials come
+  // in first and G threads turn them into weights w[cx][j] = l 2^(m - M_j)
+  // (0 for a partial without tokens) and L_j = sum w; then the partial rows
+  // (normalised, o / l) stream through in batches, each element accumulating
+  // sum_cx o w.  All
+  // loads are 16- or 4-byte buffer loads that bypass the caches, issued
+  // together.  Entries with more partials than LDS holds read memory directly.
   const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
-  const int kBatch = (kOBytes / 4) / (G * (D + 2));  // partials per LDS batch (>= 1)
-  float* po = &o_all[0][0][0];
-  float Mr[(kMaxGroupRatio * D + 255) / 256], Wr[(kMaxGroupRatio * D + 255) / 256],
-      Ar[(kMaxGroupRatio * D + 255) / 256];
+  const float* gml = a.ws_ml + p0 * G * 2;
+  const float* go = a.ws_o + p0 * G * D;
+  constexpr int kLdsFloats = kOBytes / 4;
+  constexpr int kPer = (kMaxGroupRatio * D + 255) / 256;  // output elements per thread
+  const int n_ml = nxs * G * 2;
+  float* lml = &o_all[0][0][0];       // [nxs][G] (m, l)
+  float* lw = lml + n_ml;             // [nxs][G] weights
+  float* lL = lw + nxs * G;           // [G] sums
+  float* lo = lL + 16;                // partial rows of the current batch
+  const int room = kLdsFloats - n_ml - nxs * G - 16;
+  float acc[kPer];
 #pragma unroll
-  for (int k = 0; k < (kMaxGroupRatio * D + 255) / 256; ++k) {
-    Mr[k] = -INFINITY;
-    Wr[k] = 0.0f;
-    Ar[k] = 0.0f;
-  }
-  for (int c0 = 0; c0 < nxs; c0 += kBatch) {
-    const int nb = min(kBatch, nxs - c0);
-    const int n_o = nb * G * D, n_ml = nb * G * 2;
-    float* pml = po + n_o;
-    const Rsrc ro = make_rsrc(a.ws_o + (p0 + c0) * G * D, int64_t(n_o) * 4);
-    const Rsrc rm = make_rsrc(a.ws_ml + (p0 + c0) * G * 2, int64_t(n_ml) * 4);
-    for (int v = threadIdx.x; v < n_o / 4; v += 256)
-      reinterpret_cast<u32x4*>(po)[v] =
-          __builtin_amdgcn_raw_buffer_load_b128(ro, uint32_t(v) * 16u, 0, kCoherent);
+  for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
+  if (room >= G * D) {
+    const Rsrc rm = make_rsrc(gml, int64_t(n_ml) * 4);
     for (int k = threadIdx.x; k < n_ml; k += 256)
-      pml[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+      lml[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                              rm, uint32_t(k) * 4u, 0, kCoherent));
     __syncthreads();
+    if (int(threadIdx.x) < G) {
+      const int j = threadIdx.x;
+      float M = -INFINITY;
+      for (int cx = 0; cx < nxs; ++cx) {
+        const float lx = lml[(cx * G + j) * 2 + 1];
+        M = lx > 0.0f ? fmaxf(M, lml[(cx * G + j) * 2]) : M;
+      }
+      float L = 0.0f;
+      for (int cx = 0; cx < nxs; ++cx) {
+        const float lx = lml[(cx * G + j) * 2 + 1];
+        // partial rows are normalised (o / l): their weight is l * 2^(m - M)
+        const float wgt = lx > 0.0f ? lx * __builtin_amdgcn_exp2f(lml[(cx * G + j) * 2] - M) : 0.0f;
+        lw[cx * G + j] = wgt;
+        L += wgt;
+      }
+      lL[j] = L;
+    }
+    const int kBatch = room / (G * D);
+    for (int c0 = 0; c0 < nxs; c0 += kBatch) {
+      const int nb = min(kBatch, nxs - c0);
+      const int n_o = nb * G * D;
+      const Rsrc ro = make_rsrc(go + int64_t(c0) * G * D, int64_t(n_o) * 4);
+      for (int v = threadIdx.x; v < n_o / 4; v += 256)
+        reinterpret_cast<u32x4*>(lo)[v] =
+            __builtin_amdgcn_raw_buffer_load_b128(ro, uint32_t(v) * 16u, 0, kCoherent);
+      __syncthreads();
 #pragma unroll
-    for (int k = 0; k < (kMaxGroupRatio * D + 255) / 256; ++k) {
+      for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x + 256 * k;
+        if (i < G * D) {
+          const int j = i / D;
+          for (int cx = 0; cx < nb; ++cx) acc[k] += lo[cx * G * D + i] * lw[(c0 + cx) * G + j];
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + 256 * k;
+      if (i < G * D) acc[k] *= __builtin_amdgcn_rcpf(lL[i / D]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
       const int i = threadIdx.x + 256 * k;
       if (i >= G * D) break;
       const int j = i / D;
-      for (int cx = 0; cx < nb; ++cx) {
-        const float lx = pml[(cx * G + j) * 2 + 1];
-        if (!(lx > 0.0f)) continue;  // a workgroup without tokens
-        const float mx = pml[(cx * G + j) * 2];
-        const float mnew = fmaxf(Mr[k], mx);
-        const float r = __builtin_amdgcn_exp2f(Mr[k] - mnew);  // 0 while Mr is -inf
-        const float wx = lx * __builtin_amdgcn_exp2f(mx - mnew);
-        Wr[k] = Wr[k] * r + wx;
-        Ar[k] = Ar[k] * r + wx * po[cx * G * D + i];
-        Mr[k] = mnew;
+      auto ld = [&](const float* p) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      };
+      float M = -INFINITY;
+      for (int cx = 0; cx < nxs; ++cx)
+        M = ld(&gml[(cx * G + j) * 2 + 1]) > 0.0f ? fmaxf(M, ld(&gml[(cx * G + j) * 2])) : M;
+      float L = 0.0f, A = 0.0f;
+      for (int cx = 0; cx < nxs; ++cx) {
+        const float lx = ld(&gml[(cx * G + j) * 2 + 1]);
+        const float wgt =
+            lx > 0.0f ? lx * __builtin_amdgcn_exp2f(ld(&gml[(cx * G + j) * 2]) - M) : 0.0f;
+        L += wgt;
+        A += lx > 0.0f ? wgt * ld(&go[int64_t(cx) * G * D + i]) : 0.0f;
       }
+      acc[k] = A * __builtin_amdgcn_rcpf(L);
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int k = 0; k < (kMaxGroupRatio * D + 255) / 256; ++k) {
+  for (int k = 0; k < kPer; ++k) {
     const int i = threadIdx.x + 256 * k;
-    if (i < G * D) outp[i] = __builtin_bit_cast(uint16_t, (__bf16)(Ar[k] / Wr[k]));
+    if (i < G * D) outp[i] = __builtin_bit_cast(uint16_t, (__bf16)acc[k]);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.ws_arrive[entry], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
