@@ -900,74 +900,78 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                                      __HIP_MEMORY_SCOPE_SYSTEM) == nxs - 1;
   __syncthreads();
   if (!is_last) return;
-  // Merge in LDS (the o_all storage): the (m, l) pairs of all partials come
-  // in first and G threads turn them into weights w[cx][j] = l 2^(m - M_j)
-  // (0 for a partial without tokens) and L_j = sum w; then the partial rows
-  // (normalised, o / l) stream through in batches, each element accumulating
-  // sum_cx o w.  All
+  // Merge in LDS (the stage / o_all storage): the (m, l) pairs of all
+  // partials come in with the first batch of partial rows and become weights
+  // w[cx][j] = l 2^(m - M_j) (0 for a partial without tokens); the partial
+  // rows (normalised, o / l) stream through in batches, each element
+  // accumulating sum_cx o w and sum_cx w.  All
   // loads are 16- or 4-byte buffer loads that bypass the caches, issued
   // together.  Entries with more partials than LDS holds read memory directly.
   const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
   const float* gml = a.ws_ml + p0 * G * 2;
   const float* go = a.ws_o + p0 * G * D;
-  constexpr int kLdsFloats = kOBytes / 4;
+  constexpr int kLdsFloats = kUnion / 4;  // the whole stage / o_all area
   constexpr int kPer = (kMaxGroupRatio * D + 255) / 256;  // output elements per thread
   const int n_ml = nxs * G * 2;
-  float* lml = &o_all[0][0][0];       // [nxs][G] (m, l)
-  float* lw = lml + n_ml;             // [nxs][G] weights
-  float* lL = lw + nxs * G;           // [G] sums
-  float* lo = lL + 16;                // partial rows of the current batch
-  const int room = kLdsFloats - n_ml - nxs * G - 16;
-  float acc[kPer];
+  float* lml = reinterpret_cast<float*>(big_lds);  // [nxs][G] (m, l)
+  float* lw = lml + n_ml;                           // [nxs][G] weights
+  const int lo_off = (3 * nxs * G + 3) & ~3;
+  float* lo = lml + lo_off;                         // partial rows of the current batch
+  const int room = kLdsFloats - lo_off;
+  float acc[kPer], wsum[kPer];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
+  for (int k = 0; k < kPer; ++k) {
+    acc[k] = 0.0f;
+    wsum[k] = 0.0f;
+  }
   if (room >= G * D) {
-    const Rsrc rm = make_rsrc(gml, int64_t(n_ml) * 4);
-    for (int k = threadIdx.x; k < n_ml; k += 256)
-      lml[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             rm, uint32_t(k) * 4u, 0, kCoherent));
-    __syncthreads();
-    if (int(threadIdx.x) < G) {
-      const int j = threadIdx.x;
-      float M = -INFINITY;
-      for (int cx = 0; cx < nxs; ++cx) {
-        const float lx = lml[(cx * G + j) * 2 + 1];
-        M = lx > 0.0f ? fmaxf(M, lml[(cx * G + j) * 2]) : M;
-      }
-      float L = 0.0f;
-      for (int cx = 0; cx < nxs; ++cx) {
-        const float lx = lml[(cx * G + j) * 2 + 1];
-        // partial rows are normalised (o / l): their weight is l * 2^(m - M)
-        const float wgt = lx > 0.0f ? lx * __builtin_amdgcn_exp2f(lml[(cx * G + j) * 2] - M) : 0.0f;
-        lw[cx * G + j] = wgt;
-        L += wgt;
-      }
-      lL[j] = L;
-    }
     const int kBatch = room / (G * D);
+    const Rsrc rm = make_rsrc(gml, int64_t(n_ml) * 4);
     for (int c0 = 0; c0 < nxs; c0 += kBatch) {
       const int nb = min(kBatch, nxs - c0);
       const int n_o = nb * G * D;
       const Rsrc ro = make_rsrc(go + int64_t(c0) * G * D, int64_t(n_o) * 4);
+      if (c0 > 0) __syncthreads();  // the previous batch is consumed
       for (int v = threadIdx.x; v < n_o / 4; v += 256)
         reinterpret_cast<u32x4*>(lo)[v] =
             __builtin_amdgcn_raw_buffer_load_b128(ro, uint32_t(v) * 16u, 0, kCoherent);
+      if (c0 == 0) {  // the (m, l) pairs travel with the first batch
+        for (int k = threadIdx.x; k < n_ml; k += 256)
+          lml[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rm, uint32_t(k) * 4u, 0, kCoherent));
+        __syncthreads();
+        // one thread per (partial cx, head j): M_j over all partials (every
+        // thread of head j reads the same pairs), then its own weight; the
+        // partial rows are normalised (o / l), so the weight is l 2^(m - M_j)
+        for (int t = threadIdx.x; t < nxs * G; t += 256) {
+          const int j = t % G;
+          float M = -INFINITY;
+#pragma unroll 8
+          for (int cx = 0; cx < nxs; ++cx) {
+            const float2 ml = reinterpret_cast<const float2*>(lml)[cx * G + j];
+            M = ml.y > 0.0f ? fmaxf(M, ml.x) : M;
+          }
+          const float2 me = reinterpret_cast<const float2*>(lml)[t];
+          lw[t] = me.y > 0.0f ? me.y * __builtin_amdgcn_exp2f(me.x - M) : 0.0f;
+        }
+      }
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
         const int i = threadIdx.x + 256 * k;
         if (i < G * D) {
           const int j = i / D;
-          for (int cx = 0; cx < nb; ++cx) acc[k] += lo[cx * G * D + i] * lw[(c0 + cx) * G + j];
+#pragma unroll 4
+          for (int cx = 0; cx < nb; ++cx) {
+            const float wgt = lw[(c0 + cx) * G + j];
+            acc[k] += lo[cx * G * D + i] * wgt;
+            wsum[k] += wgt;
+          }
         }
       }
-      __syncthreads();
     }
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = threadIdx.x + 256 * k;
-      if (i < G * D) acc[k] *= __builtin_amdgcn_rcpf(lL[i / D]);
-    }
+    for (int k = 0; k < kPer; ++k) acc[k] *= __builtin_amdgcn_rcpf(wsum[k]);
   } else {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
