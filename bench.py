@@ -109,6 +109,30 @@ def algorithmic_bytes(w, lens):
     return total
 
 
+KERNEL_SOURCES = ["kvq_decode_mfma.hip", "kvq_internal.h", "kvq_api.hip"]
+
+
+def counted_traffic(name):
+    """HBM bytes per decode launch (scaled FETCH_SIZE + WRITE_SIZE) from the
+    committed rocprofv3 summary of this workload, or None when there is none
+    or the kernel sources have changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_{name}.md")
+    if not os.path.exists(path):
+        return None, None
+    m = re.search(r"traffic_bytes_per_launch=(\d+) kernel_source_sha256_16=([0-9a-f]+)",
+                  open(path).read())
+    if not m:
+        return None, None
+    csrc = os.path.join(ROOT, "quantized_decode_attention_quantize_amd", "csrc")
+    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                  for f in KERNEL_SOURCES)).hexdigest()[:16]
+    if sha != m.group(2):
+        return None, os.path.relpath(path, ROOT) + " (kernel changed since; not used)"
+    return int(m.group(1)), os.path.relpath(path, ROOT)
+
+
 def timed(torch, args, enqueue):
     """Milliseconds per call of `enqueue(i)`, i = 0..K-1, measured with HIP
     events on the current stream.  By default the K calls are captured once
@@ -282,6 +306,8 @@ def main():
         del refs, wsr
 
     cpu = None if args.no_cpu else cpu_baseline(w, lens, q_bits, alg)
+    profiled = args.chunk == 0 and (w.name != "headguard_step" or args.protected == 14)
+    traffic, traffic_src = counted_traffic(w.name) if profiled else (None, None)
 
     line = {
         "metric": "decode-attn µs/step + effective HBM GB/s (% of MI355X peak), INT4/INT2 KV",
@@ -310,7 +336,9 @@ def main():
                    "timing": "eager launches" if args.eager else
                              "HIP graph of K back-to-back launches, events around the replay"},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "traffic_source": traffic_src,
+                     "algorithmic_bytes": alg,
                      "kernel": "decode_mfma_kernel (split-K, merge fused)"},
         "cpu_baseline": cpu,
     }
