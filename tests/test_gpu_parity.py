@@ -248,3 +248,46 @@ def test_decode_workspace_reuse_across_shapes():
         got = bf16_to_f64(out)[0, 0]
         ref = np.stack([p.oracle_decode(0, 0, i, n, q_bits[0, 0, i]) for i in range(w.num_q_heads)])
         assert_close(got, ref, f"reuse len {n} chunk {chunk}")
+
+
+def test_decode_long_context_full_size_sampled():
+    """B=4 x 32,768-token GQA cache (32 query / 8 KV heads, K INT4 / V INT2) at
+    full size, decoded in the default (balanced) split as the benchmark runs it;
+    two sequences are also stored by the oracle and their outputs compared."""
+    _say("decode long context 4 x 32768, sampled sequences vs oracle")
+    w = synth.long_gqa()
+    p = Pair(w)
+    sampled = [0, 3]
+    # Only the sampled sequences are stored (both sides); the others keep an
+    # all-zero cache region, which decodes like any other rows, so the launch
+    # covers the full batch exactly as the benchmark's does.
+    p.store(seqs=sampled)
+    assert p.mismatches(seqs=sampled) == 0
+    lens = [32768, 20000, 32768, 31999]
+    out, q = p.decode(lens)
+    got, ref = [], []
+    for s in sampled:
+        for i in range(w.num_q_heads):
+            ref.append(p.oracle_decode(0, s, i, lens[s], q[0, s, i]))
+            got.append(out[0, s, i])
+    assert_close(np.array(got), np.array(ref), "long context")
+
+
+def test_decode_ragged_batch_full_size_sampled():
+    """B=64 ragged lengths in [1024, 16384], K INT8 / V INT4, at full size;
+    sampled sequences (shortest, longest, two others) compared with the oracle."""
+    _say("decode ragged batch of 64, sampled sequences vs oracle")
+    w = synth.ragged_serving()
+    p = Pair(w)
+    caps = np.array(w.capacity)
+    sampled = sorted({int(np.argmin(caps)), int(np.argmax(caps)), 17, 40})
+    p.store(seqs=sampled)  # others stay all-zero (see the long-context test)
+    assert p.mismatches(seqs=sampled) == 0
+    lens = [c if s % 3 else max(1, c - 777) for s, c in enumerate(w.capacity)]
+    out, q = p.decode(lens)
+    got, ref = [], []
+    for s in sampled:
+        for i in range(w.num_q_heads):
+            ref.append(p.oracle_decode(0, s, i, lens[s], q[0, s, i]))
+            got.append(out[0, s, i])
+    assert_close(np.array(got), np.array(ref), "ragged batch")
