@@ -164,9 +164,9 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
     }
     int64_t caps = 0;
     for (int s = 0; s < B; ++s) caps += c->capacity[s];
-    // Budget: two 4-wave workgroups per CU (the kernel runs two waves per
+    // Budget: one 8-wave workgroup per CU (the kernel runs two waves per
     // SIMD), so every CU carries the same load and all waves run in one round.
-    const int64_t budget = int64_t(device_cus()) * 2;
+    const int64_t budget = int64_t(device_cus());
     constexpr int kMinWaveTokens = 128;  // keep >= 4 steps per wave
     std::vector<double> frac(B);
     int64_t used = 0;

@@ -46,7 +46,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+// Eight waves per workgroup and one workgroup per CU: two waves per SIMD,
+// both of the same workgroup, so the LDS claim counter below can even out the
+// older wave's issue advantage over the younger one.
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kLazy = 6.0f;  // p <= 2^6 between rescales
 #ifndef KVQ_RING_DEPTH
 #define KVQ_RING_DEPTH 2  // quantised steps in flight per wave
@@ -614,11 +618,34 @@ __device__ inline void stage_get(const uint8_t* lds, const Ctx& c, Step<D, KB, V
   }
 }
 
+// Dynamic work claiming inside one segment.  Two waves share each SIMD and
+// the older one issues first, so with a fixed split the younger wave of every
+// SIMD ends several microseconds behind.  The workgroup's share of a segment
+// is cut into units of kUnitSteps steps; each wave takes one unit statically
+// (`first`), then claims more from a counter in LDS that hands out base + 0,
+// base + 1, ...  A claim is issued one unit ahead of its use.
+constexpr int kUnitSteps = 4;
+struct Claim {
+  int* ctr;   // LDS counter; nullptr: the wave takes the whole segment itself
+  int first;  // this wave's static unit
+  int base;   // units handed out statically (the claims start there)
+};
+// Issued by lane 0; the result is meaningful in lane 0 (read with readlane).
+__device__ inline int claim_unit(const Claim& cl, int lane) {
+  int r = 0;
+  if (lane == 0)
+    r = cl.base + __hip_atomic_fetch_add(cl.ctr, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  return r;
+}
+
 // One segment [x0, x1) of rows of one format, rows starting at plane row
 // row0 (K and V share row numbering).  KB/VB: stored widths (16 = bf16).
+// With cl.ctr set the wave processes the units it claims of the segment,
+// otherwise all of it.
 template <int D, int NG, int KB, int VB>
 __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int64_t row0,
-                            bool visual) {
+                            bool visual, const Claim& cl = Claim{nullptr, 0, 0}) {
   constexpr int NB = D / 16;
   constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
   const uint8_t* kp = (visual ? c.kvis : c.ktxt) + row0 * KR;
@@ -645,9 +672,10 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     pl.km = make_rsrc(kmp, int64_t(rows) * MR);
     pl.v = make_rsrc(vp, int64_t(rows) * VR);
     pl.vm = make_rsrc(vmp, int64_t(rows) * MR);
+    const int s0 = cl.ctr ? cl.first * kUnitSteps : 0;  // first step this wave computes
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
-      const int st = min(k, nsteps - 1);
+      const int st = min(s0 + k, nsteps - 1);
       stage_load<D, NG, KB, VB>(pl, st, rows_in(st), c.lane, g[k]);
     }
   }
@@ -662,39 +690,70 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   Step<D, KB, VB> sa;
   if constexpr (kStaged) {
     const uint32_t vsel = v_pair_selector<D, VB>((c.n * VBY) & 3);
-    // The ring is unrolled kDepth steps deep.  Loads are unconditional (past
-    // the last step they re-read it) so the compiler's wait counts stay
-    // exact; only the compute of steps past the end is skipped.
-    for (int i = 0; i < nsteps; i += kDepth) {
+    // The ring runs over this wave's units back to back: the step kDepth
+    // ahead lies in the current unit or, near its end, in the next one
+    // (kUnitSteps > kDepth), which is claimed a unit ahead -- or, without a
+    // claim counter, simply the following unit.  Loads stay unconditional
+    // (clamped to the last step) so the compiler's wait counts stay exact;
+    // only the compute of steps past the end is skipped.
+    static_assert(kUnitSteps > kDepth, "the ring looks at most one unit ahead");
+    const int n_units = (nsteps + kUnitSteps - 1) / kUnitSteps;
+    int u_cur = cl.ctr ? cl.first : 0, off = 0;
+    int pend = cl.ctr ? claim_unit(cl, c.lane) : 1;
+    while (u_cur < n_units) {
 #pragma unroll
       for (int k = 0; k < kDepth; ++k) {
-        const int st = i + k;
-        const int nxt = min(st + kDepth, nsteps - 1);
+        const int gs = u_cur * kUnitSteps + off;
+        const bool valid = u_cur < n_units && gs < nsteps;
         stage_put<D, NG, KB, VB>(c.stage, c.lane, g[k]);
-        stage_load<D, NG, KB, VB>(pl, nxt, rows_in(nxt), c.lane, g[k]);
+        int la_u = u_cur, la_off = off + kDepth;
+        if (la_off >= kUnitSteps) {
+          la_u = __builtin_amdgcn_readlane(pend, 0);
+          la_off -= kUnitSteps;
+        }
+        int la = la_u * kUnitSteps + la_off;
+        la = (la_u < n_units && la < nsteps) ? la : nsteps - 1;
+        stage_load<D, NG, KB, VB>(pl, la, rows_in(la), c.lane, g[k]);
         stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        if (st < nsteps) compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(st), vsel);
+        if (valid) compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(gs), vsel);
+        if (++off == kUnitSteps) {
+          off = 0;
+          u_cur = __builtin_amdgcn_readlane(pend, 0);
+          pend = cl.ctr ? claim_unit(cl, c.lane) : u_cur + 1;
+        }
       }
     }
+    if (cl.ctr) __builtin_amdgcn_s_waitcnt(0);  // the last (unused) claim has landed
   } else {
+    // bf16 rows (and bf16 K with quantised V) load straight into operands,
+    // one step at a time, over the same unit sequence
     const uint32_t vsel_mem = v_pair_selector<D, VB>(0);
     Offs<D, NG, KB, VB> of;
     of.full(c);
-    const int nfull = rows / 32;
-    for (int i = 0; i < nfull; ++i) {
-      const int64_t o = int64_t(i) * 32;
-      load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of,
-                                      sa);
-      compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, 32, vsel_mem);
+    const int n_units = (nsteps + kUnitSteps - 1) / kUnitSteps;
+    int u_cur = cl.ctr ? cl.first : 0;
+    int pend = cl.ctr ? claim_unit(cl, c.lane) : 1;
+    while (u_cur < n_units) {
+      for (int off = 0; off < kUnitSteps; ++off) {
+        const int st = u_cur * kUnitSteps + off;
+        if (st >= nsteps) break;
+        const int64_t o = int64_t(st) * 32;
+        const int rl = rows_in(st);
+        if (rl == 32) {
+          load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
+                                          of, sa);
+        } else {
+          Offs<D, NG, KB, VB> oc;
+          oc.clamped(c, rl);
+          load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
+                                         oc, sa);
+        }
+        compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rl, vsel_mem);
+      }
+      u_cur = __builtin_amdgcn_readlane(pend, 0);
+      pend = cl.ctr ? claim_unit(cl, c.lane) : u_cur + 1;
     }
-    const int tail = rows - 32 * nfull;
-    if (tail > 0) {
-      const int64_t o = int64_t(nfull) * 32;
-      of.clamped(c, tail);
-      load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of,
-                                     sa);
-      compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, tail, vsel_mem);
-    }
+    if (cl.ctr) __builtin_amdgcn_s_waitcnt(0);  // the last (unused) claim has landed
   }
 
 #pragma unroll
@@ -706,7 +765,7 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
 // (protected heads), so each instance carries two row paths -- the quantised
 // one and the bf16 one that text rows use anyway -- and nothing else.
 template <int D, int NG, int KB, int VB>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NB = D / 16;
   constexpr int g = D / NG;
   const int lane = threadIdx.x & 63;
@@ -719,9 +778,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(sizeof(DecodeArgs) % 16 == 0, "argument block copied in 16-byte pieces");
   constexpr int kArgVec = int(sizeof(DecodeArgs) / 16);
   __shared__ uint4 args_lds[kArgVec];
+  __shared__ int lds_claim;  // claim counter of the visual units (see Claim)
+  if (threadIdx.x == 0) lds_claim = 0;
   {
     const uint4* src = (const uint4*)(__builtin_amdgcn_kernarg_segment_ptr());
-    for (int i = threadIdx.x; i < kArgVec; i += 256) args_lds[i] = src[i];
+    for (int i = threadIdx.x; i < kArgVec; i += kThreads) args_lds[i] = src[i];
   }
   __syncthreads();
   const DecodeArgs& t = *reinterpret_cast<const DecodeArgs*>(args_lds);
@@ -746,7 +807,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnion];
 
   // the G query rows of this KV head: G * D bf16, 16 bytes per thread
-  // (G * D / 8 <= 256 threads; rows start 16-byte aligned since D * 2 >= 128)
+  // (G * D / 8 <= 256 <= kThreads; rows start 16-byte aligned since D * 2 >= 128)
   const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
   if (int(threadIdx.x) < G * D / 8)
     reinterpret_cast<uint4*>(q_lds)[threadIdx.x] = reinterpret_cast<const uint4*>(qp)[threadIdx.x];
@@ -783,25 +844,42 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 
   int wa, wb;
   wave_range(x, wave, nxs, len, a.chunk, kWaves, wa, wb);
-  if (wa < wb) {
+  {
     const int vb = __builtin_amdgcn_readfirstlane(t.vb[sl]);
     const int ve = __builtin_amdgcn_readfirstlane(t.ve[sl]);
     const int64_t vrow0 = __builtin_amdgcn_readfirstlane(t.vrow0[sl]);
     const int64_t trow0 = __builtin_amdgcn_readfirstlane(t.trow0[sl]);
     const bool quant_vis = !(KB == 16 && VB == 16) && kbits == KB && vbits == VB;
-    // text prefix [0, vb), visual [vb, ve), text suffix [ve, cap) in order;
+    // In a balanced split the workgroup's visual rows (the union of its
+    // waves' static ranges) are claimed in units by its waves; text rows, and
+    // everything in the fixed chunk mode, follow the static split [wa, wb).
+    // The static text rows go first so the claimed part absorbs their
+    // imbalance.
+    const bool dyn = a.chunk == 0;
+    int ga, gb, gt;
+    wave_range(x, 0, nxs, len, a.chunk, kWaves, ga, gt);
+    wave_range(x, kWaves - 1, nxs, len, a.chunk, kWaves, gt, gb);
+    const Claim cl{&lds_claim, wave, kWaves};
+    // segments: text prefix [0, vb), text suffix [ve, cap), visual [vb, ve);
     // kept as a loop so each row path is emitted once
 #pragma clang loop unroll(disable)
     for (int seg = 0; seg < 3; ++seg) {
-      const int x0 = seg == 0 ? wa : seg == 1 ? max(wa, vb) : max(wa, ve);
-      const int x1 = seg == 0 ? min(wb, vb) : seg == 1 ? min(wb, ve) : wb;
+      const bool vis = seg == 2;
+      int x0, x1;
+      if (vis && dyn) {
+        x0 = max(ga, vb);
+        x1 = min(gb, ve);
+      } else {
+        x0 = seg == 0 ? wa : vis ? max(wa, vb) : max(wa, ve);
+        x1 = seg == 0 ? min(wb, vb) : vis ? min(wb, ve) : wb;
+      }
       if (x0 >= x1) continue;
-      const int64_t row0 = seg == 1 ? vrow0 + (x0 - vb)
-                                    : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
-      if (seg == 1 && quant_vis)
-        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true);
+      const int64_t row0 = vis ? vrow0 + (x0 - vb) : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
+      const Claim use = vis && dyn ? cl : Claim{nullptr, 0, 0};
+      if (vis && quant_vis)
+        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true, use);
       else  // text rows, or bf16 visual rows of a protected head
-        run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, seg == 1);
+        run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, vis, use);
     }
   }
 
@@ -862,12 +940,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
   const int64_t pidx = partial_index(l_local, s, h, x, a.B, a.Hkv, a.max_chunks);
   uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += 256) {
+  for (int i = threadIdx.x; i < G * D; i += kThreads) {
     const int j = i / D, d = i % D, cr = j * NG + d / g;
-    const f32x4 f = *reinterpret_cast<const f32x4*>(wts[cr]);
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) acc += o_all[w][cr][d] * f[w];
+    for (int w4 = 0; w4 < kWaves / 4; ++w4) {
+      const f32x4 f = *reinterpret_cast<const f32x4*>(&wts[cr][4 * w4]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += o_all[4 * w4 + w][cr][d] * f[w];
+    }
     const float L = rowL[cr];
     const float o = L > 0.0f ? acc * __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
     if (single) {
@@ -911,7 +992,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   const float* gml = a.ws_ml + p0 * G * 2;
   const float* go = a.ws_o + p0 * G * D;
   constexpr int kLdsFloats = kUnion / 4;  // the whole stage / o_all area
-  constexpr int kPer = (kMaxGroupRatio * D + 255) / 256;  // output elements per thread
+  constexpr int kPer = (kMaxGroupRatio * D + kThreads - 1) / kThreads;  // elements per thread
   const int n_ml = nxs * G * 2;
   float* lml = reinterpret_cast<float*>(big_lds);  // [nxs][G] (m, l)
   float* lw = lml + n_ml;                           // [nxs][G] weights
@@ -932,18 +1013,18 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       const int n_o = nb * G * D;
       const Rsrc ro = make_rsrc(go + int64_t(c0) * G * D, int64_t(n_o) * 4);
       if (c0 > 0) __syncthreads();  // the previous batch is consumed
-      for (int v = threadIdx.x; v < n_o / 4; v += 256)
+      for (int v = threadIdx.x; v < n_o / 4; v += kThreads)
         reinterpret_cast<u32x4*>(lo)[v] =
             __builtin_amdgcn_raw_buffer_load_b128(ro, uint32_t(v) * 16u, 0, kCoherent);
       if (c0 == 0) {  // the (m, l) pairs travel with the first batch
-        for (int k = threadIdx.x; k < n_ml; k += 256)
+        for (int k = threadIdx.x; k < n_ml; k += kThreads)
           lml[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                  rm, uint32_t(k) * 4u, 0, kCoherent));
         __syncthreads();
         // one thread per (partial cx, head j): M_j over all partials (every
         // thread of head j reads the same pairs), then its own weight; the
         // partial rows are normalised (o / l), so the weight is l 2^(m - M_j)
-        for (int t = threadIdx.x; t < nxs * G; t += 256) {
+        for (int t = threadIdx.x; t < nxs * G; t += kThreads) {
           const int j = t % G;
           float M = -INFINITY;
 #pragma unroll 8
@@ -958,7 +1039,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < kPer; ++k) {
-        const int i = threadIdx.x + 256 * k;
+        const int i = threadIdx.x + kThreads * k;
         if (i < G * D) {
           const int j = i / D;
 #pragma unroll 4
@@ -975,7 +1056,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   } else {
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      const int i = threadIdx.x + 256 * k;
+      const int i = threadIdx.x + kThreads * k;
       if (i >= G * D) break;
       const int j = i / D;
       auto ld = [&](const float* p) {
@@ -997,7 +1078,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   }
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int i = threadIdx.x + 256 * k;
+    const int i = threadIdx.x + kThreads * k;
     if (i < G * D) outp[i] = __builtin_bit_cast(uint16_t, (__bf16)acc[k]);
   }
   if (threadIdx.x == 0)
@@ -1017,7 +1098,7 @@ bool mfma_supported(int D, int g, int G) {
 // object holds every part.
 #define KVQ_LAUNCH(DD, NN, K, V)                                                           \
   if (kb == K && vb == V) {                                                                \
-    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN, K, V>), grid, dim3(256), 0, stream, a); \
+    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN, K, V>), grid, dim3(kThreads), 0, stream, a); \
     return hipGetLastError();                                                              \
   }
 #define KVQ_PART_FN(DD, NN)                                                                 \

@@ -144,7 +144,7 @@ hipError_t launch_decode_mfma_64_1(const DecodeArgs& a, int kb, int vb, hipStrea
 hipError_t launch_decode_mfma_64_2(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int nl, int n_seq_launch,
                                hipStream_t stream);
-constexpr int kMfmaWaves = 4;      // waves per workgroup of the matrix-core kernel
+constexpr int kMfmaWaves = 8;      // waves per workgroup of the matrix-core kernel
 constexpr int kSimpleWaves = 4;    // waves per workgroup of the general kernel
 
 }  // namespace kvq
