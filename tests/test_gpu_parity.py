@@ -291,3 +291,18 @@ def test_decode_ragged_batch_full_size_sampled():
             ref.append(p.oracle_decode(0, s, i, lens[s], q[0, s, i]))
             got.append(out[0, s, i])
     assert_close(np.array(got), np.array(ref), "ragged batch")
+
+
+def test_decode_merge_of_many_partials():
+    """32-token chunks over 32,768 tokens: 1,024 partials per (layer, seq, head),
+    more than the merging workgroup can stage in LDS, so the merge reads them
+    from memory directly."""
+    _say("decode 1024 partials per head (merge from memory)")
+    w = synth.llava_layer(seed=17, kbits=4, vbits=2)
+    w.capacity = [32768]
+    w.vis_end = [32768]
+    w.seq_lens = [32768]
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [32768], chunk=32, what="1024 partials")
+    _check_decode(p, [32000], chunk=0, what="balanced, same cache")
