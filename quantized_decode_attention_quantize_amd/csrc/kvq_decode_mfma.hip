@@ -620,32 +620,31 @@ __device__ inline void stage_get(const uint8_t* lds, const Ctx& c, Step<D, KB, V
 
 // Dynamic work claiming inside one segment.  Two waves share each SIMD and
 // the older one issues first, so with a fixed split the younger wave of every
-// SIMD ends several microseconds behind.  The workgroup's share of a segment
-// is cut into units of kUnitSteps steps; each wave takes one unit statically
-// (`first`), then claims more from a counter in LDS that hands out base + 0,
-// base + 1, ...  A claim is issued one unit ahead of its use.
-constexpr int kUnitSteps = 4;
+// SIMD ends several microseconds behind.  Instead the workgroup's share of a
+// segment is handed out one 32-token step at a time: each wave starts on a
+// few steps of its own (`kWaves * per_wave` of them in all), then claims the
+// following steps from a counter in LDS.  A claim is issued ahead of its use,
+// so the LDS atomic's latency stays hidden.
 struct Claim {
-  int* ctr;   // LDS counter; nullptr: the wave takes the whole segment itself
-  int first;  // this wave's static unit
-  int base;   // units handed out statically (the claims start there)
+  int* ctr;  // LDS counter; nullptr: the wave takes the whole segment itself
+  int wave;  // this wave's index in the workgroup
 };
-// Issued by lane 0; the result is meaningful in lane 0 (read with readlane).
-__device__ inline int claim_unit(const Claim& cl, int lane) {
+// Next step from the counter (claims start after the statically taken ones);
+// issued by lane 0, meaningful in lane 0 (read with readlane).
+__device__ inline int claim_step(const Claim& cl, int lane, int base) {
   int r = 0;
   if (lane == 0)
-    r = cl.base + __hip_atomic_fetch_add(cl.ctr, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+    r = base + __hip_atomic_fetch_add(cl.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return r;
 }
 
 // One segment [x0, x1) of rows of one format, rows starting at plane row
 // row0 (K and V share row numbering).  KB/VB: stored widths (16 = bf16).
-// With cl.ctr set the wave processes the units it claims of the segment,
+// With cl.ctr set the wave processes the steps it claims of the segment,
 // otherwise all of it.
 template <int D, int NG, int KB, int VB>
 __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int64_t row0,
-                            bool visual, const Claim& cl = Claim{nullptr, 0, 0}) {
+                            bool visual, const Claim& cl = Claim{nullptr, 0}) {
   constexpr int NB = D / 16;
   constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
   const uint8_t* kp = (visual ? c.kvis : c.ktxt) + row0 * KR;
@@ -672,10 +671,9 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     pl.km = make_rsrc(kmp, int64_t(rows) * MR);
     pl.v = make_rsrc(vp, int64_t(rows) * VR);
     pl.vm = make_rsrc(vmp, int64_t(rows) * MR);
-    const int s0 = cl.ctr ? cl.first * kUnitSteps : 0;  // first step this wave computes
 #pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      const int st = min(s0 + k, nsteps - 1);
+    for (int k = 0; k < kDepth; ++k) {  // this wave's first steps (taken statically)
+      const int st = min(cl.ctr ? cl.wave * kDepth + k : k, nsteps - 1);
       stage_load<D, NG, KB, VB>(pl, st, rows_in(st), c.lane, g[k]);
     }
   }
@@ -690,70 +688,54 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   Step<D, KB, VB> sa;
   if constexpr (kStaged) {
     const uint32_t vsel = v_pair_selector<D, VB>((c.n * VBY) & 3);
-    // The ring runs over this wave's units back to back: the step kDepth
-    // ahead lies in the current unit or, near its end, in the next one
-    // (kUnitSteps > kDepth), which is claimed a unit ahead -- or, without a
-    // claim counter, simply the following unit.  Loads stay unconditional
-    // (clamped to the last step) so the compiler's wait counts stay exact;
-    // only the compute of steps past the end is skipped.
-    static_assert(kUnitSteps > kDepth, "the ring looks at most one unit ahead");
-    const int n_units = (nsteps + kUnitSteps - 1) / kUnitSteps;
-    int u_cur = cl.ctr ? cl.first : 0, off = 0;
-    int pend = cl.ctr ? claim_unit(cl, c.lane) : 1;
-    while (u_cur < n_units) {
+    // Ring slot k holds step slot[k]; after a slot's step is staged, the
+    // slot is refilled with the next claimed step (or, without a counter,
+    // the step kDepth further on).  A wave's steps increase, so once slot 0
+    // is past the end so is every later one.  Loads stay unconditional
+    // (clamped to the last step) so the compiler's wait counts stay exact.
+    const int base = kWaves * kDepth;
+    int slot[kDepth];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) slot[k] = cl.ctr ? cl.wave * kDepth + k : k;
+    int pend = cl.ctr ? claim_step(cl, c.lane, base) : kDepth;
+    while (slot[0] < nsteps) {
 #pragma unroll
       for (int k = 0; k < kDepth; ++k) {
-        const int gs = u_cur * kUnitSteps + off;
-        const bool valid = u_cur < n_units && gs < nsteps;
+        const int cur = slot[k];
         stage_put<D, NG, KB, VB>(c.stage, c.lane, g[k]);
-        int la_u = u_cur, la_off = off + kDepth;
-        if (la_off >= kUnitSteps) {
-          la_u = __builtin_amdgcn_readlane(pend, 0);
-          la_off -= kUnitSteps;
-        }
-        int la = la_u * kUnitSteps + la_off;
-        la = (la_u < n_units && la < nsteps) ? la : nsteps - 1;
+        const int nxt = __builtin_amdgcn_readlane(pend, 0);
+        pend = cl.ctr ? claim_step(cl, c.lane, base) : nxt + 1;
+        const int la = min(nxt, nsteps - 1);
         stage_load<D, NG, KB, VB>(pl, la, rows_in(la), c.lane, g[k]);
+        slot[k] = nxt;
         stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        if (valid) compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(gs), vsel);
-        if (++off == kUnitSteps) {
-          off = 0;
-          u_cur = __builtin_amdgcn_readlane(pend, 0);
-          pend = cl.ctr ? claim_unit(cl, c.lane) : u_cur + 1;
-        }
+        if (cur < nsteps) compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(cur), vsel);
       }
     }
-    if (cl.ctr) __builtin_amdgcn_s_waitcnt(0);  // the last (unused) claim has landed
   } else {
     // bf16 rows (and bf16 K with quantised V) load straight into operands,
-    // one step at a time, over the same unit sequence
+    // one claimed step at a time (the next claim flies while a step runs)
     const uint32_t vsel_mem = v_pair_selector<D, VB>(0);
     Offs<D, NG, KB, VB> of;
     of.full(c);
-    const int n_units = (nsteps + kUnitSteps - 1) / kUnitSteps;
-    int u_cur = cl.ctr ? cl.first : 0;
-    int pend = cl.ctr ? claim_unit(cl, c.lane) : 1;
-    while (u_cur < n_units) {
-      for (int off = 0; off < kUnitSteps; ++off) {
-        const int st = u_cur * kUnitSteps + off;
-        if (st >= nsteps) break;
-        const int64_t o = int64_t(st) * 32;
-        const int rl = rows_in(st);
-        if (rl == 32) {
-          load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
-                                          of, sa);
-        } else {
-          Offs<D, NG, KB, VB> oc;
-          oc.clamped(c, rl);
-          load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
-                                         oc, sa);
-        }
-        compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rl, vsel_mem);
+    int st = cl.ctr ? cl.wave : 0;
+    int pend = cl.ctr ? claim_step(cl, c.lane, kWaves) : 1;
+    while (st < nsteps) {
+      const int64_t o = int64_t(st) * 32;
+      const int rl = rows_in(st);
+      if (rl == 32) {
+        load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
+                                        of, sa);
+      } else {
+        Offs<D, NG, KB, VB> oc;
+        oc.clamped(c, rl);
+        load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
+                                       oc, sa);
       }
-      u_cur = __builtin_amdgcn_readlane(pend, 0);
-      pend = cl.ctr ? claim_unit(cl, c.lane) : u_cur + 1;
+      compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rl, vsel_mem);
+      st = __builtin_amdgcn_readlane(pend, 0);
+      pend = cl.ctr ? claim_step(cl, c.lane, kWaves) : st + 1;
     }
-    if (cl.ctr) __builtin_amdgcn_s_waitcnt(0);  // the last (unused) claim has landed
   }
 
 #pragma unroll
@@ -778,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   static_assert(sizeof(DecodeArgs) % 16 == 0, "argument block copied in 16-byte pieces");
   constexpr int kArgVec = int(sizeof(DecodeArgs) / 16);
   __shared__ uint4 args_lds[kArgVec];
-  __shared__ int lds_claim;  // claim counter of the visual units (see Claim)
+  __shared__ int lds_claim;  // claim counter of the visual steps (see Claim)
   if (threadIdx.x == 0) lds_claim = 0;
   {
     const uint4* src = (const uint4*)(__builtin_amdgcn_kernarg_segment_ptr());
@@ -851,7 +833,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const int64_t trow0 = __builtin_amdgcn_readfirstlane(t.trow0[sl]);
     const bool quant_vis = !(KB == 16 && VB == 16) && kbits == KB && vbits == VB;
     // In a balanced split the workgroup's visual rows (the union of its
-    // waves' static ranges) are claimed in units by its waves; text rows, and
+    // waves' static ranges) are claimed step by step by its waves; text rows, and
     // everything in the fixed chunk mode, follow the static split [wa, wb).
     // The static text rows go first so the claimed part absorbs their
     // imbalance.
@@ -859,7 +841,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     int ga, gb, gt;
     wave_range(x, 0, nxs, len, a.chunk, kWaves, ga, gt);
     wave_range(x, kWaves - 1, nxs, len, a.chunk, kWaves, gt, gb);
-    const Claim cl{&lds_claim, wave, kWaves};
+    const Claim cl{&lds_claim, wave};
     // segments: text prefix [0, vb), text suffix [ve, cap), visual [vb, ve);
     // kept as a loop so each row path is emitted once
 #pragma clang loop unroll(disable)
@@ -875,7 +857,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       }
       if (x0 >= x1) continue;
       const int64_t row0 = vis ? vrow0 + (x0 - vb) : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
-      const Claim use = vis && dyn ? cl : Claim{nullptr, 0, 0};
+      const Claim use = vis && dyn ? cl : Claim{nullptr, 0};
       if (vis && quant_vis)
         run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true, use);
       else  // text rows, or bf16 visual rows of a protected head
