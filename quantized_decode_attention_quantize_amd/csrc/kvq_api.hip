@@ -11,6 +11,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <memory>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -129,71 +131,234 @@ int device_cus() {
 static_assert(sizeof(DecodeArgs) <= 4096, "decode kernel arguments exceed 4 KB");
 static_assert(sizeof(QuantizeArgs) <= 4096, "quantize kernel arguments exceed 4 KB");
 
+// One kernel launch of a decode call: up to kMaxLH (layer, head) slots of
+// one visual format over up to kMaxSeq sequences.  Work is laid out in units
+// (waves of the matrix-core kernel, workgroups of the general one): slot i
+// and sequence s get mult[i] * nx[s] consecutive units, slot-major.
+struct LaunchPlan {
+  int key;                  // matrix-core format key kb * 32 + vb; -1: general kernel
+  int s0, ns;               // sequences [s0, s0 + ns) of the call
+  std::vector<int> glh;     // per slot: layer-local * Hkv + head
+  std::vector<int> mult;    // per slot
+  std::vector<int> nx;      // per sequence of the launch
+  bool merge_after;         // general kernel: merge partials after this launch
+};
+
 struct DecodePlan {
-  int chunk;                  // tokens per workgroup; 0 = balanced split
-  std::vector<int> nx;        // [batch] workgroups per (layer, head) before mult
-  std::vector<uint8_t> mult;  // [num_layers * Hkv] of the call: heavy-head multiplier
-  int max_chunks;
+  int chunk;                // tokens per split; 0 = balanced split
+  std::vector<LaunchPlan> launches;
+  int max_chunks;           // partial slots per (layer, seq, head)
   int64_t entries;
   size_t o_bytes, ml_bytes, cnt_bytes, arrive_bytes, total;
 };
 
+// Relative time of one row of a (layer, head) pair on the matrix-core
+// kernel: the bytes its visual row moves plus a fixed share for the per-row
+// arithmetic (waves of INT4/INT2 and of bf16 heads at D = 128 running side by
+// side take about 1 : 3.5 per row, which this reproduces).
+double row_cost(int D, int g, int kb, int vb) {
+  double bytes = vis_row_bytes(D, kb) + vis_row_bytes(D, vb);
+  if (kb < 16) bytes += (D / g) * 4;
+  if (vb < 16) bytes += (D / g) * 4;
+  return 0.38 * D + bytes;
+}
+
+// Smallest-maximum split of `budget` units over items of weight w[k], each
+// item at least one unit: n[k] = max(1, ceil(w[k] / T)) for the least T (to
+// bisection precision) with sum n <= budget.  Needs budget >= w.size().
+void minmax_split(const std::vector<double>& w, int64_t budget, std::vector<int>& n) {
+  const int64_t K = int64_t(w.size());
+  double wmax = 0.0, wsum = 0.0;
+  for (double x : w) {
+    wmax = std::max(wmax, x);
+    wsum += x;
+  }
+  if (wmax <= 0.0) wmax = wsum = 1.0;
+  auto units = [](double x, double T) {
+    return std::max<int64_t>(1, int64_t(std::ceil(x / T)));
+  };
+  auto need = [&](double T) {
+    int64_t t = 0;
+    for (double x : w) t += units(x, T);
+    return t;
+  };
+  // sum ceil(w / T) lies in [wsum / T, wsum / T + K], so the optimum lies in
+  // [wsum / budget, wsum / (budget - K)] (and T = wmax always fits)
+  double lo = wsum / double(budget), hi = wmax;
+  if (budget > K) hi = std::min(hi, wsum / double(budget - K));
+  if (need(hi) > budget) hi = wmax;
+  for (int it = 0; it < 24; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (need(mid) <= budget) hi = mid; else lo = mid;
+  }
+  n.resize(w.size());
+  for (size_t k = 0; k < w.size(); ++k) n[k] = int(units(w[k], hi));
+}
+
+// Balanced split of one matrix-core launch over `waves` units.  Per
+// (slot i, seq s) the work is cost[i] * cap[s]; the layout gives it
+// mult[i] * nx[s] units, so the slowest unit takes
+// max_i(cost_i / mult_i) * max_s(cap_s / nx_s), which is returned.  For each
+// candidate total X of nx, nx is the smallest-maximum split of X by capacity
+// and mult that of waves / X by cost; the best candidate wins.
+double balance_units(const std::vector<double>& cost, const std::vector<double>& cap,
+                     int64_t waves, std::vector<int>& mult, std::vector<int>& nx) {
+  const int64_t S = int64_t(cost.size()), B = int64_t(cap.size());
+  const int64_t xmax = std::max<int64_t>(B, waves / S);
+  const int64_t span = xmax - B + 1;
+  const int64_t ncand = std::min<int64_t>(span, 32);
+  double best = -1.0;
+  int64_t best_units = 0;
+  std::vector<int> m, x;
+  for (int64_t k = 0; k < ncand; ++k) {
+    const int64_t X = ncand == 1 ? B : B + (span - 1) * k / (ncand - 1);
+    minmax_split(cap, X, x);
+    int64_t xs = 0;
+    for (int v : x) xs += v;
+    minmax_split(cost, std::max<int64_t>(S, waves / xs), m);
+    double tm = 0.0, tx = 0.0;
+    int64_t ms = 0;
+    for (int64_t i = 0; i < S; ++i) {
+      tm = std::max(tm, cost[i] / m[i]);
+      ms += m[i];
+    }
+    for (int64_t s = 0; s < B; ++s) tx = std::max(tx, cap[s] / x[s]);
+    const double t = tm * tx;
+    if (best < 0.0 || t < best * (1.0 - 1e-9) || (t <= best * (1.0 + 1e-9) && ms * xs < best_units)) {
+      best = t;
+      best_units = ms * xs;
+      mult = m;
+      nx = x;
+    }
+  }
+  return best;
+}
+
+// Balanced split of one matrix-core launch over `waves` wave slots, in
+// waves.  A split in whole workgroups (every entry a multiple of 8 waves)
+// keeps each (layer, seq, head) of a workgroup on one claim counter and
+// leaves fewer partials to merge; it is taken unless the wave-granular split
+// is clearly faster (the loop often runs near the memory bound, where extra
+// balance buys less than the model says).
+void balance_launch(const std::vector<double>& cost, const std::vector<double>& cap,
+                    int64_t waves, std::vector<int>& mult, std::vector<int>& nx) {
+  std::vector<int> mw, xw, mg, xg;
+  const double tw = balance_units(cost, cap, waves, mw, xw);
+  const int64_t groups = waves / kMfmaWaves;
+  if (groups >= int64_t(cost.size()) * int64_t(cap.size())) {
+    const double tg = balance_units(cost, cap, groups, mg, xg) / kMfmaWaves;
+    if (tg <= 1.15 * tw) {
+      for (int& m : mg) m *= kMfmaWaves;
+      mult = mg;
+      nx = xg;
+      return;
+    }
+  }
+  mult = mw;
+  nx = xw;
+}
+
+// Pieces (workgroups touched) of the unit range [w0, w0 + n) at `per` units
+// per workgroup.
+int64_t pieces(int64_t w0, int64_t n, int per) { return (w0 + n - 1) / per - w0 / per + 1; }
+
 // Split planning.  With chunk_tokens > 0 (or on the general kernel) every
-// workgroup takes a fixed token chunk.  Otherwise (matrix-core kernel) the
-// split is balanced: each (layer, seq, head) gets workgroups in proportion to
-// its capacity and cost so that all waves fit the device in one round
-// (8 waves per CU: the kernel runs at two waves per SIMD); all-bf16 heads move
-// ~4.6x the bytes per token of INT4/INT2 heads and take about twice as long
-// per step, so they get twice the workgroups.
+// (layer, seq, head) is cut into fixed token chunks, one workgroup each.
+// Otherwise (matrix-core kernel) each launch spreads its work over all the
+// device's wave slots (8 waves per CU, two per SIMD) with the balanced split
+// above; a workgroup may then hold waves of several (layer, seq, head)
+// entries.
 DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_tokens,
                        bool use_mfma) {
   DecodePlan p;
-  const int B = c->batch, Hkv = c->num_kv_heads;
-  p.nx.assign(B, 1);
-  p.mult.assign(size_t(nl) * Hkv, 1);
-  if (chunk_tokens > 0 || !use_mfma) {
-    p.chunk = chunk_tokens > 0 ? chunk_tokens : default_chunk(c, nl, 256, 1024);
-    for (int s = 0; s < B; ++s) p.nx[s] = (c->capacity[s] + p.chunk - 1) / p.chunk;
-  } else {
-    p.chunk = 0;
-    int64_t msum = 0;
-    for (int i = 0; i < nl * Hkv; ++i) {
-      const int l = layer_begin + i / Hkv, h = i % Hkv;
-      p.mult[i] = (bits_of(c, l, h, 0) == 16 && bits_of(c, l, h, 1) == 16) ? 2 : 1;
-      msum += p.mult[i];
-    }
-    int64_t caps = 0;
-    for (int s = 0; s < B; ++s) caps += c->capacity[s];
-    // Budget: one 8-wave workgroup per CU (the kernel runs two waves per
-    // SIMD), so every CU carries the same load and all waves run in one round.
-    const int64_t budget = int64_t(device_cus());
-    constexpr int kMinWaveTokens = 128;  // keep >= 4 steps per wave
-    std::vector<double> frac(B);
-    int64_t used = 0;
-    for (int s = 0; s < B; ++s) {
-      const double want = double(budget) * double(c->capacity[s]) / double(caps * msum);
-      const int nmax = (c->capacity[s] + kMfmaWaves * kMinWaveTokens - 1) /
-                       (kMfmaWaves * kMinWaveTokens);
-      p.nx[s] = std::max(1, std::min(int(want), nmax));
-      frac[s] = p.nx[s] < nmax ? want - std::floor(want) : -1.0;
-      used += int64_t(p.nx[s]) * msum;
-    }
-    // largest remainders take what is left of the budget
-    while (used + msum <= budget) {
-      int best = -1;
-      for (int s = 0; s < B; ++s)
-        if (frac[s] > 0.0 && (best < 0 || frac[s] > frac[best])) best = s;
-      if (best < 0) break;
-      ++p.nx[best];
-      frac[best] = -1.0;
-      used += msum;
-    }
+  const int B = c->batch, Hkv = c->num_kv_heads, D = c->head_dim, g = c->group_size;
+  const int nlh = nl * Hkv;
+  p.chunk = chunk_tokens > 0 || !use_mfma
+                ? (chunk_tokens > 0 ? chunk_tokens : default_chunk(c, nl, 256, 1024))
+                : 0;
+
+  // Heavier (layer, head) pairs first.  Matrix-core launches are per visual
+  // format: each takes the pairs whose visual K/V widths are one (kb, vb)
+  // combination, and the all-bf16 (protected) pairs ride along with the
+  // first such group.
+  std::vector<int> order(nlh);
+  for (int i = 0; i < nlh; ++i) order[i] = i;
+  auto row_bytes = [&](int glh) {
+    const int l = layer_begin + glh / Hkv, h = glh % Hkv;
+    return vis_row_bytes(D, bits_of(c, l, h, 0)) + vis_row_bytes(D, bits_of(c, l, h, 1));
+  };
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return row_bytes(x) > row_bytes(y); });
+  std::vector<int> fkey(nlh);
+  std::vector<int> groups;  // distinct keys kb * 32 + vb, in slot order
+  for (int i = 0; i < nlh; ++i) {
+    const int glh = order[i], l = layer_begin + glh / Hkv, h = glh % Hkv;
+    fkey[i] = bits_of(c, l, h, 0) * 32 + bits_of(c, l, h, 1);
   }
-  int mx = 1;
-  for (int s = 0; s < B; ++s) mx = std::max(mx, p.nx[s]);
-  int mm = 1;
-  for (uint8_t m : p.mult) mm = std::max<int>(mm, m);
-  p.max_chunks = mx * mm;
+  for (int i = 0; i < nlh; ++i)
+    if (fkey[i] != 16 * 32 + 16 && std::find(groups.begin(), groups.end(), fkey[i]) == groups.end())
+      groups.push_back(fkey[i]);
+  if (groups.empty()) groups.push_back(16 * 32 + 16);
+  if (!use_mfma) groups.assign(1, -1);  // the general kernel takes every format
+
+  const int64_t wave_slots = int64_t(kMfmaWaves) * device_cus();
+  constexpr int kMinWaveRows = 64;  // fewer rows per wave only add merge work
+  int64_t max_pieces = 1;
+  for (int s0 = 0; s0 < B; s0 += kMaxSeq) {
+    const int ns = std::min(kMaxSeq, B - s0);
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      std::vector<int> sel;
+      for (int i = 0; i < nlh; ++i)
+        if (groups[gi] < 0 || fkey[i] == groups[gi] || (gi == 0 && fkey[i] == 16 * 32 + 16))
+          sel.push_back(order[i]);
+      for (size_t k0 = 0; k0 < sel.size(); k0 += kMaxLH) {
+        LaunchPlan L;
+        L.key = groups[gi];
+        L.s0 = s0;
+        L.ns = ns;
+        L.glh.assign(sel.begin() + k0, sel.begin() + std::min(sel.size(), k0 + kMaxLH));
+        L.merge_after = false;
+        const int S = int(L.glh.size());
+        if (p.chunk > 0) {
+          // fixed chunks: one workgroup (8 waves on the matrix-core kernel) each
+          L.mult.assign(S, use_mfma ? kMfmaWaves : 1);
+          L.nx.resize(ns);
+          for (int i = 0; i < ns; ++i) L.nx[i] = (c->capacity[s0 + i] + p.chunk - 1) / p.chunk;
+        } else {
+          std::vector<double> cost(S), cap(ns);
+          double rows = 0.0;
+          for (int i = 0; i < S; ++i) {
+            const int l = layer_begin + L.glh[i] / Hkv, h = L.glh[i] % Hkv;
+            cost[i] = row_cost(D, g, bits_of(c, l, h, 0), bits_of(c, l, h, 1));
+          }
+          for (int i = 0; i < ns; ++i) {
+            cap[i] = c->capacity[s0 + i];
+            rows += cap[i] * S;
+          }
+          const int64_t waves = std::max<int64_t>(
+              1, std::min<int64_t>(wave_slots, int64_t(rows / kMinWaveRows)));
+          balance_launch(cost, cap, waves, L.mult, L.nx);
+        }
+        // partials per (layer, seq, head): workgroups its unit range touches
+        const int per = use_mfma ? kMfmaWaves : 1;
+        int64_t xs = 0, mc = 0;
+        for (int v : L.nx) xs += v;
+        for (int i = 0; i < S; ++i) {
+          int64_t xc = 0;
+          for (int s = 0; s < ns; ++s) {
+            const int64_t w0 = xs * mc + int64_t(L.mult[i]) * xc;
+            max_pieces = std::max(max_pieces, pieces(w0, int64_t(L.mult[i]) * L.nx[s], per));
+            xc += L.nx[s];
+          }
+          mc += L.mult[i];
+        }
+        p.launches.push_back(std::move(L));
+      }
+    }
+    // the general kernel leaves split partials for a separate merge
+    if (!use_mfma) p.launches.back().merge_after = true;
+  }
+  p.max_chunks = int(max_pieces);
   const int G = c->num_q_heads / c->num_kv_heads;
   p.entries = int64_t(nl) * B * Hkv * p.max_chunks;
   p.o_bytes = size_t(align256(p.entries * G * c->head_dim * 4));
@@ -202,6 +367,34 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
   p.arrive_bytes = size_t(align256(int64_t(nl) * B * Hkv * 4));
   p.total = p.o_bytes + p.ml_bytes + p.cnt_bytes + p.arrive_bytes;
   return p;
+}
+
+// Plans depend only on the call's shape (not on the sequence lengths, which
+// stay on the device), and decoding repeats one shape step after step, so the
+// last few plans are kept, keyed by everything plan_decode reads.
+std::shared_ptr<const DecodePlan> cached_plan(const kvq_config* c, int layer_begin, int nl,
+                                              int chunk_tokens, bool use_mfma) {
+  constexpr size_t kKeep = 4;
+  static std::mutex mu;
+  static std::vector<std::pair<std::vector<int32_t>, std::shared_ptr<const DecodePlan>>> kept;
+  const int Hkv = c->num_kv_heads;
+  std::vector<int32_t> key = {layer_begin, nl, chunk_tokens, int32_t(use_mfma), device_cus(),
+                              c->batch, c->num_q_heads, Hkv, c->head_dim, c->group_size};
+  key.reserve(key.size() + c->batch + size_t(nl) * Hkv);
+  for (int s = 0; s < c->batch; ++s) key.push_back(c->capacity[s]);
+  for (int i = layer_begin * Hkv; i < (layer_begin + nl) * Hkv; ++i)
+    key.push_back(c->k_bits[i] * 32 + c->v_bits[i]);
+  std::lock_guard<std::mutex> lock(mu);
+  for (size_t i = 0; i < kept.size(); ++i)
+    if (kept[i].first == key) {
+      std::rotate(kept.begin(), kept.begin() + i, kept.begin() + i + 1);  // most recent first
+      return kept.front().second;
+    }
+  auto plan = std::make_shared<const DecodePlan>(
+      plan_decode(c, layer_begin, nl, chunk_tokens, use_mfma));
+  kept.insert(kept.begin(), {std::move(key), plan});
+  if (kept.size() > kKeep) kept.pop_back();
+  return plan;
 }
 
 }  // namespace
@@ -325,7 +518,9 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
     const bool use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
-    const DecodePlan plan = plan_decode(cfg, layer_begin, num_layers, chunk_tokens, use_mfma);
+    const std::shared_ptr<const DecodePlan> plan_ptr =
+        cached_plan(cfg, layer_begin, num_layers, chunk_tokens, use_mfma);
+    const DecodePlan& plan = *plan_ptr;
     if (!workspace) {
       *workspace_bytes = plan.total;
       return KVQ_OK;
@@ -339,38 +534,16 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
     if (lay.info.total_bytes / 256 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
 
     const int Hkv = cfg->num_kv_heads;
-    const int nlh = num_layers * Hkv;
-    // Heavier (layer, head) pairs first so long workgroups start early.
-    std::vector<int> order(nlh);
-    for (int i = 0; i < nlh; ++i) order[i] = i;
-    std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
-      const int lx = layer_begin + x / Hkv, hx = x % Hkv, ly = layer_begin + y / Hkv, hy = y % Hkv;
-      const int bx = vis_row_bytes(lay.D, bits_of(cfg, lx, hx, 0)) + vis_row_bytes(lay.D, bits_of(cfg, lx, hx, 1));
-      const int by = vis_row_bytes(lay.D, bits_of(cfg, ly, hy, 0)) + vis_row_bytes(lay.D, bits_of(cfg, ly, hy, 1));
-      return bx > by;
-    });
-
-    // Matrix-core launches are per visual format: each launch takes the pairs
-    // whose visual K/V widths are one (kb, vb) combination, and the all-bf16
-    // (protected) pairs ride along with the first such group.
-    std::vector<int> fkey(nlh);
-    std::vector<int> groups;  // distinct keys kb * 32 + vb, in slot order
-    for (int i = 0; i < nlh; ++i) {
-      const int glh = order[i], l = layer_begin + glh / Hkv, h = glh % Hkv;
-      fkey[i] = bits_of(cfg, l, h, 0) * 32 + bits_of(cfg, l, h, 1);
+    // unit counts of every launch fit the kernels' 32-bit block arithmetic
+    for (const LaunchPlan& L : plan.launches) {
+      int64_t xs = 0, ms = 0;
+      for (int v : L.nx) xs += v;
+      for (int v : L.mult) ms += v;
+      if (xs * ms >= (int64_t(1) << 31) || ms > 0xFFFF) return KVQ_ERR_UNSUPPORTED;
     }
-    for (int i = 0; i < nlh; ++i)
-      if (fkey[i] != 16 * 32 + 16 && std::find(groups.begin(), groups.end(), fkey[i]) == groups.end())
-        groups.push_back(fkey[i]);
-    if (groups.empty()) groups.push_back(16 * 32 + 16);
-    if (!use_mfma) groups.assign(1, -1);  // the general kernel takes every format
-
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    std::vector<int> sel;
-    sel.reserve(nlh);
-    for (int s0 = 0; s0 < cfg->batch; s0 += kMaxSeq) {
-      const int ns_l = std::min(kMaxSeq, cfg->batch - s0);
+    for (const LaunchPlan& L : plan.launches) {
       DecodeArgs a;
       std::memset(&a, 0, sizeof(a));
       a.cache = static_cast<const uint8_t*>(cache);
@@ -391,46 +564,37 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
       a.B = cfg->batch;
       a.chunk = plan.chunk;
       a.max_chunks = plan.max_chunks;
-      a.seq_off = s0;
-      for (int i = 0; i < ns_l; ++i) {
-        const int s = s0 + i;
+      a.seq_off = L.s0;
+      a.n_seq = L.ns;
+      for (int i = 0; i < L.ns; ++i) {
+        const int s = L.s0 + i;
         a.vb[i] = cfg->vis_begin[s];
         a.ve[i] = cfg->vis_end[s];
         a.cap[i] = cfg->capacity[s];
         a.vrow0[i] = int32_t(lay.vrow0[s]);
         a.trow0[i] = int32_t(lay.trow0[s]);
-        a.nx[i] = plan.nx[s];
-        a.nxcum[i + 1] = a.nxcum[i] + plan.nx[s];
+        a.nx[i] = L.nx[i];
+        a.nxcum[i + 1] = a.nxcum[i] + L.nx[i];
       }
-      a.n_seq = ns_l;
-      for (size_t gi = 0; gi < groups.size(); ++gi) {
-        const int key = groups[gi];
-        sel.clear();
-        for (int i = 0; i < nlh; ++i)
-          if (key < 0 || fkey[i] == key || (gi == 0 && fkey[i] == 16 * 32 + 16)) sel.push_back(i);
-        for (size_t k0 = 0; k0 < sel.size(); k0 += kMaxLH) {
-          const int nlh_l = int(std::min<size_t>(kMaxLH, sel.size() - k0));
-          a.n_lh = nlh_l;
-          for (int i = 0; i < nlh_l; ++i) {
-            const int glh = order[sel[k0 + i]];  // layer-local * Hkv + head
-            const int l = layer_begin + glh / Hkv, h = glh % Hkv;
-            for (int X = 0; X < 2; ++X) {
-              a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * Hkv + h) * 2 + X] / 256);
-              a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
-            }
-            a.lh_glob[i] = uint16_t(glh);
-            a.mult[i] = plan.mult[glh];
-            a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
-          }
-          const hipError_t e = use_mfma ? launch_decode_mfma(a, key / 32, key % 32, hs)
-                                        : launch_decode_simple(a, ns_l, hs);
-          if (e != hipSuccess) return KVQ_ERR_HIP;
+      a.n_lh = int(L.glh.size());
+      for (int i = 0; i < a.n_lh; ++i) {
+        const int glh = L.glh[i];  // layer-local * Hkv + head
+        const int l = layer_begin + glh / Hkv, h = glh % Hkv;
+        for (int X = 0; X < 2; ++X) {
+          a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * Hkv + h) * 2 + X] / 256);
+          a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
         }
+        a.lh_glob[i] = uint16_t(glh);
+        a.mult[i] = uint16_t(L.mult[i]);
+        a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
       }
+      const hipError_t e = use_mfma ? launch_decode_mfma(a, L.key / 32, L.key % 32, hs)
+                                    : launch_decode_simple(a, L.ns, hs);
+      if (e != hipSuccess) return KVQ_ERR_HIP;
       // the general kernel leaves split partials for a separate merge; the
       // matrix-core kernel merges them itself
-      if (!use_mfma && plan.max_chunks > 1 &&
-          launch_decode_merge(a, num_layers, ns_l, hs) != hipSuccess)
+      if (L.merge_after && plan.max_chunks > 1 &&
+          launch_decode_merge(a, num_layers, L.ns, hs) != hipSuccess)
         return KVQ_ERR_HIP;
     }
     return KVQ_OK;

@@ -259,7 +259,10 @@ struct Ctx {
   const uint8_t* vvis;
   const uint8_t* vmeta;
   const uint8_t* vtxt;
-  const uint16_t* q_lds;   // [G][D] bf16 bits of this workgroup's queries
+  uint16_t* q_lds;         // [G][D] bf16 bits of this wave's queries
+  u32x4 qreg[4];           // the same, as loaded: 16 bytes per lane per entry (the
+                           // first D / (32 NG) used), written to q_lds once the
+                           // segment's first loads are out
   uint8_t* stage;          // this wave's LDS stage (kStageBytes)
   float qscale;
   int G;
@@ -622,12 +625,13 @@ __device__ inline void stage_get(const uint8_t* lds, const Ctx& c, Step<D, KB, V
 // the older one issues first, so with a fixed split the younger wave of every
 // SIMD ends several microseconds behind.  Instead the workgroup's share of a
 // segment is handed out one 32-token step at a time: each wave starts on a
-// few steps of its own (`kWaves * per_wave` of them in all), then claims the
-// following steps from a counter in LDS.  A claim is issued ahead of its use,
-// so the LDS atomic's latency stays hidden.
+// few steps of its own, then claims the following steps from a counter in
+// LDS shared by the workgroup's waves of the same (layer, seq, head).  A
+// claim is issued ahead of its use, so the LDS atomic's latency stays hidden.
 struct Claim {
   int* ctr;  // LDS counter; nullptr: the wave takes the whole segment itself
-  int wave;  // this wave's index in the workgroup
+  int wave;  // this wave's index among the waves sharing the counter
+  int nw;    // waves sharing the counter
 };
 // Next step from the counter (claims start after the statically taken ones);
 // issued by lane 0, meaningful in lane 0 (read with readlane).
@@ -644,7 +648,7 @@ __device__ inline int claim_step(const Claim& cl, int lane, int base) {
 // otherwise all of it.
 template <int D, int NG, int KB, int VB>
 __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int64_t row0,
-                            bool visual, const Claim& cl = Claim{nullptr, 0}) {
+                            bool visual, const Claim& cl = Claim{nullptr, 0, 1}) {
   constexpr int NB = D / 16;
   constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
   const uint8_t* kp = (visual ? c.kvis : c.ktxt) + row0 * KR;
@@ -678,6 +682,13 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     }
   }
 
+  // the query rows reach LDS only now, so their load latency overlaps the
+  // first K/V loads (the same wave reads them back: no barrier needed)
+#pragma unroll
+  for (int k = 0; k < D / (32 * NG); ++k) {
+    const int i = c.lane + 64 * k;
+    if (i < c.G * D / 8) reinterpret_cast<u32x4*>(c.q_lds)[i] = c.qreg[k];
+  }
   u32x4 qop[D / 32];
   const float qsr = build_q<D, NG, KB>(c, qop);
   const float c24 = c.qscale * 16777216.0f;  // 2^24 * qscale
@@ -693,7 +704,7 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     // the step kDepth further on).  A wave's steps increase, so once slot 0
     // is past the end so is every later one.  Loads stay unconditional
     // (clamped to the last step) so the compiler's wait counts stay exact.
-    const int base = kWaves * kDepth;
+    const int base = cl.nw * kDepth;
     int slot[kDepth];
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) slot[k] = cl.ctr ? cl.wave * kDepth + k : k;
@@ -719,7 +730,7 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     Offs<D, NG, KB, VB> of;
     of.full(c);
     int st = cl.ctr ? cl.wave : 0;
-    int pend = cl.ctr ? claim_step(cl, c.lane, kWaves) : 1;
+    int pend = cl.ctr ? claim_step(cl, c.lane, cl.nw) : 1;
     while (st < nsteps) {
       const int64_t o = int64_t(st) * 32;
       const int rl = rows_in(st);
@@ -734,7 +745,7 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
       }
       compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rl, vsel_mem);
       st = __builtin_amdgcn_readlane(pend, 0);
-      pend = cl.ctr ? claim_step(cl, c.lane, kWaves) : st + 1;
+      pend = cl.ctr ? claim_step(cl, c.lane, cl.nw) : st + 1;
     }
   }
 
@@ -742,238 +753,54 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= 1.0f / v_inflation<D, VB>(mb);
 }
 
-// One instance per (D, groups per row, visual K/V widths): a launch holds
-// only (layer, head) pairs whose visual rows have widths (KB, VB) or are bf16
-// (protected heads), so each instance carries two row paths -- the quantised
-// one and the bf16 one that text rows use anyway -- and nothing else.
-template <int D, int NG, int KB, int VB>
-__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NB = D / 16;
-  constexpr int g = D / NG;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+// Unit b of a launch -> slot, sequence index within the launch and x, the
+// unit's index among the mult[slot] * nx[seq] units of that (slot, sequence)
+// (see DecodeArgs::mult), searched by the whole wave at once: lane l tests
+// table entry l (and l + 64), and the number of entries at or below b is the
+// index.  b must be wave-uniform; the results are.
+__device__ inline void decode_unit(const DecodeArgs& t, int b, int n_lh, int n_seq, int lane,
+                                   int& slot, int& sl, int& x) {
+  static_assert(kMaxLH <= 128 && kMaxSeq <= 64, "two ballots cover the slot table, one the sequences");
+  const int per_mult = t.nxcum[n_seq];  // units of one slot with mult 1
+  const bool lo = lane < n_lh && per_mult * int(t.mcum[lane]) <= b;
+  const bool hi = lane + 64 < n_lh && per_mult * int(t.mcum[lane + 64]) <= b;
+  slot = __builtin_popcountll(__ballot(lo)) + __builtin_popcountll(__ballot(hi)) - 1;
+  const int m = t.mult[slot];
+  const int r = b - per_mult * int(t.mcum[slot]);
+  sl = __builtin_popcountll(__ballot(lane < n_seq && m * t.nxcum[lane] <= r)) - 1;
+  x = r - m * t.nxcum[sl];
+}
 
-  // The per-slot / per-sequence tables are indexed by values computed here, so
-  // reading them from the argument segment would chain a dozen dependent
-  // memory round trips.  One cooperative 16-byte copy puts the whole argument
-  // block in LDS; every table lookup below is then an LDS read.
-  static_assert(sizeof(DecodeArgs) % 16 == 0, "argument block copied in 16-byte pieces");
-  constexpr int kArgVec = int(sizeof(DecodeArgs) / 16);
-  __shared__ uint4 args_lds[kArgVec];
-  __shared__ int lds_claim;  // claim counter of the visual steps (see Claim)
-  if (threadIdx.x == 0) lds_claim = 0;
-  {
-    const uint4* src = (const uint4*)(__builtin_amdgcn_kernarg_segment_ptr());
-    for (int i = threadIdx.x; i < kArgVec; i += kThreads) args_lds[i] = src[i];
-  }
-  __syncthreads();
-  const DecodeArgs& t = *reinterpret_cast<const DecodeArgs*>(args_lds);
+// LDS the kernel reuses: the waves' stages during the loop, their outputs
+// o_all[wave][16][D] in the combine, the partials in the merge.
+template <int D>
+constexpr int kUnionBytes = kWaves * kMaxGroupRatio * D * 4 > kWaves * kStageBytes
+                                ? kWaves * kMaxGroupRatio * D * 4
+                                : kWaves * kStageBytes;
 
-  int slot, sl, x;
-  decode_block(t, blockIdx.x, a.n_seq, slot, sl, x);
-  slot = __builtin_amdgcn_readfirstlane(slot);
-  sl = __builtin_amdgcn_readfirstlane(sl);
-  x = __builtin_amdgcn_readfirstlane(x);
-  const int lh = __builtin_amdgcn_readfirstlane(int(t.lh_glob[slot]));
-  const int l_local = lh / a.Hkv, h = lh % a.Hkv;
-  const int s = a.seq_off + sl;
-  const int nxs = __builtin_amdgcn_readfirstlane(t.nx[sl] * int(t.mult[slot]));
-  const int cap = __builtin_amdgcn_readfirstlane(t.cap[sl]);
+// Split-K merge of one (layer, seq, head) by the workgroup whose partial
+// completed its arrival count: the nxs partials (normalised rows o / l with
+// their (m, l)) are combined with the log-sum-exp rule, read past the caches,
+// and the arrival counter is reset to zero for the next call.  Uses the
+// workgroup's reusable LDS (big_lds) and all its threads; starts with a
+// barrier so the LDS may still be in use when it is called.
+template <int D>
+__device__ void merge_entry(const DecodeArgs& a, uint8_t* big_lds, int l_local, int s, int h,
+                            int nxs) {
   const int G = a.G;
-
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kMaxGroupRatio * D];
-  __shared__ float ml_lds[kWaves][16][2];
-  // wave stages during the loop; per-wave outputs for the final combine after it
-  constexpr int kOBytes = kWaves * kMaxGroupRatio * D * 4;
-  constexpr int kUnion = kOBytes > kWaves * kStageBytes ? kOBytes : kWaves * kStageBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnion];
-
-  // the G query rows of this KV head: G * D bf16, 16 bytes per thread
-  // (G * D / 8 <= 256 <= kThreads; rows start 16-byte aligned since D * 2 >= 128)
-  const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-  if (int(threadIdx.x) < G * D / 8)
-    reinterpret_cast<uint4*>(q_lds)[threadIdx.x] = reinterpret_cast<const uint4*>(qp)[threadIdx.x];
-  int len = a.seq_lens[s];
-  len = len < 1 ? 1 : (len > cap ? cap : len);
-  __syncthreads();
-
-  const int kbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][0]));
-  const int vbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][1]));
-  Ctx c;
-  {
-    const int kb = kbits, vb = vbits;
-    c.kvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][0])) * 256u;
-    c.kmeta = c.kvis + meta_plane_offset(a.Rvis, D, kb);
-    c.ktxt = c.kvis + txt_plane_offset(a.Rvis, D, g, kb);
-    c.vvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][1])) * 256u;
-    c.vmeta = c.vvis + meta_plane_offset(a.Rvis, D, vb);
-    c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
-  }
-  c.q_lds = q_lds;
-  c.stage = big_lds + wave * kStageBytes;
-  c.qscale = a.qscale;
-  c.G = G;
-  c.lane = lane;
-  c.n = lane & 15;
-  c.jq = lane >> 4;
-
-  WaveState<D> st;
-#pragma unroll
-  for (int mb = 0; mb < NB; ++mb) st.o[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  st.m = -INFINITY;
-  st.l = 0.0f;
-  st.mt = 0.0f;
-
-  int wa, wb;
-  wave_range(x, wave, nxs, len, a.chunk, kWaves, wa, wb);
-  {
-    const int vb = __builtin_amdgcn_readfirstlane(t.vb[sl]);
-    const int ve = __builtin_amdgcn_readfirstlane(t.ve[sl]);
-    const int64_t vrow0 = __builtin_amdgcn_readfirstlane(t.vrow0[sl]);
-    const int64_t trow0 = __builtin_amdgcn_readfirstlane(t.trow0[sl]);
-    const bool quant_vis = !(KB == 16 && VB == 16) && kbits == KB && vbits == VB;
-    // In a balanced split the workgroup's visual rows (the union of its
-    // waves' static ranges) are claimed step by step by its waves; text rows, and
-    // everything in the fixed chunk mode, follow the static split [wa, wb).
-    // The static text rows go first so the claimed part absorbs their
-    // imbalance.
-    const bool dyn = a.chunk == 0;
-    int ga, gb, gt;
-    wave_range(x, 0, nxs, len, a.chunk, kWaves, ga, gt);
-    wave_range(x, kWaves - 1, nxs, len, a.chunk, kWaves, gt, gb);
-    const Claim cl{&lds_claim, wave};
-    // segments: text prefix [0, vb), text suffix [ve, cap), visual [vb, ve);
-    // kept as a loop so each row path is emitted once
-#pragma clang loop unroll(disable)
-    for (int seg = 0; seg < 3; ++seg) {
-      const bool vis = seg == 2;
-      int x0, x1;
-      if (vis && dyn) {
-        x0 = max(ga, vb);
-        x1 = min(gb, ve);
-      } else {
-        x0 = seg == 0 ? wa : vis ? max(wa, vb) : max(wa, ve);
-        x1 = seg == 0 ? min(wb, vb) : vis ? min(wb, ve) : wb;
-      }
-      if (x0 >= x1) continue;
-      const int64_t row0 = vis ? vrow0 + (x0 - vb) : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
-      const Claim use = vis && dyn ? cl : Claim{nullptr, 0};
-      if (vis && quant_vis)
-        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true, use);
-      else  // text rows, or bf16 visual rows of a protected head
-        run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, vis, use);
-    }
-  }
-
-  // ---- wave results -> LDS ---------------------------------------------------
-  // Row c of every wave's p.v accumulator (column (head, group) c of S) goes
-  // to o_all[wave][c][d] with the V-min term added; (m, l) per column to
-  // ml_all.  Rows of dead columns and the other groups' d are written too
-  // and simply never read.
-  __syncthreads();  // the stages are reused as o_all below
-  float l_col = st.l + __shfl_xor(st.l, 16);
-  l_col += __shfl_xor(l_col, 32);
-  float mt_col = st.mt + __shfl_xor(st.mt, 16);
-  mt_col += __shfl_xor(mt_col, 32);
-  const int n = lane & 15, jq = lane >> 4;
-  float(*o_all)[16][D] = reinterpret_cast<float(*)[16][D]>(big_lds);
-  if (jq == 0) {
-    ml_lds[wave][n][0] = st.m;
-    ml_lds[wave][n][1] = l_col;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float mt_r = __shfl(mt_col, 4 * jq + i);
-    f32x4 v[NB / 4];
-#pragma unroll
-    for (int mb = 0; mb < NB; ++mb) v[mb / 4][mb % 4] = st.o[mb][i] + mt_r;
-#pragma unroll
-    for (int k = 0; k < NB / 4; ++k)
-      reinterpret_cast<f32x4*>(&o_all[wave][4 * jq + i][NB * n])[k] = v[k];
-  }
-  __syncthreads();
-
-  // ---- combine waves; write the workgroup's partial (or the final output) ----
-  // Per row c, one thread turns the waves' (m, l) into combine weights
-  // f_w = 2^(m_w - M) (0 for a wave without tokens) and L = sum l_w f_w;
-  // every output element is then a branch-free weighted sum over the waves.
-  // Head j's value at d lives in row c = j * NG + (d / g).
-  __shared__ __attribute__((aligned(16))) float wts[16][kWaves];
-  __shared__ float rowL[16], rowM[16];
-  if (threadIdx.x < 16) {
-    const int cr = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      M = ml_lds[w][cr][1] > 0.0f ? fmaxf(M, ml_lds[w][cr][0]) : M;
-    float L = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float lw = ml_lds[w][cr][1];
-      const float f = lw > 0.0f ? __builtin_amdgcn_exp2f(ml_lds[w][cr][0] - M) : 0.0f;
-      wts[cr][w] = f;
-      L += lw * f;
-    }
-    rowL[cr] = L;
-    rowM[cr] = M;
-  }
-  __syncthreads();
-  const bool single = nxs == 1;
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
-  const int64_t pidx = partial_index(l_local, s, h, x, a.B, a.Hkv, a.max_chunks);
   uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int j = i / D, d = i % D, cr = j * NG + d / g;
-    float acc = 0.0f;
-#pragma unroll
-    for (int w4 = 0; w4 < kWaves / 4; ++w4) {
-      const f32x4 f = *reinterpret_cast<const f32x4*>(&wts[cr][4 * w4]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc += o_all[4 * w4 + w][cr][d] * f[w];
-    }
-    const float L = rowL[cr];
-    const float o = L > 0.0f ? acc * __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
-    if (single) {
-      outp[i] = __builtin_bit_cast(uint16_t, (__bf16)o);
-    } else {
-      // write-through (system-coherent) stores: the merging workgroup may sit
-      // on another XCD and reads them past its own caches
-      __hip_atomic_store(&a.ws_o[pidx * G * D + i], o, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-      if (d == 0) {
-        __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], rowM[cr], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
-        __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 1], L, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
-      }
-    }
-  }
-  if (single) return;
-
-  // ---- split-K merge by the last workgroup of this (layer, seq, head) -------
-  // Each workgroup waits until its partial has reached memory, then counts
-  // itself in; the one that completes the count merges all partials with the
-  // log-sum-exp rule (reading them past the caches) and resets the counter to
-  // zero for the next call.  No cache write-back or invalidation is needed.
-  __shared__ int is_last;
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
   __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = __hip_atomic_fetch_add(&a.ws_arrive[entry], 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_SYSTEM) == nxs - 1;
-  __syncthreads();
-  if (!is_last) return;
-  // Merge in LDS (the stage / o_all storage): the (m, l) pairs of all
-  // partials come in with the first batch of partial rows and become weights
-  // w[cx][j] = l 2^(m - M_j) (0 for a partial without tokens); the partial
-  // rows (normalised, o / l) stream through in batches, each element
-  // accumulating sum_cx o w and sum_cx w.  All
-  // loads are 16- or 4-byte buffer loads that bypass the caches, issued
+  // Merge in LDS: the (m, l) pairs of all partials come in with the first
+  // batch of partial rows and become weights w[cx][j] = l 2^(m - M_j) (0 for
+  // a partial without tokens); the partial rows (normalised, o / l) stream
+  // through in batches, each element accumulating sum_cx o w and sum_cx w.
+  // All loads are 16- or 4-byte buffer loads that bypass the caches, issued
   // together.  Entries with more partials than LDS holds read memory directly.
   const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
   const float* gml = a.ws_ml + p0 * G * 2;
   const float* go = a.ws_o + p0 * G * D;
-  constexpr int kLdsFloats = kUnion / 4;  // the whole stage / o_all area
+  constexpr int kLdsFloats = kUnionBytes<D> / 4;  // the whole stage / o_all area
   constexpr int kPer = (kMaxGroupRatio * D + kThreads - 1) / kThreads;  // elements per thread
   const int n_ml = nxs * G * 2;
   float* lml = reinterpret_cast<float*>(big_lds);  // [nxs][G] (m, l)
@@ -995,13 +822,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       const int n_o = nb * G * D;
       const Rsrc ro = make_rsrc(go + int64_t(c0) * G * D, int64_t(n_o) * 4);
       if (c0 > 0) __syncthreads();  // the previous batch is consumed
-      for (int v = threadIdx.x; v < n_o / 4; v += kThreads)
-        reinterpret_cast<u32x4*>(lo)[v] =
-            __builtin_amdgcn_raw_buffer_load_b128(ro, uint32_t(v) * 16u, 0, kCoherent);
+      // Every load of a pass is issued before the first LDS store, so a batch
+      // costs one memory round trip per kU * kThreads vectors (the (m, l)
+      // pairs, with the first batch, ride along with the first pass).
+      constexpr int kU = 4;
+      const int n_v = n_o / 4;
+      float mlr[2] = {0.0f, 0.0f};
+      for (int v0 = 0; v0 < n_v; v0 += kU * kThreads) {
+        u32x4 buf[kU];
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+          const int v = v0 + int(threadIdx.x) + kThreads * k;
+          if (v < n_v) buf[k] = __builtin_amdgcn_raw_buffer_load_b128(ro, uint32_t(v) * 16u, 0, kCoherent);
+        }
+        if (c0 == 0 && v0 == 0) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int i = int(threadIdx.x) + kThreads * k;
+            if (i < n_ml)
+              mlr[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                     rm, uint32_t(i) * 4u, 0, kCoherent));
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+          const int v = v0 + int(threadIdx.x) + kThreads * k;
+          if (v < n_v) reinterpret_cast<u32x4*>(lo)[v] = buf[k];
+        }
+      }
       if (c0 == 0) {  // the (m, l) pairs travel with the first batch
-        for (int k = threadIdx.x; k < n_ml; k += kThreads)
-          lml[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 rm, uint32_t(k) * 4u, 0, kCoherent));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int i = int(threadIdx.x) + kThreads * k;
+          if (i < n_ml) lml[i] = mlr[k];
+        }
+        for (int i = int(threadIdx.x) + 2 * kThreads; i < n_ml; i += kThreads)
+          lml[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 rm, uint32_t(i) * 4u, 0, kCoherent));
         __syncthreads();
         // one thread per (partial cx, head j): M_j over all partials (every
         // thread of head j reads the same pairs), then its own weight; the
@@ -1067,6 +924,332 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     __hip_atomic_store(&a.ws_arrive[entry], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// One instance per (D, groups per row, visual K/V widths): a launch holds
+// only (layer, head) pairs whose visual rows have widths (KB, VB) or are bf16
+// (protected heads), so each instance carries two row paths -- the quantised
+// one and the bf16 one that text rows use anyway -- and nothing else.
+//
+// Work layout: the launch's units are waves (see DecodeArgs::mult) and
+// workgroup b runs units [8b, 8b + 8).  The waves of a workgroup that belong
+// to one (layer, seq, head) form a piece: they share a claim counter, and
+// their results are combined in LDS into one partial, or into the output when
+// the piece is the whole entry.  The piece that completes an entry's arrival
+// count merges the entry's partials.
+template <int D, int NG, int KB, int VB>
+__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int NB = D / 16;
+  constexpr int g = D / NG;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+
+  // The per-slot / per-sequence tables are indexed by values computed here, so
+  // reading them from the argument segment would chain a dozen dependent
+  // memory round trips.  One cooperative 16-byte copy puts the whole argument
+  // block in LDS; every table lookup below is then an LDS read.
+  static_assert(sizeof(DecodeArgs) % 16 == 0, "argument block copied in 16-byte pieces");
+  constexpr int kArgVec = int(sizeof(DecodeArgs) / 16);
+  __shared__ uint4 args_lds[kArgVec];
+  __shared__ int lds_claim[kWaves];  // per piece (by its first wave): claim counter
+  __shared__ int lens_lds[kMaxSeq];  // attended lengths of the launch's sequences
+  if (threadIdx.x < kWaves) lds_claim[threadIdx.x] = 0;
+  {
+    const uint4* src = (const uint4*)(__builtin_amdgcn_kernarg_segment_ptr());
+    for (int i = threadIdx.x; i < kArgVec; i += kThreads) args_lds[i] = src[i];
+    // the lengths travel with the arguments so no wave waits on them later
+    if (int(threadIdx.x) < a.n_seq) lens_lds[threadIdx.x] = a.seq_lens[a.seq_off + threadIdx.x];
+  }
+  __syncthreads();
+  const DecodeArgs& t = *reinterpret_cast<const DecodeArgs*>(args_lds);
+
+  // this wave's unit -> (slot, sequence, index u among the entry's ne units).
+  // Units b8 + r (positions r) are dealt to the waves so that every piece
+  // gets older and younger waves alike: the two waves sharing a SIMD
+  // (w, w + 4) do not issue evenly (the older one goes first), and the waves
+  // of a piece rebalance only among themselves.  Positions follow the order
+  // of waves 0, 4, 1, 5, ...; when the first piece is longer than half the
+  // workgroup the positions are rotated so the short piece after it starts at
+  // wave 0.
+  const int b8 = int(blockIdx.x) * kWaves;
+  const int total = t.nxcum[a.n_seq] * int(t.mcum[a.n_lh]);  // the last block may be short
+  int rot = 0;
+  auto pos_of = [&](int w) { return ((((w & 3) << 1) | (w >> 2)) + rot) & (kWaves - 1); };
+  int slot = 0, sl = 0, u = 0;
+  if (b8 + pos_of(wave) < total) decode_unit(t, b8 + pos_of(wave), a.n_lh, a.n_seq, lane, slot, sl, u);
+  {
+    // the first piece's length: known here when this wave's entry holds the
+    // workgroup's first unit (always so when one entry fills the workgroup)
+    const int my0 = b8 + pos_of(wave) - u, myn = t.nx[sl] * int(t.mult[slot]);
+    int first = my0 <= b8 ? min(kWaves, my0 + myn - b8) : 0;
+    if (my0 > b8) {
+      int s0, l0, u0;
+      decode_unit(t, b8, a.n_lh, a.n_seq, lane, s0, l0, u0);
+      first = min(kWaves, t.nx[l0] * int(t.mult[s0]) - u0);
+    }
+    rot = __builtin_amdgcn_readfirstlane(first > kWaves / 2 && first < kWaves ? first : 0);
+    if (rot != 0 && b8 + pos_of(wave) < total)
+      decode_unit(t, b8 + pos_of(wave), a.n_lh, a.n_seq, lane, slot, sl, u);
+  }
+  const int pos = pos_of(wave);
+  const int gw = b8 + pos;
+  const bool active = gw < total;
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  sl = __builtin_amdgcn_readfirstlane(sl);
+  u = __builtin_amdgcn_readfirstlane(u);
+  const int ne = __builtin_amdgcn_readfirstlane(t.nx[sl] * int(t.mult[slot]));
+  const int w0 = gw - u;  // the entry's first unit
+  // the piece: positions [p_lo, p_hi) of this workgroup, i.e. the waves of
+  // pmask; the entry's piece px of pn (idle waves form no piece)
+  const int p_lo = active ? max(w0, b8) - b8 : 0;
+  const int p_hi = active ? min(w0 + ne, b8 + kWaves) - b8 : 0;
+  unsigned pmask = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) pmask |= pos_of(w) >= p_lo && pos_of(w) < p_hi ? 1u << w : 0u;
+  const int px = int(blockIdx.x) - w0 / kWaves;
+  const int pn = (w0 + ne - 1) / kWaves - w0 / kWaves + 1;
+  const int lh = __builtin_amdgcn_readfirstlane(int(t.lh_glob[slot]));
+  const int l_local = lh / a.Hkv, h = lh % a.Hkv;
+  const int s = a.seq_off + sl;
+  const int cap = __builtin_amdgcn_readfirstlane(t.cap[sl]);
+  const int G = a.G;
+
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kWaves][kMaxGroupRatio * D];
+  __shared__ float ml_lds[kWaves][16][2];
+  __shared__ int winfo[kWaves][8];  // per wave: pmask, -, l_local, s, h, px, pn
+  __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnionBytes<D>];
+
+  // the G query rows of this wave's KV head: G * D bf16 in 16-byte pieces
+  // (rows start 16-byte aligned since D * 2 >= 128); only this wave reads them
+  const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+  Ctx c;
+  // G * NG <= 16, so G * D / 8 <= 64 * D / (32 NG) pieces of 16 bytes
+#pragma unroll
+  for (int k = 0; k < D / (32 * NG); ++k) {
+    const int i = lane + 64 * k;
+    c.qreg[k] = active && i < G * D / 8 ? reinterpret_cast<const u32x4*>(qp)[i] : u32x4{0, 0, 0, 0};
+  }
+  int len = lens_lds[sl];
+  len = len < 1 ? 1 : (len > cap ? cap : len);
+
+  const int kbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][0]));
+  const int vbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][1]));
+  {
+    const int kb = kbits, vb = vbits;
+    c.kvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][0])) * 256u;
+    c.kmeta = c.kvis + meta_plane_offset(a.Rvis, D, kb);
+    c.ktxt = c.kvis + txt_plane_offset(a.Rvis, D, g, kb);
+    c.vvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][1])) * 256u;
+    c.vmeta = c.vvis + meta_plane_offset(a.Rvis, D, vb);
+    c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
+  }
+  c.q_lds = q_lds[wave];
+  c.stage = big_lds + wave * kStageBytes;
+  c.qscale = a.qscale;
+  c.G = G;
+  c.lane = lane;
+  c.n = lane & 15;
+  c.jq = lane >> 4;
+
+  WaveState<D> st;
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb) st.o[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  st.m = -INFINITY;
+  st.l = 0.0f;
+  st.mt = 0.0f;
+
+  if (active) {
+    // static split: chunk mode gives each workgroup (8 units) one chunk,
+    // the balanced mode deals the entry's steps over its ne units
+    int wa, wb;
+    if (a.chunk > 0)
+      wave_range(u / kWaves, u % kWaves, ne / kWaves, len, a.chunk, kWaves, wa, wb);
+    else
+      wave_range(u, 0, ne, len, 0, 1, wa, wb);
+    const int vb = __builtin_amdgcn_readfirstlane(t.vb[sl]);
+    const int ve = __builtin_amdgcn_readfirstlane(t.ve[sl]);
+    const int64_t vrow0 = __builtin_amdgcn_readfirstlane(t.vrow0[sl]);
+    const int64_t trow0 = __builtin_amdgcn_readfirstlane(t.trow0[sl]);
+    const bool quant_vis = !(KB == 16 && VB == 16) && kbits == KB && vbits == VB;
+    // In a balanced split the piece's visual rows (the union of its waves'
+    // static ranges) are claimed step by step by its waves; text rows, and
+    // everything in the fixed chunk mode, follow the static split [wa, wb).
+    // The static text rows go first so the claimed part absorbs their
+    // imbalance.
+    const bool dyn = a.chunk == 0;
+    int ga, gb, gt;
+    wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt);
+    wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb);
+    const Claim cl{&lds_claim[p_lo], pos - p_lo, p_hi - p_lo};
+    // segments: text prefix [0, vb), text suffix [ve, cap), visual [vb, ve);
+    // kept as a loop so each row path is emitted once
+#pragma clang loop unroll(disable)
+    for (int seg = 0; seg < 3; ++seg) {
+      const bool vis = seg == 2;
+      int x0, x1;
+      if (vis && dyn) {
+        x0 = max(ga, vb);
+        x1 = min(gb, ve);
+      } else {
+        x0 = seg == 0 ? wa : vis ? max(wa, vb) : max(wa, ve);
+        x1 = seg == 0 ? min(wb, vb) : vis ? min(wb, ve) : wb;
+      }
+      if (x0 >= x1) continue;
+      const int64_t row0 = vis ? vrow0 + (x0 - vb) : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
+      const Claim use = vis && dyn ? cl : Claim{nullptr, 0, 1};
+      if (vis && quant_vis)
+        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true, use);
+      else  // text rows, or bf16 visual rows of a protected head
+        run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, vis, use);
+    }
+  }
+
+  // ---- wave results -> LDS ---------------------------------------------------
+  // Row c of every wave's p.v accumulator (column (head, group) c of S) goes
+  // to o_all[wave][c][d] with the V-min term added; (m, l) per column to
+  // ml_all.  Rows of dead columns and the other groups' d are written too
+  // and simply never read.  An idle wave writes zeros and l = 0.
+  __syncthreads();  // the stages are reused as o_all below
+  float l_col = st.l + __shfl_xor(st.l, 16);
+  l_col += __shfl_xor(l_col, 32);
+  float mt_col = st.mt + __shfl_xor(st.mt, 16);
+  mt_col += __shfl_xor(mt_col, 32);
+  const int n = lane & 15, jq = lane >> 4;
+  float(*o_all)[16][D] = reinterpret_cast<float(*)[16][D]>(big_lds);
+  if (jq == 0) {
+    ml_lds[wave][n][0] = st.m;
+    ml_lds[wave][n][1] = l_col;
+  }
+  if (lane < 7) winfo[wave][lane] = lane == 0 ? int(pmask) : lane == 1 ? 0 : lane == 2 ? l_local
+                                    : lane == 3 ? s : lane == 4 ? h : lane == 5 ? px : pn;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mt_r = __shfl(mt_col, 4 * jq + i);
+    f32x4 v[NB / 4];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) v[mb / 4][mb % 4] = st.o[mb][i] + mt_r;
+#pragma unroll
+    for (int k = 0; k < NB / 4; ++k)
+      reinterpret_cast<f32x4*>(&o_all[wave][4 * jq + i][NB * n])[k] = v[k];
+  }
+  __syncthreads();
+
+  // ---- combine each piece's waves; write its partial (or the output) --------
+  // Thread (row c, wave w) turns the (m, l) of w's piece into w's combine
+  // weight f_w = 2^(m_w - M) (0 for a wave without tokens); the piece's
+  // lowest wave also keeps M and L = sum l_w f_w.  Every output element is
+  // then a weighted sum over its piece's waves.  Head j's value at d lives in
+  // row c = j * NG + (d / g).
+  __shared__ __attribute__((aligned(16))) float wts[16][kWaves];
+  __shared__ float rowL[kWaves][16], rowM[kWaves][16];
+  if (threadIdx.x < 16 * kWaves) {
+    const int cr = threadIdx.x & 15, w = threadIdx.x >> 4;
+    const unsigned pm = unsigned(winfo[w][0]);
+    float2 ml[kWaves];  // all read up front: the selects below stay branch-free
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) ml[v] = *reinterpret_cast<const float2*>(ml_lds[v][cr]);
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+      M = ((pm >> v) & 1u) != 0u & ml[v].y > 0.0f ? fmaxf(M, ml[v].x) : M;
+    float L = 0.0f, fw = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float f = ((pm >> v) & 1u) != 0u & ml[v].y > 0.0f ? __builtin_amdgcn_exp2f(ml[v].x - M)
+                                                              : 0.0f;
+      L += ml[v].y * f;
+      fw = v == w ? f : fw;
+    }
+    wts[cr][w] = fw;
+    if (pm != 0u && __builtin_ctz(pm) == w) {
+      rowL[w][cr] = L;
+      rowM[w][cr] = M;
+    }
+  }
+  // pieces of this workgroup, by their lowest waves
+  unsigned lead = 0;
+  bool any_split = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const unsigned pm = unsigned(winfo[w][0]);
+    const bool first = pm != 0u && __builtin_ctz(pm) == w;
+    lead |= first ? 1u << w : 0u;
+    any_split |= first && winfo[w][6] > 1;
+  }
+  lead = __builtin_amdgcn_readfirstlane(lead);
+  any_split = __builtin_amdgcn_readfirstlane(int(any_split)) != 0;
+  __syncthreads();
+  const int GD = G * D;
+#pragma clang loop unroll(disable)
+  for (unsigned rest = lead; rest != 0u; rest &= rest - 1u) {
+    const int wl = __builtin_ctz(rest);
+    const unsigned pm = __builtin_amdgcn_readfirstlane(winfo[wl][0]);
+    const int pl = __builtin_amdgcn_readfirstlane(winfo[wl][2]);
+    const int ps = __builtin_amdgcn_readfirstlane(winfo[wl][3]);
+    const int ph = __builtin_amdgcn_readfirstlane(winfo[wl][4]);
+    const int ppx = __builtin_amdgcn_readfirstlane(winfo[wl][5]);
+    const int ppn = __builtin_amdgcn_readfirstlane(winfo[wl][6]);
+    const int64_t pidx = partial_index(pl, ps, ph, ppx, a.B, a.Hkv, a.max_chunks);
+    uint16_t* outp = a.out + ((int64_t(pl) * a.B + ps) * a.Hq + int64_t(ph) * G) * D;
+    for (int i = threadIdx.x; i < GD; i += kThreads) {
+      const int j = i / D, d = i % D, cr = j * NG + d / g;
+      float acc = 0.0f;
+#pragma unroll
+      for (int w4 = 0; w4 < kWaves / 4; ++w4) {
+        const f32x4 f = *reinterpret_cast<const f32x4*>(&wts[cr][4 * w4]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x = o_all[4 * w4 + w][cr][d] * f[w];
+          acc += (pm >> (4 * w4 + w)) & 1u ? x : 0.0f;
+        }
+      }
+      const float L = rowL[wl][cr];
+      const float o = L > 0.0f ? acc * __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
+      if (ppn == 1) {
+        outp[i] = __builtin_bit_cast(uint16_t, (__bf16)o);
+      } else {
+        // write-through (system-coherent) stores: the merging workgroup may
+        // sit on another XCD and reads them past its own caches
+        __hip_atomic_store(&a.ws_o[pidx * GD + i], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (d == 0) {
+          __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], rowM[wl][cr], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 1], L, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
+    }
+  }
+  if (!any_split) return;
+
+  // ---- split-K merge by the last piece of each (layer, seq, head) -----------
+  // Each workgroup waits until its partials have reached memory, then counts
+  // each split piece in; the piece that completes its entry's count has this
+  // workgroup merge that entry.  No cache write-back or invalidation is
+  // needed.
+  __shared__ int is_last[kWaves];
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x < kWaves) {
+    const int w = threadIdx.x;
+    int last = 0;
+    if (((lead >> w) & 1u) && winfo[w][6] > 1) {
+      const int64_t entry = (int64_t(winfo[w][2]) * a.B + winfo[w][3]) * a.Hkv + winfo[w][4];
+      last = __hip_atomic_fetch_add(&a.ws_arrive[entry], 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM) == winfo[w][6] - 1;
+    }
+    is_last[w] = last;
+  }
+  __syncthreads();
+#pragma clang loop unroll(disable)
+  for (unsigned rest = lead; rest != 0u; rest &= rest - 1u) {
+    const int w = __builtin_ctz(rest);
+    if (__builtin_amdgcn_readfirstlane(is_last[w]))
+      merge_entry<D>(a, big_lds, __builtin_amdgcn_readfirstlane(winfo[w][2]),
+                     __builtin_amdgcn_readfirstlane(winfo[w][3]),
+                     __builtin_amdgcn_readfirstlane(winfo[w][4]),
+                     __builtin_amdgcn_readfirstlane(winfo[w][6]));
+  }
+}
+
 }  // namespace
 
 #if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 0
@@ -1086,7 +1269,8 @@ bool mfma_supported(int D, int g, int G) {
 #define KVQ_PART_FN(DD, NN)                                                                 \
   hipError_t launch_decode_mfma_##DD##_##NN(const DecodeArgs& a, int kb, int vb,           \
                                             hipStream_t stream) {                           \
-    const dim3 grid(a.nxcum[a.n_seq] * a.mcum[a.n_lh], 1, 1); /* compact block list */    \
+    /* one workgroup per kWaves units (waves) of the compact unit list */                \
+    const dim3 grid((a.nxcum[a.n_seq] * a.mcum[a.n_lh] + kWaves - 1) / kWaves, 1, 1);      \
     KVQ_LAUNCH(DD, NN, 2, 2) KVQ_LAUNCH(DD, NN, 2, 4) KVQ_LAUNCH(DD, NN, 2, 8)              \
     KVQ_LAUNCH(DD, NN, 2, 16) KVQ_LAUNCH(DD, NN, 4, 2) KVQ_LAUNCH(DD, NN, 4, 4)             \
     KVQ_LAUNCH(DD, NN, 4, 8) KVQ_LAUNCH(DD, NN, 4, 16) KVQ_LAUNCH(DD, NN, 8, 2)             \

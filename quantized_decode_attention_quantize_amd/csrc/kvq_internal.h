@@ -66,23 +66,26 @@ struct DecodeArgs {
   uint16_t lh_glob[kMaxLH];  // grid.y slot -> layer_local * Hkv + head
   uint32_t base256[kMaxLH][2];  // per slot: VIS plane offset / 256 of K and V
   uint8_t bits[kMaxLH][2];
-  uint8_t mult[kMaxLH];     // per slot: workgroup multiplier of heavy (bf16) heads
-  uint16_t mcum[kMaxLH + 1];  // per slot: sum of mult over earlier slots (compact grid)
+  // Work units (waves of the matrix-core kernel, workgroups of the general
+  // one): slot i and sequence s get mult[i] * nx[s] consecutive units,
+  // slot-major, so unit u of the launch decodes with two searches.
+  uint16_t mult[kMaxLH];    // per slot
+  uint16_t mcum[kMaxLH + 1];  // per slot: sum of mult over earlier slots
   int32_t vb[kMaxSeq], ve[kMaxSeq], cap[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
-  int32_t nx[kMaxSeq];      // per sequence: workgroups per (layer, head) before mult
+  int32_t nx[kMaxSeq];      // per sequence
   int32_t nxcum[kMaxSeq + 1];  // per sequence: sum of nx over earlier sequences
   int32_t pad_[2];          // the split kernels copy this block in 16-byte pieces
 };
 static_assert(sizeof(DecodeArgs) % 16 == 0, "DecodeArgs is copied in 16-byte pieces");
 static_assert(sizeof(DecodeArgs) <= 4096, "DecodeArgs must fit the kernel argument limit");
 
-// Compact 1-D grid of the split kernels: block b enumerates, slot-major, every
-// (slot, sequence, x < nx[seq] * mult[slot]) with no idle blocks, so the
-// round-robin dealing of blocks to the XCDs stays even.  Returns slot, the
-// sequence index within the launch and x.
+// Unit u of a launch (see DecodeArgs::mult) -> slot, the sequence index
+// within the launch and x, the unit's index among the mult[slot] * nx[seq]
+// units of that (slot, sequence).  The layout leaves no idle units, so the
+// round-robin dealing of workgroups to the XCDs stays even.
 __device__ inline void decode_block(const DecodeArgs& a, int b, int n_seq, int& slot, int& sl,
                                     int& x) {
-  const int per_mult = a.nxcum[n_seq];  // workgroups of one slot with mult 1
+  const int per_mult = a.nxcum[n_seq];  // units of one slot with mult 1
   int lo = 0, hi = a.n_lh - 1;          // last slot with per_mult * mcum[slot] <= b
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -104,8 +107,8 @@ __device__ inline void decode_block(const DecodeArgs& a, int b, int n_seq, int& 
 // Token range of wave `w` of workgroup `x` out of `nxs` workgroups of one
 // (layer, seq, head) with `len` attended tokens.  chunk > 0: workgroup x takes
 // [x * chunk, (x + 1) * chunk) and its waves split that evenly.  chunk == 0
-// (balanced): the len tokens form ceil(len / 32) steps dealt into 4 * nxs
-// nearly equal wave units.
+// (balanced): the len tokens form ceil(len / 32) steps dealt into
+// waves * nxs nearly equal wave units.
 __host__ __device__ inline void wave_range(int x, int w, int nxs, int len, int chunk,
                                            int waves, int& a, int& b) {
   if (chunk > 0) {
