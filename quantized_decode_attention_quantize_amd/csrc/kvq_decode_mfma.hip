@@ -951,7 +951,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ uint4 args_lds[kArgVec];
   __shared__ int lds_claim[kWaves];  // per piece (by its first wave): claim counter
   __shared__ int lens_lds[kMaxSeq];  // attended lengths of the launch's sequences
+  __shared__ unsigned lead_lds, split_lds;  // pieces by lowest wave; any split piece
   if (threadIdx.x < kWaves) lds_claim[threadIdx.x] = 0;
+  if (threadIdx.x == 0) lead_lds = split_lds = 0u;
   {
     const uint4* src = (const uint4*)(__builtin_amdgcn_kernarg_segment_ptr());
     for (int i = threadIdx.x; i < kArgVec; i += kThreads) args_lds[i] = src[i];
@@ -1009,12 +1011,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int lh = __builtin_amdgcn_readfirstlane(int(t.lh_glob[slot]));
   const int l_local = lh / a.Hkv, h = lh % a.Hkv;
   const int s = a.seq_off + sl;
+  // piece table for the combine, written now so it is off the tail's path
+  __shared__ int winfo[kWaves][8];  // per wave: pmask, -, l_local, s, h, px, pn
+  if (lane < 7) winfo[wave][lane] = lane == 0 ? int(pmask) : lane == 1 ? 0 : lane == 2 ? l_local
+                                    : lane == 3 ? s : lane == 4 ? h : lane == 5 ? px : pn;
+  if (lane == 0 && pmask != 0u && __builtin_ctz(pmask) == wave) {
+    __hip_atomic_fetch_or(&lead_lds, 1u << wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (pn > 1) __hip_atomic_fetch_or(&split_lds, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
   const int cap = __builtin_amdgcn_readfirstlane(t.cap[sl]);
   const int G = a.G;
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[kWaves][kMaxGroupRatio * D];
   __shared__ float ml_lds[kWaves][16][2];
-  __shared__ int winfo[kWaves][8];  // per wave: pmask, -, l_local, s, h, px, pn
   __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnionBytes<D>];
 
   // the G query rows of this wave's KV head: G * D bf16 in 16-byte pieces
@@ -1118,8 +1127,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     ml_lds[wave][n][0] = st.m;
     ml_lds[wave][n][1] = l_col;
   }
-  if (lane < 7) winfo[wave][lane] = lane == 0 ? int(pmask) : lane == 1 ? 0 : lane == 2 ? l_local
-                                    : lane == 3 ? s : lane == 4 ? h : lane == 5 ? px : pn;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float mt_r = __shfl(mt_col, 4 * jq + i);
@@ -1165,17 +1172,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     }
   }
   // pieces of this workgroup, by their lowest waves
-  unsigned lead = 0;
-  bool any_split = false;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const unsigned pm = unsigned(winfo[w][0]);
-    const bool first = pm != 0u && __builtin_ctz(pm) == w;
-    lead |= first ? 1u << w : 0u;
-    any_split |= first && winfo[w][6] > 1;
-  }
-  lead = __builtin_amdgcn_readfirstlane(lead);
-  any_split = __builtin_amdgcn_readfirstlane(int(any_split)) != 0;
+  const unsigned lead = __builtin_amdgcn_readfirstlane(lead_lds);
+  const bool any_split = __builtin_amdgcn_readfirstlane(split_lds) != 0u;
   __syncthreads();
   const int GD = G * D;
 #pragma clang loop unroll(disable)
