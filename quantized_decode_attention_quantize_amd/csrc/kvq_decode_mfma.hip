@@ -782,15 +782,14 @@ constexpr int kUnionBytes = kWaves * kMaxGroupRatio * D * 4 > kWaves * kStageByt
 // completed its arrival count: the nxs partials (normalised rows o / l with
 // their (m, l)) are combined with the log-sum-exp rule, read past the caches,
 // and the arrival counter is reset to zero for the next call.  Uses the
-// workgroup's reusable LDS (big_lds) and all its threads; starts with a
-// barrier so the LDS may still be in use when it is called.
+// workgroup's reusable LDS (big_lds) and all its threads; the caller ensures
+// no thread still uses that LDS.
 template <int D>
 __device__ void merge_entry(const DecodeArgs& a, uint8_t* big_lds, int l_local, int s, int h,
                             int nxs) {
   const int G = a.G;
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
   uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-  __syncthreads();
   // Merge in LDS: the (m, l) pairs of all partials come in with the first
   // batch of partial rows and become weights w[cx][j] = l 2^(m - M_j) (0 for
   // a partial without tokens); the partial rows (normalised, o / l) stream
@@ -1226,25 +1225,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ int is_last[kWaves];
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
   __syncthreads();
-  if (threadIdx.x < kWaves) {
-    const int w = threadIdx.x;
+  // the lowest wave of each split piece counts the piece in, with its own
+  // (wave-uniform) entry
+  if (lane == 0) {
     int last = 0;
-    if (((lead >> w) & 1u) && winfo[w][6] > 1) {
-      const int64_t entry = (int64_t(winfo[w][2]) * a.B + winfo[w][3]) * a.Hkv + winfo[w][4];
+    if (((lead >> wave) & 1u) && pn > 1) {
+      const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
       last = __hip_atomic_fetch_add(&a.ws_arrive[entry], 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_SYSTEM) == winfo[w][6] - 1;
+                                    __HIP_MEMORY_SCOPE_SYSTEM) == pn - 1;
     }
-    is_last[w] = last;
+    is_last[wave] = last;
   }
   __syncthreads();
+  bool first_merge = true;
 #pragma clang loop unroll(disable)
   for (unsigned rest = lead; rest != 0u; rest &= rest - 1u) {
     const int w = __builtin_ctz(rest);
-    if (__builtin_amdgcn_readfirstlane(is_last[w]))
+    if (__builtin_amdgcn_readfirstlane(is_last[w])) {
+      if (!first_merge) __syncthreads();  // the previous merge is done with the LDS
+      first_merge = false;
       merge_entry<D>(a, big_lds, __builtin_amdgcn_readfirstlane(winfo[w][2]),
                      __builtin_amdgcn_readfirstlane(winfo[w][3]),
                      __builtin_amdgcn_readfirstlane(winfo[w][4]),
                      __builtin_amdgcn_readfirstlane(winfo[w][6]));
+    }
   }
 }
 
