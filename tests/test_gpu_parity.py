@@ -226,6 +226,27 @@ def test_decode_per_head_formats_in_one_call():
     _check_decode(p, [397, 333], chunk=64, what="per-head formats chunk 64")
 
 
+def test_decode_wave_granular_pieces():
+    """6 layers x 4 KV heads, four of them bf16 among INT4/INT2 ones, over five
+    ragged sequences (77 to 2,000 rows).  The balanced split gives entries
+    wave counts that are not multiples of 8 (1,548 waves in all), so
+    workgroups hold up to three entries' pieces, an entry has up to 11
+    partials, and the last workgroup is partly idle.  Every output is compared
+    with the oracle, at full and at shortened lengths."""
+    _say("decode wave-granular pieces (mixed bf16 / INT4-INT2, ragged)")
+    kb = np.full(24, 4, np.uint8)
+    vb = np.full(24, 2, np.uint8)
+    kb[[1, 6, 11, 19]] = 16
+    vb[[1, 6, 11, 19]] = 16
+    caps = [300, 1200, 77, 2000, 640]
+    w = synth.Workload("pieces", 6, 5, 16, 4, 128, 64, caps, [14, 5, 0, 30, 0],
+                       [290, 1200, 77, 1990, 600], caps, kb, vb, seed=33)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, caps, what="pieces full length")
+    _check_decode(p, [1, 1199, 40, 1500, 33], what="pieces shortened")
+
+
 def test_decode_workspace_reuse_across_shapes():
     """The merge's arrival counters return to zero after every call, so one
     workspace serves consecutive calls with other lengths, layer ranges and
