@@ -88,14 +88,19 @@ __device__ inline float dpp_xor2(float v) {
 }
 // Max over lanes {l, l^16, l^32, l^48} (the four row quarters of one MFMA
 // column) with the gfx950 cross-row swaps instead of LDS permutes.
+// Maximum of two floats.  The NaN-propagating form maps to gfx950's
+// v_maximum / v_maximum3, which need no input canonicalisation (fmaxf does
+// when the compiler cannot prove its inputs canonical); the two agree on all
+// non-NaN values, -inf included.
+__device__ inline float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ inline float max_over_quarters(float v) {
   const unsigned u = __builtin_bit_cast(unsigned, v);
   const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float m = fmaxf(__builtin_bit_cast(float, unsigned(r32[0])),
+  const float m = fmax2(__builtin_bit_cast(float, unsigned(r32[0])),
                         __builtin_bit_cast(float, unsigned(r32[1])));
   const unsigned w = __builtin_bit_cast(unsigned, m);
   const auto r16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__builtin_bit_cast(float, unsigned(r16[0])), __builtin_bit_cast(float, unsigned(r16[1])));
+  return fmax2(__builtin_bit_cast(float, unsigned(r16[0])), __builtin_bit_cast(float, unsigned(r16[1])));
 }
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // f16 pair (round to nearest even) of lo * slo, hi * shi.  Written as fmas
@@ -458,7 +463,10 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
   for (int e = 0; e < 8; ++e) {
     const float a = acc[e >> 2][e & 3];
     float part;
-    if constexpr (KB < 16) part = __builtin_fmaf(f16lo(st.km[e]), a, f16hi(st.km[e]) * qsr);
+    // (mn * qsr as an fma with a zero addend: the same single rounding, in
+    // one mixed-precision instruction that reads mn as f16)
+    if constexpr (KB < 16)
+      part = __builtin_fmaf(f16lo(st.km[e]), a, __builtin_fmaf(f16hi(st.km[e]), qsr, 0.0f));
     else part = a;
     if constexpr (NG >= 2) part += dpp_xor1(part);
     if constexpr (NG >= 4) part += dpp_xor2(part);
@@ -472,10 +480,10 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
 
   // online softmax with a lazy running max: the accumulators are rescaled
   // only when a column's max grows by more than kLazy, so p <= 2^kLazy.
-  float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                   fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  float mx = fmax2(fmax2(fmax2(sc[0], sc[1]), fmax2(sc[2], sc[3])),
+                   fmax2(fmax2(sc[4], sc[5]), fmax2(sc[6], sc[7])));
   mx = max_over_quarters(mx) * cs;
-  const float mnew = fmaxf(ws.m, mx);
+  const float mnew = fmax2(ws.m, mx);
   if (__builtin_amdgcn_ballot_w64(mnew > ws.m + kLazy) != 0) {
     const float alpha = __builtin_amdgcn_exp2f(ws.m - mnew);  // 0 on the first step
     ws.l *= alpha;
