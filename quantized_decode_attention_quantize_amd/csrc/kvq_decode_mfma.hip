@@ -268,7 +268,7 @@ struct Ctx {
   u32x4 qreg[4];           // the same, as loaded: 16 bytes per lane per entry (the
                            // first D / (32 NG) used), written to q_lds once the
                            // segment's first loads are out
-  uint8_t* stage;          // this wave's LDS stage (kStageBytes)
+  uint8_t* stage;          // this wave's LDS stage (BigLds::kStage bytes)
   float qscale;
   int G;
   int lane, n, jq;         // lane, column (l % 16), quarter (l / 16)
@@ -539,8 +539,6 @@ struct Stage {
   uint32_t vm[(MP + 3) / 4];
 };
 
-// Wave-private LDS stage large enough for every quantised format.
-constexpr int kStageBytes = 2 * (32 * 128 + 32 * 16);  // INT8 K and V at D=128, NG=4
 
 // Buffer resource over `bytes` bytes from `base` (raw, unswizzled): loads
 // through it take a per-lane 32-bit offset plus a wave-uniform offset, so a
@@ -779,12 +777,20 @@ __device__ inline void decode_unit(const DecodeArgs& t, int b, int n_lh, int n_s
   x = r - m * t.nxcum[sl];
 }
 
-// LDS the kernel reuses: the waves' stages during the loop, their outputs
-// o_all[wave][16][D] in the combine, the partials in the merge.
-template <int D>
-constexpr int kUnionBytes = kWaves * kMaxGroupRatio * D * 4 > kWaves * kStageBytes
-                                ? kWaves * kMaxGroupRatio * D * 4
-                                : kWaves * kStageBytes;
+// The workgroup's large LDS area: the waves' stages during the loop, their
+// outputs o_all[wave][16][D] in the combine, the partials in the merge.
+// When both fit side by side (small formats), a wave writes its outputs as
+// soon as its own loop ends, while the others still stream; otherwise the
+// outputs reuse the stages after a barrier.
+template <int D, int NG, int KB, int VB>
+struct BigLds {
+  static constexpr int kStage = KB < 16 && VB < 16 ? (Stage<D, NG, KB, VB>::kBytes + 15) & ~15 : 0;
+  static constexpr int kOAll = kWaves * kMaxGroupRatio * D * 4;
+  static constexpr bool kApart = kOAll + kWaves * kStage <= 96 * 1024;
+  static constexpr int kStageOff = kApart ? kOAll : 0;  // where the stages start
+  static constexpr int kBytes = kApart ? kOAll + kWaves * kStage
+                                       : (kOAll > kWaves * kStage ? kOAll : kWaves * kStage);
+};
 
 // Split-K merge of one (layer, seq, head) by the workgroup whose partial
 // completed its arrival count: the nxs partials (normalised rows o / l with
@@ -792,7 +798,7 @@ constexpr int kUnionBytes = kWaves * kMaxGroupRatio * D * 4 > kWaves * kStageByt
 // and the arrival counter is reset to zero for the next call.  Uses the
 // workgroup's reusable LDS (big_lds) and all its threads; the caller ensures
 // no thread still uses that LDS.
-template <int D>
+template <int D, int kBigBytes>
 __device__ void merge_entry(const DecodeArgs& a, uint8_t* big_lds, int l_local, int s, int h,
                             int nxs) {
   const int G = a.G;
@@ -807,7 +813,7 @@ __device__ void merge_entry(const DecodeArgs& a, uint8_t* big_lds, int l_local, 
   const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
   const float* gml = a.ws_ml + p0 * G * 2;
   const float* go = a.ws_o + p0 * G * D;
-  constexpr int kLdsFloats = kUnionBytes<D> / 4;  // the whole stage / o_all area
+  constexpr int kLdsFloats = kBigBytes / 4;  // the whole stage / o_all area
   constexpr int kPer = (kMaxGroupRatio * D + kThreads - 1) / kThreads;  // elements per thread
   const int n_ml = nxs * G * 2;
   float* lml = reinterpret_cast<float*>(big_lds);  // [nxs][G] (m, l)
@@ -1031,7 +1037,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[kWaves][kMaxGroupRatio * D];
   __shared__ float ml_lds[kWaves][16][2];
-  __shared__ __attribute__((aligned(16))) uint8_t big_lds[kUnionBytes<D>];
+  using Big = BigLds<D, NG, KB, VB>;
+  __shared__ __attribute__((aligned(16))) uint8_t big_lds[Big::kBytes];
 
   // the G query rows of this wave's KV head: G * D bf16 in 16-byte pieces
   // (rows start 16-byte aligned since D * 2 >= 128); only this wave reads them
@@ -1058,7 +1065,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
   }
   c.q_lds = q_lds[wave];
-  c.stage = big_lds + wave * kStageBytes;
+  c.stage = big_lds + Big::kStageOff + wave * Big::kStage;
   c.qscale = a.qscale;
   c.G = G;
   c.lane = lane;
@@ -1123,7 +1130,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   // to o_all[wave][c][d] with the V-min term added; (m, l) per column to
   // ml_all.  Rows of dead columns and the other groups' d are written too
   // and simply never read.  An idle wave writes zeros and l = 0.
-  __syncthreads();  // the stages are reused as o_all below
+  if constexpr (!Big::kApart) __syncthreads();  // the stages are reused as o_all below
   float l_col = st.l + __shfl_xor(st.l, 16);
   l_col += __shfl_xor(l_col, 32);
   float mt_col = st.mt + __shfl_xor(st.mt, 16);
@@ -1252,7 +1259,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     if (__builtin_amdgcn_readfirstlane(is_last[w])) {
       if (!first_merge) __syncthreads();  // the previous merge is done with the LDS
       first_merge = false;
-      merge_entry<D>(a, big_lds, __builtin_amdgcn_readfirstlane(winfo[w][2]),
+      merge_entry<D, Big::kBytes>(a, big_lds, __builtin_amdgcn_readfirstlane(winfo[w][2]),
                      __builtin_amdgcn_readfirstlane(winfo[w][3]),
                      __builtin_amdgcn_readfirstlane(winfo[w][4]),
                      __builtin_amdgcn_readfirstlane(winfo[w][6]));
