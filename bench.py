@@ -406,43 +406,43 @@ def copy_ceiling(torch, dev, stream):
     return {"bytes_moved": 2 * n, "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(w, lens, q_bits, alg_bytes):
+def cpu_baseline(w, lens, q_bits, alg_bytes, budget_s=10.0):
     """Time the CPU oracle (one thread) decoding a bounded sample of the step:
-    every query head of a few layers over the full history, then scale to the
-    whole step."""
+    every query head of one (layer, sequence) after another over the full
+    history, until about budget_s seconds of decoding have been timed (or the
+    step is done), then scale to the whole step.  Storing the sampled rows is
+    not timed."""
     import oracle
     cfg = oracle.Config.from_workload(w)
     cache = oracle.new_cache(cfg)
-    n_layers = min(2, w.num_layers)
-    layers = list(range(n_layers))
-    seqs = list(range(min(w.batch, 2)))
-    for l in layers:
-        for s in seqs:
-            for h in range(w.num_kv_heads):
-                T = lens[s] - 1
-                oracle.store_rows(cfg, cache, l, s, h, 0, 0, T,
-                                  _f32(w.k_rows(l, s, h, 0, T)))
-                oracle.store_rows(cfg, cache, l, s, h, 1, 0, T,
-                                  _f32(w.v_rows(l, s, h, 0, T)))
-                oracle.store_rows(cfg, cache, l, s, h, 0, T, T + 1, np.zeros((1, w.head_dim),
-                                                                             np.float32))
-                oracle.store_rows(cfg, cache, l, s, h, 1, T, T + 1, np.zeros((1, w.head_dim),
-                                                                             np.float32))
-    t0 = time.perf_counter()
+    units = [(l, s) for l in range(w.num_layers) for s in range(w.batch)]
+    dt = 0.0
     n_heads = 0
-    for l in layers:
-        for s in seqs:
-            for i in range(w.num_q_heads):
-                oracle.decode_one(cfg, cache, l, s, i, lens[s], q_bits[l, s, i], w.sm_scale)
-                n_heads += 1
-    dt = time.perf_counter() - t0
-    total_heads = w.num_layers * w.batch * w.num_q_heads
-    step_s = dt * total_heads / n_heads
+    done = []
+    for l, s in units:
+        T = lens[s] - 1
+        for h in range(w.num_kv_heads):
+            oracle.store_rows(cfg, cache, l, s, h, 0, 0, T, _f32(w.k_rows(l, s, h, 0, T)))
+            oracle.store_rows(cfg, cache, l, s, h, 1, 0, T, _f32(w.v_rows(l, s, h, 0, T)))
+            zero = np.zeros((1, w.head_dim), np.float32)
+            oracle.store_rows(cfg, cache, l, s, h, 0, T, T + 1, zero)
+            oracle.store_rows(cfg, cache, l, s, h, 1, T, T + 1, zero)
+        t0 = time.perf_counter()
+        for i in range(w.num_q_heads):
+            oracle.decode_one(cfg, cache, l, s, i, lens[s], q_bits[l, s, i], w.sm_scale)
+        dt += time.perf_counter() - t0
+        n_heads += w.num_q_heads
+        done.append((l, s))
+        if dt >= budget_s:
+            break
+    # the bytes of the sampled (layer, seq) units against the whole step's
+    frac = n_heads / (w.num_layers * w.batch * w.num_q_heads)
+    step_s = dt / frac
     return {"value": round(alg_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds_per_step": round(step_s, 3),
             "sample": f"{n_heads} (layer, seq, query-head) decodes over the full history "
-                      f"({n_layers} layers x {len(seqs)} seqs x {w.num_q_heads} heads), "
-                      f"{dt:.2f} s, scaled x{total_heads / n_heads:.1f} to one step"}
+                      f"({len(done)} of {len(units)} (layer, seq) units, every query head), "
+                      f"{dt:.2f} s timed on one thread, scaled x{1 / frac:.2f} to one step"}
 
 
 def _f32(a):
