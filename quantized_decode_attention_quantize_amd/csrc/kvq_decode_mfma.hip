@@ -544,9 +544,12 @@ struct Stage {
 // through it take a per-lane 32-bit offset plus a wave-uniform offset, so a
 // step's loads need no per-lane address arithmetic.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
-// Cache-policy operand of buffer loads: sc0 | sc1, i.e. system-coherent (the
-// load is served past this XCD's caches).
+// Cache-policy operands of buffer loads.  kCoherent: sc0 | sc1, i.e.
+// system-coherent (the load is served past this XCD's caches).  kStream: nt,
+// non-temporal: cache rows are read once per call, so they are streamed
+// without displacing what the caches hold.
 constexpr int kCoherent = 1 | 16;
+constexpr int kStream = 2;
 __device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            int(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
@@ -557,16 +560,16 @@ __device__ inline void buf_load(Rsrc r, uint32_t voff, uint32_t soff, uint32_t* 
   if constexpr (NBYTES >= 16) {
 #pragma unroll
     for (int i = 0; i < NBYTES / 16; ++i) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, kStream);
       out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
     }
   } else if constexpr (NBYTES == 8) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStream);
     out[0] = v[0]; out[1] = v[1];
   } else if constexpr (NBYTES == 4) {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream);
   } else {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream);
   }
 }
 
@@ -937,6 +940,90 @@ __device__ void merge_entry(const DecodeArgs& a, uint8_t* big_lds, int l_local, 
     __hip_atomic_store(&a.ws_arrive[entry], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Split-K merge, wave-parallel form.  The m entries a workgroup completed
+// are spread over its waves: wave w merges entry w % m, slice w / m of that
+// entry's G * D outputs, so several merges run side by side with no
+// workgroup barrier and no LDS.  A lane holds one 16-byte vector of outputs
+// per t < kWmT and reads that vector of each of the entry's nxs partials
+// (plus one (m, l) pair per lane), all loads issued before the first use.
+// Entries whose partials do not fit that (nxs > kWmX, nxs * G > 64, or more
+// than kWmT vectors per lane) go through merge_entry instead.
+constexpr int kWmX = 8, kWmT = 2;
+__device__ inline bool wave_merge_fits(int nxs, int G, int D, int waves) {
+  const int per_wave = (G * D / 4 + waves - 1) / waves;  // 16-byte vectors per wave
+  return nxs <= kWmX && nxs * G <= 64 && per_wave <= 64 * kWmT;
+}
+template <int D>
+__device__ void merge_entry_wave(const DecodeArgs& a, int l_local, int s, int h, int nxs,
+                                 int slice, int waves, int lane) {
+  const int G = a.G;
+  const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
+  const int64_t p0 = partial_index(l_local, s, h, 0, a.B, a.Hkv, a.max_chunks);
+  const int nv = G * D / 4;
+  const int per_wave = (nv + waves - 1) / waves;
+  const int v_lo = slice * per_wave, v_hi = min(nv, v_lo + per_wave);
+  const Rsrc ro = make_rsrc(a.ws_o + p0 * G * D, int64_t(nxs) * G * D * 4);
+  const Rsrc rm = make_rsrc(a.ws_ml + p0 * G * 2, int64_t(nxs) * G * 8);
+  // every load first: this lane's (m, l) pair (lane = cx * G + j) and its
+  // vectors of every partial
+  float mlm = 0.0f, mll = 0.0f;
+  if (lane < nxs * G) {
+    mlm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        rm, uint32_t(lane) * 8u, 0, kCoherent));
+    mll = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        rm, uint32_t(lane) * 8u + 4u, 0, kCoherent));
+  }
+  u32x4 buf[kWmT][kWmX];
+#pragma unroll
+  for (int t = 0; t < kWmT; ++t) {
+    const int v = v_lo + lane + 64 * t;
+#pragma unroll
+    for (int cx = 0; cx < kWmX; ++cx)
+      if (v < v_hi && cx < nxs)
+        buf[t][cx] = __builtin_amdgcn_raw_buffer_load_b128(
+            ro, uint32_t(cx * G * D + 4 * v) * 4u, 0, kCoherent);
+  }
+  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+#pragma unroll
+  for (int t = 0; t < kWmT; ++t) {
+    const int v = v_lo + lane + 64 * t;
+    const int j = min(4 * v / D, G - 1);  // head of this vector (clamped for idle lanes)
+    // weights l 2^(m - M_j) of the partials of head j (0 for one without tokens)
+    float mj[kWmX], lj[kWmX];
+    float M = -INFINITY;
+#pragma unroll
+    for (int cx = 0; cx < kWmX; ++cx) {
+      mj[cx] = __shfl(mlm, cx * G + j);
+      lj[cx] = __shfl(mll, cx * G + j);
+      if (cx < nxs && lj[cx] > 0.0f) M = fmaxf(M, mj[cx]);
+    }
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float wsum = 0.0f;
+#pragma unroll
+    for (int cx = 0; cx < kWmX; ++cx) {
+      if (cx < nxs && lj[cx] > 0.0f && v < v_hi) {
+        const float w = lj[cx] * __builtin_amdgcn_exp2f(mj[cx] - M);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)  // (the element as a value: bit_cast of a vector
+                                      // element reference reads element 0)
+          acc[e] += __builtin_bit_cast(float, uint32_t(buf[t][cx][e])) * w;
+      }
+    }
+    if (v < v_hi) {
+      const float r = __builtin_amdgcn_rcpf(wsum);
+      uint2 o;
+      o.x = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[0] * r))) |
+            (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[1] * r))) << 16);
+      o.y = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[2] * r))) |
+            (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[3] * r))) << 16);
+      *reinterpret_cast<uint2*>(outp + 4 * v) = o;
+    }
+  }
+  if (slice == 0 && lane == 0)
+    __hip_atomic_store(&a.ws_arrive[entry], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // One instance per (D, groups per row, visual K/V widths): a launch holds
 // only (layer, head) pairs whose visual rows have widths (KB, VB) or are bf16
 // (protected heads), so each instance carries two row paths -- the quantised
@@ -1252,6 +1339,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     is_last[wave] = last;
   }
   __syncthreads();
+  // the entries this workgroup completed (by their pieces' lowest waves)
+  unsigned done = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) done |= is_last[w] != 0 ? 1u << w : 0u;
+  done = __builtin_amdgcn_readfirstlane(done);
+  if (done == 0u) return;
+  {
+    const int m = __popc(done);
+    bool fits = true;
+    int k = 0;
+    for (unsigned rest = done; rest != 0u; rest &= rest - 1u, ++k) {
+      const int w = __builtin_ctz(rest);
+      fits = fits && wave_merge_fits(winfo[w][6], G, D, (kWaves - k + m - 1) / m);
+    }
+    if (__builtin_amdgcn_readfirstlane(int(fits))) {
+      // wave `wave` takes the (wave % m)-th completed entry, slice wave / m
+      const int kk = wave % m;
+      unsigned rest = done;
+      for (int i = 0; i < kk; ++i) rest &= rest - 1u;
+      const int w = __builtin_ctz(rest);
+      merge_entry_wave<D>(a, __builtin_amdgcn_readfirstlane(winfo[w][2]),
+                          __builtin_amdgcn_readfirstlane(winfo[w][3]),
+                          __builtin_amdgcn_readfirstlane(winfo[w][4]),
+                          __builtin_amdgcn_readfirstlane(winfo[w][6]), wave / m,
+                          (kWaves - kk + m - 1) / m, lane);
+      return;
+    }
+  }
   bool first_merge = true;
 #pragma clang loop unroll(disable)
   for (unsigned rest = lead; rest != 0u; rest &= rest - 1u) {
