@@ -5,9 +5,10 @@ One step = the hot path of one decode step over a whole model:
      positions [T, T+1): a generated token, so a bf16 row), then
   2. kvq_decode_attention attends over [0, T+1) for every layer, KV head and
      query head (split-K over token chunks + log-sum-exp merge).
-The cache is rotated over several replicas (>= 512 MB in total) so each step
-reads HBM, not the 256 MB Infinity Cache.  Inputs are resident in HBM before
-the timed region.
+The cache is rotated over several replicas (>= 2 GB in total) so each step
+reads HBM, not the 256 MB Infinity Cache: at 2 GB even the bf16 rows of the
+protected heads alone (about 40 % of a step's bytes) span far more than that
+cache holds.  Inputs are resident in HBM before the timed region.
 
 Printed: one JSON line (rank 0).  `value` is effective HBM GB/s of the whole
 step (algorithmic bytes / step time); `roofline` refers to the decode
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--workload", default="headguard_step",
                     choices=["headguard_step", "long_gqa", "llava_layer", "ragged_serving"])
     ap.add_argument("--chunk", type=int, default=0, help="split chunk in tokens (0 = library)")
-    ap.add_argument("--replica-mb", type=int, default=512)
+    ap.add_argument("--replica-mb", type=int, default=2048)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the bf16 reference, quantize block and copy measurements")

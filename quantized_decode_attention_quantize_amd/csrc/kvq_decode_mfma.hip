@@ -544,12 +544,9 @@ struct Stage {
 // through it take a per-lane 32-bit offset plus a wave-uniform offset, so a
 // step's loads need no per-lane address arithmetic.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
-// Cache-policy operands of buffer loads.  kCoherent: sc0 | sc1, i.e.
-// system-coherent (the load is served past this XCD's caches).  kStream: nt,
-// non-temporal: cache rows are read once per call, so they are streamed
-// without displacing what the caches hold.
+// Cache-policy operand of buffer loads: sc0 | sc1, i.e. system-coherent (the
+// load is served past this XCD's caches).
 constexpr int kCoherent = 1 | 16;
-constexpr int kStream = 2;
 __device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            int(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
@@ -560,16 +557,16 @@ __device__ inline void buf_load(Rsrc r, uint32_t voff, uint32_t soff, uint32_t* 
   if constexpr (NBYTES >= 16) {
 #pragma unroll
     for (int i = 0; i < NBYTES / 16; ++i) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, kStream);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, 0);
       out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
     }
   } else if constexpr (NBYTES == 8) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStream);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
     out[0] = v[0]; out[1] = v[1];
   } else if constexpr (NBYTES == 4) {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
   } else {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
   }
 }
 
