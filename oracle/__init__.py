@@ -40,7 +40,7 @@ class _Cfg(C.Structure):
                 ("head_dim", C.c_int32), ("group_size", C.c_int32),
                 ("capacity", C.POINTER(C.c_int32)), ("vis_begin", C.POINTER(C.c_int32)),
                 ("vis_end", C.POINTER(C.c_int32)), ("k_bits", C.POINTER(C.c_uint8)),
-                ("v_bits", C.POINTER(C.c_uint8))]
+                ("v_bits", C.POINTER(C.c_uint8)), ("rotate_k", C.c_int32)]
 
 
 class _Info(C.Structure):
@@ -81,6 +81,12 @@ def lib():
                                      C.c_int, C.c_int, C.c_int, P]
         L.orc_load_row.argtypes = [C.POINTER(_Cfg), P, C.c_int, C.c_int, C.c_int,
                                    C.c_int, C.c_int, P]
+        L.orc_load_row_stored.argtypes = [C.POINTER(_Cfg), P, C.c_int, C.c_int, C.c_int,
+                                          C.c_int, C.c_int, P]
+        L.orc_hadamard_rotate.restype = None
+        L.orc_hadamard_rotate.argtypes = [P, C.c_int]
+        L.orc_hadamard_unrotate.restype = None
+        L.orc_hadamard_unrotate.argtypes = [P, C.c_int]
         L.orc_attention.restype = None
         L.orc_attention.argtypes = [P, P, P, C.c_int, C.c_int, C.c_double, P, P]
         L.orc_decode_one.argtypes = [C.POINTER(_Cfg), P, C.c_int, C.c_int, C.c_int,
@@ -101,7 +107,7 @@ class Config:
     """Holds a C config plus the numpy arrays it points into."""
 
     def __init__(self, num_layers, batch, num_q_heads, num_kv_heads, head_dim,
-                 group_size, capacity, vis_begin, vis_end, k_bits, v_bits):
+                 group_size, capacity, vis_begin, vis_end, k_bits, v_bits, rotate_k=False):
         self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
         self.vis_begin = np.ascontiguousarray(vis_begin, dtype=np.int32)
         self.vis_end = np.ascontiguousarray(vis_end, dtype=np.int32)
@@ -112,14 +118,14 @@ class Config:
                       self.vis_begin.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_end.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.k_bits.ctypes.data_as(C.POINTER(C.c_uint8)),
-                      self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)))
+                      self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)), int(bool(rotate_k)))
 
     @classmethod
     def from_workload(cls, w) -> "Config":
         a = w.config_arrays()
         return cls(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                    w.group_size, a["capacity"], a["vis_begin"], a["vis_end"],
-                   a["k_bits"], a["v_bits"])
+                   a["k_bits"], a["v_bits"], getattr(w, "rotate_k", False))
 
     @property
     def ref(self):
@@ -205,6 +211,29 @@ def load_row(cfg: Config, cache: np.ndarray, layer: int, seq: int, head: int, X:
     if lib().orc_load_row(cfg.ref, _ptr(cache), layer, seq, head, X, t, _ptr(out)):
         raise ValueError("load_row failed")
     return out
+
+
+def load_row_stored(cfg: Config, cache: np.ndarray, layer: int, seq: int, head: int, X: int,
+                    t: int) -> np.ndarray:
+    """The row's dequantised values as stored (rotated domain for rotated K rows)."""
+    out = np.zeros(cfg.c.head_dim, dtype=np.float64)
+    if lib().orc_load_row_stored(cfg.ref, _ptr(cache), layer, seq, head, X, t, _ptr(out)):
+        raise ValueError("load_row_stored failed")
+    return out
+
+
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """Forward Walsh-Hadamard rotation of one row in binary32 (see kvq_oracle.h)."""
+    y = np.ascontiguousarray(x, dtype=np.float32).copy()
+    lib().orc_hadamard_rotate(_ptr(y), y.size)
+    return y
+
+
+def hadamard_unrotate(y: np.ndarray) -> np.ndarray:
+    """Inverse rotation of one row in binary64."""
+    x = np.ascontiguousarray(y, dtype=np.float64).copy()
+    lib().orc_hadamard_unrotate(_ptr(x), x.size)
+    return x
 
 
 def new_cache(cfg: Config) -> np.ndarray:

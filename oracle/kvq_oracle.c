@@ -191,6 +191,7 @@ int orc_validate(const orc_config *c) {
     return 2;
   if (c->num_q_heads % c->num_kv_heads) return 2;
   if (c->head_dim < 1 || c->group_size < 1 || c->head_dim % c->group_size) return 3;
+  if (c->rotate_k && (c->head_dim & (c->head_dim - 1))) return 3; /* rotation: D = 2^k */
   for (i = 0; i < c->num_layers * c->num_kv_heads; i++) {
     if (!bits_ok(c->k_bits[i]) || !bits_ok(c->v_bits[i])) return 3;
     if ((c->head_dim * c->k_bits[i]) % 8 || (c->head_dim * c->v_bits[i]) % 8) return 3;
@@ -306,12 +307,47 @@ static void put_u16(uint8_t *p, uint16_t v) {
 
 static uint16_t get_u16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
+/* ---- rotation (WSVD section 2-C, weight-free Walsh-Hadamard form) ------- */
+
+static int log2_int(int D) {
+  int k = 0;
+  while ((1 << k) < D) k++;
+  return k;
+}
+
+void orc_hadamard_rotate(float *x, int D) {
+  int s, i;
+  const float scale = ldexpf(1.0f, -((log2_int(D) + 1) / 2));
+  for (s = 1; s < D; s <<= 1)
+    for (i = 0; i < D; i++)
+      if (!(i & s)) {
+        const float a = x[i], b = x[i + s];
+        x[i] = a + b;
+        x[i + s] = a - b;
+      }
+  for (i = 0; i < D; i++) x[i] = x[i] * scale;
+}
+
+void orc_hadamard_unrotate(double *y, int D) {
+  int s, i;
+  const double scale = ldexp(1.0, -(log2_int(D) / 2));
+  for (s = 1; s < D; s <<= 1)
+    for (i = 0; i < D; i++)
+      if (!(i & s)) {
+        const double a = y[i], b = y[i + s];
+        y[i] = a + b;
+        y[i + s] = a - b;
+      }
+  for (i = 0; i < D; i++) y[i] *= scale;
+}
+
 int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
                    int head, int X, int t0, int t1, const float *src) {
   uint64_t vis, meta, txt;
   int D = c->head_dim, g = c->group_size, t, d, j;
   int b;
   uint8_t codes[1024];
+  float rot[1024];
   if (orc_plane_offsets(c, layer, head, X, &vis, &meta, &txt)) return 1;
   if (D > 1024 || t0 < 0 || t1 > c->capacity[seq] || t0 > t1) return 2;
   b = X ? c->v_bits[layer * c->num_kv_heads + head] : c->k_bits[layer * c->num_kv_heads + head];
@@ -324,6 +360,11 @@ int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
       uint64_t rb = (uint64_t)D * b / 8;
       uint8_t *r = cache + vis + (uint64_t)row * rb;
       uint8_t *m = cache + meta + (uint64_t)row * (uint64_t)(D / g) * 4u;
+      if (X == 0 && c->rotate_k) {  /* coded K rows are rotated first */
+        memcpy(rot, x, sizeof(float) * (size_t)D);
+        orc_hadamard_rotate(rot, D);
+        x = rot;
+      }
       memset(r, 0, rb);
       for (j = 0; j < D / g; j++) {
         uint16_t s16, m16;
@@ -366,8 +407,8 @@ static void load_row_at(const orc_config *c, const uint8_t *cache, uint64_t vis,
   }
 }
 
-int orc_load_row(const orc_config *c, const uint8_t *cache, int layer, int seq,
-                 int head, int X, int t, double *out) {
+int orc_load_row_stored(const orc_config *c, const uint8_t *cache, int layer, int seq,
+                        int head, int X, int t, double *out) {
   uint64_t vis, meta, txt;
   int b, plane;
   int64_t row;
@@ -375,6 +416,18 @@ int orc_load_row(const orc_config *c, const uint8_t *cache, int layer, int seq,
   if (orc_row_of(c, seq, t, &plane, &row)) return 2;
   b = X ? c->v_bits[layer * c->num_kv_heads + head] : c->k_bits[layer * c->num_kv_heads + head];
   load_row_at(c, cache, vis, meta, txt, b, plane, row, out);
+  return 0;
+}
+
+int orc_load_row(const orc_config *c, const uint8_t *cache, int layer, int seq,
+                 int head, int X, int t, double *out) {
+  int plane, b, rc;
+  int64_t row;
+  rc = orc_load_row_stored(c, cache, layer, seq, head, X, t, out);
+  if (rc) return rc;
+  orc_row_of(c, seq, t, &plane, &row);
+  b = X ? c->v_bits[layer * c->num_kv_heads + head] : c->k_bits[layer * c->num_kv_heads + head];
+  if (X == 0 && c->rotate_k && plane == 0 && b < 16) orc_hadamard_unrotate(out, c->head_dim);
   return 0;
 }
 
@@ -431,6 +484,7 @@ int orc_decode_one(const orc_config *c, const uint8_t *cache, int layer,
     int plane = (t >= vb && t < ve) ? 0 : 2;
     int64_t row = plane == 0 ? vbase + (t - vb) : tbase + (t < vb ? t : t - (ve - vb));
     load_row_at(c, cache, off[0][0], off[0][1], off[0][2], kb, plane, row, K + (size_t)t * D);
+    if (c->rotate_k && plane == 0 && kb < 16) orc_hadamard_unrotate(K + (size_t)t * D, D);
     load_row_at(c, cache, off[1][0], off[1][1], off[1][2], vbits, plane, row, V + (size_t)t * D);
   }
   orc_attention(q, K, V, len, D, (double)sm_scale, out, lse);

@@ -40,6 +40,8 @@ typedef struct {
   const int32_t *vis_end;
   const uint8_t *k_bits; /* [num_layers*num_kv_heads] in {2,4,8,16} */
   const uint8_t *v_bits;
+  int32_t rotate_k;      /* nonzero: K rows stored as codes are rotated first
+                            (orc_hadamard_rotate); every other row is not */
 } orc_config;
 
 typedef struct {
@@ -53,6 +55,19 @@ uint16_t orc_f16_round_up(float x);   /* smallest binary16 >= x; zero -> +0 */
 double orc_f16_value(uint16_t h);
 uint16_t orc_bf16_round_nearest_even(float x);
 double orc_bf16_value(uint16_t b);
+
+/* ---- rotation ------------------------------------------------------------ */
+/* Weight-free stand-in for the outlier-removing rotation that gist.science
+ * 2604.02570 (WSVD, section 2-C) places before quantisation: the normalised
+ * Walsh-Hadamard matrix in Sylvester order, H[i][j] = (-1)^popcount(i & j).
+ * Forward, in binary32: for s = 1, 2, 4, ..., D/2 every pair (i, i + s) with
+ * bit s of i clear becomes (x_i + x_(i+s), x_i - x_(i+s)); then every value is
+ * scaled by 2^-ceil(log2(D)/2) (exact).  The matching scale on the query side
+ * is 2^-floor(log2(D)/2), so the two scales times D are exactly 1 and
+ * <rot_q(q), rot_k(k)> = <q, k> in exact arithmetic.  D a power of two. */
+void orc_hadamard_rotate(float *x, int D);
+/* Inverse of the forward rotation in binary64: x = 2^-floor(log2(D)/2) H y. */
+void orc_hadamard_unrotate(double *y, int D);
 
 /* ---- quantiser ---------------------------------------------------------- */
 /* One group of g values -> g codes plus fp16 (scale, min) bit patterns. */
@@ -77,6 +92,11 @@ int orc_row_of(const orc_config *c, int seq, int t, int *plane, int64_t *row);
 int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
                    int head, int X, int t0, int t1, const float *src);
 /* Dequantised row of position t as exact doubles [D]. */
+/* The row's stored values, dequantised, in the stored (for rotated K rows,
+ * rotated) domain; orc_load_row returns the reconstruction in the original
+ * domain (the rotation undone in binary64). */
+int orc_load_row_stored(const orc_config *c, const uint8_t *cache, int layer, int seq,
+                        int head, int X, int t, double *out);
 int orc_load_row(const orc_config *c, const uint8_t *cache, int layer, int seq,
                  int head, int X, int t, double *out);
 

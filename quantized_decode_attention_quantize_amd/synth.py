@@ -181,6 +181,7 @@ class Workload:
     v_std: float = 1.0
     seed: int = 0
     protected: Optional[np.ndarray] = None  # flat (layer*Hkv + head) ids kept bf16
+    rotate_k: bool = False  # coded K rows stored Walsh-Hadamard rotated
 
     @property
     def group_ratio(self) -> int:

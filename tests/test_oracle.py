@@ -460,3 +460,154 @@ def test_question_tokens_stay_bf16(orc):
         assert np.array_equal(got, torch.from_numpy(x[t]).to(torch.bfloat16).double().numpy())
     got = orc.load_row(cfg, cache, 0, 0, 0, 0, 5)
     assert not np.array_equal(got, torch.from_numpy(x[5]).to(torch.bfloat16).double().numpy())
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard rotation of coded K rows (gist.science 2604.02570, section
+# 2-C: a rotation ahead of quantisation removes per-channel outliers; here the
+# weight-free Sylvester-Hadamard form)
+
+
+def _sylvester(D):
+    """H_D by the Kronecker recursion H_2n = [[H, H], [H, -H]] (not the
+    butterfly the oracle uses), checked against (-1)^popcount(i & j)."""
+    H = np.array([[1.0]])
+    while H.shape[0] < D:
+        H = np.block([[H, H], [H, -H]])
+    i = np.arange(D)
+    pop = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    assert np.array_equal(H, (-1.0) ** pop)
+    return H
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_hadamard_rotate_matches_sylvester_matrix(orc, D):
+    """Forward rotation = 2^-ceil(log2(D)/2) H x: exactly on small integers
+    (every binary32 sum is exact there), within the butterfly's rounding on
+    Gaussian rows."""
+    H = _sylvester(D)
+    sk = 2.0 ** -((int(math.log2(D)) + 1) // 2)
+    rng = np.random.default_rng(D)
+    for _ in range(20):
+        x = rng.integers(-50, 51, D).astype(np.float32)
+        assert np.array_equal(orc.hadamard_rotate(x).astype(np.float64), sk * (H @ x))
+    for _ in range(20):
+        x = (rng.standard_normal(D) * 3).astype(np.float32)
+        y = orc.hadamard_rotate(x).astype(np.float64)
+        ref = sk * (H @ x.astype(np.float64))
+        # log2(D) roundings, each at most half an ulp of a partial sum bounded by sum |x|
+        bound = math.log2(D) * 2.0 ** -24 * np.abs(x).sum() * sk
+        assert np.max(np.abs(y - ref)) <= bound
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_hadamard_unrotate_inverts_and_preserves_products(orc, D):
+    """The query-side scale makes the pair orthonormal: unrotate(rotate(x)) =
+    x (exact on integers), and <unrotate-side q, rotated k> keeps q.k."""
+    H = _sylvester(D)
+    sq = 2.0 ** -(int(math.log2(D)) // 2)
+    rng = np.random.default_rng(3 * D)
+    x = rng.integers(-50, 51, D).astype(np.float32)
+    assert np.array_equal(orc.hadamard_unrotate(orc.hadamard_rotate(x)), x.astype(np.float64))
+    q = rng.standard_normal(D)
+    k = rng.integers(-20, 21, D).astype(np.float32)
+    kr = orc.hadamard_rotate(k).astype(np.float64)
+    assert abs(np.dot(sq * (H @ q), kr) - np.dot(q, k)) <= 1e-12 * np.abs(q).sum() * 20
+
+
+def _rot_workload(rotate, kbits=4, vbits=4, seed=5):
+    w = synth.llava_layer(seed=seed, kbits=kbits, vbits=vbits)
+    # a short history keeps the oracle quick; same value recipe (RoPE, x8 outliers)
+    T = 14 + 300
+    return synth.Workload("rot", 1, 1, 28, 4, 128, 64, [T], [14], [T], [T], w.k_bits, w.v_bits,
+                          seed=seed, rotate_k=rotate)
+
+
+def test_rotation_touches_only_coded_k_rows(orc):
+    """Text rows, V rows and bf16 (protected) K rows are byte-identical with
+    and without rotation; every coded K row is stored differently."""
+    for kb in (4, 16):
+        caches = []
+        for rot in (False, True):
+            w = _rot_workload(rot)
+            w.k_bits[:] = kb
+            cfg = orc.Config.from_workload(w)
+            caches.append((cfg, orc.build_cache(w, cfg)))
+        (c0, a), (c1, b) = caches
+        for h in range(4):
+            for X in (0, 1):
+                vis, meta, txt = orc.plane_offsets(c0, 0, h, X)
+                # planes nest (layer, head, X): the next block starts the end of this one
+                nxt = (orc.plane_offsets(c0, 0, h, 1)[0] if X == 0 else
+                       orc.plane_offsets(c0, 0, h + 1, 0)[0] if h < 3 else len(a))
+                if X == 0 and kb < 16:
+                    # every coded row differs; the text plane does not
+                    rb = 128 * kb // 8
+                    for r in range(300):
+                        assert not np.array_equal(a[vis + r * rb: vis + (r + 1) * rb],
+                                                  b[vis + r * rb: vis + (r + 1) * rb])
+                    assert np.array_equal(a[txt:txt + 14 * 256], b[txt:txt + 14 * 256])
+                else:
+                    assert np.array_equal(a[vis:nxt], b[vis:nxt])
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_rotated_rows_keep_the_error_bound_in_the_stored_domain(orc, bits):
+    """The quantiser's bound |x^ - x| <= sc (1/2 + 2^-14) holds for the
+    rotated row, and the reconstruction is the stored values rotated back."""
+    w = _rot_workload(True, kbits=bits)
+    cfg = orc.Config.from_workload(w)
+    cache = orc.build_cache(w, cfg)
+    k = orc._as_f32(w.k_rows(0, 0, 1, 0, w.capacity[0]))
+    for t in (14, 15, 100, 313):
+        x = orc.hadamard_rotate(k[t]).astype(np.float64)
+        stored = orc.load_row_stored(cfg, cache, 0, 0, 1, 0, t)
+        vis, meta, _ = orc.plane_offsets(cfg, 0, 1, 0)
+        m = cache[meta + (t - 14) * 8: meta + (t - 14) * 8 + 8].view(np.uint16)
+        for j in range(2):
+            sc = _f16_bits_to_float(int(m[2 * j]))
+            err = np.abs(stored[64 * j: 64 * (j + 1)] - x[64 * j: 64 * (j + 1)])
+            assert err.max() <= sc * (0.5 + 2.0 ** -14)
+        assert np.allclose(orc.load_row(cfg, cache, 0, 0, 1, 0, t),
+                           orc.hadamard_unrotate(stored), rtol=0, atol=1e-12)
+
+
+def test_rotation_reduces_error_on_outlier_channels(orc):
+    """K with x8 outlier channels (post-RoPE, the pages' K statistics): the
+    rotation spreads the outliers, so the INT4 reconstruction error of K and
+    the decode output's error against exact attention both drop."""
+    errs, outs = {}, {}
+    w0 = _rot_workload(False)
+    k = orc._as_f32(w0.k_rows(0, 0, 0, 0, w0.capacity[0])).astype(np.float64)
+    v = orc._as_f32(w0.v_rows(0, 0, 0, 0, w0.capacity[0])).astype(np.float64)
+    q_bits = w0.q_bits(0)[0, 0]
+    q = (q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exact = orc.attention(q, k, v, w0.sm_scale)[0]
+    for rot in (False, True):
+        w = _rot_workload(rot)
+        cfg = orc.Config.from_workload(w)
+        cache = orc.build_cache(w, cfg)
+        khat = np.stack([orc.load_row(cfg, cache, 0, 0, 0, 0, t) for t in range(14, 314)])
+        errs[rot] = np.sqrt(np.mean((khat - k[14:314]) ** 2))
+        outs[rot] = np.linalg.norm(orc.decode_one(cfg, cache, 0, 0, 0, 314, q_bits,
+                                                  w.sm_scale)[0] - exact)
+    assert errs[True] < 0.8 * errs[False]
+    assert outs[True] < outs[False]
+
+
+def test_rotated_decode_closed_forms(orc):
+    """With rotation on, identical visual K rows still give the mean of V for
+    any query, and one attended row gives that row's V."""
+    D, g, T = 64, 32, 40
+    cfg = orc.Config(1, 1, 2, 1, D, g, [T], [0], [T], [4], [4], rotate_k=True)
+    cache = orc.new_cache(cfg)
+    rng = np.random.default_rng(11)
+    k_row = (rng.standard_normal(D) * np.where(np.arange(D) % 9 == 0, 8, 1)).astype(np.float32)
+    orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, T, np.tile(k_row, (T, 1)))
+    orc.store_rows(cfg, cache, 0, 0, 0, 1, 0, T, rng.standard_normal((T, D)).astype(np.float32))
+    vhat = np.stack([orc.load_row(cfg, cache, 0, 0, 0, 1, t) for t in range(T)])
+    qb = (rng.standard_normal(D).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out, _ = orc.decode_one(cfg, cache, 0, 0, 1, T, qb, 0.125)
+    assert np.allclose(out, vhat.mean(0), atol=1e-12)
+    out, _ = orc.decode_one(cfg, cache, 0, 0, 0, 1, qb, 0.125)
+    assert np.allclose(out, vhat[0], atol=1e-14)
