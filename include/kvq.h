@@ -102,7 +102,24 @@ typedef struct {
   const int32_t *vis_end;   /* [B]                                              */
   const uint8_t *k_bits;    /* [L*Hkv] K width per (layer, KV head), 16 = bf16 */
   const uint8_t *v_bits;    /* [L*Hkv] V width per (layer, KV head)            */
+  int32_t rotate_k;         /* nonzero: K rows stored as codes are rotated     */
+                            /* before quantisation (see below); 0: none        */
 } kvq_config;
+
+/* K rotation (rotate_k != 0).  gist.science 2604.02570 (WSVD, section 2-C)
+ * rotates vectors ahead of quantisation to remove per-channel outliers; the
+ * library uses the weight-free normalised Walsh-Hadamard matrix (Sylvester
+ * order, H[i][j] = (-1)^popcount(i & j)).  Every K row that is stored as
+ * codes (visual position, k_bits < 16) is transformed before its groups are
+ * quantised, in binary32: for s = 1, 2, 4, ..., D/2 every pair (i, i + s)
+ * with bit s of i clear becomes (x_i + x_(i+s), x_i - x_(i+s)), then every
+ * value is multiplied by 2^-ceil(log2(D)/2).  Text rows, V rows and bf16
+ * rows are never rotated.  kvq_decode_attention applies the matching
+ * transform, scaled by 2^-floor(log2(D)/2), to the query for those rows, so
+ * scores are q.k in exact arithmetic.  The stored bytes of a rotated cache
+ * differ from an unrotated one only in those K code and meta rows; the
+ * cache's size does not change.  A cache must be decoded with the rotate_k
+ * it was stored with. */
 
 typedef struct {
   uint64_t total_bytes;       /* bytes to allocate: payload + plane padding    */

@@ -469,6 +469,7 @@ extern "C" kvq_status kvq_quantize(const kvq_config* cfg, void* cache, int32_t l
         a.D = lay.D;
         a.g = lay.g;
         a.src_bf16 = src_dtype == KVQ_SRC_BF16;
+        a.rotate_k = cfg->rotate_k != 0;
         a.tok_begin = tok_begin;
         a.n_tok = tok_end - tok_begin;
         a.num_seqs_total = num_seqs;
@@ -518,6 +519,8 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
     const bool use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
+    // the general kernel has no rotated-query path
+    if (cfg->rotate_k && !use_mfma) return KVQ_ERR_UNSUPPORTED;
     const std::shared_ptr<const DecodePlan> plan_ptr =
         cached_plan(cfg, layer_begin, num_layers, chunk_tokens, use_mfma);
     const DecodePlan& plan = *plan_ptr;
@@ -563,6 +566,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
       a.Hq = cfg->num_q_heads;
       a.B = cfg->batch;
       a.chunk = plan.chunk;
+      a.rotate_k = cfg->rotate_k != 0;
       a.max_chunks = plan.max_chunks;
       a.seq_off = L.s0;
       a.n_seq = L.ns;

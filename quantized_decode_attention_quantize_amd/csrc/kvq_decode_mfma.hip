@@ -271,15 +271,51 @@ struct Ctx {
   uint8_t* stage;          // this wave's LDS stage (BigLds::kStage bytes)
   float qscale;
   int G;
+  bool rotate_k;           // coded K rows are stored Walsh-Hadamard rotated
   int lane, n, jq;         // lane, column (l % 16), quarter (l / 16)
 };
+
+// The wave's G query rows in q_lds (bf16) -> the rotated queries as f16, in
+// place, for K rows stored rotated (include/kvq.h; gist.science 2604.02570,
+// section 2-C): the same butterflies as the stored rows (lane l holds
+// elements l and l + 64 of each row), then 2^-floor(log2(D)/2), so the
+// product with a rotated K row is q.k.  Lanes exchange values with shuffles;
+// each lane reads and writes only its own elements.
+template <int D>
+__device__ inline void rotate_q(const Ctx& c) {
+  constexpr int E = D / 64;  // elements per lane per row
+  for (int h = 0; h < c.G; ++h) {
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = bf16f(c.q_lds[h * D + c.lane + 64 * e]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {  // strides 1 .. 32: across lanes
+      const bool upper = (c.lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float other = __shfl_xor(v[e], m);
+        v[e] = upper ? other - v[e] : v[e] + other;
+      }
+    }
+    if constexpr (E == 2) {  // stride 64: inside the lane
+      const float lo = v[0], hi = v[1];
+      v[0] = lo + hi;
+      v[1] = lo - hi;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      c.q_lds[h * D + c.lane + 64 * e] =
+          __builtin_bit_cast(uint16_t, _Float16(v[e] * 0.125f));  // 2^-floor(log2(D)/2)
+  }
+}
 
 // Build Q' for k format KB: per k-step, 8 slots of this lane's column.
 // Returns the sum of q over the column's (head, group), times 2^-24 (the unit
 // of the code products): each lane's slots cover its quarter of the head dim
-// exactly once, so a sum over the four quarters completes it.
+// exactly once, so a sum over the four quarters completes it.  f16q: q_lds
+// holds f16 (rotated) queries instead of bf16.
 template <int D, int NG, int KB>
-__device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
+__device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32], bool f16q) {
   constexpr int g = D / NG;
   const int h = c.n / NG, gj = c.n % NG;
   const bool live = c.n < c.G * NG;
@@ -294,7 +330,8 @@ __device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32]) {
         int d;
         float w;
         kslot<D, KB>(s, c.jq, 2 * e2 + hf, d, w);
-        const float qv = bf16f(c.q_lds[(live ? h : 0) * D + d]);
+        const uint16_t qb = c.q_lds[(live ? h : 0) * D + d];
+        const float qv = f16q ? f16lo(qb) : bf16f(qb);
         const bool in = live && d / g == gj;
         qs += in ? qv : 0.0f;
         v2[hf] = in ? qv * (1.0f / w) : 0.0f;  // w: power of two
@@ -696,7 +733,10 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     if (i < c.G * D / 8) reinterpret_cast<u32x4*>(c.q_lds)[i] = c.qreg[k];
   }
   u32x4 qop[D / 32];
-  const float qsr = build_q<D, NG, KB>(c, qop);
+  // coded K rows of a rotated cache meet the rotated query
+  const bool rot = KB < 16 && visual && c.rotate_k;
+  if (rot) rotate_q<D>(c);
+  const float qsr = build_q<D, NG, KB>(c, qop, rot);
   const float c24 = c.qscale * 16777216.0f;  // 2^24 * qscale
 
 #pragma unroll
@@ -1152,6 +1192,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   c.stage = big_lds + Big::kStageOff + wave * Big::kStage;
   c.qscale = a.qscale;
   c.G = G;
+  c.rotate_k = a.rotate_k != 0;
   c.lane = lane;
   c.n = lane & 15;
   c.jq = lane >> 4;

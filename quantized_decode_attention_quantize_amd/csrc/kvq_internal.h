@@ -35,6 +35,7 @@ struct QuantizeArgs {
   const void* v_src;
   int64_t Rvis;
   int D, g, src_bf16;
+  int rotate_k;           // coded K rows are Walsh-Hadamard rotated first
   int tok_begin, n_tok;   // positions [tok_begin, tok_begin + n_tok)
   int num_seqs_total;     // seq count of the source tensors
   int seq_off;            // first source sequence covered by this launch
@@ -74,7 +75,8 @@ struct DecodeArgs {
   int32_t vb[kMaxSeq], ve[kMaxSeq], cap[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
   int32_t nx[kMaxSeq];      // per sequence
   int32_t nxcum[kMaxSeq + 1];  // per sequence: sum of nx over earlier sequences
-  int32_t pad_[2];          // the split kernels copy this block in 16-byte pieces
+  int32_t rotate_k;         // coded K rows are stored rotated: rotate q for them
+  int32_t pad_[1];          // the split kernels copy this block in 16-byte pieces
 };
 static_assert(sizeof(DecodeArgs) % 16 == 0, "DecodeArgs is copied in 16-byte pieces");
 static_assert(sizeof(DecodeArgs) <= 4096, "DecodeArgs must fit the kernel argument limit");

@@ -100,6 +100,36 @@ __device__ inline uint64_t quantize8(const float (&x)[8], int bits, uint32_t& me
   return packed;
 }
 
+// Walsh-Hadamard rotation of one row (include/kvq.h; gist.science 2604.02570,
+// section 2-C), held as 8 values in each of the row's D/8 lanes: butterflies
+// of stride 1, 2, 4 inside the lane, then 8 .. D/2 across lanes (the lower
+// index of a pair keeps the sum, the upper one lower - upper), then the exact
+// scaling by 2^-ceil(log2(D)/2).  Every lane of the row must be active.
+template <int D>
+__device__ inline void hadamard_row(float (&x)[8], int lane_in_row) {
+#pragma unroll
+  for (int s = 1; s < 8; s <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(i & s)) {
+        const float lo = x[i], hi = x[i + s];
+        x[i] = lo + hi;
+        x[i + s] = lo - hi;
+      }
+#pragma unroll
+  for (int m = 1; m < D / 8; m <<= 1) {
+    const bool upper = (lane_in_row & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float other = __shfl_xor(x[i], m);
+      x[i] = upper ? other - x[i] : x[i] + other;
+    }
+  }
+  constexpr float kScale = D == 128 ? 0.0625f : 0.125f;  // 2^-ceil(log2(D)/2)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x[i] * kScale;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   constexpr int LPR = D / 8;             // lanes per row
@@ -147,6 +177,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   if (visual && bits < 16) {
     uint32_t meta;
     uint64_t packed;
+    if (a.rotate_k && X == 0) hadamard_row<D>(x, lane_in_row);
     if (a.g == 32) packed = quantize8<4>(x, bits, meta);
     else if (a.g == 64) packed = quantize8<8>(x, bits, meta);
     else packed = quantize8<16>(x, bits, meta);

@@ -327,3 +327,48 @@ def test_decode_merge_of_many_partials():
     p.store()
     _check_decode(p, [32768], chunk=32, what="1024 partials")
     _check_decode(p, [32000], chunk=0, what="balanced, same cache")
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard rotated K rows (include/kvq.h; gist.science 2604.02570,
+# section 2-C)
+
+
+def test_quantize_rotated_bitexact():
+    """Coded K rows rotated before quantisation: every stored byte equals the
+    oracle's (fp32 D=64 g32 INT4, bf16 D=128 g64 INT2 and INT8)."""
+    for w in (synth.tiny(), synth.llava_layer(kbits=2, vbits=4),
+              synth.llava_layer(kbits=8, vbits=2)):
+        _say("quantize rotated", w.name, int(w.k_bits[0]))
+        w.rotate_k = True
+        p = Pair(w)
+        p.store()
+        assert p.mismatches() == 0
+
+
+def test_decode_rotated():
+    """Decode over a rotated cache against the oracle (which undoes the
+    rotation of the stored rows in binary64): tiny, the full LLaVA layer in
+    the balanced split and in 1,024-token chunks (wave-parallel merge), and a
+    call mixing coded and bf16 K heads (only the coded ones are rotated)."""
+    _say("decode rotated tiny")
+    w = synth.tiny()
+    w.rotate_k = True
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [256], what="rotated tiny")
+    _say("decode rotated llava layer")
+    w = synth.llava_layer(seed=9, kbits=4, vbits=2)
+    w.rotate_k = True
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [6287], what="rotated llava")
+    _check_decode(p, [5000], chunk=1024, what="rotated llava chunk 1024")
+    _say("decode rotated per-head formats")
+    kb = np.array([4, 16, 16, 8, 2, 4, 16, 8], np.uint8)
+    vb = np.array([2, 16, 2, 4, 2, 2, 16, 8], np.uint8)
+    w = synth.Workload("perhead_rot", 2, 2, 16, 4, 128, 64, [400, 333], [14, 5], [390, 333],
+                       [400, 333], kb, vb, seed=23, rotate_k=True)
+    p = Pair(w)
+    p.store()
+    _check_decode(p, [400, 300], what="rotated per-head formats")

@@ -175,6 +175,19 @@ def test_decode_workspace_query(L):
     assert st == kvq.KVQ_OK and n > 0
 
 
+def test_decode_rotation_needs_the_matrix_core_kernel(L):
+    """The general kernel (more than 16 (head, group) columns) has no rotated
+    query path: a rotated cache of that shape is refused before any launch."""
+    # G = 7 query heads per KV head, 4 groups per row: 28 columns
+    cfg = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4)
+    assert _dec(L, cfg, ws=None)[0] == kvq.KVQ_OK
+    rot = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4, rotate_k=True)
+    assert _dec(L, rot, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    rot_ok = kvq.Config(1, 1, 28, 4, 128, 64, [256], [16], [256], [4] * 4, [2] * 4,
+                        rotate_k=True)
+    assert _dec(L, rot_ok, ws=None)[0] == kvq.KVQ_OK
+
+
 def test_decode_validation(L):
     cfg = _cfg()
     need = kvq.workspace_bytes(cfg, 1, 64)
