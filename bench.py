@@ -302,9 +302,11 @@ def main():
             "us": round(r_ms * 1e3, 2), "algorithmic_bytes": ref_alg,
             "gbps": round(ref_alg / (r_ms * 1e-3) / 1e9, 1),
             "speedup_of_quantized": round(r_ms / dec_avg, 3)}
+        del refs, wsr
+        extras["rotated_k_decode"] = rotated_decode(torch, kvq, w, args, dev, T, lens_d, q, out,
+                                                    to_dev, dec_avg, alg)
         extras["quantize_block"] = quantize_block(torch, kvq, synth, dev, stream, args)
         extras["copy_ceiling"] = copy_ceiling(torch, dev, stream)
-        del refs, wsr
 
     cpu = None if args.no_cpu else cpu_baseline(w, lens, q_bits, alg)
     profiled = args.chunk == 0 and (w.name != "headguard_step" or args.protected == 14)
@@ -345,6 +347,38 @@ def main():
     }
     line.update(extras)
     print(json.dumps(line), flush=True)
+
+
+def rotated_decode(torch, kvq, w, args, dev, T, lens_d, q, out, to_dev, dec_avg, alg):
+    """The same workload stored with Walsh-Hadamard rotated K codes (rotate_k):
+    same bytes, plus the query rotation inside the kernel."""
+    import copy
+    rw = copy.deepcopy(w)
+    rw.rotate_k = True
+    cfg = kvq.Config.from_workload(rw)
+    nbytes = kvq.kvq_cache_bytes(cfg)["total_bytes"]
+    R = max(2, math.ceil(args.replica_mb * 2 ** 20 / nbytes))
+    c0 = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    for l in range(rw.num_layers):
+        for s in range(rw.batch):
+            k = to_dev(rw.sources(l, [s], 0, T[s] + 1, "k")[None])
+            v = to_dev(rw.sources(l, [s], 0, T[s] + 1, "v")[None])
+            kvq.kvq_quantize(cfg, c0, l, 1, [s], 0, T[s] + 1, k, v)
+    caches = [c0] + [c0.clone() for _ in range(R - 1)]
+    ws = torch.zeros(kvq.workspace_bytes(cfg, rw.num_layers, args.chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def dec(i):
+        kvq.kvq_decode_attention(cfg, caches[i % R], 0, rw.num_layers, lens_d, q, out,
+                                 rw.sm_scale, args.chunk, ws)
+
+    for i in range(args.warmup):
+        dec(i)
+    ms = timed(torch, args, dec)
+    del caches, ws
+    return {"us": round(ms * 1e3, 2), "algorithmic_bytes": alg,
+            "gbps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "vs_unrotated": round(ms / dec_avg, 3)}
 
 
 def _bf16_like(w):

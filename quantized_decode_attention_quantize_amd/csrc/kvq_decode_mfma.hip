@@ -277,35 +277,47 @@ struct Ctx {
 
 // The wave's G query rows in q_lds (bf16) -> the rotated queries as f16, in
 // place, for K rows stored rotated (include/kvq.h; gist.science 2604.02570,
-// section 2-C): the same butterflies as the stored rows (lane l holds
-// elements l and l + 64 of each row), then 2^-floor(log2(D)/2), so the
-// product with a rotated K row is q.k.  Lanes exchange values with shuffles;
-// each lane reads and writes only its own elements.
+// section 2-C): the same butterflies as the stored rows, then
+// 2^-floor(log2(D)/2), so the product with a rotated K row is q.k.  A lane
+// holds 16 consecutive elements of one row (D/16 lanes per row, all rows of a
+// pass side by side): strides 1..8 run inside the lane, 16..D/2 across lanes.
+// Each lane reads and writes only its own elements.
 template <int D>
 __device__ inline void rotate_q(const Ctx& c) {
-  constexpr int E = D / 64;  // elements per lane per row
-  for (int h = 0; h < c.G; ++h) {
-    float v[E];
+  constexpr int EL = 16;           // elements per lane
+  constexpr int LPR = D / EL;      // lanes per row
+  constexpr int RPP = 64 / LPR;    // rows per pass
+  const int part = c.lane % LPR;
+  for (int h0 = 0; h0 < c.G; h0 += RPP) {
+    const int h = h0 + c.lane / LPR;
+    const bool live = h < c.G;
+    uint16_t* row = c.q_lds + (live ? h : 0) * D + part * EL;
+    float v[EL];
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = bf16f(c.q_lds[h * D + c.lane + 64 * e]);
+    for (int i = 0; i < EL; ++i) v[i] = bf16f(row[i]);
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {  // strides 1 .. 32: across lanes
-      const bool upper = (c.lane & m) != 0;
+    for (int s = 1; s < EL; s <<= 1)
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float other = __shfl_xor(v[e], m);
-        v[e] = upper ? other - v[e] : v[e] + other;
+      for (int i = 0; i < EL; ++i)
+        if (!(i & s)) {
+          const float lo = v[i], hi = v[i + s];
+          v[i] = lo + hi;
+          v[i + s] = lo - hi;
+        }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+      const bool upper = (part & m) != 0;
+#pragma unroll
+      for (int i = 0; i < EL; ++i) {
+        const float other = __shfl_xor(v[i], m);
+        v[i] = upper ? other - v[i] : v[i] + other;
       }
     }
-    if constexpr (E == 2) {  // stride 64: inside the lane
-      const float lo = v[0], hi = v[1];
-      v[0] = lo + hi;
-      v[1] = lo - hi;
-    }
+    if (live) {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      c.q_lds[h * D + c.lane + 64 * e] =
-          __builtin_bit_cast(uint16_t, _Float16(v[e] * 0.125f));  // 2^-floor(log2(D)/2)
+      for (int i = 0; i < EL; ++i)
+        row[i] = __builtin_bit_cast(uint16_t, _Float16(v[i] * 0.125f));  // 2^-floor(log2(D)/2)
+    }
   }
 }
 
