@@ -185,7 +185,9 @@ kvq_status kvq_quantize(const kvq_config *cfg, void *cache, int32_t layer_begin,
  *              (and, for chunk_tokens == 0, on the current device's
  *              compute-unit count).  The workspace must be zero-filled before
  *              its first use; every call leaves it ready for the next one, so a
- *              workspace can be reused across calls of any shape that fits it.
+ *              workspace can be reused across calls of any shape that fits it
+ *              on caches of the same kvq_config shape (layers, batch, KV
+ *              heads); zero-fill it again before using it with another.
  *              Calls that may overlap in time must use distinct workspaces.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN,
  * KVQ_ERR_RANGE (layer range), KVQ_ERR_WORKSPACE, KVQ_ERR_HIP. */

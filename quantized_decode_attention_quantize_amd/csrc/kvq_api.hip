@@ -361,11 +361,15 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
   p.max_chunks = int(max_pieces);
   const int G = c->num_q_heads / c->num_kv_heads;
   p.entries = int64_t(nl) * B * Hkv * p.max_chunks;
+  // The arrival counters come first and are sized by the cache configuration
+  // (every layer, sequence and KV head), not by this call: every call on one
+  // cache finds them at the same offsets, and no call's partials ever land on
+  // them, so a workspace zero-filled once stays valid for calls of any shape.
+  p.arrive_bytes = size_t(align256(int64_t(c->num_layers) * B * Hkv * 4));
   p.o_bytes = size_t(align256(p.entries * G * c->head_dim * 4));
   p.ml_bytes = size_t(align256(p.entries * G * 2 * 4));
   p.cnt_bytes = size_t(align256(int64_t(nl) * B * Hkv * 4));
-  p.arrive_bytes = size_t(align256(int64_t(nl) * B * Hkv * 4));
-  p.total = p.o_bytes + p.ml_bytes + p.cnt_bytes + p.arrive_bytes;
+  p.total = p.arrive_bytes + p.o_bytes + p.ml_bytes + p.cnt_bytes;
   return p;
 }
 
@@ -553,10 +557,10 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
       a.seq_lens = seq_lens;
       a.q = static_cast<const uint16_t*>(q);
       a.out = static_cast<uint16_t*>(out);
-      a.ws_o = reinterpret_cast<float*>(ws);
-      a.ws_ml = reinterpret_cast<float*>(ws + plan.o_bytes);
-      a.ws_cnt = reinterpret_cast<int32_t*>(ws + plan.o_bytes + plan.ml_bytes);
-      a.ws_arrive = reinterpret_cast<int32_t*>(ws + plan.o_bytes + plan.ml_bytes + plan.cnt_bytes);
+      a.ws_arrive = reinterpret_cast<int32_t*>(ws);
+      a.ws_o = reinterpret_cast<float*>(ws + plan.arrive_bytes);
+      a.ws_ml = reinterpret_cast<float*>(ws + plan.arrive_bytes + plan.o_bytes);
+      a.ws_cnt = reinterpret_cast<int32_t*>(ws + plan.arrive_bytes + plan.o_bytes + plan.ml_bytes);
       a.qscale = sm_scale * 1.4426950408889634f;
       a.Rvis = lay.Rvis;
       a.D = lay.D;

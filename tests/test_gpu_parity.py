@@ -248,20 +248,23 @@ def test_decode_wave_granular_pieces():
 
 
 def test_decode_workspace_reuse_across_shapes():
-    """The merge's arrival counters return to zero after every call, so one
-    workspace serves consecutive calls with other lengths, layer ranges and
-    split sizes."""
+    """The merge's arrival counters return to zero after every call and sit
+    where no call's partials go, so one workspace serves consecutive calls
+    with other lengths, layer ranges and split sizes."""
     _say("decode workspace reuse")
     import torch
     from kvq_testlib import bf16_device, bf16_to_f64
     w = synth.llava_layer(seed=13, kbits=4, vbits=2)
     p = Pair(w)
     p.store()
-    ws = torch.zeros(max(kvq.workspace_bytes(p.cfg, 1, c) for c in (0, 64, 1024)),
+    ws = torch.zeros(max(kvq.workspace_bytes(p.cfg, 1, c) for c in (0, 32, 64, 1024)),
                      dtype=torch.uint8, device="cuda")
     q_bits = w.q_bits(0)[None]
     q = bf16_device(q_bits)
-    for n, chunk in [(6287, 0), (1000, 64), (6287, 1024), (37, 0), (6287, 0)]:
+    # 32-token chunks fill ~2.8 MB with partials; the balanced call after them
+    # must still find its arrival counters at zero
+    for n, chunk in [(6287, 0), (6287, 32), (6287, 0), (1000, 64), (6287, 1024), (37, 0),
+                     (6287, 0)]:
         out = torch.empty_like(q)
         lens = torch.tensor([n], dtype=torch.int32, device="cuda")
         kvq.kvq_decode_attention(p.cfg, p.cache, 0, 1, lens, q, out, w.sm_scale, chunk, ws)

@@ -168,8 +168,9 @@ def test_decode_workspace_query(L):
         assert st == kvq.KVQ_OK
         entries = 1 * 4 * 8 * (-(-32768 // chunk))
         G = 4
-        expect = ((-(-(entries * G * 128 * 4) // 256) * 256) + (-(-(entries * G * 2 * 4) // 256) * 256)
-                  + 2 * 256)  # partials, (m, l) pairs, then partial counts and arrivals
+        expect = (256 + (-(-(entries * G * 128 * 4) // 256) * 256)
+                  + (-(-(entries * G * 2 * 4) // 256) * 256)
+                  + 256)  # arrivals, partials, (m, l) pairs, partial counts
         assert n == expect == kvq.workspace_bytes(cfg, 1, chunk)
     st, n = _dec(L, cfg, ws=None, chunk=0)
     assert st == kvq.KVQ_OK and n > 0
