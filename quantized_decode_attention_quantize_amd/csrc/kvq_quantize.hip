@@ -86,15 +86,38 @@ __device__ inline uint64_t quantize8(const float (&x)[8], int bits, uint32_t& me
   const float range = hi - mn;
   uint16_t sc16 = 0;
   uint64_t packed = 0;
-  if (range != 0.0f) {
-    sc16 = f16_round_up(range / n);
-    const float sc = f16_float(sc16);
+  // Each code is rint of the IEEE quotient fl(d / sc).  d * rcp(sc) is within
+  // 1.5 * 2^-23 relative of d / sc (rcp within 1 ulp, one rounding), i.e.
+  // within 2^-14 for quotients up to 255, and fl(d / sc) within 2^-16 of it:
+  // unless the estimate lies within 2^-13 of a half-integer, both round to the
+  // same integer.  When any lane of the wave has such a value, the whole wave
+  // takes the IEEE divide for its values (a wave-uniform branch: about one
+  // wave in eight).  A zero-range group keeps scale 0 and all-zero codes.
+  const bool live = range != 0.0f;
+  if (live) sc16 = f16_round_up(range / n);
+  const float sc = f16_float(sc16);
+  const float r = __builtin_amdgcn_rcpf(live ? sc : 1.0f);
+  float d[8], q[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    d[i] = x[i] - mn;  // >= 0: mn <= every value of the group
+    q[i] = d[i] * r;
+    near |= __builtin_fabsf(__builtin_amdgcn_fractf(q[i]) - 0.5f) < 0x1p-13f;  // q >= 0
+  }
+  if (__builtin_amdgcn_ballot_w64(live && near) != 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = live ? d[i] / sc : 0.0f;
+  }
+  if (live) {
+    uint32_t lo32 = 0, hi32 = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float c = __builtin_rintf((x[i] - mn) / sc);
-      c = fminf(fmaxf(c, 0.0f), n);
-      packed |= uint64_t(uint32_t(c)) << (i * bits);
+      const uint32_t c = uint32_t(__builtin_amdgcn_fmed3f(__builtin_rintf(q[i]), 0.0f, n));
+      if (i * bits < 32) lo32 |= c << (i * bits);
+      else hi32 |= c << (i * bits - 32);
     }
+    packed = uint64_t(lo32) | (uint64_t(hi32) << 32);
   }
   meta = uint32_t(sc16) | (uint32_t(mn16) << 16);
   return packed;
