@@ -375,3 +375,52 @@ def test_decode_rotated():
     p = Pair(w)
     p.store()
     _check_decode(p, [400, 300], what="rotated per-head formats")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_quantize_grid_points_and_ties_bitexact(bits):
+    """Values exactly on the code grid and exactly halfway between two codes
+    (ties go to the even code): the cases where the kernel's reciprocal
+    estimate of the quotient defers to the IEEE divide.  Every group holds its
+    own fp16 min and scale (element 0 = min, element 1 = min + n * scale, so
+    both are stored exactly); stored bytes equal the oracle's."""
+    import torch
+    import oracle
+    from kvq_testlib import to_device_src
+    _say("quantize grid points and ties", bits)
+    D, g, T = 128, 64, 512
+    n = (1 << bits) - 1
+    rng = np.random.default_rng(bits)
+    x = np.empty((T, D), np.float64)
+    for t in range(T):
+        for j in range(D // g):
+            # multiples of 1/16 and of 2^-6: every value below is a multiple
+            # of 2^-7 under 2^13, exact in fp32 and the min and scale in fp16
+            mn = -float(rng.integers(0, 64)) / 16.0
+            sc = float(2.0 ** rng.integers(-6, 0) * rng.integers(1, 64))
+            k = rng.integers(0, n, g).astype(np.float64)
+            half = rng.integers(0, 2, g) * 0.5  # ties on about half of the values
+            grp = mn + (k + half) * sc
+            grp[0], grp[1] = mn, mn + n * sc
+            x[t, j * g:(j + 1) * g] = grp
+    xs = x.astype(np.float32)
+    assert np.array_equal(xs.astype(np.float64), x)  # every value exact in fp32
+    w = synth.Workload("ties", 1, 1, 4, 1, D, g, [T], [0], [T], [T],
+                       np.array([bits], np.uint8), np.array([bits], np.uint8), src="f32")
+    cfg = kvq.Config.from_workload(w)
+    ocfg = oracle.Config.from_workload(w)
+    cache = torch.zeros(kvq.kvq_cache_bytes(cfg)["total_bytes"], dtype=torch.uint8,
+                        device="cuda")
+    src = to_device_src(xs[None, None, None])
+    kvq.kvq_quantize(cfg, cache, 0, 1, [0], 0, T, src, src)
+    ocache = oracle.new_cache(ocfg)
+    for X in (0, 1):
+        oracle.store_rows(ocfg, ocache, 0, 0, 0, X, 0, T, xs)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    info = kvq.kvq_cache_bytes(cfg)
+    for X in (0, 1):
+        vis, meta, _ = oracle.plane_offsets(ocfg, 0, 0, X)
+        for a, b in ((vis, vis + T * D * bits // 8), (meta, meta + T * (D // g) * 4)):
+            assert np.array_equal(got[a:b], ocache[a:b]), (bits, X, a)
+    assert info["quantized_values"] == 2 * T * D
