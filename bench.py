@@ -258,10 +258,8 @@ def main():
         c = caches[i % R]
         if same_T:
             kvq.kvq_quantize(cfg, c, 0, w.num_layers, seq_ids, T[0], T[0] + 1, k_new, v_new)
-        else:
-            for s in range(w.batch):
-                kvq.kvq_quantize(cfg, c, 0, w.num_layers, [s], T[s], T[s] + 1,
-                                 k_new_s[s], v_new_s[s])
+        else:  # ragged batch: every sequence appends at its own length, one launch
+            kvq.kvq_quantize_ragged(cfg, c, 0, w.num_layers, seq_ids, T, 1, k_new, v_new)
         kvq.kvq_decode_attention(cfg, c, 0, w.num_layers, lens_d, q, out, w.sm_scale,
                                  args.chunk, ws)
 
@@ -269,9 +267,6 @@ def main():
         kvq.kvq_decode_attention(cfg, caches[i % R], 0, w.num_layers, lens_d, q, out,
                                  w.sm_scale, args.chunk, ws)
 
-    if not same_T:
-        k_new_s = [k_new[:, s:s + 1].contiguous() for s in range(w.batch)]
-        v_new_s = [v_new[:, s:s + 1].contiguous() for s in range(w.batch)]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -159,6 +159,26 @@ kvq_status kvq_quantize(const kvq_config *cfg, void *cache, int32_t layer_begin,
                         int32_t tok_begin, int32_t tok_end, const void *k_src,
                         const void *v_src, kvq_src_dtype src_dtype, void *stream);
 
+/* kvq_quantize with a start position per sequence: sequence seq_ids[i]
+ * stores positions [tok_begin[i], tok_begin[i] + num_tokens), one launch for
+ * the whole batch.  It is the decode-time append of a ragged batch, where each
+ * sequence's next token sits at its own length (nuiw.github.io
+ * "VLM_KV_Quantization" section 1: generated tokens join the cache in full
+ * precision; they are text positions, so they are stored bf16).  Rows are
+ * stored exactly as kvq_quantize stores them.
+ *
+ *   tok_begin  HOST int32 [num_seqs], each >= 0 and tok_begin[i] + num_tokens
+ *              <= capacity[seq_ids[i]]
+ *   k_src,
+ *   v_src      device, 16-byte aligned, contiguous
+ *              [num_layers, num_seqs, num_kv_heads, num_tokens, D]
+ * Other arguments and errors as kvq_quantize; num_tokens == 0 is a no-op. */
+kvq_status kvq_quantize_ragged(const kvq_config *cfg, void *cache, int32_t layer_begin,
+                               int32_t num_layers, int32_t num_seqs, const int32_t *seq_ids,
+                               const int32_t *tok_begin, int32_t num_tokens,
+                               const void *k_src, const void *v_src, kvq_src_dtype src_dtype,
+                               void *stream);
+
 /* One decode step of attention for layers [layer_begin, layer_begin +
  * num_layers): for every layer l, sequence s and query head i,
  *   out[l,s,i,:] = softmax(sm_scale * K^ q) V^   over positions [0, seq_lens[s])

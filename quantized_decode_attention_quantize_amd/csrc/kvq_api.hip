@@ -434,72 +434,103 @@ extern "C" kvq_status kvq_cache_bytes(const kvq_config* cfg, kvq_cache_info* inf
   }
 }
 
+// Shared body of the two store calls: sequence seq_ids[i] stores positions
+// [tok0[i], tok0[i] + n_tok).
+kvq_status quantize_rows(const kvq_config* cfg, void* cache, int32_t layer_begin,
+                         int32_t num_layers, int32_t num_seqs, const int32_t* seq_ids,
+                         const int32_t* tok0, int32_t n_tok, const void* k_src,
+                         const void* v_src, kvq_src_dtype src_dtype, void* stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (src_dtype != KVQ_SRC_F32 && src_dtype != KVQ_SRC_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (num_layers < 1 || num_seqs < 0 || n_tok < 0) return KVQ_ERR_SHAPE;
+  if (layer_begin < 0 || layer_begin > cfg->num_layers - num_layers) return KVQ_ERR_RANGE;
+  if (num_seqs == 0 || n_tok == 0) return KVQ_OK;
+  if (!cache || !k_src || !v_src || !seq_ids || !tok0) return KVQ_ERR_NULL;
+  if (!aligned(cache, 256) || !aligned(k_src, 16) || !aligned(v_src, 16)) return KVQ_ERR_ALIGN;
+  std::vector<char> seen(cfg->batch, 0);
+  for (int i = 0; i < num_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (s < 0 || s >= cfg->batch) return KVQ_ERR_RANGE;
+    if (seen[s]) return KVQ_ERR_SHAPE;
+    seen[s] = 1;
+    if (tok0[i] < 0) return KVQ_ERR_SHAPE;
+    if (int64_t(tok0[i]) + n_tok > cfg->capacity[s]) return KVQ_ERR_RANGE;
+  }
+  Layout lay(cfg);
+  if (lay.info.total_bytes / 256 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
+
+  const int nlh = num_layers * cfg->num_kv_heads;
+  for (int lh0 = 0; lh0 < nlh; lh0 += kMaxLH) {
+    const int nlh_l = std::min(kMaxLH, nlh - lh0);
+    for (int s0 = 0; s0 < num_seqs; s0 += kMaxSeq) {
+      const int ns_l = std::min(kMaxSeq, num_seqs - s0);
+      QuantizeArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.cache = static_cast<uint8_t*>(cache);
+      a.k_src = k_src;
+      a.v_src = v_src;
+      a.Rvis = lay.Rvis;
+      a.D = lay.D;
+      a.g = lay.g;
+      a.src_bf16 = src_dtype == KVQ_SRC_BF16;
+      a.rotate_k = cfg->rotate_k != 0;
+      a.n_tok = n_tok;
+      a.num_seqs_total = num_seqs;
+      a.seq_off = s0;
+      a.Hkv = cfg->num_kv_heads;
+      a.lh_off = lh0;
+      for (int i = 0; i < nlh_l; ++i) {
+        const int glh = lh0 + i;
+        const int l = layer_begin + glh / cfg->num_kv_heads, h = glh % cfg->num_kv_heads;
+        for (int X = 0; X < 2; ++X) {
+          a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * cfg->num_kv_heads + h) * 2 + X] / 256);
+          a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
+        }
+      }
+      for (int i = 0; i < ns_l; ++i) {
+        const int s = seq_ids[s0 + i];
+        a.vb[i] = cfg->vis_begin[s];
+        a.ve[i] = cfg->vis_end[s];
+        a.vrow0[i] = int32_t(lay.vrow0[s]);
+        a.trow0[i] = int32_t(lay.trow0[s]);
+        a.tok0[i] = tok0[s0 + i];
+      }
+      if (launch_quantize(a, nlh_l, ns_l, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return KVQ_ERR_HIP;
+    }
+  }
+  return KVQ_OK;
+}
+
 extern "C" kvq_status kvq_quantize(const kvq_config* cfg, void* cache, int32_t layer_begin,
                                    int32_t num_layers, int32_t num_seqs, const int32_t* seq_ids,
                                    int32_t tok_begin, int32_t tok_end, const void* k_src,
                                    const void* v_src, kvq_src_dtype src_dtype, void* stream) {
   try {
-    kvq_status st = check_config(cfg);
-    if (st != KVQ_OK) return st;
-    if (src_dtype != KVQ_SRC_F32 && src_dtype != KVQ_SRC_BF16) return KVQ_ERR_UNSUPPORTED;
-    if (num_layers < 1 || num_seqs < 0 || tok_begin < 0 || tok_end < tok_begin)
-      return KVQ_ERR_SHAPE;
-    if (layer_begin < 0 || layer_begin > cfg->num_layers - num_layers) return KVQ_ERR_RANGE;
-    if (num_seqs == 0 || tok_end == tok_begin) return KVQ_OK;
-    if (!cache || !k_src || !v_src || !seq_ids) return KVQ_ERR_NULL;
-    if (!aligned(cache, 256) || !aligned(k_src, 16) || !aligned(v_src, 16)) return KVQ_ERR_ALIGN;
-    std::vector<char> seen(cfg->batch, 0);
-    for (int i = 0; i < num_seqs; ++i) {
-      const int s = seq_ids[i];
-      if (s < 0 || s >= cfg->batch) return KVQ_ERR_RANGE;
-      if (seen[s]) return KVQ_ERR_SHAPE;
-      seen[s] = 1;
-      if (tok_end > cfg->capacity[s]) return KVQ_ERR_RANGE;
+    if (tok_begin < 0 || tok_end < tok_begin) {
+      const kvq_status st = check_config(cfg);
+      return st != KVQ_OK ? st : KVQ_ERR_SHAPE;
     }
-    Layout lay(cfg);
-    if (lay.info.total_bytes / 256 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
+    const std::vector<int32_t> tok0(size_t(std::max(num_seqs, 0)), tok_begin);
+    return quantize_rows(cfg, cache, layer_begin, num_layers, num_seqs, seq_ids, tok0.data(),
+                         tok_end - tok_begin, k_src, v_src, src_dtype, stream);
+  } catch (const std::bad_alloc&) {
+    return KVQ_ERR_INTERNAL;
+  } catch (...) {
+    return KVQ_ERR_INTERNAL;
+  }
+}
 
-    const int nlh = num_layers * cfg->num_kv_heads;
-    for (int lh0 = 0; lh0 < nlh; lh0 += kMaxLH) {
-      const int nlh_l = std::min(kMaxLH, nlh - lh0);
-      for (int s0 = 0; s0 < num_seqs; s0 += kMaxSeq) {
-        const int ns_l = std::min(kMaxSeq, num_seqs - s0);
-        QuantizeArgs a;
-        std::memset(&a, 0, sizeof(a));
-        a.cache = static_cast<uint8_t*>(cache);
-        a.k_src = k_src;
-        a.v_src = v_src;
-        a.Rvis = lay.Rvis;
-        a.D = lay.D;
-        a.g = lay.g;
-        a.src_bf16 = src_dtype == KVQ_SRC_BF16;
-        a.rotate_k = cfg->rotate_k != 0;
-        a.tok_begin = tok_begin;
-        a.n_tok = tok_end - tok_begin;
-        a.num_seqs_total = num_seqs;
-        a.seq_off = s0;
-        a.Hkv = cfg->num_kv_heads;
-        a.lh_off = lh0;
-        for (int i = 0; i < nlh_l; ++i) {
-          const int glh = lh0 + i;
-          const int l = layer_begin + glh / cfg->num_kv_heads, h = glh % cfg->num_kv_heads;
-          for (int X = 0; X < 2; ++X) {
-            a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * cfg->num_kv_heads + h) * 2 + X] / 256);
-            a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
-          }
-        }
-        for (int i = 0; i < ns_l; ++i) {
-          const int s = seq_ids[s0 + i];
-          a.vb[i] = cfg->vis_begin[s];
-          a.ve[i] = cfg->vis_end[s];
-          a.vrow0[i] = int32_t(lay.vrow0[s]);
-          a.trow0[i] = int32_t(lay.trow0[s]);
-        }
-        if (launch_quantize(a, nlh_l, ns_l, static_cast<hipStream_t>(stream)) != hipSuccess)
-          return KVQ_ERR_HIP;
-      }
-    }
-    return KVQ_OK;
+extern "C" kvq_status kvq_quantize_ragged(const kvq_config* cfg, void* cache,
+                                          int32_t layer_begin, int32_t num_layers,
+                                          int32_t num_seqs, const int32_t* seq_ids,
+                                          const int32_t* tok_begin, int32_t num_tokens,
+                                          const void* k_src, const void* v_src,
+                                          kvq_src_dtype src_dtype, void* stream) {
+  try {
+    return quantize_rows(cfg, cache, layer_begin, num_layers, num_seqs, seq_ids, tok_begin,
+                         num_tokens, k_src, v_src, src_dtype, stream);
   } catch (const std::bad_alloc&) {
     return KVQ_ERR_INTERNAL;
   } catch (...) {

@@ -36,7 +36,7 @@ struct QuantizeArgs {
   int64_t Rvis;
   int D, g, src_bf16;
   int rotate_k;           // coded K rows are Walsh-Hadamard rotated first
-  int tok_begin, n_tok;   // positions [tok_begin, tok_begin + n_tok)
+  int n_tok;              // rows per sequence: positions [tok0[s], tok0[s] + n_tok)
   int num_seqs_total;     // seq count of the source tensors
   int seq_off;            // first source sequence covered by this launch
   int Hkv;
@@ -44,7 +44,10 @@ struct QuantizeArgs {
   uint32_t base256[kMaxLH][2];  // VIS plane offset / 256 per (lh, X)
   uint8_t bits[kMaxLH][2];
   int32_t vb[kMaxSeq], ve[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
+  int32_t tok0[kMaxSeq];  // per sequence: first position stored (the call's
+                          // n_tok rows start there)
 };
+static_assert(sizeof(QuantizeArgs) <= 4096, "QuantizeArgs must fit the kernel argument limit");
 
 struct DecodeArgs {
   const uint8_t* cache;

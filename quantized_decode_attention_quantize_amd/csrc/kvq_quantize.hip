@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   const int r = blockIdx.x * RPB + row_in_block;  // token within [0, n_tok)
   const bool active = r < a.n_tok;
   const int rr = active ? r : a.n_tok - 1;  // keep inactive lanes in bounds
-  const int t = a.tok_begin + rr;
+  const int t = a.tok0[sl] + rr;
 
   // source element offset: [nl, num_seqs, Hkv, n_tok, D]
   const int glh = a.lh_off + lh;         // layer-local * Hkv + head

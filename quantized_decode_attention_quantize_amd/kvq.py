@@ -28,7 +28,8 @@ KVQ_ERR_INTERNAL = 8
 KVQ_SRC_F32 = 0
 KVQ_SRC_BF16 = 1
 
-EXPORTS = ("kvq_cache_bytes", "kvq_quantize", "kvq_decode_attention", "kvq_status_string")
+EXPORTS = ("kvq_cache_bytes", "kvq_quantize", "kvq_quantize_ragged", "kvq_decode_attention",
+           "kvq_status_string")
 
 
 class KvqError(RuntimeError):
@@ -70,6 +71,10 @@ def lib(path: str = LIB_PATH):
         L.kvq_quantize.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, C.c_int32,
                                    C.POINTER(C.c_int32), C.c_int32, C.c_int32, P, P,
                                    C.c_int, P]
+        L.kvq_quantize_ragged.restype = C.c_int
+        L.kvq_quantize_ragged.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, C.c_int32,
+                                          C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                          C.c_int32, P, P, C.c_int, P]
         L.kvq_decode_attention.restype = C.c_int
         L.kvq_decode_attention.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, P, P, P,
                                            C.c_float, C.c_int32, P, C.POINTER(C.c_size_t), P]
@@ -163,6 +168,31 @@ def kvq_quantize(cfg: Config, cache, layer_begin: int, num_layers: int,
                               len(ids), ids.ctypes.data_as(C.POINTER(C.c_int32)),
                               tok_begin, tok_end, _dev_ptr(k_src, "k_src"),
                               _dev_ptr(v_src, "v_src"), dt, _stream(stream)), "kvq_quantize")
+
+
+def kvq_quantize_ragged(cfg: Config, cache, layer_begin: int, num_layers: int,
+                        seq_ids: Sequence[int], tok_begin: Sequence[int], num_tokens: int,
+                        k_src, v_src, stream=None) -> None:
+    """Sequence seq_ids[i] stores positions [tok_begin[i], tok_begin[i] + num_tokens);
+    k_src/v_src: device float32 or bfloat16 [num_layers, len(seq_ids), Hkv, num_tokens, D]."""
+    import torch
+    if k_src.dtype != v_src.dtype:
+        raise ValueError("k_src and v_src must share a dtype")
+    if k_src.dtype == torch.bfloat16:
+        dt = KVQ_SRC_BF16
+    elif k_src.dtype == torch.float32:
+        dt = KVQ_SRC_F32
+    else:
+        raise ValueError("sources must be float32 or bfloat16")
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+    t0 = np.ascontiguousarray(tok_begin, dtype=np.int32)
+    if t0.shape != ids.shape:
+        raise ValueError("one start position per sequence")
+    _check(lib().kvq_quantize_ragged(cfg.ref, _dev_ptr(cache, "cache"), layer_begin, num_layers,
+                                     len(ids), ids.ctypes.data_as(C.POINTER(C.c_int32)),
+                                     t0.ctypes.data_as(C.POINTER(C.c_int32)), num_tokens,
+                                     _dev_ptr(k_src, "k_src"), _dev_ptr(v_src, "v_src"), dt,
+                                     _stream(stream)), "kvq_quantize_ragged")
 
 
 def workspace_bytes(cfg: Config, num_layers: int, chunk_tokens: int = 0) -> int:

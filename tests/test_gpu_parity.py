@@ -434,3 +434,45 @@ def test_quantize_grid_points_and_ties_bitexact(bits):
         for a, b in ((vis, vis + T * D * bits // 8), (meta, meta + T * (D // g) * 4)):
             assert np.array_equal(got[a:b], ocache[a:b]), (bits, X, a)
     assert info["quantized_values"] == 2 * T * D
+
+
+def test_quantize_ragged_append_bitexact():
+    """A ragged batch appends its next tokens in one call, each sequence at
+    its own position (kvq_quantize_ragged): after a prefix store, one token
+    per sequence and then three more, across a visual span end and into the
+    text suffix; every stored byte equals the oracle's per-sequence stores,
+    and the decode that follows matches the oracle."""
+    import oracle
+    from kvq_testlib import to_device_src, as_f32
+    from quantized_decode_attention_quantize_amd.synth import TAG_APPEND_K, TAG_APPEND_V
+    _say("quantize ragged append")
+    caps = [300, 180, 257, 90, 400]
+    vb = [14, 0, 5, 10, 14]
+    ve = [290, 170, 250, 88, 390]  # sequence 3's appends cross its span end
+    w = synth.Workload("ragged_app", 2, 5, 8, 2, 128, 64, caps, vb, ve, caps,
+                       np.array([4, 16, 8, 2], np.uint8), np.array([2, 16, 4, 2], np.uint8),
+                       seed=31)
+    p = Pair(w)
+    T = [c - 5 for c in caps]  # history before the appends
+    for s in range(w.batch):
+        p.store(seqs=[s], t0=0, t1=T[s])
+    seqs = list(range(w.batch))
+    for t_off, n in ((0, 1), (1, 3)):
+        t0 = [T[s] + t_off for s in seqs]
+        k = np.stack([np.stack([np.stack([w.k_rows(l, s, h, t0[s], t0[s] + n, TAG_APPEND_K)
+                                          for h in range(w.num_kv_heads)]) for s in seqs])
+                      for l in range(w.num_layers)])
+        v = np.stack([np.stack([np.stack([w.v_rows(l, s, h, t0[s], t0[s] + n, TAG_APPEND_V)
+                                          for h in range(w.num_kv_heads)]) for s in seqs])
+                      for l in range(w.num_layers)])
+        kvq.kvq_quantize_ragged(p.cfg, p.cache, 0, w.num_layers, seqs, t0, n,
+                                to_device_src(k), to_device_src(v))
+        for l in range(w.num_layers):
+            for s in seqs:
+                for h in range(w.num_kv_heads):
+                    oracle.store_rows(p.ocfg, p.ocache, l, s, h, 0, t0[s], t0[s] + n,
+                                      as_f32(k[l, s, h]))
+                    oracle.store_rows(p.ocfg, p.ocache, l, s, h, 1, t0[s], t0[s] + n,
+                                      as_f32(v[l, s, h]))
+    assert p.mismatches() == 0
+    _check_decode(p, [T[s] + 4 for s in seqs], what="after ragged append")

@@ -150,6 +150,32 @@ def test_quantize_validation(L):
     assert _quant(L, _cfg(head_dim=80)) == kvq.KVQ_ERR_UNSUPPORTED
 
 
+def _quant_ragged(L, cfg, seq_ids=(0, 1), t0=(3, 7), n=1, cache=A256, k=A16, v=A16):
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+    tb = np.ascontiguousarray(t0, dtype=np.int32)
+    return L.kvq_quantize_ragged(cfg.ref, C.c_void_p(cache) if cache else None, 0, 1, len(ids),
+                                 ids.ctypes.data_as(C.POINTER(C.c_int32)),
+                                 tb.ctypes.data_as(C.POINTER(C.c_int32)), n,
+                                 C.c_void_p(k) if k else None, C.c_void_p(v) if v else None,
+                                 kvq.KVQ_SRC_BF16, None)
+
+
+def test_quantize_ragged_validation(L):
+    """Per-sequence start positions are checked against each sequence's own
+    capacity before any launch."""
+    cfg = _cfg(batch=2, capacity=[256, 100], vis_begin=[16, 0], vis_end=[256, 50])
+    assert _quant_ragged(L, cfg, t0=(255, 100)) == kvq.KVQ_ERR_RANGE   # seq 1 ends at 100
+    assert _quant_ragged(L, cfg, t0=(250, 90), n=11) == kvq.KVQ_ERR_RANGE
+    assert _quant_ragged(L, cfg, t0=(-1, 3)) == kvq.KVQ_ERR_SHAPE
+    assert _quant_ragged(L, cfg, seq_ids=(1, 1)) == kvq.KVQ_ERR_SHAPE
+    assert _quant_ragged(L, cfg, seq_ids=(0, 2)) == kvq.KVQ_ERR_RANGE
+    assert _quant_ragged(L, cfg, n=-1) == kvq.KVQ_ERR_SHAPE
+    assert _quant_ragged(L, cfg, cache=None) == kvq.KVQ_ERR_NULL
+    assert _quant_ragged(L, cfg, cache=A256 + 64) == kvq.KVQ_ERR_ALIGN
+    assert _quant_ragged(L, cfg, n=0) == kvq.KVQ_OK        # nothing to store
+    assert _quant_ragged(L, cfg, seq_ids=(), t0=()) == kvq.KVQ_OK
+
+
 def _dec(L, cfg, cache=A256, layer_begin=0, num_layers=1, lens=A16, q=A16, out=A16 + 4096,
          chunk=0, ws=A256 + 4096, ws_bytes=1 << 30):
     n = C.c_size_t(ws_bytes)
