@@ -205,15 +205,14 @@ def test_decode_empty_visual_span_and_all_visual():
 
 def test_decode_deterministic():
     """Fixed token chunks (chunk_tokens > 0) assign every token statically, so
-    repeated calls give identical bytes; so does the tiny case in the default
-    split, where every step is one of a wave's static first steps.  (The
-    default split otherwise hands steps out dynamically: the summation order,
-    and so the last bits of the output, may differ between calls.)"""
+    repeated calls give identical bytes.  (The default split hands steps out
+    dynamically: the summation order, and so the last bits of the output, may
+    differ between calls.)"""
     _say("decode determinism")
     p = Pair(synth.tiny(seed=8))
     p.store(oracle_too=False)
-    a, _ = p.decode([256])
-    b, _ = p.decode([256])
+    a, _ = p.decode([256], chunk=64)
+    b, _ = p.decode([256], chunk=64)
     assert np.array_equal(a, b)
     p = Pair(synth.llava_layer(seed=8, kbits=4, vbits=2))
     p.store(oracle_too=False)
