@@ -180,7 +180,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
               "multi-GPU path: the decode kernel runs on one GPU's share and sharding is "
-              "described in DESIGN.md", file=sys.stderr)
+              "left to the caller (independent (layer, sequence, KV head) entries)", file=sys.stderr)
         sys.exit(2)
     import torch
     from quantized_decode_attention_quantize_amd import kvq, synth
