@@ -178,7 +178,7 @@ class Events:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the library has no "
               "multi-GPU path: the decode kernel runs on one GPU's share and sharding is "
               "left to the caller (independent (layer, sequence, KV head) entries)", file=sys.stderr)
         sys.exit(2)
