@@ -282,6 +282,19 @@ def main():
         f"{dec_gbs:.0f} GB/s")
 
     extras = {}
+    if not args.no_extras and w.num_layers > 1:
+        # the same step as a layer-by-layer serving loop issues it: one
+        # decode launch per layer, back to back
+        def per_layer(i):
+            c = caches[i % R]
+            for l in range(w.num_layers):
+                kvq.kvq_decode_attention(cfg, c, l, 1, lens_d, q[l:l + 1], out[l:l + 1],
+                                         w.sm_scale, args.chunk, ws)
+        pl_ms = timed(torch, args, per_layer)
+        extras["per_layer_launches"] = {
+            "launches": w.num_layers, "us": round(pl_ms * 1e3, 2),
+            "us_per_layer": round(pl_ms * 1e3 / w.num_layers, 2),
+            "vs_one_launch": round(pl_ms / dec_avg, 3)}
     if not args.no_extras:
         # bf16 reference: same shapes, every row bf16 (bandwidth reference)
         ref_alg = algorithmic_bytes(_bf16_like(w), lens)
