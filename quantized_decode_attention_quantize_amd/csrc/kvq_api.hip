@@ -302,7 +302,7 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
   if (!use_mfma) groups.assign(1, -1);  // the general kernel takes every format
 
   const int64_t wave_slots = int64_t(kMfmaWaves) * device_cus();
-  constexpr int kMinWaveRows = 128;  // fewer rows per wave only add merge work
+  constexpr int kMinWaveRows = 64;  // fewer rows per wave only add merge work
   int64_t max_pieces = 1;
   for (int s0 = 0; s0 < B; s0 += kMaxSeq) {
     const int ns = std::min(kMaxSeq, B - s0);
