@@ -7,12 +7,12 @@
 // HeadGuard briefing: protected heads keep bf16).  The quantiser's exact
 // arithmetic is spelled out in include/kvq.h.
 //
-// Mapping: one row (token) of D values is handled by D/8 consecutive lanes,
-// 8 values per lane (one 16-byte bf16 load or two for fp32).  A quantisation
-// group of g values spans g/8 lanes; its min/max is a butterfly over those
-// lanes.  Codes of one lane are contiguous in the packed row (8*b bits, b
-// bytes), so each lane issues one store of b bytes; the first lane of a group
-// writes the group's 4-byte (scale, min) pair.
+// Mapping: one row (token) of D values is handled by D/16 consecutive lanes,
+// 16 values per lane (two 16-byte bf16 loads or four for fp32).  A
+// quantisation group of g values spans g/16 lanes; its min/max is a butterfly
+// over those lanes.  Codes of one lane are contiguous in the packed row (16*b
+// bits, 2b bytes), so each lane issues one store of 2b bytes; the first lane
+// of a group writes the group's 4-byte (scale, min) pair.
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
@@ -68,13 +68,23 @@ __device__ inline float group_max(float v) {
   return v;
 }
 
-// Quantise this lane's 8 values (part of a group spanning GL lanes) and
-// return the packed codes (8*bits bits).  Writes (scale | min << 16) to meta.
+// Values of one row held by each lane.  The work that depends only on the
+// group (its min/max reduction, the two directed fp16 roundings, the scale
+// divide, the meta store, the addressing) is shared by a lane's E values, so
+// a wave covers twice the values for little more than the instructions of a
+// wave holding 8.
+constexpr int kE = 16;
+
+// Quantise this lane's kE values (part of a group spanning GL lanes) into
+// packed codes (bit i * bits of the lane's kE * bits bits, as 32-bit words;
+// bits divides 32, so no code straddles a word).  Writes (scale | min << 16)
+// to meta.
 template <int GL>
-__device__ inline uint64_t quantize8(const float (&x)[8], int bits, uint32_t& meta) {
+__device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&packed)[4],
+                                     uint32_t& meta) {
   float lo = x[0], hi = x[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
+  for (int i = 1; i < kE; ++i) {
     lo = fminf(lo, x[i]);
     hi = fmaxf(hi, x[i]);
   }
@@ -85,77 +95,77 @@ __device__ inline uint64_t quantize8(const float (&x)[8], int bits, uint32_t& me
   const float n = float((1 << bits) - 1);
   const float range = hi - mn;
   uint16_t sc16 = 0;
-  uint64_t packed = 0;
   // Each code is rint of the IEEE quotient fl(d / sc).  d * rcp(sc) is within
   // 1.5 * 2^-23 relative of d / sc (rcp within 1 ulp, one rounding), i.e.
   // within 2^-14 for quotients up to 255, and fl(d / sc) within 2^-16 of it:
   // unless the estimate lies within 2^-13 of a half-integer, both round to the
   // same integer.  When any lane of the wave has such a value, the whole wave
-  // takes the IEEE divide for its values (a wave-uniform branch: about one
-  // wave in eight).  A zero-range group keeps scale 0 and all-zero codes.
+  // takes the IEEE divide for its values (a wave-uniform branch).  A
+  // zero-range group keeps scale 0 and all-zero codes.
   const bool live = range != 0.0f;
   if (live) sc16 = f16_round_up(range / n);
   const float sc = f16_float(sc16);
   const float r = __builtin_amdgcn_rcpf(live ? sc : 1.0f);
-  float d[8], q[8];
+  float d[kE], q[kE];
   bool near = false;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kE; ++i) {
     d[i] = x[i] - mn;  // >= 0: mn <= every value of the group
     q[i] = d[i] * r;
     near |= __builtin_fabsf(__builtin_amdgcn_fractf(q[i]) - 0.5f) < 0x1p-13f;  // q >= 0
   }
   if (__builtin_amdgcn_ballot_w64(live && near) != 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = live ? d[i] / sc : 0.0f;
+    for (int i = 0; i < kE; ++i) q[i] = live ? d[i] / sc : 0.0f;
   }
-  if (live) {
-    uint32_t lo32 = 0, hi32 = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+  for (int k = 0; k < 4; ++k) packed[k] = 0u;
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < kE; ++i) {
       const uint32_t c = uint32_t(__builtin_amdgcn_fmed3f(__builtin_rintf(q[i]), 0.0f, n));
-      if (i * bits < 32) lo32 |= c << (i * bits);
-      else hi32 |= c << (i * bits - 32);
+      const int bit = i * bits;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if ((bit >> 5) == k) packed[k] |= c << (bit & 31);
     }
-    packed = uint64_t(lo32) | (uint64_t(hi32) << 32);
   }
   meta = uint32_t(sc16) | (uint32_t(mn16) << 16);
-  return packed;
 }
 
 // Walsh-Hadamard rotation of one row (include/kvq.h; gist.science 2604.02570,
-// section 2-C), held as 8 values in each of the row's D/8 lanes: butterflies
-// of stride 1, 2, 4 inside the lane, then 8 .. D/2 across lanes (the lower
+// section 2-C), held as kE values in each of the row's D/kE lanes: butterflies
+// of stride 1 .. kE/2 inside the lane, then kE .. D/2 across lanes (the lower
 // index of a pair keeps the sum, the upper one lower - upper), then the exact
 // scaling by 2^-ceil(log2(D)/2).  Every lane of the row must be active.
 template <int D>
-__device__ inline void hadamard_row(float (&x)[8], int lane_in_row) {
+__device__ inline void hadamard_row(float (&x)[kE], int lane_in_row) {
 #pragma unroll
-  for (int s = 1; s < 8; s <<= 1)
+  for (int s = 1; s < kE; s <<= 1)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kE; ++i)
       if (!(i & s)) {
         const float lo = x[i], hi = x[i + s];
         x[i] = lo + hi;
         x[i + s] = lo - hi;
       }
 #pragma unroll
-  for (int m = 1; m < D / 8; m <<= 1) {
+  for (int m = 1; m < D / kE; m <<= 1) {
     const bool upper = (lane_in_row & m) != 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kE; ++i) {
       const float other = __shfl_xor(x[i], m);
       x[i] = upper ? other - x[i] : x[i] + other;
     }
   }
   constexpr float kScale = D == 128 ? 0.0625f : 0.125f;  // 2^-ceil(log2(D)/2)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = x[i] * kScale;
+  for (int i = 0; i < kE; ++i) x[i] = x[i] * kScale;
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
-  constexpr int LPR = D / 8;             // lanes per row
+  constexpr int LPR = D / kE;            // lanes per row
   constexpr int RPB = 256 / LPR;         // rows per block
   const int lane_in_row = threadIdx.x % LPR;
   const int row_in_block = threadIdx.x / LPR;
@@ -173,22 +183,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   const int64_t src_row =
       ((int64_t(l_local) * a.num_seqs_total + (a.seq_off + sl)) * a.Hkv + h) * a.n_tok + rr;
   const void* src = X ? a.v_src : a.k_src;
-  float x[8];
+  float x[kE];
   if (a.src_bf16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(
-        static_cast<const uint16_t*>(src) + src_row * D + lane_in_row * 8);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) +
+                                                    src_row * D + lane_in_row * kE);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-      x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    for (int k = 0; k < kE / 8; ++k) {
+      const uint4 v = p[k];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * k + 2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        x[8 * k + 2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+      }
     }
   } else {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) +
-                                                      src_row * D + lane_in_row * 8);
-    const float4 u = p[0], v = p[1];
-    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+                                                      src_row * D + lane_in_row * kE);
+#pragma unroll
+    for (int k = 0; k < kE / 4; ++k) {
+      const float4 u = p[k];
+      x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
+    }
   }
 
   const int bits = a.bits[lh][X];
@@ -199,18 +215,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   // Every lane of a row takes the same branch; groups never straddle rows.
   if (visual && bits < 16) {
     uint32_t meta;
-    uint64_t packed;
+    uint32_t packed[4];
     if (a.rotate_k && X == 0) hadamard_row<D>(x, lane_in_row);
-    if (a.g == 32) packed = quantize8<4>(x, bits, meta);
-    else if (a.g == 64) packed = quantize8<8>(x, bits, meta);
-    else packed = quantize8<16>(x, bits, meta);
+    if (a.g == 32) quantize_lane<32 / kE>(x, bits, packed, meta);
+    else if (a.g == 64) quantize_lane<64 / kE>(x, bits, packed, meta);
+    else quantize_lane<128 / kE>(x, bits, packed, meta);
     if (!active) return;
     const int64_t row = a.vrow0[sl] + (t - vb);
-    uint8_t* rowp = vis + row * (D * bits / 8) + lane_in_row * bits;
-    if (bits == 2) *reinterpret_cast<uint16_t*>(rowp) = uint16_t(packed);
-    else if (bits == 4) *reinterpret_cast<uint32_t*>(rowp) = uint32_t(packed);
-    else *reinterpret_cast<uint2*>(rowp) = make_uint2(uint32_t(packed), uint32_t(packed >> 32));
-    const int gl = a.g / 8;
+    uint8_t* rowp = vis + row * (D * bits / 8) + lane_in_row * (kE * bits / 8);
+    if (bits == 2) *reinterpret_cast<uint32_t*>(rowp) = packed[0];
+    else if (bits == 4) *reinterpret_cast<uint2*>(rowp) = make_uint2(packed[0], packed[1]);
+    else *reinterpret_cast<uint4*>(rowp) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    const int gl = a.g / kE;
     if (lane_in_row % gl == 0) {
       uint8_t* metap = vis + meta_plane_offset(a.Rvis, D, bits) + row * ((D / a.g) * 4);
       *reinterpret_cast<uint32_t*>(metap + (lane_in_row / gl) * 4) = meta;
@@ -224,12 +240,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
       const int64_t trow = a.trow0[sl] + (t < vb ? t : t - (ve - vb));
       rowp = vis + txt_plane_offset(a.Rvis, D, a.g, bits) + trow * int64_t(2 * D);
     }
-    uint4 o;
-    o.x = uint32_t(bf16_rne(x[0])) | (uint32_t(bf16_rne(x[1])) << 16);
-    o.y = uint32_t(bf16_rne(x[2])) | (uint32_t(bf16_rne(x[3])) << 16);
-    o.z = uint32_t(bf16_rne(x[4])) | (uint32_t(bf16_rne(x[5])) << 16);
-    o.w = uint32_t(bf16_rne(x[6])) | (uint32_t(bf16_rne(x[7])) << 16);
-    *reinterpret_cast<uint4*>(rowp + lane_in_row * 16) = o;
+#pragma unroll
+    for (int k = 0; k < kE / 8; ++k) {
+      uint4 o;
+      o.x = uint32_t(bf16_rne(x[8 * k + 0])) | (uint32_t(bf16_rne(x[8 * k + 1])) << 16);
+      o.y = uint32_t(bf16_rne(x[8 * k + 2])) | (uint32_t(bf16_rne(x[8 * k + 3])) << 16);
+      o.z = uint32_t(bf16_rne(x[8 * k + 4])) | (uint32_t(bf16_rne(x[8 * k + 5])) << 16);
+      o.w = uint32_t(bf16_rne(x[8 * k + 6])) | (uint32_t(bf16_rne(x[8 * k + 7])) << 16);
+      reinterpret_cast<uint4*>(rowp + lane_in_row * (2 * kE))[k] = o;
+    }
   }
 }
 
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
 
 hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
                            hipStream_t stream) {
-  const int rpb = 256 / (a.D / 8);
+  const int rpb = 256 / (a.D / kE);  // rows per block
   dim3 grid((a.n_tok + rpb - 1) / rpb, n_seq_launch, n_lh_launch * 2);
   if (a.D == 128)
     hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, a);
