@@ -79,8 +79,9 @@ constexpr int kE = 16;
 // packed codes (bit i * bits of the lane's kE * bits bits, as 32-bit words;
 // bits divides 32, so no code straddles a word).  Writes (scale | min << 16)
 // to meta.
+constexpr int kWords = kE / 4;  // 32-bit words of an 8-bit lane chunk
 template <int GL>
-__device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&packed)[4],
+__device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&packed)[kWords],
                                      uint32_t& meta) {
   float lo = x[0], hi = x[0];
 #pragma unroll
@@ -119,14 +120,14 @@ __device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&
     for (int i = 0; i < kE; ++i) q[i] = live ? d[i] / sc : 0.0f;
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) packed[k] = 0u;
+  for (int k = 0; k < kWords; ++k) packed[k] = 0u;
   if (live) {
 #pragma unroll
     for (int i = 0; i < kE; ++i) {
       const uint32_t c = uint32_t(__builtin_amdgcn_fmed3f(__builtin_rintf(q[i]), 0.0f, n));
       const int bit = i * bits;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < kWords; ++k)
         if ((bit >> 5) == k) packed[k] |= c << (bit & 31);
     }
   }
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   // Every lane of a row takes the same branch; groups never straddle rows.
   if (visual && bits < 16) {
     uint32_t meta;
-    uint32_t packed[4];
+    uint32_t packed[kWords];
     if (a.rotate_k && X == 0) hadamard_row<D>(x, lane_in_row);
     if (a.g == 32) quantize_lane<32 / kE>(x, bits, packed, meta);
     else if (a.g == 64) quantize_lane<64 / kE>(x, bits, packed, meta);
@@ -223,9 +224,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
     if (!active) return;
     const int64_t row = a.vrow0[sl] + (t - vb);
     uint8_t* rowp = vis + row * (D * bits / 8) + lane_in_row * (kE * bits / 8);
-    if (bits == 2) *reinterpret_cast<uint32_t*>(rowp) = packed[0];
-    else if (bits == 4) *reinterpret_cast<uint2*>(rowp) = make_uint2(packed[0], packed[1]);
-    else *reinterpret_cast<uint4*>(rowp) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    // the lane's kE * bits / 32 words, in 16-byte pieces where they fill one
+    const int words = kE * bits / 32;
+    if (words >= 4) {
+#pragma unroll
+      for (int k = 0; k < kWords / 4; ++k)
+        if (4 * k < words)
+          reinterpret_cast<uint4*>(rowp)[k] =
+              make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
+    } else if (words == 2) {
+      *reinterpret_cast<uint2*>(rowp) = make_uint2(packed[0], packed[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(rowp) = packed[0];
+    }
     const int gl = a.g / kE;
     if (lane_in_row % gl == 0) {
       uint8_t* metap = vis + meta_plane_offset(a.Rvis, D, bits) + row * ((D / a.g) * 4);
