@@ -475,3 +475,53 @@ def test_quantize_ragged_append_bitexact():
                                       as_f32(v[l, s, h]))
     assert p.mismatches() == 0
     _check_decode(p, [T[s] + 4 for s in seqs], what="after ragged append")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_quantize_degenerate_groups_bitexact(bits):
+    """Groups that stress the fp16 directed roundings and the zero-scale path:
+    all zeros, -0, one non-zero constant (its fp16 min may sit below it, so the
+    scale rounds up to a tiny non-zero value), a tiny range on a large offset,
+    values near the fp16 limit, and values far below the fp16 subnormal step.
+    Stored bytes equal the oracle's."""
+    import torch
+    import oracle
+    from kvq_testlib import to_device_src
+    _say("quantize degenerate groups", bits)
+    D, g = 128, 64
+    rng = np.random.default_rng(100 + bits)
+    rows = []
+    for kind in range(7):
+        for rep in range(16):
+            r = np.empty(D, np.float64)
+            for j in range(D // g):
+                c = rng.standard_normal()
+                grp = {0: np.zeros(g),
+                       1: -np.zeros(g),
+                       2: np.full(g, c * 10),
+                       3: 100.0 + 1e-3 * rng.standard_normal(g),
+                       4: rng.uniform(-65000, 65000, g),
+                       5: 1e-9 * rng.standard_normal(g),
+                       6: np.concatenate([[c], np.full(g - 1, c + 2.0 ** -20)])}[kind]
+                r[j * g:(j + 1) * g] = grp
+            rows.append(r)
+    xs = np.array(rows, dtype=np.float32)
+    T = len(rows)
+    w = synth.Workload("degen", 1, 1, 4, 1, D, g, [T], [0], [T], [T],
+                       np.array([bits], np.uint8), np.array([bits], np.uint8), src="f32")
+    cfg = kvq.Config.from_workload(w)
+    ocfg = oracle.Config.from_workload(w)
+    cache = torch.zeros(kvq.kvq_cache_bytes(cfg)["total_bytes"], dtype=torch.uint8,
+                        device="cuda")
+    src = to_device_src(xs[None, None, None])
+    kvq.kvq_quantize(cfg, cache, 0, 1, [0], 0, T, src, src)
+    ocache = oracle.new_cache(ocfg)
+    for X in (0, 1):
+        oracle.store_rows(ocfg, ocache, 0, 0, 0, X, 0, T, xs)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    for X in (0, 1):
+        vis, meta, _ = oracle.plane_offsets(ocfg, 0, 0, X)
+        for a, b in ((vis, vis + T * D * bits // 8), (meta, meta + T * (D // g) * 4)):
+            bad = np.flatnonzero(got[a:b] != ocache[a:b])
+            assert bad.size == 0, (bits, X, a, bad[:8])
