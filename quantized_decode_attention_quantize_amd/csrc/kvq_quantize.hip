@@ -80,6 +80,17 @@ constexpr int kE = 16;
 // bits divides 32, so no code straddles a word).  Writes (scale | min << 16)
 // to meta.
 constexpr int kWords = kE / 4;  // 32-bit words of an 8-bit lane chunk
+
+// Codes rint(q) clamped to [0, n], B bits each, packed little-endian.
+template <int B>
+__device__ inline void pack_codes(const float (&q)[kE], float n, uint32_t (&packed)[kWords]) {
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const uint32_t c = uint32_t(__builtin_amdgcn_fmed3f(__builtin_rintf(q[i]), 0.0f, n));
+    packed[(i * B) / 32] |= c << ((i * B) % 32);
+  }
+}
+
 template <int GL>
 __device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&packed)[kWords],
                                      uint32_t& meta) {
@@ -122,14 +133,11 @@ __device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&
 #pragma unroll
   for (int k = 0; k < kWords; ++k) packed[k] = 0u;
   if (live) {
-#pragma unroll
-    for (int i = 0; i < kE; ++i) {
-      const uint32_t c = uint32_t(__builtin_amdgcn_fmed3f(__builtin_rintf(q[i]), 0.0f, n));
-      const int bit = i * bits;
-#pragma unroll
-      for (int k = 0; k < kWords; ++k)
-        if ((bit >> 5) == k) packed[k] |= c << (bit & 31);
-    }
+    // the width is the same for the whole workgroup: one branch, and each
+    // code's word and shift are constants
+    if (bits == 2) pack_codes<2>(q, n, packed);
+    else if (bits == 4) pack_codes<4>(q, n, packed);
+    else pack_codes<8>(q, n, packed);
   }
   meta = uint32_t(sc16) | (uint32_t(mn16) << 16);
 }
