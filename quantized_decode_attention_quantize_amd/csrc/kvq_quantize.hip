@@ -81,13 +81,13 @@ constexpr int kE = 16;
 // to meta.
 constexpr int kWords = kE / 4;  // 32-bit words of an 8-bit lane chunk
 
-// Codes rint(q) clamped to [0, n], B bits each, packed little-endian.
+// Rounded quotients c clamped to [0, n], B bits each, packed little-endian.
 template <int B>
-__device__ inline void pack_codes(const float (&q)[kE], float n, uint32_t (&packed)[kWords]) {
+__device__ inline void pack_codes(const float (&c)[kE], float n, uint32_t (&packed)[kWords]) {
 #pragma unroll
   for (int i = 0; i < kE; ++i) {
-    const uint32_t c = uint32_t(__builtin_amdgcn_fmed3f(__builtin_rintf(q[i]), 0.0f, n));
-    packed[(i * B) / 32] |= c << ((i * B) % 32);
+    const uint32_t code = uint32_t(__builtin_amdgcn_fmed3f(c[i], 0.0f, n));
+    packed[(i * B) / 32] |= code << ((i * B) % 32);
   }
 }
 
@@ -118,26 +118,28 @@ __device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&
   if (live) sc16 = f16_round_up(range / n);
   const float sc = f16_float(sc16);
   const float r = __builtin_amdgcn_rcpf(live ? sc : 1.0f);
-  float d[kE], q[kE];
+  float d[kE], c[kE];
   bool near = false;
 #pragma unroll
   for (int i = 0; i < kE; ++i) {
     d[i] = x[i] - mn;  // >= 0: mn <= every value of the group
-    q[i] = d[i] * r;
-    near |= __builtin_fabsf(__builtin_amdgcn_fractf(q[i]) - 0.5f) < 0x1p-13f;  // q >= 0
+    const float q = d[i] * r;
+    c[i] = __builtin_rintf(q);
+    // within 2^-13 of a half-integer: q - c is exact, and |q - c| <= 1/2
+    near |= __builtin_fabsf(q - c[i]) > 0.5f - 0x1p-13f;
   }
   if (__builtin_amdgcn_ballot_w64(live && near) != 0) {
 #pragma unroll
-    for (int i = 0; i < kE; ++i) q[i] = live ? d[i] / sc : 0.0f;
+    for (int i = 0; i < kE; ++i) c[i] = live ? __builtin_rintf(d[i] / sc) : 0.0f;
   }
 #pragma unroll
   for (int k = 0; k < kWords; ++k) packed[k] = 0u;
   if (live) {
     // the width is the same for the whole workgroup: one branch, and each
     // code's word and shift are constants
-    if (bits == 2) pack_codes<2>(q, n, packed);
-    else if (bits == 4) pack_codes<4>(q, n, packed);
-    else pack_codes<8>(q, n, packed);
+    if (bits == 2) pack_codes<2>(c, n, packed);
+    else if (bits == 4) pack_codes<4>(c, n, packed);
+    else pack_codes<8>(c, n, packed);
   }
   meta = uint32_t(sc16) | (uint32_t(mn16) << 16);
 }
