@@ -193,14 +193,16 @@ kvq_status kvq_quantize_ragged(const kvq_config *cfg, void *cache, int32_t layer
  *   out        device bf16 [num_layers, batch, Hq, D], 16-byte aligned; must
  *              not alias q, cache or workspace
  *   sm_scale   softmax scale applied to q.k (e.g. 1/sqrt(D)), fp32
- *   chunk_tokens  0 = library choice: each (layer, seq, KV head) is split into
- *              workgroups in proportion to its capacity and per-token cost so
- *              that all waves of the call fit the device at once, and its
- *              32-token steps are handed out to those waves as they finish
- *              (the summation order, hence the output's last bits, can differ
- *              between calls); otherwise a positive multiple of 32 = tokens
- *              per split-K workgroup, assigned statically (repeated calls give
- *              identical bytes)
+ *   chunk_tokens  0 = library choice.  A call with at least one 32-token step
+ *              per wave slot of the device splits each (layer, seq, KV head)
+ *              into workgroups in proportion to its capacity and per-token
+ *              cost, so that all waves of the call fit the device at once, and
+ *              hands its steps to those waves as they finish (the summation
+ *              order, hence the output's last bits, can differ between
+ *              calls); a smaller call (latency-bound) takes fixed 1024-token
+ *              chunks.  Otherwise a positive multiple of 32 = tokens per
+ *              split-K workgroup.  Fixed chunks are assigned statically:
+ *              repeated calls give identical bytes.
  *   workspace  device scratch for split partials and the merge's arrival
  *              counters, 256-byte aligned.  If workspace == NULL the call only
  *              writes the required size to *workspace_bytes and launches
