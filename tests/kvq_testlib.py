@@ -165,6 +165,7 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
     half a bf16 ulp of the reference (rounding the exact value to bf16 alone
     costs up to that half ulp), and relative L2 error <= 2e-3."""
     max_abs, rel = errors(got, ref)
+    print(f"[close] {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
     assert np.all(np.isfinite(got)), what
     assert max_abs <= MAX_ABS and rel <= REL_L2, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
     return max_abs, rel
