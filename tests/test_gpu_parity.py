@@ -525,3 +525,31 @@ def test_quantize_degenerate_groups_bitexact(bits):
         for a, b in ((vis, vis + T * D * bits // 8), (meta, meta + T * (D // g) * 4)):
             bad = np.flatnonzero(got[a:b] != ocache[a:b])
             assert bad.size == 0, (bits, X, a, bad[:8])
+
+
+def test_calls_split_over_several_launches():
+    """Calls larger than one launch's tables: 70 sequences (over the 64 a
+    launch holds) and 40 layers x 4 KV heads = 160 (layer, head) pairs (over
+    the 128 a launch holds) are stored and decoded in several launches; every
+    output and every stored byte matches the oracle."""
+    _say("calls over several launches: 70 sequences")
+    rng = np.random.default_rng(77)
+    caps = [int(c) for c in rng.integers(40, 260, 70)]
+    vb = [min(14, c) for c in caps]
+    ve = [max(b, c - int(rng.integers(0, 3))) for b, c in zip(vb, caps)]
+    w = synth.Workload("seqs70", 1, 70, 8, 2, 128, 64, caps, vb, ve, caps,
+                       np.array([4, 16], np.uint8), np.array([2, 16], np.uint8), seed=41)
+    p = Pair(w)
+    p.store()
+    assert p.mismatches() == 0
+    _check_decode(p, caps, what="70 sequences")
+    _check_decode(p, [max(1, c - 7) for c in caps], what="70 sequences shortened")
+    _say("calls over several launches: 160 (layer, head) pairs")
+    kb = np.where(np.arange(160) % 9 == 0, 16, 4).astype(np.uint8)
+    vbits = np.where(np.arange(160) % 9 == 0, 16, 2).astype(np.uint8)
+    w = synth.Workload("pairs160", 40, 1, 16, 4, 128, 64, [150], [5], [140], [150], kb, vbits,
+                       seed=43)
+    p = Pair(w)
+    p.store()
+    assert p.mismatches() == 0
+    _check_decode(p, [150], what="160 pairs")
