@@ -1338,26 +1338,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const int ppn = __builtin_amdgcn_readfirstlane(winfo[wl][6]);
     const int64_t pidx = partial_index(pl, ps, ph, ppx, a.B, a.Hkv, a.max_chunks);
     uint16_t* outp = a.out + ((int64_t(pl) * a.B + ps) * a.Hq + int64_t(ph) * G) * D;
-    for (int i = threadIdx.x; i < GD; i += kThreads) {
+    // four consecutive outputs per thread (one head, one group: D and g are
+    // multiples of 4): 16-byte LDS reads and one 16-byte store
+    const Rsrc rpo = make_rsrc(a.ws_o + pidx * GD, int64_t(GD) * 4);
+    for (int i4 = threadIdx.x; i4 < GD / 4; i4 += kThreads) {
+      const int i = 4 * i4;
       const int j = i / D, d = i % D, cr = j * NG + d / g;
-      float acc = 0.0f;
+      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int w4 = 0; w4 < kWaves / 4; ++w4) {
         const f32x4 f = *reinterpret_cast<const f32x4*>(&wts[cr][4 * w4]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float x = o_all[4 * w4 + w][cr][d] * f[w];
-          acc += (pm >> (4 * w4 + w)) & 1u ? x : 0.0f;
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&o_all[4 * w4 + w][cr][d]);
+          const float fw = (pm >> (4 * w4 + w)) & 1u ? f[w] : 0.0f;
+          acc += x * fw;
         }
       }
       const float L = rowL[wl][cr];
-      const float o = L > 0.0f ? acc * __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
+      const float rl = L > 0.0f ? __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
+      const f32x4 o = acc * rl;
       if (ppn == 1) {
-        outp[i] = __builtin_bit_cast(uint16_t, (__bf16)o);
+        uint2 ob;
+        ob.x = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o[0])) |
+               (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o[1])) << 16);
+        ob.y = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o[2])) |
+               (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o[3])) << 16);
+        *reinterpret_cast<uint2*>(outp + i) = ob;
       } else {
-        // write-through (system-coherent) stores: the merging workgroup may
-        // sit on another XCD and reads them past its own caches
-        __hip_atomic_store(&a.ws_o[pidx * GD + i], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        // write-through (system-coherent) store: the merging workgroup may
+        // sit on another XCD and reads it past its own caches
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rpo,
+                                               uint32_t(i) * 4u, 0, kCoherent);
         if (d == 0) {
           __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], rowM[wl][cr], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_SYSTEM);
