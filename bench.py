@@ -334,7 +334,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16/bf16 MFMA operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": describe(w), "name": w.name, "layers": w.num_layers,
                    "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,

@@ -49,8 +49,13 @@
  * Ownership, streams, errors
  * --------------------------
  * Every device pointer is owned by the caller (typically torch tensors);
- * libkvq never allocates, frees or retains device memory; its only global
- * state is a per-device cache of the compute-unit count.  Host arrays are read only during the call.
+ * libkvq never allocates, frees or retains device memory.  Host-side global
+ * state is limited to two memo tables that never change a result: the
+ * compute-unit count of each device, read once, and the last four decode
+ * split plans, keyed by everything a plan depends on (call shape, cache
+ * configuration, device CU count) and guarded by a mutex, so a decode call
+ * repeated step after step skips about 2 us of host planning.  Host arrays
+ * are read only during the call.
  * kvq_quantize and kvq_decode_attention only enqueue work on `stream`
  * (a hipStream_t; NULL = the default stream) and never synchronise; faults
  * inside kernels surface at the caller's next synchronisation.  Every entry
@@ -60,8 +65,10 @@
  *
  * Supported shapes: head_dim D in {64, 128}; group_size g in {32, 64, 128}
  * with g dividing D; bits in {2, 4, 8, 16}; num_q_heads a multiple of
- * num_kv_heads.  Values whose stored fp16 scale/min would overflow binary16
- * (|x| > 65504) are outside the supported range.
+ * num_kv_heads (KVQ_ERR_UNSUPPORTED otherwise); kvq_decode_attention also
+ * needs num_q_heads / num_kv_heads <= 16 (KVQ_ERR_UNSUPPORTED otherwise).
+ * Values whose stored fp16 scale/min would overflow binary16 (|x| > 65504)
+ * are outside the supported range.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -132,12 +139,25 @@ typedef struct {
   uint64_t stored_values;     /* all K/V scalars: 2*L*Hkv*D*sum(capacity)      */
 } kvq_cache_info;
 
-/* Storage size of the cache `cfg` describes.  Host only, pure, synchronous.
+/* Storage size of the cache `cfg` describes, split so that the true cost of
+ * a width can be read off: code and meta bytes against the values stored as
+ * codes give bits per value including the fp16 (scale, min) overhead (the
+ * opening checklist of nuiw.github.io "VLM_KV_Quantization" asks whether a
+ * nominal INT2 cache really costs 2 bits per value, and whether the count
+ * of quantised tokens is non-zero: quantized_values answers that).
+ *   cfg    HOST, validated as described above
+ *   info   HOST, written on success
+ * Host only, pure, synchronous, touches no device.
  * Errors: KVQ_ERR_NULL (cfg/info/arrays), KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_cache_bytes(const kvq_config *cfg, kvq_cache_info *info);
 
 /* Store positions [tok_begin, tok_end) of the sequences seq_ids[0..num_seqs)
  * for layers [layer_begin, layer_begin + num_layers) into `cache`.
+ * Passages: nuiw.github.io "VLM_KV_Quantization" section 1 (only the
+ * historical cache is compressed, with the Visual/Text and K/V axes handled
+ * separately) and section 2 (K is stored after RoPE; the visual block sits
+ * between the system text and the question); the HeadGuard briefing (a few
+ * physical KV heads keep visual K, optionally V, at high precision).
  *
  * Each row's format follows from its position and head: a visual position in
  * a head whose width is < 16 is quantised (codes + meta); every other row
@@ -180,7 +200,11 @@ kvq_status kvq_quantize_ragged(const kvq_config *cfg, void *cache, int32_t layer
                                void *stream);
 
 /* One decode step of attention for layers [layer_begin, layer_begin +
- * num_layers): for every layer l, sequence s and query head i,
+ * num_layers).  Passages: gist.science 2604.02570 section 2-D (rows are
+ * rebuilt on chip inside a fused flash-decoding kernel and never written back
+ * to memory); nuiw.github.io "VLM_KV_Quantization" section 2 (GQA: the
+ * stored KV heads serve several query heads each).  For every layer l,
+ * sequence s and query head i,
  *   out[l,s,i,:] = softmax(sm_scale * K^ q) V^   over positions [0, seq_lens[s])
  * of KV head floor(i * Hkv / Hq), with K^, V^ the stored rows reconstructed
  * on chip (codes * scale + min, or bf16).  Split-K over token chunks with a
@@ -223,7 +247,8 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const void *cache,
                                 float sm_scale, int32_t chunk_tokens, void *workspace,
                                 size_t *workspace_bytes, void *stream);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL; unknown codes get a
+ * generic string).  A utility of the ABI, not a step of the method. */
 const char *kvq_status_string(kvq_status s);
 
 #ifdef __cplusplus

@@ -459,21 +459,14 @@ void orc_attention(const double *q, const double *K, const double *V, int T,
 int orc_decode_one(const orc_config *c, const uint8_t *cache, int layer,
                    int seq, int qhead, int len, const uint16_t *q_bf16,
                    float sm_scale, double *out, double *lse, double *scores) {
-  int D = c->head_dim, t, d, kv, X, vb, ve, kb, vbits;
+  int D = c->head_dim, t, d, kv, X, kb, vbits;
   uint64_t off[2][3];
-  int64_t vbase = 0, tbase = 0;
   double *K, *V, *q;
   if (orc_validate(c) || seq < 0 || seq >= c->batch) return 1;
   if (len < 1 || len > c->capacity[seq]) return 1;
   kv = (int)((int64_t)qhead * c->num_kv_heads / c->num_q_heads);
   for (X = 0; X < 2; X++)
     if (orc_plane_offsets(c, layer, kv, X, &off[X][0], &off[X][1], &off[X][2])) return 2;
-  for (t = 0; t < seq; t++) {
-    vbase += c->vis_end[t] - c->vis_begin[t];
-    tbase += c->capacity[t] - (c->vis_end[t] - c->vis_begin[t]);
-  }
-  vb = c->vis_begin[seq];
-  ve = c->vis_end[seq];
   kb = c->k_bits[layer * c->num_kv_heads + kv];
   vbits = c->v_bits[layer * c->num_kv_heads + kv];
   K = (double *)malloc(sizeof(double) * (size_t)len * D);
@@ -481,8 +474,9 @@ int orc_decode_one(const orc_config *c, const uint8_t *cache, int layer,
   q = (double *)malloc(sizeof(double) * (size_t)D);
   for (d = 0; d < D; d++) q[d] = orc_bf16_value(q_bf16[d]);
   for (t = 0; t < len; t++) {
-    int plane = (t >= vb && t < ve) ? 0 : 2;
-    int64_t row = plane == 0 ? vbase + (t - vb) : tbase + (t < vb ? t : t - (ve - vb));
+    int plane;
+    int64_t row;
+    orc_row_of(c, seq, t, &plane, &row); /* t < len <= capacity: in range */
     load_row_at(c, cache, off[0][0], off[0][1], off[0][2], kb, plane, row, K + (size_t)t * D);
     if (c->rotate_k && plane == 0 && kb < 16) orc_hadamard_unrotate(K + (size_t)t * D, D);
     load_row_at(c, cache, off[1][0], off[1][1], off[1][2], vbits, plane, row, V + (size_t)t * D);

@@ -31,7 +31,7 @@ kvq_status check_config(const kvq_config* c) {
   if (c->num_layers < 1 || c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1 ||
       c->head_dim < 1 || c->group_size < 1)
     return KVQ_ERR_SHAPE;
-  if (c->num_q_heads % c->num_kv_heads) return KVQ_ERR_SHAPE;
+  if (c->num_q_heads % c->num_kv_heads) return KVQ_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
   if (c->group_size != 32 && c->group_size != 64 && c->group_size != 128)
     return KVQ_ERR_UNSUPPORTED;
@@ -386,7 +386,8 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
 
 // Plans depend only on the call's shape (not on the sequence lengths, which
 // stay on the device), and decoding repeats one shape step after step, so the
-// last few plans are kept, keyed by everything plan_decode reads.
+// last few plans are kept, keyed by everything plan_decode reads: the layer
+// count of the cache sizes the arrival counters, so it is part of the key.
 std::shared_ptr<const DecodePlan> cached_plan(const kvq_config* c, int layer_begin, int nl,
                                               int chunk_tokens, bool use_mfma) {
   constexpr size_t kKeep = 4;
@@ -394,7 +395,8 @@ std::shared_ptr<const DecodePlan> cached_plan(const kvq_config* c, int layer_beg
   static std::vector<std::pair<std::vector<int32_t>, std::shared_ptr<const DecodePlan>>> kept;
   const int Hkv = c->num_kv_heads;
   std::vector<int32_t> key = {layer_begin, nl, chunk_tokens, int32_t(use_mfma), device_cus(),
-                              c->batch, c->num_q_heads, Hkv, c->head_dim, c->group_size};
+                              c->num_layers, c->batch, c->num_q_heads, Hkv, c->head_dim,
+                              c->group_size};
   key.reserve(key.size() + c->batch + size_t(nl) * Hkv);
   for (int s = 0; s < c->batch; ++s) key.push_back(c->capacity[s]);
   for (int i = layer_begin * Hkv; i < (layer_begin + nl) * Hkv; ++i)

@@ -137,6 +137,38 @@ def _dev_ptr(t, name: str):
     return C.c_void_p(t.data_ptr())
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_cache(cfg: "Config", cache) -> None:
+    import torch
+    if cache.dtype != torch.uint8:
+        raise ValueError("cache must be a uint8 tensor")
+    need = kvq_cache_bytes(cfg)["total_bytes"]
+    if cache.numel() < need:
+        raise ValueError(f"cache holds {cache.numel()} bytes, the config needs {need}")
+
+
+def _check_sources(cfg: "Config", k_src, v_src, num_layers: int, num_seqs: int,
+                   num_tokens: int):
+    """-> the source dtype code; shapes must be [num_layers, num_seqs, Hkv, num_tokens, D]."""
+    import torch
+    if k_src.dtype != v_src.dtype:
+        raise ValueError("k_src and v_src must share a dtype")
+    if k_src.dtype == torch.bfloat16:
+        dt = KVQ_SRC_BF16
+    elif k_src.dtype == torch.float32:
+        dt = KVQ_SRC_F32
+    else:
+        raise ValueError("sources must be float32 or bfloat16")
+    want = (num_layers, num_seqs, cfg.num_kv_heads, num_tokens, cfg.head_dim)
+    for name, t in (("k_src", k_src), ("v_src", v_src)):
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+    return dt
+
+
 def _stream(stream) -> Optional[C.c_void_p]:
     if stream is None:
         import torch
@@ -154,16 +186,9 @@ def kvq_quantize(cfg: Config, cache, layer_begin: int, num_layers: int,
                  seq_ids: Sequence[int], tok_begin: int, tok_end: int, k_src, v_src,
                  stream=None) -> None:
     """k_src/v_src: device float32 or bfloat16 [num_layers, len(seq_ids), Hkv, n_tok, D]."""
-    import torch
-    if k_src.dtype != v_src.dtype:
-        raise ValueError("k_src and v_src must share a dtype")
-    if k_src.dtype == torch.bfloat16:
-        dt = KVQ_SRC_BF16
-    elif k_src.dtype == torch.float32:
-        dt = KVQ_SRC_F32
-    else:
-        raise ValueError("sources must be float32 or bfloat16")
     ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+    _check_cache(cfg, cache)
+    dt = _check_sources(cfg, k_src, v_src, num_layers, len(ids), max(0, tok_end - tok_begin))
     _check(lib().kvq_quantize(cfg.ref, _dev_ptr(cache, "cache"), layer_begin, num_layers,
                               len(ids), ids.ctypes.data_as(C.POINTER(C.c_int32)),
                               tok_begin, tok_end, _dev_ptr(k_src, "k_src"),
@@ -175,19 +200,12 @@ def kvq_quantize_ragged(cfg: Config, cache, layer_begin: int, num_layers: int,
                         k_src, v_src, stream=None) -> None:
     """Sequence seq_ids[i] stores positions [tok_begin[i], tok_begin[i] + num_tokens);
     k_src/v_src: device float32 or bfloat16 [num_layers, len(seq_ids), Hkv, num_tokens, D]."""
-    import torch
-    if k_src.dtype != v_src.dtype:
-        raise ValueError("k_src and v_src must share a dtype")
-    if k_src.dtype == torch.bfloat16:
-        dt = KVQ_SRC_BF16
-    elif k_src.dtype == torch.float32:
-        dt = KVQ_SRC_F32
-    else:
-        raise ValueError("sources must be float32 or bfloat16")
     ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
     t0 = np.ascontiguousarray(tok_begin, dtype=np.int32)
     if t0.shape != ids.shape:
         raise ValueError("one start position per sequence")
+    _check_cache(cfg, cache)
+    dt = _check_sources(cfg, k_src, v_src, num_layers, len(ids), max(0, num_tokens))
     _check(lib().kvq_quantize_ragged(cfg.ref, _dev_ptr(cache, "cache"), layer_begin, num_layers,
                                      len(ids), ids.ctypes.data_as(C.POINTER(C.c_int32)),
                                      t0.ctypes.data_as(C.POINTER(C.c_int32)), num_tokens,
@@ -209,9 +227,17 @@ def kvq_decode_attention(cfg: Config, cache, layer_begin: int, num_layers: int, 
     """seq_lens: device int32 [batch]; q/out: device bf16 [num_layers, batch, Hq, D].
     workspace: device uint8 tensor of at least workspace_bytes(...) bytes, zero-filled
     before its first use (e.g. torch.zeros); each call leaves it ready for reuse."""
+    import torch
     if workspace is None:
         raise ValueError("workspace tensor required (see workspace_bytes)")
-    n = C.c_size_t(workspace.numel() * workspace.element_size())
+    _check_cache(cfg, cache)
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != cfg.batch:
+        raise ValueError(f"seq_lens must be int32 [{cfg.batch}]")
+    want = (num_layers, cfg.batch, cfg.num_q_heads, cfg.head_dim)
+    for name, t in (("q", q), ("out", out)):
+        if t.dtype != torch.bfloat16 or t.numel() != int(np.prod(want)):
+            raise ValueError(f"{name} must be bfloat16 with {want} elements in that layout")
+    n = C.c_size_t(_nbytes(workspace))
     _check(lib().kvq_decode_attention(cfg.ref, _dev_ptr(cache, "cache"), layer_begin,
                                       num_layers, _dev_ptr(seq_lens, "seq_lens"),
                                       _dev_ptr(q, "q"), _dev_ptr(out, "out"), float(sm_scale),

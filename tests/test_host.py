@@ -92,7 +92,8 @@ def _cfg(**over):
     (dict(head_dim=64, group_size=128), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(k_bits=[3]), kvq.KVQ_ERR_UNSUPPORTED),
     (dict(v_bits=[1]), kvq.KVQ_ERR_UNSUPPORTED),
-    (dict(num_q_heads=6, num_kv_heads=4, k_bits=[4] * 4, v_bits=[4] * 4), kvq.KVQ_ERR_SHAPE),
+    (dict(num_q_heads=6, num_kv_heads=4, k_bits=[4] * 4, v_bits=[4] * 4),
+     kvq.KVQ_ERR_UNSUPPORTED),
     (dict(vis_begin=[20], vis_end=[10]), kvq.KVQ_ERR_SHAPE),
     (dict(vis_end=[300]), kvq.KVQ_ERR_SHAPE),
     (dict(vis_begin=[-1]), kvq.KVQ_ERR_SHAPE),
@@ -237,3 +238,65 @@ def test_decode_validation(L):
                                   None) == kvq.KVQ_ERR_NULL
     assert L.kvq_decode_attention(None, None, 0, 1, None, None, None, 1.0, 0, None,
                                   C.byref(n), None) == kvq.KVQ_ERR_NULL
+
+
+def _headguard_like(num_layers):
+    return kvq.Config(num_layers, 1, 28, 4, 128, 64, [6288], [14], [6287], [4] * 4 * num_layers,
+                      [2] * 4 * num_layers)
+
+
+def test_workspace_size_depends_on_cache_layer_count(L):
+    """The arrival counters are sized by the cache's layer count, so two caches
+    that differ only in it need different workspaces, whatever was planned
+    before in the same process (the plans are cached per call shape)."""
+    code = ("from quantized_decode_attention_quantize_amd import kvq\n"
+            "def h(n): return kvq.Config(n, 1, 28, 4, 128, 64, [6288], [14], [6287], "
+            "[4] * 4 * n, [2] * 4 * n)\n"
+            "print(kvq.workspace_bytes(h(28), 1), kvq.workspace_bytes(h(1), 1))")
+    fresh = subprocess.run(["python", "-c", code], capture_output=True, text=True, check=True,
+                           cwd=ROOT).stdout.split()
+    a1 = kvq.workspace_bytes(_headguard_like(1), 1)
+    a28 = kvq.workspace_bytes(_headguard_like(28), 1)
+    b1 = kvq.workspace_bytes(_headguard_like(1), 1)
+    assert [str(a28), str(a1)] == fresh
+    assert a1 == b1 and a28 > a1
+
+
+def test_binding_rejects_wrong_dtypes_and_sizes(L):
+    """The Python binding checks dtypes and element counts against the config
+    before it hands any pointer to the library (CPU tensors: every check below
+    fires before the device check)."""
+    import torch
+    cfg = _cfg(batch=2, capacity=[64, 40], vis_begin=[8, 0], vis_end=[64, 20])
+    need = kvq.kvq_cache_bytes(cfg)["total_bytes"]
+    cache = torch.zeros(need, dtype=torch.uint8)
+    lens = torch.tensor([64, 40], dtype=torch.int32)
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    out = torch.zeros_like(q)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+
+    def dec(**over):
+        a = dict(cache=cache, seq_lens=lens, q=q, out=out, workspace=ws)
+        a.update(over)
+        kvq.kvq_decode_attention(cfg, a["cache"], 0, 1, a["seq_lens"], a["q"], a["out"], 0.125,
+                                 0, a["workspace"])
+
+    bad = [dict(cache=torch.zeros(need - 1, dtype=torch.uint8)),
+           dict(cache=torch.zeros(need, dtype=torch.int32)),
+           dict(seq_lens=lens.long()), dict(seq_lens=lens[:1]),
+           dict(q=q.float()), dict(q=q[:, :1]), dict(out=out.half()),
+           dict(out=torch.zeros(1, 2, 4, 32, dtype=torch.bfloat16))]
+    for over in bad:
+        with pytest.raises(ValueError):
+            dec(**over)
+    with pytest.raises(ValueError, match="device tensor"):
+        dec()  # everything well-formed but on the host
+    k = torch.zeros(1, 2, 1, 8, 64, dtype=torch.bfloat16)
+    for kk, vv in [(k.float(), k), (k.half(), k.half()), (k[:, :1], k[:, :1]),
+                   (torch.zeros(1, 2, 1, 7, 64, dtype=torch.bfloat16),) * 2]:
+        with pytest.raises(ValueError):
+            kvq.kvq_quantize(cfg, cache, 0, 1, [0, 1], 0, 8, kk, vv)
+        with pytest.raises(ValueError):
+            kvq.kvq_quantize_ragged(cfg, cache, 0, 1, [0, 1], [0, 3], 8, kk, vv)
+    with pytest.raises(ValueError, match="device tensor"):
+        kvq.kvq_quantize(cfg, cache, 0, 1, [0, 1], 0, 8, k, k)

@@ -419,6 +419,133 @@ def test_decode_all_bf16_equals_sdpa(orc):
                            atol=1e-13)
 
 
+# A cache of several sequences and layers whose rows the oracle must fetch
+# by (sequence, position): every sequence has its own visual span (one empty,
+# one covering the whole sequence, one ending at capacity), and every (layer,
+# KV head) its own widths.  The expected output is built without the oracle's
+# layout: text rows and 16-bit rows are the bf16-rounded sources (torch's
+# conversion), coded rows are per-group quantise/dequantise of the source row
+# (orc.quantize_group, pinned above), and attention is textbook SDPA.
+_MS = dict(L=3, B=4, Hq=4, Hkv=2, D=64, g=32, cap=[37, 50, 9, 64], vb=[5, 7, 0, 20],
+           ve=[30, 7, 9, 64])
+
+
+def _ms_sources(seed):
+    rng = np.random.default_rng(seed)
+    m = _MS
+    return {(l, s, h, X): rng.standard_normal((m["cap"][s], m["D"])).astype(np.float32)
+            for l in range(m["L"]) for s in range(m["B"]) for h in range(m["Hkv"])
+            for X in (0, 1)}
+
+
+def _ms_cache(orc, kbits, vbits, rotate=False, seed=21):
+    m = _MS
+    cfg = orc.Config(m["L"], m["B"], m["Hq"], m["Hkv"], m["D"], m["g"], m["cap"], m["vb"],
+                     m["ve"], kbits, vbits, rotate_k=rotate)
+    src = _ms_sources(seed)
+    cache = orc.new_cache(cfg)
+    for (l, s, h, X), rows in src.items():
+        orc.store_rows(cfg, cache, l, s, h, X, 0, m["cap"][s], rows)
+    return cfg, cache, src
+
+
+def _expected_row(orc, x, bits, visual, g, rotate_k):
+    """Reconstruction of one source row without the cache layout."""
+    if not visual or bits == 16:
+        return torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    y = orc.hadamard_rotate(x) if rotate_k else x
+    r = np.concatenate([_dequant(*orc.quantize_group(y[j:j + g], bits))
+                        for j in range(0, y.size, g)])
+    return orc.hadamard_unrotate(r) if rotate_k else r
+
+
+def _ms_expected(orc, src, kbits, vbits, l0, nl, lens, q, scale, rotate=False):
+    m = _MS
+    out = np.zeros((nl, m["B"], m["Hq"], m["D"]))
+    for li in range(nl):
+        l = l0 + li
+        for s in range(m["B"]):
+            vis = [m["vb"][s] <= t < m["ve"][s] for t in range(lens[s])]
+            for i in range(m["Hq"]):
+                kv = i * m["Hkv"] // m["Hq"]
+                kb, vbb = kbits[l * m["Hkv"] + kv], vbits[l * m["Hkv"] + kv]
+                K = np.stack([_expected_row(orc, src[(l, s, kv, 0)][t], kb, vis[t], m["g"],
+                                            rotate) for t in range(lens[s])])
+                V = np.stack([_expected_row(orc, src[(l, s, kv, 1)][t], vbb, vis[t], m["g"],
+                                            False) for t in range(lens[s])])
+                qh = synth.bf16_bits_to_f32(q[li, s, i]).astype(np.float64)
+                out[li, s, i] = _attn_sdpa(qh, K, V, scale)
+    return out
+
+
+def _ms_query(nl, seed=3):
+    m = _MS
+    x = np.random.default_rng(seed).standard_normal((nl, m["B"], m["Hq"], m["D"]))
+    return synth.f32_to_bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("bits", ["bf16", "mixed"])
+def test_decode_all_multiseq_multilayer_addressing(orc, bits):
+    """decode_all over layers [1, 3) of a 3-layer, 4-sequence cache equals
+    attention over rows rebuilt from the sources by position: wrong row bases
+    per sequence, a wrong visual/text plane test at the span ends, or a wrong
+    layer offset each change the output by far more than the tolerance."""
+    m = _MS
+    nlh = m["L"] * m["Hkv"]
+    if bits == "bf16":
+        kbits, vbits = [16] * nlh, [16] * nlh
+    else:
+        kbits, vbits = [4, 2, 8, 16, 2, 4], [2, 4, 16, 8, 4, 2]
+    cfg, cache, src = _ms_cache(orc, kbits, vbits)
+    lens = np.array([37, 41, 9, 60], dtype=np.int32)
+    q = _ms_query(2)
+    got = orc.decode_all(cfg, cache, 1, 2, lens, q, 0.125)
+    ref = _ms_expected(orc, src, kbits, vbits, 1, 2, lens, q, 0.125)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+    # the same heads decoded one by one agree with the batched call
+    for li, s, i in [(0, 0, 3), (1, 3, 0), (1, 1, 2)]:
+        one, _ = orc.decode_one(cfg, cache, 1 + li, s, i, int(lens[s]), q[li, s, i], 0.125)
+        assert np.array_equal(one, got[li, s, i])
+
+
+def test_decode_all_multiseq_rotated(orc):
+    """The same multi-sequence check on a cache with rotated K codes: coded K
+    rows come back as the un-rotated reconstruction, every other row as is."""
+    m = _MS
+    kbits, vbits = [4, 2, 8, 16, 2, 4], [2, 4, 16, 8, 4, 2]
+    cfg, cache, src = _ms_cache(orc, kbits, vbits, rotate=True, seed=8)
+    lens = np.array(m["cap"], dtype=np.int32)
+    q = _ms_query(3, seed=9)
+    scale = float(np.float32(0.2))  # the call takes the scale as binary32
+    got = orc.decode_all(cfg, cache, 0, 3, lens, q, scale)
+    ref = _ms_expected(orc, src, kbits, vbits, 0, 3, lens, q, scale, rotate=True)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_one_uniform_keys_any_query(orc):
+    """Every K row of the sequence (text and visual alike) reconstructs to the
+    same vector, so every score is equal and the output is the mean of the V
+    rows for any query.  The K row lies on a lossless INT4 grid (each group
+    spans exactly 0..3.75 in steps of 0.25), so its codes and its bf16 copy
+    are both exact."""
+    D, g, T = 64, 32, 40
+    rng = np.random.default_rng(12)
+    k = (0.25 * rng.integers(0, 16, size=D)).astype(np.float32)
+    k[0], k[1], k[32], k[33] = 0.0, 3.75, 0.0, 3.75
+    cfg = orc.Config(1, 1, 4, 1, D, g, [T], [6], [31], [4], [2])
+    cache = orc.new_cache(cfg)
+    orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, T, np.tile(k, (T, 1)))
+    orc.store_rows(cfg, cache, 0, 0, 0, 1, 0, T, rng.standard_normal((T, D)).astype(np.float32))
+    for t in (0, 6, 30, 31, 39):
+        assert np.array_equal(orc.load_row(cfg, cache, 0, 0, 0, 0, t), k.astype(np.float64))
+    vhat = np.stack([orc.load_row(cfg, cache, 0, 0, 0, 1, t) for t in range(T)])
+    for i in range(4):
+        q = synth.f32_to_bf16_bits((3.0 * rng.standard_normal(D)).astype(np.float32))
+        for n in (T, 31, 7):
+            out, _ = orc.decode_one(cfg, cache, 0, 0, i, n, q, 0.5)
+            assert np.allclose(out, vhat[:n].mean(0), atol=1e-13)
+
+
 def test_kl_properties(orc):
     """KL(P_ref || P_q) >= 0; = 0 when nothing is quantised; = 0 when only V is
     quantised (scores depend on K alone)."""
