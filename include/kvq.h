@@ -247,6 +247,33 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const void *cache,
                                 float sm_scale, int32_t chunk_tokens, void *workspace,
                                 size_t *workspace_bytes, void *stream);
 
+/* kvq_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics and kernels as
+ * kvq_decode_attention minus workspace/workspace_bytes: the split partials
+ * and the merge's arrival counters live in a fixed 16 MiB device array inside
+ * the library, one per device, held until the process ends.  The call itself
+ * allocates nothing.  The first call on a device looks the array up and
+ * clears its counter area with a kernel on `stream`.
+ *
+ * Limits: the cache's num_layers * batch * num_kv_heads must be <= 16384, and
+ * the call's partials must fit the remaining 16 MiB - 64 KiB (the default
+ * split of every shape this header supports at up to 64 sequences of 16K
+ * tokens fits; kvq_decode_attention's size query on the same call reports
+ * what it needs, minus the counter area).  A call beyond either limit returns
+ * KVQ_ERR_WORKSPACE and launches nothing.
+ *
+ * All calls on one device share the array: calls that may overlap in time on
+ * one device (different streams without ordering between them) race and
+ * give wrong results.  Calls ordered on one stream, or otherwise serialised,
+ * are safe, whatever their shapes.
+ * Errors: as kvq_decode_attention, with KVQ_ERR_WORKSPACE for the limits
+ * above and KVQ_ERR_HIP if the array cannot be found on the current device. */
+kvq_status kvq_decode_attention_noalloc(const kvq_config *cfg, const void *cache,
+                                        int32_t layer_begin, int32_t num_layers,
+                                        const int32_t *seq_lens, const void *q, void *out,
+                                        float sm_scale, int32_t chunk_tokens, void *stream);
+
 /* Static description of a status code (never NULL; unknown codes get a
  * generic string).  A utility of the ABI, not a step of the method. */
 const char *kvq_status_string(kvq_status s);

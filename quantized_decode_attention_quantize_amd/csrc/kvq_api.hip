@@ -551,6 +551,111 @@ extern "C" kvq_status kvq_quantize_ragged(const kvq_config* cfg, void* cache,
   }
 }
 
+// Workspace regions of one decode call: the merge's arrival counters, the
+// partial rows, their (m, l) pairs and the per-entry partial counts.
+struct WsRegions {
+  uint8_t* arrive;
+  uint8_t* rest;  // partials, (m, l) pairs and counts follow here, as planned
+};
+
+// Checks shared by both decode entry points; on success *plan holds the call's
+// split plan and *use_mfma the kernel family.
+static kvq_status decode_prologue(const kvq_config* cfg, int32_t layer_begin, int32_t num_layers,
+                           int32_t chunk_tokens, std::shared_ptr<const DecodePlan>* plan,
+                           bool* use_mfma) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (num_layers < 1) return KVQ_ERR_SHAPE;
+  if (layer_begin < 0 || layer_begin > cfg->num_layers - num_layers) return KVQ_ERR_RANGE;
+  if (chunk_tokens < 0 || chunk_tokens % 32) return KVQ_ERR_SHAPE;
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
+  *use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
+  // the general kernel has no rotated-query path
+  if (cfg->rotate_k && !*use_mfma) return KVQ_ERR_UNSUPPORTED;
+  *plan = cached_plan(cfg, layer_begin, num_layers, chunk_tokens, *use_mfma);
+  return KVQ_OK;
+}
+
+// Launches of one validated decode call over workspace regions `wr`.
+static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_t layer_begin,
+                         int32_t num_layers, const int32_t* seq_lens, const void* q, void* out,
+                         float sm_scale, const DecodePlan& plan, bool use_mfma, WsRegions wr,
+                         void* stream) {
+  if (!cache || !seq_lens || !q || !out) return KVQ_ERR_NULL;
+  if (!aligned(cache, 256) || !aligned(q, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
+    return KVQ_ERR_ALIGN;
+  Layout lay(cfg);
+  if (lay.info.total_bytes / 256 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
+
+  const int Hkv = cfg->num_kv_heads;
+  const int G = cfg->num_q_heads / Hkv;
+  // unit counts of every launch fit the kernels' 32-bit block arithmetic
+  for (const LaunchPlan& L : plan.launches) {
+    int64_t xs = 0, ms = 0;
+    for (int v : L.nx) xs += v;
+    for (int v : L.mult) ms += v;
+    if (xs * ms >= (int64_t(1) << 31) || ms > 0xFFFF) return KVQ_ERR_UNSUPPORTED;
+  }
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  for (const LaunchPlan& L : plan.launches) {
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.cache = static_cast<const uint8_t*>(cache);
+    a.seq_lens = seq_lens;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.ws_arrive = reinterpret_cast<int32_t*>(wr.arrive);
+    a.ws_o = reinterpret_cast<float*>(wr.rest);
+    a.ws_ml = reinterpret_cast<float*>(wr.rest + plan.o_bytes);
+    a.ws_cnt = reinterpret_cast<int32_t*>(wr.rest + plan.o_bytes + plan.ml_bytes);
+    a.qscale = sm_scale * 1.4426950408889634f;
+    a.Rvis = lay.Rvis;
+    a.D = lay.D;
+    a.g = lay.g;
+    a.G = G;
+    a.Hkv = Hkv;
+    a.Hq = cfg->num_q_heads;
+    a.B = cfg->batch;
+    a.chunk = plan.chunk;
+    a.rotate_k = cfg->rotate_k != 0;
+    a.max_chunks = plan.max_chunks;
+    a.seq_off = L.s0;
+    a.n_seq = L.ns;
+    for (int i = 0; i < L.ns; ++i) {
+      const int s = L.s0 + i;
+      a.vb[i] = cfg->vis_begin[s];
+      a.ve[i] = cfg->vis_end[s];
+      a.cap[i] = cfg->capacity[s];
+      a.vrow0[i] = int32_t(lay.vrow0[s]);
+      a.trow0[i] = int32_t(lay.trow0[s]);
+      a.nx[i] = L.nx[i];
+      a.nxcum[i + 1] = a.nxcum[i] + L.nx[i];
+    }
+    a.n_lh = int(L.glh.size());
+    for (int i = 0; i < a.n_lh; ++i) {
+      const int glh = L.glh[i];  // layer-local * Hkv + head
+      const int l = layer_begin + glh / Hkv, h = glh % Hkv;
+      for (int X = 0; X < 2; ++X) {
+        a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * Hkv + h) * 2 + X] / 256);
+        a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
+      }
+      a.lh_glob[i] = uint16_t(glh);
+      a.mult[i] = uint16_t(L.mult[i]);
+      a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
+    }
+    const hipError_t e = use_mfma ? launch_decode_mfma(a, L.key / 32, L.key % 32, hs)
+                                  : launch_decode_simple(a, L.ns, hs);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+    // the general kernel leaves split partials for a separate merge; the
+    // matrix-core kernel merges them itself
+    if (L.merge_after && plan.max_chunks > 1 &&
+        launch_decode_merge(a, num_layers, L.ns, hs) != hipSuccess)
+      return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}
+
 extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* cache,
                                            int32_t layer_begin, int32_t num_layers,
                                            const int32_t* seq_lens, const void* q, void* out,
@@ -558,98 +663,88 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
                                            void* workspace, size_t* workspace_bytes,
                                            void* stream) {
   try {
-    kvq_status st = check_config(cfg);
+    std::shared_ptr<const DecodePlan> plan;
+    bool use_mfma = false;
+    kvq_status st = decode_prologue(cfg, layer_begin, num_layers, chunk_tokens, &plan, &use_mfma);
     if (st != KVQ_OK) return st;
     if (!workspace_bytes) return KVQ_ERR_NULL;
-    if (num_layers < 1) return KVQ_ERR_SHAPE;
-    if (layer_begin < 0 || layer_begin > cfg->num_layers - num_layers) return KVQ_ERR_RANGE;
-    if (chunk_tokens < 0 || chunk_tokens % 32) return KVQ_ERR_SHAPE;
-    const int G = cfg->num_q_heads / cfg->num_kv_heads;
-    if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
-    const bool use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
-    // the general kernel has no rotated-query path
-    if (cfg->rotate_k && !use_mfma) return KVQ_ERR_UNSUPPORTED;
-    const std::shared_ptr<const DecodePlan> plan_ptr =
-        cached_plan(cfg, layer_begin, num_layers, chunk_tokens, use_mfma);
-    const DecodePlan& plan = *plan_ptr;
     if (!workspace) {
-      *workspace_bytes = plan.total;
+      *workspace_bytes = plan->total;
       return KVQ_OK;
     }
     if (!cache || !seq_lens || !q || !out) return KVQ_ERR_NULL;
-    if (*workspace_bytes < plan.total) return KVQ_ERR_WORKSPACE;
-    if (!aligned(cache, 256) || !aligned(workspace, 256) || !aligned(q, 16) || !aligned(out, 16) ||
-        !aligned(seq_lens, 4))
-      return KVQ_ERR_ALIGN;
-    Layout lay(cfg);
-    if (lay.info.total_bytes / 256 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
-
-    const int Hkv = cfg->num_kv_heads;
-    // unit counts of every launch fit the kernels' 32-bit block arithmetic
-    for (const LaunchPlan& L : plan.launches) {
-      int64_t xs = 0, ms = 0;
-      for (int v : L.nx) xs += v;
-      for (int v : L.mult) ms += v;
-      if (xs * ms >= (int64_t(1) << 31) || ms > 0xFFFF) return KVQ_ERR_UNSUPPORTED;
-    }
+    if (*workspace_bytes < plan->total) return KVQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KVQ_ERR_ALIGN;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    for (const LaunchPlan& L : plan.launches) {
-      DecodeArgs a;
-      std::memset(&a, 0, sizeof(a));
-      a.cache = static_cast<const uint8_t*>(cache);
-      a.seq_lens = seq_lens;
-      a.q = static_cast<const uint16_t*>(q);
-      a.out = static_cast<uint16_t*>(out);
-      a.ws_arrive = reinterpret_cast<int32_t*>(ws);
-      a.ws_o = reinterpret_cast<float*>(ws + plan.arrive_bytes);
-      a.ws_ml = reinterpret_cast<float*>(ws + plan.arrive_bytes + plan.o_bytes);
-      a.ws_cnt = reinterpret_cast<int32_t*>(ws + plan.arrive_bytes + plan.o_bytes + plan.ml_bytes);
-      a.qscale = sm_scale * 1.4426950408889634f;
-      a.Rvis = lay.Rvis;
-      a.D = lay.D;
-      a.g = lay.g;
-      a.G = G;
-      a.Hkv = Hkv;
-      a.Hq = cfg->num_q_heads;
-      a.B = cfg->batch;
-      a.chunk = plan.chunk;
-      a.rotate_k = cfg->rotate_k != 0;
-      a.max_chunks = plan.max_chunks;
-      a.seq_off = L.s0;
-      a.n_seq = L.ns;
-      for (int i = 0; i < L.ns; ++i) {
-        const int s = L.s0 + i;
-        a.vb[i] = cfg->vis_begin[s];
-        a.ve[i] = cfg->vis_end[s];
-        a.cap[i] = cfg->capacity[s];
-        a.vrow0[i] = int32_t(lay.vrow0[s]);
-        a.trow0[i] = int32_t(lay.trow0[s]);
-        a.nx[i] = L.nx[i];
-        a.nxcum[i + 1] = a.nxcum[i] + L.nx[i];
-      }
-      a.n_lh = int(L.glh.size());
-      for (int i = 0; i < a.n_lh; ++i) {
-        const int glh = L.glh[i];  // layer-local * Hkv + head
-        const int l = layer_begin + glh / Hkv, h = glh % Hkv;
-        for (int X = 0; X < 2; ++X) {
-          a.base256[i][X] = uint32_t(lay.vis_off[(size_t(l) * Hkv + h) * 2 + X] / 256);
-          a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
-        }
-        a.lh_glob[i] = uint16_t(glh);
-        a.mult[i] = uint16_t(L.mult[i]);
-        a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
-      }
-      const hipError_t e = use_mfma ? launch_decode_mfma(a, L.key / 32, L.key % 32, hs)
-                                    : launch_decode_simple(a, L.ns, hs);
-      if (e != hipSuccess) return KVQ_ERR_HIP;
-      // the general kernel leaves split partials for a separate merge; the
-      // matrix-core kernel merges them itself
-      if (L.merge_after && plan.max_chunks > 1 &&
-          launch_decode_merge(a, num_layers, L.ns, hs) != hipSuccess)
-        return KVQ_ERR_HIP;
-    }
-    return KVQ_OK;
+    return decode_launch(cfg, cache, layer_begin, num_layers, seq_lens, q, out, sm_scale, *plan,
+                         use_mfma, WsRegions{ws, ws + plan->arrive_bytes}, stream);
+  } catch (...) {
+    return KVQ_ERR_INTERNAL;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace.  The split partials and arrival counters
+// live in `scratch`, one copy per device (each GPU the library runs on holds
+// it until the process ends).  Its first kScratchCounterBytes hold the arrival
+// counters of every cache shape (indexed by (layer, seq, KV head), at most
+// kScratchCounterBytes / 4 of them); the partials follow, so no call's
+// partials ever land on another shape's counters.  Every call leaves the
+// counters it used at zero, so the counter area stays zero between calls.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchCounterBytes = size_t(64) << 10;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static __global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = int(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of this device's `scratch` (the array's name is only a
+// host-side stand-in).  Looked up once per device, with that device current;
+// the first call on a device also clears the counter area with a kernel on
+// the caller's stream (a kernel, not a memset, so a graph may capture it).
+static kvq_status scratch_for_device(hipStream_t stream, uint8_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint8_t* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_HIP;
+    constexpr int n = int(kScratchCounterBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), n);
+    if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+    ptrs[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = ptrs[dev];
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const void* cache,
+                                                   int32_t layer_begin, int32_t num_layers,
+                                                   const int32_t* seq_lens, const void* q,
+                                                   void* out, float sm_scale,
+                                                   int32_t chunk_tokens, void* stream) {
+  try {
+    std::shared_ptr<const DecodePlan> plan;
+    bool use_mfma = false;
+    kvq_status st = decode_prologue(cfg, layer_begin, num_layers, chunk_tokens, &plan, &use_mfma);
+    if (st != KVQ_OK) return st;
+    if (!cache || !seq_lens || !q || !out) return KVQ_ERR_NULL;
+    // counters of this cache shape, then the call's partials, must fit
+    const int64_t counters = int64_t(cfg->num_layers) * cfg->batch * cfg->num_kv_heads;
+    if (counters * 4 > int64_t(kScratchCounterBytes) ||
+        plan->total - plan->arrive_bytes > kScratchBytes - kScratchCounterBytes)
+      return KVQ_ERR_WORKSPACE;
+    uint8_t* base = nullptr;
+    st = scratch_for_device(static_cast<hipStream_t>(stream), &base);
+    if (st != KVQ_OK) return st;
+    return decode_launch(cfg, cache, layer_begin, num_layers, seq_lens, q, out, sm_scale, *plan,
+                         use_mfma, WsRegions{base, base + kScratchCounterBytes}, stream);
   } catch (...) {
     return KVQ_ERR_INTERNAL;
   }

@@ -29,7 +29,7 @@ KVQ_SRC_F32 = 0
 KVQ_SRC_BF16 = 1
 
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize", "kvq_quantize_ragged", "kvq_decode_attention",
-           "kvq_status_string")
+           "kvq_decode_attention_noalloc", "kvq_status_string")
 
 
 class KvqError(RuntimeError):
@@ -78,6 +78,9 @@ def lib(path: str = LIB_PATH):
         L.kvq_decode_attention.restype = C.c_int
         L.kvq_decode_attention.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, P, P, P,
                                            C.c_float, C.c_int32, P, C.POINTER(C.c_size_t), P]
+        L.kvq_decode_attention_noalloc.restype = C.c_int
+        L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, P,
+                                                   P, P, C.c_float, C.c_int32, P]
         L.kvq_status_string.restype = C.c_char_p
         L.kvq_status_string.argtypes = [C.c_int]
         _lib = L
@@ -169,6 +172,17 @@ def _check_sources(cfg: "Config", k_src, v_src, num_layers: int, num_seqs: int,
     return dt
 
 
+def _check_decode_args(cfg: "Config", cache, num_layers: int, seq_lens, q, out) -> None:
+    import torch
+    _check_cache(cfg, cache)
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != cfg.batch:
+        raise ValueError(f"seq_lens must be int32 [{cfg.batch}]")
+    want = (num_layers, cfg.batch, cfg.num_q_heads, cfg.head_dim)
+    for name, t in (("q", q), ("out", out)):
+        if t.dtype != torch.bfloat16 or t.numel() != int(np.prod(want)):
+            raise ValueError(f"{name} must be bfloat16 with {want} elements in that layout")
+
+
 def _stream(stream) -> Optional[C.c_void_p]:
     if stream is None:
         import torch
@@ -227,19 +241,26 @@ def kvq_decode_attention(cfg: Config, cache, layer_begin: int, num_layers: int, 
     """seq_lens: device int32 [batch]; q/out: device bf16 [num_layers, batch, Hq, D].
     workspace: device uint8 tensor of at least workspace_bytes(...) bytes, zero-filled
     before its first use (e.g. torch.zeros); each call leaves it ready for reuse."""
-    import torch
     if workspace is None:
         raise ValueError("workspace tensor required (see workspace_bytes)")
-    _check_cache(cfg, cache)
-    if seq_lens.dtype != torch.int32 or seq_lens.numel() != cfg.batch:
-        raise ValueError(f"seq_lens must be int32 [{cfg.batch}]")
-    want = (num_layers, cfg.batch, cfg.num_q_heads, cfg.head_dim)
-    for name, t in (("q", q), ("out", out)):
-        if t.dtype != torch.bfloat16 or t.numel() != int(np.prod(want)):
-            raise ValueError(f"{name} must be bfloat16 with {want} elements in that layout")
+    _check_decode_args(cfg, cache, num_layers, seq_lens, q, out)
     n = C.c_size_t(_nbytes(workspace))
     _check(lib().kvq_decode_attention(cfg.ref, _dev_ptr(cache, "cache"), layer_begin,
                                       num_layers, _dev_ptr(seq_lens, "seq_lens"),
                                       _dev_ptr(q, "q"), _dev_ptr(out, "out"), float(sm_scale),
                                       chunk_tokens, _dev_ptr(workspace, "workspace"),
                                       C.byref(n), _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(cfg: Config, cache, layer_begin: int, num_layers: int,
+                                 seq_lens, q, out, sm_scale: float, chunk_tokens: int = 0,
+                                 stream=None) -> None:
+    """kvq_decode_attention with the library's own per-device scratch instead of a
+    workspace (for callers that cannot allocate).  Calls that overlap in time on
+    one device race; calls ordered on one stream are safe."""
+    _check_decode_args(cfg, cache, num_layers, seq_lens, q, out)
+    _check(lib().kvq_decode_attention_noalloc(cfg.ref, _dev_ptr(cache, "cache"), layer_begin,
+                                              num_layers, _dev_ptr(seq_lens, "seq_lens"),
+                                              _dev_ptr(q, "q"), _dev_ptr(out, "out"),
+                                              float(sm_scale), chunk_tokens, _stream(stream)),
+           "kvq_decode_attention_noalloc")
