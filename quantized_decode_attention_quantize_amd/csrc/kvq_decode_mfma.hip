@@ -123,28 +123,25 @@ struct Fmt {
   static constexpr int kVBytes = kRowBytes / 16;    // per lane column
 };
 
-// Slot map of the q.k A operand: k-step s, lane quarter jq, slot e (0..7) ->
-// head-dim index d and the power-of-two weight w of the stored code bits
-// (operand value = code * w * 2^-24).  Must mirror k_operand() below.
+// Slot map of the q.k A operand: k-step s, slot e (0..7) -> the head-dim
+// offset within the lane's quarter (d - jq * D / 4) and the power-of-two
+// weight w of the stored code bits (operand value = code * w * 2^-24).  Must
+// mirror k_operand() below.  Every format's slots of k-steps 2i and 2i + 1
+// cover quarter offsets [16 i, 16 i + 16) exactly once.
 template <int D, int B>
-__device__ inline void kslot(int s, int jq, int e, int& d, float& w) {
-  const int c0 = jq * (D / 4);
+__device__ constexpr int kslot_off(int s, int e) {
   const int kp = e >> 1, hf = e & 1;
-  if (B == 16) {
-    d = c0 + 8 * s + e;
-    w = 1.0f;
-  } else if (B == 8) {
-    const int di = 2 * s + (kp >> 1);
-    d = c0 + 4 * di + (kp & 1) + 2 * hf;
-    w = 1.0f;
-  } else if (B == 4) {
-    d = c0 + 8 * s + kp + 4 * hf;
-    w = (kp & 1) ? 16.0f : 1.0f;
-  } else {  // B == 2
-    const int odd = s & 1;
-    d = c0 + 16 * (s >> 1) + (odd ? 4 : 0) + kp + 8 * hf;
-    w = (!odd || kp) ? float(1 << (2 * kp)) : 256.0f;
-  }
+  if (B == 16) return 8 * s + e;
+  if (B == 8) return 4 * (2 * s + (kp >> 1)) + (kp & 1) + 2 * hf;
+  if (B == 4) return 8 * s + kp + 4 * hf;
+  return 16 * (s >> 1) + ((s & 1) ? 4 : 0) + kp + 8 * hf;
+}
+template <int D, int B>
+__device__ constexpr float kslot_w(int s, int e) {
+  const int kp = e >> 1;
+  if (B == 16 || B == 8) return 1.0f;
+  if (B == 4) return (kp & 1) ? 16.0f : 1.0f;
+  return ((s & 1) == 0 || kp) ? float(1 << (2 * kp)) : 256.0f;
 }
 
 // A operand (4 dwords) of k-step s from this lane's raw K dwords.
@@ -264,10 +261,8 @@ struct Ctx {
   const uint8_t* vvis;
   const uint8_t* vmeta;
   const uint8_t* vtxt;
-  uint16_t* q_lds;         // [G][D] bf16 bits of this wave's queries
-  u32x4 qreg[4];           // the same, as loaded: 16 bytes per lane per entry (the
-                           // first D / (32 NG) used), written to q_lds once the
-                           // segment's first loads are out
+  u32x4* qq;               // this lane's D/64 16-byte pieces in LDS: quarter jq of
+                           // the query of column n's head (head 0 for dead columns)
   uint8_t* stage;          // this wave's LDS stage (BigLds::kStage bytes)
   float qscale;
   int G;
@@ -275,62 +270,62 @@ struct Ctx {
   int lane, n, jq;         // lane, column (l % 16), quarter (l / 16)
 };
 
-// The wave's G query rows in q_lds (bf16) -> the rotated queries as f16, in
-// place, for K rows stored rotated (include/kvq.h; gist.science 2604.02570,
-// section 2-C): the same butterflies as the stored rows, then
-// 2^-floor(log2(D)/2), so the product with a rotated K row is q.k.  A lane
-// holds 16 consecutive elements of one row (D/16 lanes per row, all rows of a
-// pass side by side): strides 1..8 run inside the lane, 16..D/2 across lanes.
-// Each lane reads and writes only its own elements.
+// The lane's quarter of its head's query (bf16 pairs) -> fp32 values.
 template <int D>
-__device__ inline void rotate_q(const Ctx& c) {
-  constexpr int EL = 16;           // elements per lane
-  constexpr int LPR = D / EL;      // lanes per row
-  constexpr int RPP = 64 / LPR;    // rows per pass
-  const int part = c.lane % LPR;
-  for (int h0 = 0; h0 < c.G; h0 += RPP) {
-    const int h = h0 + c.lane / LPR;
-    const bool live = h < c.G;
-    uint16_t* row = c.q_lds + (live ? h : 0) * D + part * EL;
-    float v[EL];
+__device__ inline void unpack_quarter(const Ctx& c, float (&v)[D / 4]) {
 #pragma unroll
-    for (int i = 0; i < EL; ++i) v[i] = bf16f(row[i]);
+  for (int k = 0; k < D / 32; ++k) {
+    const u32x4 w = c.qq[k];
 #pragma unroll
-    for (int s = 1; s < EL; s <<= 1)
-#pragma unroll
-      for (int i = 0; i < EL; ++i)
-        if (!(i & s)) {
-          const float lo = v[i], hi = v[i + s];
-          v[i] = lo + hi;
-          v[i + s] = lo - hi;
-        }
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-      const bool upper = (part & m) != 0;
-#pragma unroll
-      for (int i = 0; i < EL; ++i) {
-        const float other = __shfl_xor(v[i], m);
-        v[i] = upper ? other - v[i] : v[i] + other;
-      }
-    }
-    if (live) {
-#pragma unroll
-      for (int i = 0; i < EL; ++i)
-        row[i] = __builtin_bit_cast(uint16_t, _Float16(v[i] * 0.125f));  // 2^-floor(log2(D)/2)
+    for (int i = 0; i < 4; ++i) {
+      v[8 * k + 2 * i] = bf16f(w[i] & 0xFFFFu);
+      v[8 * k + 2 * i + 1] = bf16f(w[i] >> 16);
     }
   }
+}
+
+// The lane's quarter of the query -> the same quarter of the rotated query,
+// for K rows stored rotated (include/kvq.h; gist.science 2604.02570, section
+// 2-C): the butterflies of the stored rows, then 2^-floor(log2(D)/2), so the
+// product with a rotated K row is q.k.  Strides below D/4 run inside the
+// lane; strides D/4 and D/2 pair quarter jq with jq ^ 1 and jq ^ 2, which sit
+// 16 and 32 lanes away (lane = 16 jq + column).
+template <int D>
+__device__ inline void rotate_quarter(const Ctx& c, float (&v)[D / 4]) {
+  constexpr int Q = D / 4;
+#pragma unroll
+  for (int st = 1; st < Q; st <<= 1)
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+      if (!(i & st)) {
+        const float lo = v[i], hi = v[i + st];
+        v[i] = lo + hi;
+        v[i + st] = lo - hi;
+      }
+#pragma unroll
+  for (int m = 1; m <= 2; m <<= 1) {
+    const bool upper = (c.jq & m) != 0;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const float other = __shfl_xor(v[i], 16 * m);
+      v[i] = upper ? other - v[i] : v[i] + other;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Q; ++i) v[i] *= 0.125f;  // 2^-floor(log2(D)/2), D in {64, 128}
 }
 
 // Build Q' for k format KB: per k-step, 8 slots of this lane's column.
 // Returns the sum of q over the column's (head, group), times 2^-24 (the unit
 // of the code products): each lane's slots cover its quarter of the head dim
-// exactly once, so a sum over the four quarters completes it.  f16q: q_lds
-// holds f16 (rotated) queries instead of bf16.
+// exactly once, so a sum over the four quarters completes it.  qv: the lane's
+// quarter of the (possibly rotated) query.
 template <int D, int NG, int KB>
-__device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32], bool f16q) {
+__device__ inline float build_q(const Ctx& c, const float (&qv)[D / 4], u32x4 (&qop)[D / 32]) {
   constexpr int g = D / NG;
-  const int h = c.n / NG, gj = c.n % NG;
+  const int gj = c.n % NG;
   const bool live = c.n < c.G * NG;
+  const int c0 = c.jq * (D / 4);
   float qs = 0.0f;
 #pragma unroll
   for (int s = 0; s < D / 32; ++s) {
@@ -339,14 +334,12 @@ __device__ inline float build_q(const Ctx& c, u32x4 (&qop)[D / 32], bool f16q) {
       float v2[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        int d;
-        float w;
-        kslot<D, KB>(s, c.jq, 2 * e2 + hf, d, w);
-        const uint16_t qb = c.q_lds[(live ? h : 0) * D + d];
-        const float qv = f16q ? f16lo(qb) : bf16f(qb);
-        const bool in = live && d / g == gj;
-        qs += in ? qv : 0.0f;
-        v2[hf] = in ? qv * (1.0f / w) : 0.0f;  // w: power of two
+        const int off = kslot_off<D, KB>(s, 2 * e2 + hf);
+        const float w = kslot_w<D, KB>(s, 2 * e2 + hf);
+        const float q = qv[off];
+        const bool in = live && (c0 + off) / g == gj;
+        qs += in ? q : 0.0f;
+        v2[hf] = in ? q * (1.0f / w) : 0.0f;  // w: power of two
       }
       qop[s][e2] = KB == 16 ? pack_bf16(v2[0], v2[1]) : pack_f16(v2[0], v2[1]);
     }
@@ -624,19 +617,52 @@ struct SegPlanes {
   Rsrc k, km, v, vm;
 };
 
-// Lane piece of tile rows [0, 32) of step `step` (wave-uniform): row l/2,
-// half l%2 of every plane's tile.  Only the first `rows` (1..32) rows exist;
-// lanes of the others re-read the step's last row.
+// Lane l's share of a 32-row tile of row size R (P = R / 2 bytes per lane).
+// A 32-byte lane piece is taken as two 16-byte chunks, chunk i at tile
+// offset (64 i + l) * 16, so each load instruction covers 1 KB of
+// consecutive bytes (0.6 us off the 28-layer HeadGuard step against a
+// 32-byte lane stride); other pieces are bytes [l P, (l + 1) P) (for 64-byte
+// pieces, INT8 K at D = 128, the chunked form costs registers the kernel does
+// not have).  Only the first `rows` (1..32) rows exist: a chunk in a later
+// row re-reads the same columns of the last row.  The chunk offsets without
+// that clamp say where tile_put stores the data.
+template <int R, int P>
+__device__ inline void tile_load(Rsrc r, uint32_t soff, int rows, int lane, uint32_t* out) {
+  if constexpr (P == 32) {
+#pragma unroll
+    for (int i = 0; i < P / 16; ++i) {
+      const uint32_t off = uint32_t(i * 64 + lane) * 16u;
+      const uint32_t row = min(off / R, uint32_t(rows - 1)), col = off % R;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, row * R + col, soff, 0);
+      out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
+    }
+  } else {
+    const uint32_t row = min(uint32_t(lane >> 1), uint32_t(rows - 1)), half = uint32_t(lane & 1);
+    buf_load<P>(r, row * R + half * P, soff, out);
+  }
+}
+template <int P>
+__device__ inline void tile_put(uint8_t* lds, int lane, const uint32_t* in) {
+  if constexpr (P == 32) {
+#pragma unroll
+    for (int i = 0; i < P / 16; ++i)
+      reinterpret_cast<uint4*>(lds)[i * 64 + lane] =
+          make_uint4(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
+  } else {
+    store_bytes<P>(lds + lane * P, in);
+  }
+}
+
+// Lane share of every plane's tile of step `step` (wave-uniform).
 template <int D, int NG, int KB, int VB>
 __device__ inline void stage_load(const SegPlanes& pl, int step, int rows, int lane,
                                   Stage<D, NG, KB, VB>& st) {
   using S = Stage<D, NG, KB, VB>;
-  const uint32_t row = min(uint32_t(lane >> 1), uint32_t(rows - 1)), half = uint32_t(lane & 1);
   const uint32_t r0 = uint32_t(step) * 32u;
-  buf_load<S::KP>(pl.k, row * S::KR + half * S::KP, r0 * S::KR, st.k);
-  buf_load<S::MP>(pl.km, row * S::MR + half * S::MP, r0 * S::MR, st.km);
-  buf_load<S::VP>(pl.v, row * S::VR + half * S::VP, r0 * S::VR, st.v);
-  buf_load<S::MP>(pl.vm, row * S::MR + half * S::MP, r0 * S::MR, st.vm);
+  tile_load<S::KR, S::KP>(pl.k, r0 * S::KR, rows, lane, st.k);
+  tile_load<S::MR, S::MP>(pl.km, r0 * S::MR, rows, lane, st.km);
+  tile_load<S::VR, S::VP>(pl.v, r0 * S::VR, rows, lane, st.v);
+  tile_load<S::MR, S::MP>(pl.vm, r0 * S::MR, rows, lane, st.vm);
 }
 
 // Lanes exchange data through the stage, so the compiler must not move one
@@ -647,10 +673,10 @@ template <int D, int NG, int KB, int VB>
 __device__ inline void stage_put(uint8_t* lds, int lane, const Stage<D, NG, KB, VB>& st) {
   using S = Stage<D, NG, KB, VB>;
   __builtin_amdgcn_wave_barrier();
-  store_bytes<S::KP>(lds + lane * S::KP, st.k);
-  store_bytes<S::MP>(lds + S::kOffKM + lane * S::MP, st.km);
-  store_bytes<S::VP>(lds + S::kOffV + lane * S::VP, st.v);
-  store_bytes<S::MP>(lds + S::kOffVM + lane * S::MP, st.vm);
+  tile_put<S::KP>(lds, lane, st.k);
+  tile_put<S::MP>(lds + S::kOffKM, lane, st.km);
+  tile_put<S::VP>(lds + S::kOffV, lane, st.v);
+  tile_put<S::MP>(lds + S::kOffVM, lane, st.vm);
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -703,7 +729,8 @@ __device__ inline int claim_step(const Claim& cl, int lane, int base) {
 // otherwise all of it.
 template <int D, int NG, int KB, int VB>
 __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int64_t row0,
-                            bool visual, const Claim& cl = Claim{nullptr, 0, 1}) {
+                            bool visual, const Claim& cl, const u32x4 (&qreg)[D / 32],
+                            bool& q_pending) {
   constexpr int NB = D / 16;
   constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
   const uint8_t* kp = (visual ? c.kvis : c.ktxt) + row0 * KR;
@@ -737,24 +764,51 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
     }
   }
 
-  // the query rows reach LDS only now, so their load latency overlaps the
-  // first K/V loads (the same wave reads them back: no barrier needed)
-#pragma unroll
-  for (int k = 0; k < D / (32 * NG); ++k) {
-    const int i = c.lane + 64 * k;
-    if (i < c.G * D / 8) reinterpret_cast<u32x4*>(c.q_lds)[i] = c.qreg[k];
+  // bf16 rows load straight into operands: the first step goes out now
+  const uint32_t vsel_mem = v_pair_selector<D, VB>(0);
+  Offs<D, NG, KB, VB> of;
+  of.full(c);
+  Step<D, KB, VB> sa;
+  auto load_direct = [&](int st) {
+    const int64_t o = int64_t(st) * 32;
+    const int rl = rows_in(st);
+    if (rl == 32) {
+      load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, of,
+                                      sa);
+    } else {
+      Offs<D, NG, KB, VB> oc;
+      oc.clamped(c, rl);
+      load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR, oc,
+                                     sa);
+    }
+  };
+  int st_d = cl.ctr ? cl.wave : 0;
+  if constexpr (!kStaged) {
+    if (st_d < nsteps) load_direct(st_d);
   }
+  // the wave's query quarter reaches its LDS slot once the first K/V loads
+  // are out, so the two latencies overlap
+  if (q_pending) {
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) c.qq[k] = qreg[k];
+    q_pending = false;
+  }
+
+  // the query in the operand layout; coded K rows of a rotated cache meet
+  // the rotated query
   u32x4 qop[D / 32];
-  // coded K rows of a rotated cache meet the rotated query
-  const bool rot = KB < 16 && visual && c.rotate_k;
-  if (rot) rotate_q<D>(c);
-  const float qsr = build_q<D, NG, KB>(c, qop, rot);
+  float qsr;
+  {
+    float qv[D / 4];
+    unpack_quarter<D>(c, qv);
+    if (KB < 16 && visual && c.rotate_k) rotate_quarter<D>(c, qv);
+    qsr = build_q<D, NG, KB>(c, qv, qop);
+  }
   const float c24 = c.qscale * 16777216.0f;  // 2^24 * qscale
 
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= v_inflation<D, VB>(mb);
 
-  Step<D, KB, VB> sa;
   if constexpr (kStaged) {
     const uint32_t vsel = v_pair_selector<D, VB>((c.n * VBY) & 3);
     // Ring slot k holds step slot[k]; after a slot's step is staged, the
@@ -782,51 +836,20 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
       }
     }
   } else {
-    // bf16 rows (and bf16 K with quantised V) load straight into operands,
-    // one claimed step at a time (the next claim flies while a step runs)
-    const uint32_t vsel_mem = v_pair_selector<D, VB>(0);
-    Offs<D, NG, KB, VB> of;
-    of.full(c);
-    int st = cl.ctr ? cl.wave : 0;
+    // bf16 rows (and bf16 K with quantised V): one claimed step at a time
+    // (the next claim flies while a step runs), each loaded straight into
+    // operands after the previous one is computed
     int pend = cl.ctr ? claim_step(cl, c.lane, cl.nw) : 1;
-    while (st < nsteps) {
-      const int64_t o = int64_t(st) * 32;
-      const int rl = rows_in(st);
-      if (rl == 32) {
-        load_step<D, NG, KB, VB, false>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
-                                        of, sa);
-      } else {
-        Offs<D, NG, KB, VB> oc;
-        oc.clamped(c, rl);
-        load_step<D, NG, KB, VB, true>(kp + o * KR, kmp + o * MR, vp + o * VR, vmp + o * MR,
-                                       oc, sa);
-      }
-      compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rl, vsel_mem);
-      st = __builtin_amdgcn_readlane(pend, 0);
-      pend = cl.ctr ? claim_step(cl, c.lane, cl.nw) : st + 1;
+    while (st_d < nsteps) {
+      compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(st_d), vsel_mem);
+      st_d = __builtin_amdgcn_readlane(pend, 0);
+      pend = cl.ctr ? claim_step(cl, c.lane, cl.nw) : st_d + 1;
+      if (st_d < nsteps) load_direct(st_d);
     }
   }
 
 #pragma unroll
   for (int mb = 0; mb < NB; ++mb) ws.o[mb] *= 1.0f / v_inflation<D, VB>(mb);
-}
-
-// Unit b of a launch -> slot, sequence index within the launch and x, the
-// unit's index among the mult[slot] * nx[seq] units of that (slot, sequence)
-// (see DecodeArgs::mult), searched by the whole wave at once: lane l tests
-// table entry l (and l + 64), and the number of entries at or below b is the
-// index.  b must be wave-uniform; the results are.
-__device__ inline void decode_unit(const DecodeArgs& t, int b, int n_lh, int n_seq, int lane,
-                                   int& slot, int& sl, int& x) {
-  static_assert(kMaxLH <= 128 && kMaxSeq <= 64, "two ballots cover the slot table, one the sequences");
-  const int per_mult = t.nxcum[n_seq];  // units of one slot with mult 1
-  const bool lo = lane < n_lh && per_mult * int(t.mcum[lane]) <= b;
-  const bool hi = lane + 64 < n_lh && per_mult * int(t.mcum[lane + 64]) <= b;
-  slot = __builtin_popcountll(__ballot(lo)) + __builtin_popcountll(__ballot(hi)) - 1;
-  const int m = t.mult[slot];
-  const int r = b - per_mult * int(t.mcum[slot]);
-  sl = __builtin_popcountll(__ballot(lane < n_seq && m * t.nxcum[lane] <= r)) - 1;
-  x = r - m * t.nxcum[sl];
 }
 
 // The workgroup's large LDS area: the waves' stages during the loop, their
@@ -844,6 +867,60 @@ struct BigLds {
                                        : (kOAll > kWaves * kStage ? kOAll : kWaves * kStage);
 };
 
+// The launch's scalar arguments, wave-uniform.  The kernel reads them from
+// its LDS copy of the argument block: the argument segment itself is a slow
+// round trip away, and every scalar load from it in the set-up or the tail
+// would sit on the critical path.
+struct Launch {
+  const uint8_t* cache;
+  const uint16_t* q;
+  uint16_t* out;
+  float* ws_o;
+  float* ws_ml;
+  int32_t* ws_arrive;
+  int64_t Rvis;
+  float qscale;
+  int G, Hkv, Hq, B, chunk, max_chunks, seq_off, n_lh, n_seq, rotate_k;
+};
+// A device pointer read from LDS, made wave-uniform and marked as a global
+// (not generic) address, so accesses through it compile to global or buffer
+// instructions rather than flat ones (which would also count against the LDS
+// wait counter).
+template <class T>
+__device__ inline T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  // (readfirstlane returns int: go through uint32_t, or a low word with bit
+  // 31 set would be sign-extended over the high word)
+  const uint64_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v)));
+  const uint64_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(v >> 32)));
+  return (T*)((__attribute__((address_space(1))) T*)(hi << 32 | lo));
+}
+__device__ inline int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline Launch launch_scalars(const DecodeArgs& t) {
+  Launch L;
+  L.cache = uniform_ptr(t.cache);
+  L.q = uniform_ptr(t.q);
+  L.out = uniform_ptr(t.out);
+  L.ws_o = uniform_ptr(t.ws_o);
+  L.ws_ml = uniform_ptr(t.ws_ml);
+  L.ws_arrive = uniform_ptr(t.ws_arrive);
+  const uint64_t rv = uint64_t(t.Rvis);
+  L.Rvis = int64_t(uint64_t(uint32_t(uniform_int(int(uint32_t(rv >> 32))))) << 32 |
+                   uint32_t(uniform_int(int(uint32_t(rv)))));
+  L.qscale = __builtin_bit_cast(float, uniform_int(__builtin_bit_cast(int, t.qscale)));
+  L.G = uniform_int(t.G);
+  L.Hkv = uniform_int(t.Hkv);
+  L.Hq = uniform_int(t.Hq);
+  L.B = uniform_int(t.B);
+  L.chunk = uniform_int(t.chunk);
+  L.max_chunks = uniform_int(t.max_chunks);
+  L.seq_off = uniform_int(t.seq_off);
+  L.n_lh = uniform_int(t.n_lh);
+  L.n_seq = uniform_int(t.n_seq);
+  L.rotate_k = uniform_int(t.rotate_k);
+  return L;
+}
+
 // Split-K merge of one (layer, seq, head) by the workgroup whose partial
 // completed its arrival count: the nxs partials (normalised rows o / l with
 // their (m, l)) are combined with the log-sum-exp rule, read past the caches,
@@ -851,7 +928,7 @@ struct BigLds {
 // workgroup's reusable LDS (big_lds) and all its threads; the caller ensures
 // no thread still uses that LDS.
 template <int D, int kBigBytes>
-__device__ void merge_entry(const DecodeArgs& a, uint8_t* big_lds, int l_local, int s, int h,
+__device__ void merge_entry(const Launch& a, uint8_t* big_lds, int l_local, int s, int h,
                             int nxs) {
   const int G = a.G;
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
@@ -1003,7 +1080,7 @@ __device__ inline bool wave_merge_fits(int nxs, int G, int D, int waves) {
   return nxs <= kWmX && nxs * G <= 64 && per_wave <= 64 * kWmT;
 }
 template <int D>
-__device__ void merge_entry_wave(const DecodeArgs& a, int l_local, int s, int h, int nxs,
+__device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int nxs,
                                  int slice, int waves, int lane) {
   const int G = a.G;
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
@@ -1091,26 +1168,63 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
 
-  // The per-slot / per-sequence tables are indexed by values computed here, so
-  // reading them from the argument segment would chain a dozen dependent
-  // memory round trips.  One cooperative 16-byte copy puts the whole argument
-  // block in LDS; every table lookup below is then an LDS read.
+  // The per-slot / per-sequence tables are indexed by values computed here.
+  // One cooperative 16-byte pass copies the whole argument block to LDS; the
+  // launch's sequence lengths are loaded in the same round trip.
   static_assert(sizeof(DecodeArgs) % 16 == 0, "argument block copied in 16-byte pieces");
   constexpr int kArgVec = int(sizeof(DecodeArgs) / 16);
+  static_assert(kArgVec <= kThreads, "one 16-byte piece per thread");
   __shared__ uint4 args_lds[kArgVec];
   __shared__ int lds_claim[kWaves];  // per piece (by its first wave): claim counter
   __shared__ int lens_lds[kMaxSeq];  // attended lengths of the launch's sequences
   __shared__ unsigned lead_lds, split_lds;  // pieces by lowest wave; any split piece
-  if (threadIdx.x < kWaves) lds_claim[threadIdx.x] = 0;
-  if (threadIdx.x == 0) lead_lds = split_lds = 0u;
   {
+    // branch-free, so both loads go out before the first wait
     const uint4* src = (const uint4*)(__builtin_amdgcn_kernarg_segment_ptr());
-    for (int i = threadIdx.x; i < kArgVec; i += kThreads) args_lds[i] = src[i];
-    // the lengths travel with the arguments so no wave waits on them later
-    if (int(threadIdx.x) < a.n_seq) lens_lds[threadIdx.x] = a.seq_lens[a.seq_off + threadIdx.x];
+    const int ti = int(threadIdx.x);
+    const uint4 v = src[min(ti, kArgVec - 1)];
+    const int len_v = a.seq_lens[a.seq_off + min(min(ti, kMaxSeq - 1), a.n_seq - 1)];
+    if (ti < kWaves) lds_claim[ti] = 0;
+    if (ti == 0) lead_lds = split_lds = 0u;
+    if (ti < kArgVec) args_lds[ti] = v;
+    if (ti < kMaxSeq) lens_lds[ti] = len_v;
   }
   __syncthreads();
   const DecodeArgs& t = *reinterpret_cast<const DecodeArgs*>(args_lds);
+  const Launch La = launch_scalars(t);
+
+  // Lane-parallel copies of the launch tables: lane l holds slots l and l + 64
+  // and sequence l, read in one batch of independent LDS reads.  Every lookup
+  // below is then a ballot or a readlane, not a chain of dependent reads.
+  static_assert(kMaxLH <= 128 && kMaxSeq <= 64, "two lanes' worth of slots, one of sequences");
+  const int n_lh = La.n_lh, n_seq = La.n_seq;
+  const int sA = lane, sB = min(lane + 64, kMaxLH - 1);
+  const int mcA = t.mcum[sA], mcB = t.mcum[sB];
+  const int mA = t.mult[sA], mB = t.mult[sB];
+  const int lhA = t.lh_glob[sA], lhB = t.lh_glob[sB];
+  const int bitsA = int(t.bits[sA][0]) | int(t.bits[sA][1]) << 8;
+  const int bitsB = int(t.bits[sB][0]) | int(t.bits[sB][1]) << 8;
+  const uint32_t kbaseA = t.base256[sA][0], kbaseB = t.base256[sB][0];
+  const uint32_t vbaseA = t.base256[sA][1], vbaseB = t.base256[sB][1];
+  const int nxc = t.nxcum[lane], nxl = t.nx[lane];
+  const int vbl = t.vb[lane], vel = t.ve[lane], capl = t.cap[lane];
+  const int vr0l = t.vrow0[lane], tr0l = t.trow0[lane], lenl = lens_lds[lane];
+  const int per_mult = t.nxcum[n_seq];  // units of one slot with mult 1
+  auto pick = [&](int vA, int vB, int i) {  // slot table value of (uniform) slot i
+    return __builtin_amdgcn_readlane(i < 64 ? vA : vB, i & 63);
+  };
+  // unit b (wave-uniform) -> slot, sequence index within the launch and x,
+  // the unit's index among the mult[slot] * nx[seq] units of that pair
+  auto unit_of = [&](int b, int& slot_, int& sl_, int& x_) {
+    const int cA = __builtin_popcountll(__ballot(lane < n_lh && per_mult * mcA <= b));
+    const int cB = __builtin_popcountll(__ballot(lane + 64 < n_lh && per_mult * mcB <= b));
+    slot_ = __builtin_amdgcn_readfirstlane(cA + cB - 1);
+    const int m = pick(mA, mB, slot_);
+    const int r = b - per_mult * pick(mcA, mcB, slot_);
+    sl_ = __builtin_amdgcn_readfirstlane(
+        __builtin_popcountll(__ballot(lane < n_seq && m * nxc <= r)) - 1);
+    x_ = r - m * __builtin_amdgcn_readlane(nxc, sl_);
+  };
 
   // this wave's unit -> (slot, sequence, index u among the entry's ne units).
   // Units b8 + r (positions r) are dealt to the waves so that every piece
@@ -1121,32 +1235,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   // workgroup the positions are rotated so the short piece after it starts at
   // wave 0.
   const int b8 = int(blockIdx.x) * kWaves;
-  const int total = t.nxcum[a.n_seq] * int(t.mcum[a.n_lh]);  // the last block may be short
+  const int total = per_mult * t.mcum[n_lh];  // the last block may be short
   int rot = 0;
   auto pos_of = [&](int w) { return ((((w & 3) << 1) | (w >> 2)) + rot) & (kWaves - 1); };
-  int slot = 0, sl = 0, u = 0;
-  if (b8 + pos_of(wave) < total) decode_unit(t, b8 + pos_of(wave), a.n_lh, a.n_seq, lane, slot, sl, u);
   {
-    // the first piece's length: known here when this wave's entry holds the
-    // workgroup's first unit (always so when one entry fills the workgroup)
-    const int my0 = b8 + pos_of(wave) - u, myn = t.nx[sl] * int(t.mult[slot]);
-    int first = my0 <= b8 ? min(kWaves, my0 + myn - b8) : 0;
-    if (my0 > b8) {
-      int s0, l0, u0;
-      decode_unit(t, b8, a.n_lh, a.n_seq, lane, s0, l0, u0);
-      first = min(kWaves, t.nx[l0] * int(t.mult[s0]) - u0);
-    }
+    // the first piece's length (units of the block's first entry)
+    int s0, l0, u0;
+    unit_of(b8, s0, l0, u0);
+    const int first = min(kWaves, __builtin_amdgcn_readlane(nxl, l0) * pick(mA, mB, s0) - u0);
     rot = __builtin_amdgcn_readfirstlane(first > kWaves / 2 && first < kWaves ? first : 0);
-    if (rot != 0 && b8 + pos_of(wave) < total)
-      decode_unit(t, b8 + pos_of(wave), a.n_lh, a.n_seq, lane, slot, sl, u);
   }
+  int slot = 0, sl = 0, u = 0;
+  if (b8 + pos_of(wave) < total) unit_of(b8 + pos_of(wave), slot, sl, u);
   const int pos = pos_of(wave);
   const int gw = b8 + pos;
   const bool active = gw < total;
-  slot = __builtin_amdgcn_readfirstlane(slot);
-  sl = __builtin_amdgcn_readfirstlane(sl);
-  u = __builtin_amdgcn_readfirstlane(u);
-  const int ne = __builtin_amdgcn_readfirstlane(t.nx[sl] * int(t.mult[slot]));
+  const int ne = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(nxl, sl) *
+                                                pick(mA, mB, slot));
   const int w0 = gw - u;  // the entry's first unit
   // the piece: positions [p_lo, p_hi) of this workgroup, i.e. the waves of
   // pmask; the entry's piece px of pn (idle waves form no piece)
@@ -1157,9 +1262,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   for (int w = 0; w < kWaves; ++w) pmask |= pos_of(w) >= p_lo && pos_of(w) < p_hi ? 1u << w : 0u;
   const int px = int(blockIdx.x) - w0 / kWaves;
   const int pn = (w0 + ne - 1) / kWaves - w0 / kWaves + 1;
-  const int lh = __builtin_amdgcn_readfirstlane(int(t.lh_glob[slot]));
-  const int l_local = lh / a.Hkv, h = lh % a.Hkv;
-  const int s = a.seq_off + sl;
+  const int lh = __builtin_amdgcn_readfirstlane(pick(lhA, lhB, slot));
+  const int l_local = lh / La.Hkv, h = lh % La.Hkv;
+  const int s = La.seq_off + sl;
   // piece table for the combine, written now so it is off the tail's path
   __shared__ int winfo[kWaves][8];  // per wave: pmask, -, l_local, s, h, px, pn
   if (lane < 7) winfo[wave][lane] = lane == 0 ? int(pmask) : lane == 1 ? 0 : lane == 2 ? l_local
@@ -1168,43 +1273,48 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     __hip_atomic_fetch_or(&lead_lds, 1u << wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (pn > 1) __hip_atomic_fetch_or(&split_lds, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  const int cap = __builtin_amdgcn_readfirstlane(t.cap[sl]);
-  const int G = a.G;
+  const int cap = __builtin_amdgcn_readlane(capl, sl);
+  const int G = La.G;
 
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kWaves][kMaxGroupRatio * D];
   __shared__ float ml_lds[kWaves][16][2];
   using Big = BigLds<D, NG, KB, VB>;
   __shared__ __attribute__((aligned(16))) uint8_t big_lds[Big::kBytes];
 
-  // the G query rows of this wave's KV head: G * D bf16 in 16-byte pieces
-  // (rows start 16-byte aligned since D * 2 >= 128); only this wave reads them
-  const uint16_t* qp = a.q + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+  // quarter jq of the query of column n's head (head 0 for dead columns):
+  // D/4 bf16, 16-byte aligned, loaded now and parked in the lane's own LDS
+  // slot once the first K/V loads are out (only this lane reads it back)
   Ctx c;
-  // G * NG <= 16, so G * D / 8 <= 64 * D / (32 NG) pieces of 16 bytes
+  __shared__ __attribute__((aligned(16))) u32x4 q_lds[kWaves][64][D / 32];
+  u32x4 qreg[D / 32];
+  {
+    const int qh = (lane & 15) < G * NG ? (lane & 15) / NG : 0;
+    const uint16_t* qp = La.q + ((int64_t(l_local) * La.B + s) * La.Hq + int64_t(h) * G + qh) * D +
+                         (lane >> 4) * (D / 4);
 #pragma unroll
-  for (int k = 0; k < D / (32 * NG); ++k) {
-    const int i = lane + 64 * k;
-    c.qreg[k] = active && i < G * D / 8 ? reinterpret_cast<const u32x4*>(qp)[i] : u32x4{0, 0, 0, 0};
+    for (int k = 0; k < D / 32; ++k)
+      qreg[k] = active ? reinterpret_cast<const u32x4*>(qp)[k] : u32x4{0, 0, 0, 0};
   }
-  int len = lens_lds[sl];
+  c.qq = q_lds[wave][lane];
+  bool q_pending = true;
+  int len = __builtin_amdgcn_readlane(lenl, sl);
   len = len < 1 ? 1 : (len > cap ? cap : len);
 
-  const int kbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][0]));
-  const int vbits = __builtin_amdgcn_readfirstlane(int(t.bits[slot][1]));
+  const int bits2 = pick(bitsA, bitsB, slot);
+  const int kbits = bits2 & 0xFF;
+  const int vbits = bits2 >> 8;
   {
     const int kb = kbits, vb = vbits;
-    c.kvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][0])) * 256u;
-    c.kmeta = c.kvis + meta_plane_offset(a.Rvis, D, kb);
-    c.ktxt = c.kvis + txt_plane_offset(a.Rvis, D, g, kb);
-    c.vvis = a.cache + uint64_t(__builtin_amdgcn_readfirstlane(t.base256[slot][1])) * 256u;
-    c.vmeta = c.vvis + meta_plane_offset(a.Rvis, D, vb);
-    c.vtxt = c.vvis + txt_plane_offset(a.Rvis, D, g, vb);
+    c.kvis = La.cache + uint64_t(uint32_t(pick(int(kbaseA), int(kbaseB), slot))) * 256u;
+    c.kmeta = c.kvis + meta_plane_offset(La.Rvis, D, kb);
+    c.ktxt = c.kvis + txt_plane_offset(La.Rvis, D, g, kb);
+    c.vvis = La.cache + uint64_t(uint32_t(pick(int(vbaseA), int(vbaseB), slot))) * 256u;
+    c.vmeta = c.vvis + meta_plane_offset(La.Rvis, D, vb);
+    c.vtxt = c.vvis + txt_plane_offset(La.Rvis, D, g, vb);
   }
-  c.q_lds = q_lds[wave];
   c.stage = big_lds + Big::kStageOff + wave * Big::kStage;
-  c.qscale = a.qscale;
+  c.qscale = La.qscale;
   c.G = G;
-  c.rotate_k = a.rotate_k != 0;
+  c.rotate_k = La.rotate_k != 0;
   c.lane = lane;
   c.n = lane & 15;
   c.jq = lane >> 4;
@@ -1220,21 +1330,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // static split: chunk mode gives each workgroup (8 units) one chunk,
     // the balanced mode deals the entry's steps over its ne units
     int wa, wb;
-    if (a.chunk > 0)
-      wave_range(u / kWaves, u % kWaves, ne / kWaves, len, a.chunk, kWaves, wa, wb);
+    if (La.chunk > 0)
+      wave_range(u / kWaves, u % kWaves, ne / kWaves, len, La.chunk, kWaves, wa, wb);
     else
       wave_range(u, 0, ne, len, 0, 1, wa, wb);
-    const int vb = __builtin_amdgcn_readfirstlane(t.vb[sl]);
-    const int ve = __builtin_amdgcn_readfirstlane(t.ve[sl]);
-    const int64_t vrow0 = __builtin_amdgcn_readfirstlane(t.vrow0[sl]);
-    const int64_t trow0 = __builtin_amdgcn_readfirstlane(t.trow0[sl]);
+    const int vb = __builtin_amdgcn_readlane(vbl, sl);
+    const int ve = __builtin_amdgcn_readlane(vel, sl);
+    const int64_t vrow0 = __builtin_amdgcn_readlane(vr0l, sl);
+    const int64_t trow0 = __builtin_amdgcn_readlane(tr0l, sl);
     const bool quant_vis = !(KB == 16 && VB == 16) && kbits == KB && vbits == VB;
     // In a balanced split the piece's visual rows (the union of its waves'
     // static ranges) are claimed step by step by its waves; text rows, and
     // everything in the fixed chunk mode, follow the static split [wa, wb).
     // The static text rows go first so the claimed part absorbs their
     // imbalance.
-    const bool dyn = a.chunk == 0;
+    const bool dyn = La.chunk == 0;
     int ga, gb, gt;
     wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt);
     wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb);
@@ -1256,9 +1366,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       const int64_t row0 = vis ? vrow0 + (x0 - vb) : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
       const Claim use = vis && dyn ? cl : Claim{nullptr, 0, 1};
       if (vis && quant_vis)
-        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true, use);
+        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true, use, qreg, q_pending);
       else  // text rows, or bf16 visual rows of a protected head
-        run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, vis, use);
+        run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, vis, use, qreg, q_pending);
     }
   }
 
@@ -1291,41 +1401,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __syncthreads();
 
   // ---- combine each piece's waves; write its partial (or the output) --------
-  // Thread (row c, wave w) turns the (m, l) of w's piece into w's combine
-  // weight f_w = 2^(m_w - M) (0 for a wave without tokens); the piece's
-  // lowest wave also keeps M and L = sum l_w f_w.  Every output element is
-  // then a weighted sum over its piece's waves.  Head j's value at d lives in
-  // row c = j * NG + (d / g).
-  __shared__ __attribute__((aligned(16))) float wts[16][kWaves];
-  __shared__ float rowL[kWaves][16], rowM[kWaves][16];
-  if (threadIdx.x < 16 * kWaves) {
-    const int cr = threadIdx.x & 15, w = threadIdx.x >> 4;
-    const unsigned pm = unsigned(winfo[w][0]);
-    float2 ml[kWaves];  // all read up front: the selects below stay branch-free
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) ml[v] = *reinterpret_cast<const float2*>(ml_lds[v][cr]);
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-      M = ((pm >> v) & 1u) != 0u & ml[v].y > 0.0f ? fmaxf(M, ml[v].x) : M;
-    float L = 0.0f, fw = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float f = ((pm >> v) & 1u) != 0u & ml[v].y > 0.0f ? __builtin_amdgcn_exp2f(ml[v].x - M)
-                                                              : 0.0f;
-      L += ml[v].y * f;
-      fw = v == w ? f : fw;
-    }
-    wts[cr][w] = fw;
-    if (pm != 0u && __builtin_ctz(pm) == w) {
-      rowL[w][cr] = L;
-      rowM[w][cr] = M;
-    }
-  }
+  // Every output element is a weighted sum over its piece's waves: wave w's
+  // weight is f_w = 2^(m_w - M) against the piece's maximum M (0 for a wave
+  // without tokens), and L = sum l_w f_w.  Each thread forms the weights of
+  // its own row from the (m, l) pairs, so one barrier separates the waves'
+  // writes from the combine.  Head j's value at d lives in row
+  // c = j * NG + (d / g).
   // pieces of this workgroup, by their lowest waves
   const unsigned lead = __builtin_amdgcn_readfirstlane(lead_lds);
   const bool any_split = __builtin_amdgcn_readfirstlane(split_lds) != 0u;
-  __syncthreads();
   const int GD = G * D;
 #pragma clang loop unroll(disable)
   for (unsigned rest = lead; rest != 0u; rest &= rest - 1u) {
@@ -1336,26 +1420,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const int ph = __builtin_amdgcn_readfirstlane(winfo[wl][4]);
     const int ppx = __builtin_amdgcn_readfirstlane(winfo[wl][5]);
     const int ppn = __builtin_amdgcn_readfirstlane(winfo[wl][6]);
-    const int64_t pidx = partial_index(pl, ps, ph, ppx, a.B, a.Hkv, a.max_chunks);
-    uint16_t* outp = a.out + ((int64_t(pl) * a.B + ps) * a.Hq + int64_t(ph) * G) * D;
+    const int64_t pidx = partial_index(pl, ps, ph, ppx, La.B, La.Hkv, La.max_chunks);
+    uint16_t* outp = La.out + ((int64_t(pl) * La.B + ps) * La.Hq + int64_t(ph) * G) * D;
     // four consecutive outputs per thread (one head, one group: D and g are
     // multiples of 4): 16-byte LDS reads and one 16-byte store
-    const Rsrc rpo = make_rsrc(a.ws_o + pidx * GD, int64_t(GD) * 4);
+    const Rsrc rpo = make_rsrc(La.ws_o + pidx * GD, int64_t(GD) * 4);
     for (int i4 = threadIdx.x; i4 < GD / 4; i4 += kThreads) {
       const int i = 4 * i4;
       const int j = i / D, d = i % D, cr = j * NG + d / g;
+      float2 ml[kWaves];  // all read up front: the selects below stay branch-free
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) ml[v] = *reinterpret_cast<const float2*>(ml_lds[v][cr]);
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v)
+        M = (((pm >> v) & 1u) != 0u && ml[v].y > 0.0f) ? fmaxf(M, ml[v].x) : M;
+      float L = 0.0f;
       f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int w4 = 0; w4 < kWaves / 4; ++w4) {
-        const f32x4 f = *reinterpret_cast<const f32x4*>(&wts[cr][4 * w4]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&o_all[4 * w4 + w][cr][d]);
-          const float fw = (pm >> (4 * w4 + w)) & 1u ? f[w] : 0.0f;
-          acc += x * fw;
-        }
+      for (int v = 0; v < kWaves; ++v) {
+        const float f = (((pm >> v) & 1u) != 0u && ml[v].y > 0.0f)
+                            ? __builtin_amdgcn_exp2f(ml[v].x - M) : 0.0f;
+        L += ml[v].y * f;
+        acc += *reinterpret_cast<const f32x4*>(&o_all[v][cr][d]) * f;
       }
-      const float L = rowL[wl][cr];
       const float rl = L > 0.0f ? __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
       const f32x4 o = acc * rl;
       if (ppn == 1) {
@@ -1371,9 +1459,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rpo,
                                                uint32_t(i) * 4u, 0, kCoherent);
         if (d == 0) {
-          __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 0], rowM[wl][cr], __ATOMIC_RELAXED,
+          __hip_atomic_store(&La.ws_ml[(pidx * G + j) * 2 + 0], M, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_SYSTEM);
-          __hip_atomic_store(&a.ws_ml[(pidx * G + j) * 2 + 1], L, __ATOMIC_RELAXED,
+          __hip_atomic_store(&La.ws_ml[(pidx * G + j) * 2 + 1], L, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_SYSTEM);
         }
       }
@@ -1394,8 +1482,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   if (lane == 0) {
     int last = 0;
     if (((lead >> wave) & 1u) && pn > 1) {
-      const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
-      last = __hip_atomic_fetch_add(&a.ws_arrive[entry], 1, __ATOMIC_RELAXED,
+      const int64_t entry = (int64_t(l_local) * La.B + s) * La.Hkv + h;
+      last = __hip_atomic_fetch_add(&La.ws_arrive[entry], 1, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_SYSTEM) == pn - 1;
     }
     is_last[wave] = last;
@@ -1421,7 +1509,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       unsigned rest = done;
       for (int i = 0; i < kk; ++i) rest &= rest - 1u;
       const int w = __builtin_ctz(rest);
-      merge_entry_wave<D>(a, __builtin_amdgcn_readfirstlane(winfo[w][2]),
+      merge_entry_wave<D>(La, __builtin_amdgcn_readfirstlane(winfo[w][2]),
                           __builtin_amdgcn_readfirstlane(winfo[w][3]),
                           __builtin_amdgcn_readfirstlane(winfo[w][4]),
                           __builtin_amdgcn_readfirstlane(winfo[w][6]), wave / m,
@@ -1436,7 +1524,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     if (__builtin_amdgcn_readfirstlane(is_last[w])) {
       if (!first_merge) __syncthreads();  // the previous merge is done with the LDS
       first_merge = false;
-      merge_entry<D, Big::kBytes>(a, big_lds, __builtin_amdgcn_readfirstlane(winfo[w][2]),
+      merge_entry<D, Big::kBytes>(La, big_lds, __builtin_amdgcn_readfirstlane(winfo[w][2]),
                      __builtin_amdgcn_readfirstlane(winfo[w][3]),
                      __builtin_amdgcn_readfirstlane(winfo[w][4]),
                      __builtin_amdgcn_readfirstlane(winfo[w][6]));
