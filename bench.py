@@ -13,8 +13,11 @@ cache holds.  Inputs are resident in HBM before the timed region.
 Printed: one JSON line (rank 0).  `value` is effective HBM GB/s of the whole
 step (algorithmic bytes / step time); `roofline` refers to the decode
 attention launch, timed with HIP events on the stream it runs on.
-`cpu_baseline` times the CPU oracle (single thread) on a bounded sample of the
-same workload, scaled to one step.
+`cpu_baseline` times the CPU oracle on all host threads (and on one) over a
+bounded sample of the same workload, scaled to one step.  Extras: the bf16
+reference decode, the long-context (32K) decode, a read-only stream kernel
+as the practical HBM ceiling, a device copy, the quantize block, rotated K,
+and the layer-by-layer launch pattern.
 """
 from __future__ import annotations
 
@@ -316,6 +319,9 @@ def main():
                                                     to_dev, dec_avg, alg)
         extras["quantize_block"] = quantize_block(torch, kvq, synth, dev, stream, args)
         extras["copy_ceiling"] = copy_ceiling(torch, dev, stream)
+        extras["read_stream_ceiling"] = read_stream_ceiling(torch, dev, args, alg, dec_avg)
+        if w.name != "long_gqa" and args.chunk == 0:
+            extras["long_gqa_decode"] = long_context_decode(torch, kvq, args, dev)
 
     cpu = None if args.no_cpu else cpu_baseline(w, lens, q_bits, alg)
     profiled = args.chunk == 0 and (w.name != "headguard_step" or args.protected == 14)
@@ -448,20 +454,126 @@ def copy_ceiling(torch, dev, stream):
     return {"bytes_moved": 2 * n, "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(w, lens, q_bits, alg_bytes, budget_s=10.0):
-    """Time the CPU oracle (one thread) decoding a bounded sample of the step:
-    every query head of one (layer, sequence) after another over the full
-    history, until about budget_s seconds of decoding have been timed (or the
-    step is done), then scale to the whole step.  Storing the sampled rows is
-    not timed."""
+def read_stream_ceiling(torch, dev, args, decode_bytes, decode_ms):
+    """The practical HBM ceiling: a hand-written read-only stream kernel
+    (libkvqbench.so) timed like the decode, once reading as many bytes per
+    launch as the decode's algorithmic bytes and once 1 GiB per launch, each
+    launch reading the next region of a >= 2 GiB buffer so the reads come
+    from HBM."""
+    import ctypes as C
+    from quantized_decode_attention_quantize_amd import build
+    lib = C.CDLL(build.BENCH_LIB)
+    lib.kvqb_read_stream.restype = C.c_int
+    lib.kvqb_read_stream.argtypes = [C.c_void_p, C.c_uint64, C.c_int, C.c_void_p, C.c_void_p]
+    total = max(2 << 30, 4 * (1 << 30))
+    buf = torch.ones(total, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nbytes, grid in (("decode_bytes", decode_bytes // 16 * 16, 4096),
+                               ("one_gib", 1 << 30, 4096)):
+        R = total // nbytes
+
+        def launch(i):
+            # the stream current at the call: under graph capture, the capturing one
+            st = torch.cuda.current_stream().cuda_stream
+            rc = lib.kvqb_read_stream(C.c_void_p(buf.data_ptr() + (i % R) * nbytes), nbytes, grid,
+                                      C.c_void_p(sink.data_ptr()), C.c_void_p(st))
+            assert rc == 0, rc
+        for i in range(5):
+            launch(i)
+        torch.cuda.synchronize()
+        ms = timed(torch, types.SimpleNamespace(eager=False, steps=50 if nbytes < 1 << 28 else 10),
+                   launch)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "gbps": round(gbs, 1),
+                     "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    d = out["decode_bytes"]
+    out["decode_vs_stream"] = round(d["us"] / (decode_ms * 1e3), 4)
+    out["kernel"] = "kvqb_read_stream: 4096 workgroups x 512 threads, 8 x 16-byte loads in flight"
+    del buf
+    return out
+
+
+def long_context_decode(torch, kvq, args, dev):
+    """Decode-only timing of the long-context workload (B=4 x 32K tokens,
+    32/8 heads, K INT4 / V INT2), the second configuration the bandwidth
+    target names, with its roofline fraction and counted traffic."""
+    w = workload("long_gqa")
+    T = [c - 1 for c in w.capacity]
+    lens = [t + 1 for t in T]
+    cfg = kvq.Config.from_workload(w)
+    nbytes = kvq.kvq_cache_bytes(cfg)["total_bytes"]
+    R = max(2, math.ceil(args.replica_mb * 2 ** 20 / nbytes))
+    c0 = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    for s in range(w.batch):
+        k = to_dev(w.sources(0, [s], 0, lens[s], "k")[None])
+        v = to_dev(w.sources(0, [s], 0, lens[s], "v")[None])
+        kvq.kvq_quantize(cfg, c0, 0, 1, [s], 0, lens[s], k, v)
+    torch.cuda.synchronize()
+    caches = [c0] + [c0.clone() for _ in range(R - 1)]
+    q = to_dev(np.stack([w.q_bits(0)]))
+    out = torch.empty_like(q)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ws = torch.zeros(kvq.workspace_bytes(cfg, 1, 0), dtype=torch.uint8, device=dev)
+
+    def dec(i):
+        kvq.kvq_decode_attention(cfg, caches[i % R], 0, 1, lens_d, q, out, w.sm_scale, 0, ws)
+
+    for i in range(args.warmup):
+        dec(i)
+    ms = timed(torch, args, dec)
+    alg = algorithmic_bytes(w, lens)
+    gbs = alg / (ms * 1e-3) / 1e9
+    traffic, src = counted_traffic(w.name)
+    del caches, ws
+    return {"workload": describe(w), "us": round(ms * 1e3, 2), "algorithmic_bytes": alg,
+            "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "traffic_source": src, "cache_replicas": R}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Worker threads for the all-core timing: the CPUs this process may run
+    on, at most 16 (the host share of one GPU on the boxes this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(w, lens, q_bits, alg_bytes, budget_s=8.0):
+    """Time the CPU oracle decoding the step, on one thread and on all host
+    threads.  A work unit is one (layer, sequence, KV head): its query heads
+    over the full history.  The per-unit oracle stays single-threaded (the C
+    calls release the GIL, so Python threads run units side by side).  Storing the
+    rows is not timed.  One thread decodes units until about budget_s seconds
+    are timed; the all-thread run then takes as many units as fill about
+    budget_s seconds of wall time at that rate (every unit when the step fits)
+    and both figures are scaled to one step."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     cfg = oracle.Config.from_workload(w)
     cache = oracle.new_cache(cfg)
-    units = [(l, s) for l in range(w.num_layers) for s in range(w.batch)]
-    dt = 0.0
-    n_heads = 0
-    done = []
-    for l, s in units:
+    G = w.num_q_heads // w.num_kv_heads
+    units = [(l, s, h) for l in range(w.num_layers) for s in range(w.batch)
+             for h in range(w.num_kv_heads)]
+    stored = set()
+
+    def store(l, s):
         T = lens[s] - 1
         for h in range(w.num_kv_heads):
             oracle.store_rows(cfg, cache, l, s, h, 0, 0, T, _f32(w.k_rows(l, s, h, 0, T)))
@@ -469,22 +581,46 @@ def cpu_baseline(w, lens, q_bits, alg_bytes, budget_s=10.0):
             zero = np.zeros((1, w.head_dim), np.float32)
             oracle.store_rows(cfg, cache, l, s, h, 0, T, T + 1, zero)
             oracle.store_rows(cfg, cache, l, s, h, 1, T, T + 1, zero)
-        t0 = time.perf_counter()
-        for i in range(w.num_q_heads):
+        stored.add((l, s))
+
+    def decode(unit):
+        l, s, h = unit
+        for i in range(h * G, (h + 1) * G):
             oracle.decode_one(cfg, cache, l, s, i, lens[s], q_bits[l, s, i], w.sm_scale)
-        dt += time.perf_counter() - t0
-        n_heads += w.num_q_heads
-        done.append((l, s))
-        if dt >= budget_s:
+
+    # one thread
+    dt1, n1 = 0.0, 0
+    for u in units:
+        if u[:2] not in stored:
+            store(*u[:2])
+        t0 = time.perf_counter()
+        decode(u)
+        dt1 += time.perf_counter() - t0
+        n1 += 1
+        if dt1 >= budget_s:
             break
-    # the bytes of the sampled (layer, seq) units against the whole step's
-    frac = n_heads / (w.num_layers * w.batch * w.num_q_heads)
-    step_s = dt / frac
-    return {"value": round(alg_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds_per_step": round(step_s, 3),
-            "sample": f"{n_heads} (layer, seq, query-head) decodes over the full history "
-                      f"({len(done)} of {len(units)} (layer, seq) units, every query head), "
-                      f"{dt:.2f} s timed on one thread, scaled x{1 / frac:.2f} to one step"}
+    step1 = dt1 * len(units) / n1
+    # every host thread, over as many units as fill about budget_s of wall time
+    nt = host_threads()
+    n_all = min(len(units), max(nt, int(budget_s * nt / (dt1 / n1))))
+    sample = units[:n_all]
+    for u in sample:
+        if u[:2] not in stored:
+            store(*u[:2])
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nt) as ex:
+        list(ex.map(decode, sample))
+    dtn = time.perf_counter() - t0
+    stepn = dtn * len(units) / n_all
+    return {"value": round(alg_bytes / stepn / 1e9, 4), "unit": "GB/s", "cores": nt,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "seconds_per_step": round(stepn, 3),
+            "sample": f"{n_all} of {len(units)} (layer, seq, KV head) units, their query heads "
+                      f"over the full history, {dtn:.2f} s wall on {nt} threads, scaled "
+                      f"x{len(units) / n_all:.2f} to one step",
+            "one_thread": {"value": round(alg_bytes / step1 / 1e9, 4), "cores": 1,
+                           "seconds_per_step": round(step1, 3),
+                           "sample": f"{n1} units, {dt1:.2f} s, scaled x{len(units) / n1:.2f}"}}
 
 
 def _f32(a):

@@ -16,6 +16,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip"]
+# The benchmark's read-only HBM stream kernel: a library of its own, so
+# libkvq's exports stay exactly the ABI of include/kvq.h.
+BENCH_LIB = os.path.join(HERE, "libkvqbench.so")
+BENCH_SOURCE = "kvq_bench_stream.hip"
 
 # -packed-fp32-ops: keep the compiler from emitting v_pk_{add,mul,fma}_f32.
 HIP_FLAGS = [
@@ -77,6 +81,13 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("libkvq link failed")
     os.replace(tmp, LIB)
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-shared", os.path.join(CSRC, BENCH_SOURCE), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("libkvqbench build failed")
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 
