@@ -169,3 +169,24 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
     assert np.all(np.isfinite(got)), what
     assert max_abs <= MAX_ABS and rel <= REL_L2, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
     return max_abs, rel
+
+
+def kernel_error(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    """Split the output error into the bf16 rounding of the output itself and
+    the kernel's own arithmetic (f16/bf16 operands, fp32 accumulation):
+    relative L2 of got vs the exact reference, of the exact reference rounded
+    to bf16 vs itself, of got vs that rounded reference (zero when every
+    element rounds to the same bf16 the exact value does), and the excess of
+    the first over the second in quadrature.  Returns the last: the part of
+    the error the kernel adds to what rounding the exact output to bf16
+    costs by itself."""
+    t = torch()
+    ref16 = t.from_numpy(np.ascontiguousarray(ref)).to(t.bfloat16).double().numpy()
+    nr = max(float(np.linalg.norm(ref)), 1e-300)
+    tot = float(np.linalg.norm(got - ref)) / nr
+    rnd = float(np.linalg.norm(ref16 - ref)) / nr
+    k16 = float(np.linalg.norm(got - ref16)) / nr
+    exc = max(0.0, tot * tot - rnd * rnd) ** 0.5
+    print(f"[err] {what}: total={tot:.3e} bf16_rounding={rnd:.3e} vs_rounded_ref={k16:.3e} "
+          f"excess_in_quadrature={exc:.3e}", flush=True)
+    return exc

@@ -12,7 +12,7 @@ import pytest
 
 from quantized_decode_attention_quantize_amd import kvq, synth
 
-from kvq_testlib import Pair, assert_close, errors
+from kvq_testlib import Pair, assert_close, errors, kernel_error
 
 pytestmark = pytest.mark.gpu
 
@@ -116,18 +116,33 @@ def _check_decode(p: Pair, lens, layers=None, chunk=0, what=""):
     return assert_close(np.array(got), np.array(ref), what)
 
 
+def _decode_vs_oracle(p: Pair, lens, chunk=0):
+    w = p.w
+    out, q = p.decode(lens, chunk=chunk)
+    got = np.array([out[0, s, i] for s in range(w.batch) for i in range(w.num_q_heads)])
+    ref = np.array([p.oracle_decode(0, s, i, lens[s], q[0, s, i])
+                    for s in range(w.batch) for i in range(w.num_q_heads)])
+    return got, ref
+
+
 def test_decode_tiny():
     _say("decode tiny")
     p = Pair(synth.tiny())
     p.store()
-    _check_decode(p, [256], what="tiny")
+    got, ref = _decode_vs_oracle(p, [256])
+    assert_close(got, ref, "tiny")
+    # the kernel's own error, apart from the bf16 rounding of the output
+    # (2.5e-4 when measured, against 1.86e-3 for the rounding itself)
+    assert kernel_error(got, ref, "tiny") <= 8e-4
 
 
 def test_decode_llava_layer():
     _say("decode llava layer")
     p = Pair(synth.llava_layer())
     p.store()
-    _check_decode(p, [6287], what="llava")
+    got, ref = _decode_vs_oracle(p, [6287])
+    assert_close(got, ref, "llava")
+    assert kernel_error(got, ref, "llava") <= 8e-4
 
 
 @pytest.mark.parametrize("chunk", [32, 64, 224, 1024, 8192])
@@ -285,25 +300,26 @@ def test_decode_workspace_reuse_across_shapes():
 
 def test_decode_long_context_full_size_sampled():
     """B=4 x 32,768-token GQA cache (32 query / 8 KV heads, K INT4 / V INT2) at
-    full size, decoded in the default (balanced) split as the benchmark runs it;
-    two sequences are also stored by the oracle and their outputs compared."""
-    _say("decode long context 4 x 32768, sampled sequences vs oracle")
+    full size, decoded in the default (balanced) split as the benchmark runs it.
+    Every sequence is stored on both sides; sequences 0 and 3 are compared on
+    every query head, 1 and 2 on four query heads each (spread over the KV
+    heads), since the oracle takes a while per 32K-token head."""
+    _say("decode long context 4 x 32768 vs oracle")
     w = synth.long_gqa()
     p = Pair(w)
-    sampled = [0, 3]
-    # Only the sampled sequences are stored (both sides); the others keep an
-    # all-zero cache region, which decodes like any other rows, so the launch
-    # covers the full batch exactly as the benchmark's does.
-    p.store(seqs=sampled)
-    assert p.mismatches(seqs=sampled) == 0
+    p.store()
+    assert p.mismatches(seqs=[0, 3]) == 0
     lens = [32768, 20000, 32768, 31999]
     out, q = p.decode(lens)
     got, ref = [], []
-    for s in sampled:
-        for i in range(w.num_q_heads):
+    for s in range(w.batch):
+        heads = range(w.num_q_heads) if s in (0, 3) else (0, 9, 18, 31)
+        for i in heads:
             ref.append(p.oracle_decode(0, s, i, lens[s], q[0, s, i]))
             got.append(out[0, s, i])
-    assert_close(np.array(got), np.array(ref), "long context")
+    got, ref = np.array(got), np.array(ref)
+    assert_close(got, ref, "long context")
+    assert kernel_error(got, ref, "long context") <= 1.2e-3
 
 
 def test_decode_ragged_batch_full_size_sampled():
