@@ -40,7 +40,8 @@ class _Cfg(C.Structure):
                 ("head_dim", C.c_int32), ("group_size", C.c_int32),
                 ("capacity", C.POINTER(C.c_int32)), ("vis_begin", C.POINTER(C.c_int32)),
                 ("vis_end", C.POINTER(C.c_int32)), ("k_bits", C.POINTER(C.c_uint8)),
-                ("v_bits", C.POINTER(C.c_uint8)), ("rotate_k", C.c_int32)]
+                ("v_bits", C.POINTER(C.c_uint8)), ("rotate_k", C.c_int32),
+                ("k_per_channel", C.c_int32)]
 
 
 class _Info(C.Structure):
@@ -77,6 +78,7 @@ def lib():
                                         C.POINTER(C.c_uint64)]
         L.orc_row_of.argtypes = [C.POINTER(_Cfg), C.c_int, C.c_int, C.POINTER(C.c_int),
                                  C.POINTER(C.c_int64)]
+        L.orc_coded_end.argtypes = [C.POINTER(_Cfg), C.c_int]
         L.orc_store_rows.argtypes = [C.POINTER(_Cfg), P, C.c_int, C.c_int, C.c_int,
                                      C.c_int, C.c_int, C.c_int, P]
         L.orc_load_row.argtypes = [C.POINTER(_Cfg), P, C.c_int, C.c_int, C.c_int,
@@ -107,7 +109,8 @@ class Config:
     """Holds a C config plus the numpy arrays it points into."""
 
     def __init__(self, num_layers, batch, num_q_heads, num_kv_heads, head_dim,
-                 group_size, capacity, vis_begin, vis_end, k_bits, v_bits, rotate_k=False):
+                 group_size, capacity, vis_begin, vis_end, k_bits, v_bits, rotate_k=False,
+                 k_per_channel=False):
         self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
         self.vis_begin = np.ascontiguousarray(vis_begin, dtype=np.int32)
         self.vis_end = np.ascontiguousarray(vis_end, dtype=np.int32)
@@ -118,14 +121,16 @@ class Config:
                       self.vis_begin.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_end.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.k_bits.ctypes.data_as(C.POINTER(C.c_uint8)),
-                      self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)), int(bool(rotate_k)))
+                      self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)), int(bool(rotate_k)),
+                      int(bool(k_per_channel)))
 
     @classmethod
     def from_workload(cls, w) -> "Config":
         a = w.config_arrays()
         return cls(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                    w.group_size, a["capacity"], a["vis_begin"], a["vis_end"],
-                   a["k_bits"], a["v_bits"], getattr(w, "rotate_k", False))
+                   a["k_bits"], a["v_bits"], getattr(w, "rotate_k", False),
+                   getattr(w, "k_per_channel", False))
 
     @property
     def ref(self):
@@ -185,6 +190,11 @@ def plane_offsets(cfg: Config, layer: int, head: int, X: int):
     if rc:
         raise ValueError(rc)
     return int(v.value), int(m.value), int(t.value)
+
+
+def coded_end(cfg: Config, seq: int) -> int:
+    """End of the coded part of the visual span (see kvq_oracle.h)."""
+    return int(lib().orc_coded_end(cfg.ref, seq))
 
 
 def row_of(cfg: Config, seq: int, t: int):

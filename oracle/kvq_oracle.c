@@ -192,6 +192,7 @@ int orc_validate(const orc_config *c) {
   if (c->num_q_heads % c->num_kv_heads) return 2;
   if (c->head_dim < 1 || c->group_size < 1 || c->head_dim % c->group_size) return 3;
   if (c->rotate_k && (c->head_dim & (c->head_dim - 1))) return 3; /* rotation: D = 2^k */
+  if (c->rotate_k && c->k_per_channel) return 3; /* one grouping of rotated rows only */
   for (i = 0; i < c->num_layers * c->num_kv_heads; i++) {
     if (!bits_ok(c->k_bits[i]) || !bits_ok(c->v_bits[i])) return 3;
     if ((c->head_dim * c->k_bits[i]) % 8 || (c->head_dim * c->v_bits[i]) % 8) return 3;
@@ -204,11 +205,16 @@ int orc_validate(const orc_config *c) {
   return 0;
 }
 
+int orc_coded_end(const orc_config *c, int seq) {
+  int vb = c->vis_begin[seq], ve = c->vis_end[seq], g = c->group_size;
+  return c->k_per_channel ? vb + (ve - vb) / g * g : ve;
+}
+
 static void row_totals(const orc_config *c, uint64_t *rvis, uint64_t *rtxt) {
   uint64_t v = 0, all = 0;
   int s;
   for (s = 0; s < c->batch; s++) {
-    v += (uint64_t)(c->vis_end[s] - c->vis_begin[s]);
+    v += (uint64_t)(orc_coded_end(c, s) - c->vis_begin[s]);
     all += (uint64_t)c->capacity[s];
   }
   *rvis = v;
@@ -284,12 +290,12 @@ int orc_row_of(const orc_config *c, int seq, int t, int *plane, int64_t *row) {
   int s, vb, ve;
   if (seq < 0 || seq >= c->batch || t < 0 || t >= c->capacity[seq]) return 1;
   for (s = 0; s < seq; s++) {
-    int nv = c->vis_end[s] - c->vis_begin[s];
+    int nv = orc_coded_end(c, s) - c->vis_begin[s];
     vbase += nv;
     tbase += c->capacity[s] - nv;
   }
   vb = c->vis_begin[seq];
-  ve = c->vis_end[seq];
+  ve = orc_coded_end(c, seq);
   if (t >= vb && t < ve) {
     *plane = 0;
     *row = vbase + (t - vb);
@@ -341,6 +347,49 @@ void orc_hadamard_unrotate(double *y, int D) {
   for (i = 0; i < D; i++) y[i] *= scale;
 }
 
+/* Per-channel K (k_per_channel, b < 16): coded positions in whole blocks of
+ * g tokens, one group per (block, channel); everything else bf16. */
+static int store_k_blocks(const orc_config *c, uint8_t *cache, uint64_t vis, uint64_t meta,
+                          uint64_t txt, int b, int seq, int t0, int t1, const float *src) {
+  int D = c->head_dim, g = c->group_size, t, d, i;
+  int vb = c->vis_begin[seq], qe = orc_coded_end(c, seq);
+  int lo = t0 > vb ? t0 : vb, hi = t1 < qe ? t1 : qe; /* coded positions stored */
+  uint64_t rb = (uint64_t)D * b / 8;
+  float col[128];
+  uint8_t codes[128];
+  if (g > 128) return 2;
+  if (lo < hi && ((lo - vb) % g || (hi - vb) % g)) return 5; /* a block cut apart */
+  for (t = t0; t < t1; t++) { /* bf16 rows: text, and the residual window */
+    int plane;
+    int64_t row;
+    if (orc_row_of(c, seq, t, &plane, &row)) return 3;
+    if (plane == 2) {
+      uint8_t *r = cache + txt + (uint64_t)row * 2u * D;
+      for (d = 0; d < D; d++) put_u16(r + 2 * d, orc_bf16_round_nearest_even(src[(size_t)(t - t0) * D + d]));
+    }
+  }
+  for (t = lo; t < hi; t += g) { /* block [t, t + g) */
+    int plane;
+    int64_t row;
+    orc_row_of(c, seq, t, &plane, &row); /* the block's first VIS row */
+    uint8_t *m = cache + meta + (uint64_t)(row / g) * (uint64_t)D * 4u;
+    for (i = 0; i < g; i++) memset(cache + vis + (uint64_t)(row + i) * rb, 0, rb);
+    for (d = 0; d < D; d++) {
+      uint16_t s16, m16;
+      for (i = 0; i < g; i++) col[i] = src[(size_t)(t + i - t0) * D + d];
+      orc_quantize_group(col, g, b, codes, &s16, &m16);
+      put_u16(m + 4 * d, s16);
+      put_u16(m + 4 * d + 2, m16);
+      for (i = 0; i < g; i++) {
+        uint8_t *r = cache + vis + (uint64_t)(row + i) * rb;
+        int bit = d * b;
+        r[bit / 8] = (uint8_t)(r[bit / 8] | (codes[i] << (bit % 8)));
+      }
+    }
+  }
+  return 0;
+}
+
 int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
                    int head, int X, int t0, int t1, const float *src) {
   uint64_t vis, meta, txt;
@@ -351,6 +400,8 @@ int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
   if (orc_plane_offsets(c, layer, head, X, &vis, &meta, &txt)) return 1;
   if (D > 1024 || t0 < 0 || t1 > c->capacity[seq] || t0 > t1) return 2;
   b = X ? c->v_bits[layer * c->num_kv_heads + head] : c->k_bits[layer * c->num_kv_heads + head];
+  if (X == 0 && c->k_per_channel && b < 16)
+    return store_k_blocks(c, cache, vis, meta, txt, b, seq, t0, t1, src);
   for (t = t0; t < t1; t++) {
     const float *x = src + (size_t)(t - t0) * D;
     int plane;
@@ -388,14 +439,17 @@ int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
  * at vis/meta/txt and whose visual rows use b bits. */
 static void load_row_at(const orc_config *c, const uint8_t *cache, uint64_t vis,
                         uint64_t meta, uint64_t txt, int b, int plane, int64_t row,
-                        double *out) {
+                        int per_channel, double *out) {
   int D = c->head_dim, g = c->group_size, d;
   if (plane == 0 && b < 16) {
     uint64_t rb = (uint64_t)D * b / 8;
     const uint8_t *r = cache + vis + (uint64_t)row * rb;
-    const uint8_t *m = cache + meta + (uint64_t)row * (uint64_t)(D / g) * 4u;
+    /* per token: D/g pairs in the row's META row; per channel: D pairs in
+     * the META row of block row / g, pair d for channel d */
+    const uint8_t *m = per_channel ? cache + meta + (uint64_t)(row / g) * (uint64_t)D * 4u
+                                   : cache + meta + (uint64_t)row * (uint64_t)(D / g) * 4u;
     for (d = 0; d < D; d++) {
-      int bit = d * b, j = d / g;
+      int bit = d * b, j = per_channel ? d : d / g;
       int code = (r[bit / 8] >> (bit % 8)) & ((1 << b) - 1);
       double sc = orc_f16_value(get_u16(m + 4 * j));
       double mn = orc_f16_value(get_u16(m + 4 * j + 2));
@@ -415,7 +469,7 @@ int orc_load_row_stored(const orc_config *c, const uint8_t *cache, int layer, in
   if (orc_plane_offsets(c, layer, head, X, &vis, &meta, &txt)) return 1;
   if (orc_row_of(c, seq, t, &plane, &row)) return 2;
   b = X ? c->v_bits[layer * c->num_kv_heads + head] : c->k_bits[layer * c->num_kv_heads + head];
-  load_row_at(c, cache, vis, meta, txt, b, plane, row, out);
+  load_row_at(c, cache, vis, meta, txt, b, plane, row, X == 0 && c->k_per_channel, out);
   return 0;
 }
 
@@ -477,9 +531,11 @@ int orc_decode_one(const orc_config *c, const uint8_t *cache, int layer,
     int plane;
     int64_t row;
     orc_row_of(c, seq, t, &plane, &row); /* t < len <= capacity: in range */
-    load_row_at(c, cache, off[0][0], off[0][1], off[0][2], kb, plane, row, K + (size_t)t * D);
+    load_row_at(c, cache, off[0][0], off[0][1], off[0][2], kb, plane, row, c->k_per_channel,
+                K + (size_t)t * D);
     if (c->rotate_k && plane == 0 && kb < 16) orc_hadamard_unrotate(K + (size_t)t * D, D);
-    load_row_at(c, cache, off[1][0], off[1][1], off[1][2], vbits, plane, row, V + (size_t)t * D);
+    load_row_at(c, cache, off[1][0], off[1][1], off[1][2], vbits, plane, row, 0,
+                V + (size_t)t * D);
   }
   orc_attention(q, K, V, len, D, (double)sm_scale, out, lse);
   if (scores) {

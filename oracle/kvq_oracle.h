@@ -42,6 +42,9 @@ typedef struct {
   const uint8_t *v_bits;
   int32_t rotate_k;      /* nonzero: K rows stored as codes are rotated first
                             (orc_hadamard_rotate); every other row is not */
+  int32_t k_per_channel; /* nonzero: K codes are grouped per channel over
+                            blocks of group_size consecutive visual tokens
+                            (see orc_store_rows); V stays per token */
 } orc_config;
 
 typedef struct {
@@ -83,12 +86,28 @@ int orc_cache_bytes(const orc_config *c, orc_cache_info *info);
  * A plane that has no rows gets its offset anyway (size 0). */
 int orc_plane_offsets(const orc_config *c, int layer, int head, int X,
                       uint64_t *vis, uint64_t *meta, uint64_t *txt);
+/* End of the coded part of sequence s's visual span.  Per-token grouping
+ * codes the whole span [vis_begin, vis_end).  With k_per_channel the span is
+ * coded in whole blocks of group_size tokens from vis_begin; the tail that
+ * does not fill a block (the newest visual tokens, a residual window of
+ * fewer than group_size tokens) is stored bf16 like text, for K and V.     */
+int orc_coded_end(const orc_config *c, int seq);
 /* Where the row of position t of sequence s lives: plane 0 = VIS, 2 = TXT;
- * row index within that plane. */
+ * row index within that plane.  A position is in the VIS plane when
+ * vis_begin <= t < orc_coded_end. */
 int orc_row_of(const orc_config *c, int seq, int t, int *plane, int64_t *row);
 
 /* ---- store / load ---------------------------------------------------------- */
-/* Store rows t0..t1-1 of (layer, seq, head, X) from float32 src [(t1-t0), D]. */
+/* Store rows t0..t1-1 of (layer, seq, head, X) from float32 src [(t1-t0), D].
+ * Per-token groups (V always, K unless k_per_channel): each coded row's D
+ * values form D/g groups along the head dimension, one (scale, min) pair per
+ * group in the row's META row.  Per-channel K (k_per_channel, coded K rows):
+ * block j of a sequence is its coded positions [vis_begin + j g,
+ * vis_begin + (j + 1) g); for each channel d the g values of the block form
+ * one group, quantised exactly as a per-token group; codes sit in each
+ * token's VIS row as usual, and the block's META row holds D (scale, min)
+ * pairs in channel order (VIS row r belongs to block row r / g).  Such a
+ * store must cover every block it touches entirely (return 5 otherwise). */
 int orc_store_rows(const orc_config *c, uint8_t *cache, int layer, int seq,
                    int head, int X, int t0, int t1, const float *src);
 /* Dequantised row of position t as exact doubles [D]. */

@@ -182,6 +182,7 @@ class Workload:
     seed: int = 0
     protected: Optional[np.ndarray] = None  # flat (layer*Hkv + head) ids kept bf16
     rotate_k: bool = False  # coded K rows stored Walsh-Hadamard rotated
+    k_per_channel: bool = False  # K codes grouped per channel over token blocks
 
     @property
     def group_ratio(self) -> int:

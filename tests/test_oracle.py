@@ -738,3 +738,206 @@ def test_rotated_decode_closed_forms(orc):
     assert np.allclose(out, vhat.mean(0), atol=1e-12)
     out, _ = orc.decode_one(cfg, cache, 0, 0, 0, 1, qb, 0.125)
     assert np.allclose(out, vhat[0], atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Per-channel K groups with a bf16 residual window (nuiw.github.io
+# "VLM_KV_Quantization" section 4: K is stored after RoPE and is the more
+# sensitive side; grouping K along tokens per channel follows its channel
+# structure).  Expected bytes and values below are rebuilt from the sources
+# column by column with orc.quantize_group, independently of the oracle's
+# layout code.
+
+
+def _pc_cfg(orc, kbits, vbits, g=32, D=64, caps=(80, 40), vb=(3, 0), ve=(72, 32), L=1,
+            Hkv=1, Hq=2):
+    return orc.Config(L, len(caps), Hq, Hkv, D, g, list(caps), list(vb), list(ve),
+                      kbits, vbits, k_per_channel=True)
+
+
+def _pack_row(codes, bits):
+    D = codes.size
+    row = np.zeros(D * bits // 8, dtype=np.uint8)
+    for d in range(D):
+        bit = d * bits
+        row[bit // 8] |= np.uint8(int(codes[d]) << (bit % 8))
+    return row
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_per_channel_bytes_rebuilt_column_wise(orc, bits):
+    g, D = 32, 64
+    cfg = _pc_cfg(orc, [bits], [4])
+    rng = np.random.default_rng(bits)
+    caps, vb, ve = (80, 40), (3, 0), (72, 32)
+    src = {(s, X): rng.standard_normal((caps[s], D)).astype(np.float32) * (1 + 3 * X)
+           for s in range(2) for X in (0, 1)}
+    cache = orc.new_cache(cfg)
+    for (s, X), x in src.items():
+        orc.store_rows(cfg, cache, 0, s, 0, X, 0, caps[s], x)
+    # coded spans: seq 0 [3, 67) (two blocks, residual 67..71), seq 1 [0, 32)
+    assert [orc.coded_end(cfg, 0), orc.coded_end(cfg, 1)] == [67, 32]
+    vis, meta, txt = orc.plane_offsets(cfg, 0, 0, 0)
+    rb = D * bits // 8
+    vrow = 0
+    for s, qe in ((0, 67), (1, 32)):
+        for blk in range((qe - vb[s]) // g):
+            t0 = vb[s] + blk * g
+            rows = np.zeros((g, D), dtype=np.uint8)
+            mt = np.zeros(D * 2, dtype=np.uint16)
+            for d in range(D):
+                codes, s16, m16 = orc.quantize_group(src[(s, 0)][t0:t0 + g, d], bits)
+                rows[:, d] = codes
+                mt[2 * d], mt[2 * d + 1] = s16, m16
+            for i in range(g):
+                r = vrow + blk * g + i
+                assert np.array_equal(cache[vis + r * rb:vis + (r + 1) * rb], _pack_row(rows[i], bits))
+            b0 = meta + ((vrow + blk * g) // g) * D * 4
+            assert cache[b0:b0 + 4 * D].tobytes() == mt.tobytes()
+        vrow += qe - vb[s]
+    # the residual window of seq 0 is stored bf16 in the text plane, after
+    # the three text rows before the span (TXT rows 3..7 for positions 67..71)
+    for t in range(67, 72):
+        r = t - 64
+        got = cache[txt + r * 2 * D:txt + (r + 1) * 2 * D].view(np.uint16)
+        assert np.array_equal(got, synth.f32_to_bf16_bits(src[(0, 0)][t]))
+
+
+def test_per_channel_lossless_grid_and_error_bound(orc):
+    g, D = 32, 64
+    rng = np.random.default_rng(3)
+    for bits in (2, 4, 8):
+        n = (1 << bits) - 1
+        cfg = _pc_cfg(orc, [bits], [bits], caps=(32,), vb=(0,), ve=(32,))
+        # channel d on the grid mn_d + k sc_d, every code 0..n used somewhere
+        mn = np.array([orc.f16_value(orc.f16_round_down(v)) for v in rng.uniform(-4, 4, D)])
+        sc = 2.0 ** rng.integers(-6, 0, D)
+        k = rng.integers(0, n + 1, (g, D))
+        k[0], k[1] = 0, n
+        x = (mn[None, :] + k * sc[None, :]).astype(np.float32)
+        assert np.array_equal(x.astype(np.float64), mn[None, :] + k * sc[None, :])
+        cache = orc.new_cache(cfg)
+        orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, 32, x)
+        for t in (0, 7, 31):
+            assert np.array_equal(orc.load_row(cfg, cache, 0, 0, 0, 0, t), x[t].astype(np.float64))
+        # random block: every element within its channel's scale * (1/2 + 2^-14)
+        y = (rng.standard_normal((32, D)) * rng.uniform(0.1, 5, D)).astype(np.float32)
+        orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, 32, y)
+        _, meta, _ = orc.plane_offsets(cfg, 0, 0, 0)
+        s16 = cache[meta:meta + 4 * D].view(np.uint16)[0::2]
+        scale = np.array([orc.f16_value(int(h)) for h in s16])
+        rec = np.stack([orc.load_row(cfg, cache, 0, 0, 0, 0, t) for t in range(32)])
+        assert np.all(np.abs(rec - y) <= scale[None, :] * (0.5 + 2.0 ** -14))
+
+
+def test_per_channel_counts_and_block_cutting_stores(orc):
+    """Residual positions are text rows: they are never coded, and the coded
+    count is whole blocks only.  A store that would cut a block is refused."""
+    cfg = _pc_cfg(orc, [4], [2], g=32, caps=(80, 40), vb=(3, 0), ve=(72, 32))
+    info = orc.cache_info(cfg)
+    assert info["quantized_values"] == (64 + 32) * 64 * 2
+    assert info["bf16_text_bytes"] == 2 * (120 - 96) * 128
+    cache = orc.new_cache(cfg)
+    x = np.ones((80, 64), np.float32)
+    with pytest.raises(ValueError):
+        orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, 40, x[:40])   # cuts [35, 67)
+    with pytest.raises(ValueError):
+        orc.store_rows(cfg, cache, 0, 0, 0, 0, 10, 80, x[10:])  # cuts [3, 35)
+    orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, 35, x[:35])       # whole blocks: fine
+    orc.store_rows(cfg, cache, 0, 0, 0, 0, 67, 80, x[67:])      # residual and text only
+    orc.store_rows(cfg, cache, 0, 0, 0, 1, 10, 20, x[10:20])    # V rows are per token
+    # without per-channel grouping the same spans code every visual position
+    plain = orc.Config(1, 2, 2, 1, 64, 32, [80, 40], [3, 0], [72, 32], [4], [2])
+    assert orc.cache_info(plain)["quantized_values"] == (69 + 32) * 64 * 2
+
+
+def _pc_expected_row(orc, xs, t, bits, vb, qe, g, X):
+    """Reconstruction of position t of a sequence with sources xs [T, D]."""
+    if not (vb <= t < qe) or bits == 16:
+        return torch.from_numpy(xs[t]).to(torch.bfloat16).double().numpy()
+    if X == 1:  # per token along D
+        return np.concatenate([_dequant(*orc.quantize_group(xs[t, j:j + g], bits))
+                               for j in range(0, xs.shape[1], g)])
+    t0 = vb + (t - vb) // g * g
+    out = np.zeros(xs.shape[1])
+    for d in range(xs.shape[1]):
+        codes, s16, m16 = orc.quantize_group(xs[t0:t0 + g, d], bits)
+        out[d] = _dequant(codes[t - t0:t - t0 + 1], s16, m16)[0]
+    return out
+
+
+def test_per_channel_decode_multiseq_matches_sdpa(orc):
+    """decode_all on a 2-layer, 3-sequence per-channel cache (residual windows
+    of 5 and 0 tokens, one sequence without a visual span, mixed widths
+    including bf16 heads) against SDPA over rows rebuilt from the sources."""
+    g, D, L, Hkv, Hq = 32, 64, 2, 2, 4
+    caps, vb, ve = [80, 40, 20], [3, 0, 5], [72, 32, 5]
+    kbits, vbits = [4, 16, 2, 8], [2, 4, 16, 8]
+    cfg = orc.Config(L, 3, Hq, Hkv, D, g, caps, vb, ve, kbits, vbits, k_per_channel=True)
+    rng = np.random.default_rng(17)
+    src = {}
+    cache = orc.new_cache(cfg)
+    for l in range(L):
+        for s in range(3):
+            for h in range(Hkv):
+                for X in (0, 1):
+                    x = rng.standard_normal((caps[s], D)).astype(np.float32)
+                    x[:, 5] *= 8.0  # an outlier channel
+                    src[(l, s, h, X)] = x
+                    orc.store_rows(cfg, cache, l, s, h, X, 0, caps[s], x)
+    lens = np.array([80, 37, 20], dtype=np.int32)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((L, 3, Hq, D)).astype(np.float32))
+    got = orc.decode_all(cfg, cache, 0, L, lens, q, 0.125)
+    for l in range(L):
+        for s in range(3):
+            qe = orc.coded_end(cfg, s)
+            for i in range(Hq):
+                kv = i * Hkv // Hq
+                K = np.stack([_pc_expected_row(orc, src[(l, s, kv, 0)], t, kbits[l * Hkv + kv],
+                                               vb[s], qe, g, 0) for t in range(lens[s])])
+                V = np.stack([_pc_expected_row(orc, src[(l, s, kv, 1)], t, vbits[l * Hkv + kv],
+                                               vb[s], qe, g, 1) for t in range(lens[s])])
+                qh = synth.bf16_bits_to_f32(q[l, s, i]).astype(np.float64)
+                assert np.allclose(got[l, s, i], _attn_sdpa(qh, K, V, 0.125), rtol=1e-12,
+                                   atol=1e-13)
+
+
+def test_per_channel_uniform_keys_any_query(orc):
+    """Every K row of a block equal and fp16-exact: each channel is constant,
+    so its scale is 0 and every coded row reconstructs to the row itself, as
+    the bf16 text and residual rows do; all scores are equal and the output
+    is the mean of V for any query."""
+    D, g, T = 64, 32, 75
+    rng = np.random.default_rng(4)
+    k = (0.25 * rng.integers(-12, 12, size=D)).astype(np.float32)
+    cfg = orc.Config(1, 1, 2, 1, D, g, [T], [4], [70], [4], [2], k_per_channel=True)
+    cache = orc.new_cache(cfg)
+    orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, T, np.tile(k, (T, 1)))
+    orc.store_rows(cfg, cache, 0, 0, 0, 1, 0, T, rng.standard_normal((T, D)).astype(np.float32))
+    for t in (0, 4, 35, 67, 69, 74):
+        assert np.array_equal(orc.load_row(cfg, cache, 0, 0, 0, 0, t), k.astype(np.float64))
+    vhat = np.stack([orc.load_row(cfg, cache, 0, 0, 0, 1, t) for t in range(T)])
+    for i in range(2):
+        q = synth.f32_to_bf16_bits((3.0 * rng.standard_normal(D)).astype(np.float32))
+        out, _ = orc.decode_one(cfg, cache, 0, 0, i, T, q, 0.5)
+        assert np.allclose(out, vhat.mean(0), atol=1e-13)
+
+
+def test_per_channel_grouping_follows_channel_outliers(orc):
+    """Post-RoPE LLaVA-layer keys (four x8 channels before RoPE): grouping K
+    per channel over 64-token blocks reconstructs K better than grouping it
+    per token along the head dimension at the same width and group size
+    (the same bits per value), because each channel gets its own range."""
+    w = synth.llava_layer(seed=1, kbits=4, vbits=4)
+    x = synth.bf16_bits_to_f32(w.k_rows(0, 0, 0, 14, 14 + 1024))
+    for bits in (2, 4):
+        errs = []
+        for pc in (False, True):
+            cfg = orc.Config(1, 1, 1, 1, 128, 64, [1024], [0], [1024], [bits], [bits],
+                             k_per_channel=pc)
+            cache = orc.new_cache(cfg)
+            orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, 1024, x)
+            rec = np.stack([orc.load_row(cfg, cache, 0, 0, 0, 0, t) for t in range(1024)])
+            errs.append(np.linalg.norm(rec - x) / np.linalg.norm(x))
+        print(f"[per-channel] INT{bits}: per token {errs[0]:.4f}, per channel {errs[1]:.4f}")
+        assert errs[1] < errs[0]
