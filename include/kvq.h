@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 typedef enum {
   KVQ_OK = 0,
@@ -111,7 +111,28 @@ typedef struct {
   const uint8_t *v_bits;    /* [L*Hkv] V width per (layer, KV head)            */
   int32_t rotate_k;         /* nonzero: K rows stored as codes are rotated     */
                             /* before quantisation (see below); 0: none        */
+  int32_t k_per_channel;    /* nonzero: K codes grouped per channel over token */
+                            /* blocks, with a bf16 residual window (below)     */
 } kvq_config;
+
+/* Per-channel K groups (k_per_channel != 0).  nuiw.github.io
+ * "VLM_KV_Quantization" section 4: K is stored after RoPE, its error reaches
+ * every query head of the group, and it is the more sensitive side; its
+ * structure runs along channels.  With this flag each channel's K values
+ * over a block of group_size consecutive visual tokens form one quantisation
+ * group (the same quantiser as above); V stays grouped per token along D.
+ * Sequence s's visual span is coded in whole blocks from vis_begin[s]: the
+ * coded span is [vis_begin, vis_begin + floor((vis_end - vis_begin) / g) g).
+ * The tail that does not fill a block (the newest visual tokens, fewer than
+ * g) is a residual window stored bf16 as text, for K and V alike: every rule
+ * of the layout that names vis_end uses the end of the coded span instead.
+ * A K META row then belongs to a block, not a token: VIS row r's (scale,
+ * min) pairs are META row r / g, which holds D pairs, pair d for channel d.
+ * The plane sizes are the same as with per-token groups.  kvq_quantize must
+ * store whole blocks: a call whose positions cut a block of the coded span
+ * apart returns KVQ_ERR_SHAPE.  Not combinable with rotate_k, and decoding
+ * needs the matrix-core kernel's shapes (Hq / Hkv * D / g <= 16); otherwise
+ * KVQ_ERR_UNSUPPORTED. */
 
 /* K rotation (rotate_k != 0).  gist.science 2604.02570 (WSVD, section 2-C)
  * rotates vectors ahead of quantisation to remove per-channel outliers; the

@@ -47,7 +47,16 @@ kvq_status check_config(const kvq_config* c) {
     total += c->capacity[s];
   }
   if (total >= (int64_t(1) << 31)) return KVQ_ERR_UNSUPPORTED;  // row indices are 32-bit
+  if (c->k_per_channel && c->rotate_k) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
+}
+
+// End of the coded part of sequence s's visual span: all of it with per-token
+// groups; whole g-token blocks from vis_begin with per-channel K (the tail is
+// the bf16 residual window).
+int coded_end(const kvq_config* c, int s) {
+  const int vb = c->vis_begin[s], ve = c->vis_end[s], g = c->group_size;
+  return c->k_per_channel ? vb + (ve - vb) / g * g : ve;
 }
 
 // Plane geometry of a validated config.
@@ -63,7 +72,7 @@ struct Layout {
         D(c->head_dim), g(c->group_size), G(c->num_q_heads / c->num_kv_heads),
         vrow0(c->batch), trow0(c->batch), vis_off(size_t(c->num_layers) * c->num_kv_heads * 2) {
     for (int s = 0; s < B; ++s) {
-      const int64_t nv = c->vis_end[s] - c->vis_begin[s];
+      const int64_t nv = coded_end(c, s) - c->vis_begin[s];
       vrow0[s] = Rvis;
       trow0[s] = Rtxt;
       Rvis += nv;
@@ -470,6 +479,20 @@ kvq_status quantize_rows(const kvq_config* cfg, void* cache, int32_t layer_begin
     if (tok0[i] < 0) return KVQ_ERR_SHAPE;
     if (int64_t(tok0[i]) + n_tok > cfg->capacity[s]) return KVQ_ERR_RANGE;
   }
+  // per-channel K: the stored positions must not cut a block of the coded span
+  std::vector<int> kb0(num_seqs, 0), kbn(num_seqs, 0);
+  if (cfg->k_per_channel) {
+    const int g = cfg->group_size;
+    for (int i = 0; i < num_seqs; ++i) {
+      const int s = seq_ids[i], vb = cfg->vis_begin[s], qe = coded_end(cfg, s);
+      const int lo = std::max(tok0[i], vb), hi = std::min(tok0[i] + n_tok, qe);
+      if (lo < hi) {
+        if ((lo - vb) % g || (hi - vb) % g) return KVQ_ERR_SHAPE;
+        kb0[i] = (lo - vb) / g;
+        kbn[i] = (hi - lo) / g;
+      }
+    }
+  }
   Layout lay(cfg);
   if (lay.info.total_bytes / 256 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
 
@@ -501,15 +524,24 @@ kvq_status quantize_rows(const kvq_config* cfg, void* cache, int32_t layer_begin
           a.bits[i][X] = uint8_t(bits_of(cfg, l, h, X));
         }
       }
+      a.k_per_channel = cfg->k_per_channel != 0;
+      int max_blocks = 0;
       for (int i = 0; i < ns_l; ++i) {
         const int s = seq_ids[s0 + i];
         a.vb[i] = cfg->vis_begin[s];
-        a.ve[i] = cfg->vis_end[s];
+        a.ve[i] = coded_end(cfg, s);
         a.vrow0[i] = int32_t(lay.vrow0[s]);
         a.trow0[i] = int32_t(lay.trow0[s]);
         a.tok0[i] = tok0[s0 + i];
+        a.kblk0[i] = kb0[s0 + i];
+        a.kblkn[i] = kbn[s0 + i];
+        max_blocks = std::max(max_blocks, kbn[s0 + i]);
       }
       if (launch_quantize(a, nlh_l, ns_l, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return KVQ_ERR_HIP;
+      if (a.k_per_channel &&
+          launch_quantize_kblocks(a, nlh_l, ns_l, max_blocks, static_cast<hipStream_t>(stream)) !=
+              hipSuccess)
         return KVQ_ERR_HIP;
     }
   }
@@ -571,8 +603,16 @@ static kvq_status decode_prologue(const kvq_config* cfg, int32_t layer_begin, in
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
   *use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
-  // the general kernel has no rotated-query path
-  if (cfg->rotate_k && !*use_mfma) return KVQ_ERR_UNSUPPORTED;
+  // the general kernel has no rotated-query or per-channel path
+  if ((cfg->rotate_k || cfg->k_per_channel) && !*use_mfma) return KVQ_ERR_UNSUPPORTED;
+  if (cfg->k_per_channel) {
+    // per-channel K runs on the staged path (coded K with coded V), and its
+    // 32-token steps must fall on the block grid: fixed chunks in multiples
+    // of 256 tokens (eight waves of whole steps)
+    if (chunk_tokens % 256) return KVQ_ERR_UNSUPPORTED;
+    for (int i = layer_begin * cfg->num_kv_heads; i < (layer_begin + num_layers) * cfg->num_kv_heads; ++i)
+      if (cfg->k_bits[i] < 16 && cfg->v_bits[i] == 16) return KVQ_ERR_UNSUPPORTED;
+  }
   *plan = cached_plan(cfg, layer_begin, num_layers, chunk_tokens, *use_mfma);
   return KVQ_OK;
 }
@@ -619,13 +659,14 @@ static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_
     a.B = cfg->batch;
     a.chunk = plan.chunk;
     a.rotate_k = cfg->rotate_k != 0;
+    a.k_per_channel = cfg->k_per_channel != 0;
     a.max_chunks = plan.max_chunks;
     a.seq_off = L.s0;
     a.n_seq = L.ns;
     for (int i = 0; i < L.ns; ++i) {
       const int s = L.s0 + i;
       a.vb[i] = cfg->vis_begin[s];
-      a.ve[i] = cfg->vis_end[s];
+      a.ve[i] = coded_end(cfg, s);
       a.cap[i] = cfg->capacity[s];
       a.vrow0[i] = int32_t(lay.vrow0[s]);
       a.trow0[i] = int32_t(lay.trow0[s]);

@@ -266,6 +266,7 @@ struct Ctx {
   uint8_t* stage;          // this wave's LDS stage (BigLds::kStage bytes)
   float qscale;
   int G;
+  int64_t kmeta_bytes;     // size of the K META plane (per-channel block loads)
   bool rotate_k;           // coded K rows are stored Walsh-Hadamard rotated
   int lane, n, jq;         // lane, column (l % 16), quarter (l / 16)
 };
@@ -347,6 +348,67 @@ __device__ inline float build_q(const Ctx& c, const float (&qv)[D / 4], u32x4 (&
   qs += __shfl_xor(qs, 16);
   qs += __shfl_xor(qs, 32);
   return qs * 5.9604644775390625e-08f;  // * 2^-24, exact
+}
+
+// Q' of one per-channel K block: the block's META row (D (scale, min) fp16
+// pairs, pair d for channel d) at pairs, in LDS.  The channel scale goes into
+// the query operand and the min into one constant per column:
+//   q.k^ = sum_d q_d (s_d c_d + m_d) = sum_d (q_d s_d) c_d + sum_d q_d m_d.
+// The operand is q_d s_d 2^4 / w (the 2^4 keeps small products out of the
+// binary16 subnormals), so products with the codes come out in units of
+// 2^-20; the returned constant of the lane's column (head, group), summed over
+// its four quarters, is in the same units.  q_d s_d needs up to 19
+// significant bits (bf16 times fp16), more than binary16 holds, so it is
+// carried as a binary16 pair hi + lo (qop, qlo): two products per code, error
+// about 2^-22 relative, where one binary16 operand alone (2^-12) cost the
+// LLaVA-shaped layer 1.5e-3 of relative L2 error in the output.
+template <int D, int NG, int KB>
+__device__ inline float build_q_pc(const Ctx& c, const uint32_t* pairs, u32x4 (&qop)[D / 32],
+                                   u32x4 (&qlo)[D / 32]) {
+  constexpr int g = D / NG;
+  const int gj = c.n % NG;
+  const bool live = c.n < c.G * NG;
+  const int c0 = c.jq * (D / 4);
+  float mt = 0.0f;
+  // k-steps 2i and 2i + 1 cover quarter offsets [16 i, 16 i + 16): read
+  // those 16 query values and (scale, min) pairs, then fill both k-steps
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    uint32_t qw[8], sm[16];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const u32x4 w = c.qq[2 * i + k];
+      qw[4 * k] = w[0]; qw[4 * k + 1] = w[1]; qw[4 * k + 2] = w[2]; qw[4 * k + 3] = w[3];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 w4 = reinterpret_cast<const uint4*>(pairs + c0 + 16 * i)[k];
+      sm[4 * k] = w4.x; sm[4 * k + 1] = w4.y; sm[4 * k + 2] = w4.z; sm[4 * k + 3] = w4.w;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int s = 2 * i + s2;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float v2[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int off = kslot_off<D, KB>(s, 2 * e2 + hf), o16 = off - 16 * i;
+          const float w = kslot_w<D, KB>(s, 2 * e2 + hf);
+          const bool in = live && (c0 + off) / g == gj;
+          const float q = bf16f((qw[o16 >> 1] >> (16 * (o16 & 1))) & 0xFFFFu);
+          mt += in ? q * f16hi(sm[o16]) : 0.0f;
+          v2[hf] = in ? q * f16lo(sm[o16]) * (16.0f / w) : 0.0f;  // w: power of two
+        }
+        qop[s][e2] = pack_f16(v2[0], v2[1]);
+        // the remainders are exact in fp32 (v minus its binary16 rounding)
+        qlo[s][e2] = pack_f16(v2[0] - f16lo(qop[s][e2]), v2[1] - f16hi(qop[s][e2]));
+      }
+    }
+  }
+  mt += __shfl_xor(mt, 16);
+  mt += __shfl_xor(mt, 32);
+  return mt * 9.5367431640625e-07f;  // * 2^-20, exact
 }
 
 template <int NBYTES>
@@ -480,10 +542,11 @@ __device__ inline void finish_step(WaveState<D>& ws, const Step<D, KB, VB>& st,
 
 // q.k, softmax and p.v of one 32-token step of which the first rows_left
 // (1..32, wave-uniform) rows are real.  vsel: see v_pair_selector.
-template <int D, int NG, int KB, int VB>
+template <int D, int NG, int KB, int VB, bool PC = false>
 __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D, KB, VB>& st,
                                     const u32x4 (&qop)[D / 32], float qsr, float c24,
-                                    int rows_left, uint32_t vsel) {
+                                    int rows_left, uint32_t vsel,
+                                    const u32x4 (*qlo)[D / 32] = nullptr) {
   constexpr int KS = D / 32;
   constexpr int NB = D / 16;
   f32x4 acc[2];
@@ -494,12 +557,15 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
     for (int s = 0; s < KS; ++s) {
       const u32x4 a = k_operand<D, KB>(st.k[tau], s);
       acc[tau] = KB == 16 ? mfma_bf16(a, qop[s], acc[tau]) : mfma_f16(a, qop[s], acc[tau]);
+      if constexpr (PC) acc[tau] = mfma_f16(a, (*qlo)[s], acc[tau]);
     }
   }
   // scaled scores v: score (log2 units) = v * cs.  Quantised K: v = sc * acc +
   // mn * qsr with acc in units of 2^-24 (see build_q), so cs = 2^24 * qscale
-  // and qsr = 2^-24 * sum(q over the group); bf16 K: v = acc, cs = qscale.
-  const float cs = KB < 16 ? c24 : c.qscale;
+  // and qsr = 2^-24 * sum(q over the group); per-channel K: v = acc + qsr
+  // in units of 2^-20 (see build_q_pc), cs = 2^20 * qscale; bf16 K: v = acc,
+  // cs = qscale.
+  const float cs = PC ? c24 * 0.0625f : KB < 16 ? c24 : c.qscale;
   float sc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -507,7 +573,9 @@ __device__ inline void compute_step(const Ctx& c, WaveState<D>& ws, const Step<D
     float part;
     // (mn * qsr as an fma with a zero addend: the same single rounding, in
     // one mixed-precision instruction that reads mn as f16)
-    if constexpr (KB < 16)
+    if constexpr (PC)
+      part = a + qsr;
+    else if constexpr (KB < 16)
       part = __builtin_fmaf(f16lo(st.km[e]), a, __builtin_fmaf(f16hi(st.km[e]), qsr, 0.0f));
     else part = a;
     if constexpr (NG >= 2) part += dpp_xor1(part);
@@ -573,10 +641,15 @@ template <int D, int NG, int KB, int VB>
 struct Stage {
   static constexpr int KR = Fmt<D, KB>::kRowBytes, VR = Fmt<D, VB>::kRowBytes, MR = NG * 4;
   static constexpr int KP = KR / 2, VP = VR / 2, MP = MR / 2;  // bytes per lane per tile
-  static constexpr int kOffKM = 32 * KR, kOffV = kOffKM + 32 * MR, kOffVM = kOffV + 32 * VR;
+  // The K meta region holds either the step's 32 META rows (per-token
+  // groups) or its block's META row of D (scale, min) pairs (per-channel K,
+  // D / 16 bytes per lane).
+  static constexpr int PCP = D / 16;
+  static constexpr int KMB = 32 * MR > 4 * D ? 32 * MR : 4 * D;
+  static constexpr int kOffKM = 32 * KR, kOffV = kOffKM + KMB, kOffVM = kOffV + 32 * VR;
   static constexpr int kBytes = kOffVM + 32 * MR;
   uint32_t k[KP / 4];
-  uint32_t km[(MP + 3) / 4];
+  uint32_t km[((MP > PCP ? MP : PCP) + 3) / 4];
   uint32_t v[VP / 4];
   uint32_t vm[(MP + 3) / 4];
 };
@@ -653,14 +726,18 @@ __device__ inline void tile_put(uint8_t* lds, int lane, const uint32_t* in) {
   }
 }
 
-// Lane share of every plane's tile of step `step` (wave-uniform).
-template <int D, int NG, int KB, int VB>
+// Lane share of every plane's tile of step `step` (wave-uniform).  PC: the
+// K meta is the META row of the step's block, at byte kmblk of the plane.
+template <int D, int NG, int KB, int VB, bool PC>
 __device__ inline void stage_load(const SegPlanes& pl, int step, int rows, int lane,
-                                  Stage<D, NG, KB, VB>& st) {
+                                  Stage<D, NG, KB, VB>& st, uint32_t kmblk) {
   using S = Stage<D, NG, KB, VB>;
   const uint32_t r0 = uint32_t(step) * 32u;
   tile_load<S::KR, S::KP>(pl.k, r0 * S::KR, rows, lane, st.k);
-  tile_load<S::MR, S::MP>(pl.km, r0 * S::MR, rows, lane, st.km);
+  if constexpr (PC)
+    buf_load<S::PCP>(pl.km, uint32_t(lane) * S::PCP, kmblk, st.km);
+  else
+    tile_load<S::MR, S::MP>(pl.km, r0 * S::MR, rows, lane, st.km);
   tile_load<S::VR, S::VP>(pl.v, r0 * S::VR, rows, lane, st.v);
   tile_load<S::MR, S::MP>(pl.vm, r0 * S::MR, rows, lane, st.vm);
 }
@@ -669,19 +746,22 @@ __device__ inline void stage_load(const SegPlanes& pl, int step, int rows, int l
 // lane's LDS accesses across another's: wave barriers order the previous
 // step's reads before these writes, and these writes before the next reads
 // (LDS executes one wave's instructions in order).
-template <int D, int NG, int KB, int VB>
+template <int D, int NG, int KB, int VB, bool PC>
 __device__ inline void stage_put(uint8_t* lds, int lane, const Stage<D, NG, KB, VB>& st) {
   using S = Stage<D, NG, KB, VB>;
   __builtin_amdgcn_wave_barrier();
   tile_put<S::KP>(lds, lane, st.k);
-  tile_put<S::MP>(lds + S::kOffKM, lane, st.km);
+  if constexpr (PC)
+    store_bytes<S::PCP>(lds + S::kOffKM + lane * S::PCP, st.km);
+  else
+    tile_put<S::MP>(lds + S::kOffKM, lane, st.km);
   tile_put<S::VP>(lds + S::kOffV, lane, st.v);
   tile_put<S::MP>(lds + S::kOffVM, lane, st.vm);
   __builtin_amdgcn_wave_barrier();
 }
 
 // Operand gather from the LDS stage into the layout compute_step expects.
-template <int D, int NG, int KB, int VB>
+template <int D, int NG, int KB, int VB, bool PC>
 __device__ inline void stage_get(const uint8_t* lds, const Ctx& c, Step<D, KB, VB>& st) {
   using S = Stage<D, NG, KB, VB>;
   constexpr int KQ = S::KR / 4, VBY = Fmt<D, VB>::kVBytes;
@@ -692,7 +772,8 @@ __device__ inline void stage_get(const uint8_t* lds, const Ctx& c, Step<D, KB, V
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int r = 16 * (e >> 2) + 4 * c.jq + (e & 3);
-    st.km[e] = *reinterpret_cast<const uint32_t*>(lds + S::kOffKM + r * S::MR + gj * 4);
+    if constexpr (!PC)
+      st.km[e] = *reinterpret_cast<const uint32_t*>(lds + S::kOffKM + r * S::MR + gj * 4);
     st.vm[e] = *reinterpret_cast<const uint32_t*>(lds + S::kOffVM + r * S::MR + gj * 4);
     if constexpr (VBY <= 2)  // the aligned dword holding the slice; see v_pair_selector
       st.v[e][0] = *reinterpret_cast<const uint32_t*>(lds + S::kOffV + r * S::VR +
@@ -726,8 +807,11 @@ __device__ inline int claim_step(const Claim& cl, int lane, int base) {
 // One segment [x0, x1) of rows of one format, rows starting at plane row
 // row0 (K and V share row numbering).  KB/VB: stored widths (16 = bf16).
 // With cl.ctr set the wave processes the steps it claims of the segment,
-// otherwise all of it.
-template <int D, int NG, int KB, int VB>
+// otherwise all of it.  PC: coded K rows with per-channel groups over
+// g-token blocks; every step then lies inside one block (row0 is a multiple
+// of 32 from the block grid, see wave_range), whose META row is staged with
+// the step and folded into Q' whenever the block changes.
+template <int D, int NG, int KB, int VB, bool PC = false>
 __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int64_t row0,
                             bool visual, const Claim& cl, const u32x4 (&qreg)[D / 32],
                             bool& q_pending) {
@@ -748,19 +832,25 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   // before Q' is built so the latencies overlap.  bf16 steps carry 64 VGPRs
   // of data and load straight into operands.
   constexpr bool kStaged = KB < 16 && VB < 16;
+  static_assert(!PC || kStaged, "per-channel K runs on the staged path");
   using S = Stage<D, NG, KB, VB>;
+  constexpr int g = D / NG;
+  // per-channel K: byte offset of the META row of the block of step st
+  auto kmblk = [&](int st) {
+    return PC ? uint32_t((row0 + 32 * int64_t(st)) / g) * uint32_t(4 * D) : 0u;
+  };
   constexpr int kDepth = S::KP + S::VP <= 48 ? KVQ_RING_DEPTH : 2;
-  S g[kDepth];
+  S g_[kDepth];
   SegPlanes pl;
   if constexpr (kStaged) {
     pl.k = make_rsrc(kp, int64_t(rows) * KR);
-    pl.km = make_rsrc(kmp, int64_t(rows) * MR);
+    pl.km = PC ? make_rsrc(c.kmeta, c.kmeta_bytes) : make_rsrc(kmp, int64_t(rows) * MR);
     pl.v = make_rsrc(vp, int64_t(rows) * VR);
     pl.vm = make_rsrc(vmp, int64_t(rows) * MR);
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {  // this wave's first steps (taken statically)
       const int st = min(cl.ctr ? cl.wave * kDepth + k : k, nsteps - 1);
-      stage_load<D, NG, KB, VB>(pl, st, rows_in(st), c.lane, g[k]);
+      stage_load<D, NG, KB, VB, PC>(pl, st, rows_in(st), c.lane, g_[k], kmblk(st));
     }
   }
 
@@ -797,8 +887,9 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
   // the query in the operand layout; coded K rows of a rotated cache meet
   // the rotated query
   u32x4 qop[D / 32];
-  float qsr;
-  {
+  u32x4 qlo[PC ? D / 32 : 1];  // per-channel K: low binary16 parts of Q'
+  float qsr = 0.0f;
+  if constexpr (!PC) {  // per-channel K builds Q' per block, in the loop
     float qv[D / 4];
     unpack_quarter<D>(c, qv);
     if (KB < 16 && visual && c.rotate_k) rotate_quarter<D>(c, qv);
@@ -821,18 +912,32 @@ __device__ void run_segment(const Ctx& c, WaveState<D>& ws, int x0, int x1, int6
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) slot[k] = cl.ctr ? cl.wave * kDepth + k : k;
     int pend = cl.ctr ? claim_step(cl, c.lane, base) : kDepth;
+    int qblk = -1;  // per-channel K: the block Q' was built for
     while (slot[0] < nsteps) {
 #pragma unroll
       for (int k = 0; k < kDepth; ++k) {
         const int cur = slot[k];
-        stage_put<D, NG, KB, VB>(c.stage, c.lane, g[k]);
+        stage_put<D, NG, KB, VB, PC>(c.stage, c.lane, g_[k]);
         const int nxt = __builtin_amdgcn_readlane(pend, 0);
         pend = cl.ctr ? claim_step(cl, c.lane, base) : nxt + 1;
         const int la = min(nxt, nsteps - 1);
-        stage_load<D, NG, KB, VB>(pl, la, rows_in(la), c.lane, g[k]);
+        stage_load<D, NG, KB, VB, PC>(pl, la, rows_in(la), c.lane, g_[k], kmblk(la));
         slot[k] = nxt;
-        stage_get<D, NG, KB, VB>(c.stage, c, sa);
-        if (cur < nsteps) compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(cur), vsel);
+        stage_get<D, NG, KB, VB, PC>(c.stage, c, sa);
+        if constexpr (PC) {
+          const int blk = int((row0 + 32 * int64_t(cur)) / g);
+          if (cur < nsteps && blk != qblk) {  // wave-uniform
+            qsr = build_q_pc<D, NG, KB>(
+                c, reinterpret_cast<const uint32_t*>(c.stage + S::kOffKM), qop, qlo);
+            qblk = blk;
+          }
+        }
+        if (cur < nsteps) {
+          if constexpr (PC)
+            compute_step<D, NG, KB, VB, true>(c, ws, sa, qop, qsr, c24, rows_in(cur), vsel, &qlo);
+          else
+            compute_step<D, NG, KB, VB>(c, ws, sa, qop, qsr, c24, rows_in(cur), vsel);
+        }
       }
     }
   } else {
@@ -880,7 +985,7 @@ struct Launch {
   int32_t* ws_arrive;
   int64_t Rvis;
   float qscale;
-  int G, Hkv, Hq, B, chunk, max_chunks, seq_off, n_lh, n_seq, rotate_k;
+  int G, Hkv, Hq, B, chunk, max_chunks, seq_off, n_lh, n_seq, rotate_k, k_per_channel;
 };
 // A device pointer read from LDS, made wave-uniform and marked as a global
 // (not generic) address, so accesses through it compile to global or buffer
@@ -918,6 +1023,7 @@ __device__ inline Launch launch_scalars(const DecodeArgs& t) {
   L.n_lh = uniform_int(t.n_lh);
   L.n_seq = uniform_int(t.n_seq);
   L.rotate_k = uniform_int(t.rotate_k);
+  L.k_per_channel = uniform_int(t.k_per_channel);
   return L;
 }
 
@@ -1161,7 +1267,7 @@ __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int
 // their results are combined in LDS into one partial, or into the output when
 // the piece is the whole entry.  The piece that completes an entry's arrival
 // count merges the entry's partials.
-template <int D, int NG, int KB, int VB>
+template <int D, int NG, int KB, int VB, bool PC>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NB = D / 16;
   constexpr int g = D / NG;
@@ -1315,6 +1421,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   c.qscale = La.qscale;
   c.G = G;
   c.rotate_k = La.rotate_k != 0;
+  c.kmeta_bytes = La.Rvis * (D / g) * 4;
+  const bool kpc = PC;  // launches of per-channel caches use the PC instances
   c.lane = lane;
   c.n = lane & 15;
   c.jq = lane >> 4;
@@ -1329,12 +1437,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   if (active) {
     // static split: chunk mode gives each workgroup (8 units) one chunk,
     // the balanced mode deals the entry's steps over its ne units
+    const int vb = __builtin_amdgcn_readlane(vbl, sl);
+    // per-channel K: shift the step grid so steps of the coded span start on
+    // multiples of 32 from vis_begin (each then lies inside one block)
+    const int phase = kpc ? (32 - vb % 32) % 32 : 0;
     int wa, wb;
     if (La.chunk > 0)
-      wave_range(u / kWaves, u % kWaves, ne / kWaves, len, La.chunk, kWaves, wa, wb);
+      wave_range(u / kWaves, u % kWaves, ne / kWaves, len, La.chunk, kWaves, wa, wb, phase);
     else
-      wave_range(u, 0, ne, len, 0, 1, wa, wb);
-    const int vb = __builtin_amdgcn_readlane(vbl, sl);
+      wave_range(u, 0, ne, len, 0, 1, wa, wb, phase);
     const int ve = __builtin_amdgcn_readlane(vel, sl);
     const int64_t vrow0 = __builtin_amdgcn_readlane(vr0l, sl);
     const int64_t trow0 = __builtin_amdgcn_readlane(tr0l, sl);
@@ -1346,8 +1457,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // imbalance.
     const bool dyn = La.chunk == 0;
     int ga, gb, gt;
-    wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt);
-    wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb);
+    wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt, phase);
+    wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb, phase);
     const Claim cl{&lds_claim[p_lo], pos - p_lo, p_hi - p_lo};
     // segments: text prefix [0, vb), text suffix [ve, cap), visual [vb, ve);
     // kept as a loop so each row path is emitted once
@@ -1365,10 +1476,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       if (x0 >= x1) continue;
       const int64_t row0 = vis ? vrow0 + (x0 - vb) : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
       const Claim use = vis && dyn ? cl : Claim{nullptr, 0, 1};
-      if (vis && quant_vis)
-        run_segment<D, NG, KB, VB>(c, st, x0, x1, row0, true, use, qreg, q_pending);
-      else  // text rows, or bf16 visual rows of a protected head
+      if (vis && quant_vis) {
+        run_segment<D, NG, KB, VB, PC>(c, st, x0, x1, row0, true, use, qreg, q_pending);
+      } else {  // text rows, or bf16 visual rows of a protected head
         run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, vis, use, qreg, q_pending);
+      }
     }
   }
 
@@ -1544,8 +1656,16 @@ bool mfma_supported(int D, int g, int G) {
 // parallel (-DKVQ_MFMA_PART=0..4, one object each); without the macro one
 // object holds every part.
 #define KVQ_LAUNCH(DD, NN, K, V)                                                           \
-  if (kb == K && vb == V) {                                                                \
-    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN, K, V>), grid, dim3(kThreads), 0, stream, a); \
+  if (kb == K && vb == V && !pc) {                                                         \
+    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN, K, V, false>), grid, dim3(kThreads), 0, \
+                       stream, a);                                                         \
+    return hipGetLastError();                                                              \
+  }
+// per-channel K instances exist for coded K with coded V only
+#define KVQ_LAUNCH_PC(DD, NN, K, V)                                                        \
+  if (kb == K && vb == V && pc) {                                                          \
+    hipLaunchKernelGGL((decode_mfma_kernel<DD, NN, K, V, true>), grid, dim3(kThreads), 0,  \
+                       stream, a);                                                         \
     return hipGetLastError();                                                              \
   }
 #define KVQ_PART_FN(DD, NN)                                                                 \
@@ -1553,12 +1673,16 @@ bool mfma_supported(int D, int g, int G) {
                                             hipStream_t stream) {                           \
     /* one workgroup per kWaves units (waves) of the compact unit list */                \
     const dim3 grid((a.nxcum[a.n_seq] * a.mcum[a.n_lh] + kWaves - 1) / kWaves, 1, 1);      \
+    const bool pc = a.k_per_channel != 0;                                                   \
     KVQ_LAUNCH(DD, NN, 2, 2) KVQ_LAUNCH(DD, NN, 2, 4) KVQ_LAUNCH(DD, NN, 2, 8)              \
     KVQ_LAUNCH(DD, NN, 2, 16) KVQ_LAUNCH(DD, NN, 4, 2) KVQ_LAUNCH(DD, NN, 4, 4)             \
     KVQ_LAUNCH(DD, NN, 4, 8) KVQ_LAUNCH(DD, NN, 4, 16) KVQ_LAUNCH(DD, NN, 8, 2)             \
     KVQ_LAUNCH(DD, NN, 8, 4) KVQ_LAUNCH(DD, NN, 8, 8) KVQ_LAUNCH(DD, NN, 8, 16)             \
     KVQ_LAUNCH(DD, NN, 16, 2) KVQ_LAUNCH(DD, NN, 16, 4) KVQ_LAUNCH(DD, NN, 16, 8)           \
     KVQ_LAUNCH(DD, NN, 16, 16)                                                              \
+    KVQ_LAUNCH_PC(DD, NN, 2, 2) KVQ_LAUNCH_PC(DD, NN, 2, 4) KVQ_LAUNCH_PC(DD, NN, 2, 8)     \
+    KVQ_LAUNCH_PC(DD, NN, 4, 2) KVQ_LAUNCH_PC(DD, NN, 4, 4) KVQ_LAUNCH_PC(DD, NN, 4, 8)     \
+    KVQ_LAUNCH_PC(DD, NN, 8, 2) KVQ_LAUNCH_PC(DD, NN, 8, 4) KVQ_LAUNCH_PC(DD, NN, 8, 8)     \
     return hipErrorInvalidValue;                                                            \
   }
 #if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 0
@@ -1577,6 +1701,7 @@ KVQ_PART_FN(64, 1)
 KVQ_PART_FN(64, 2)
 #endif
 #undef KVQ_PART_FN
+#undef KVQ_LAUNCH_PC
 #undef KVQ_LAUNCH
 
 #if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 0

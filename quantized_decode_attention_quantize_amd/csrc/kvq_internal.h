@@ -46,6 +46,9 @@ struct QuantizeArgs {
   int32_t vb[kMaxSeq], ve[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
   int32_t tok0[kMaxSeq];  // per sequence: first position stored (the call's
                           // n_tok rows start there)
+  int32_t k_per_channel;  // K codes grouped per channel over g-token blocks
+  int32_t kblk0[kMaxSeq];  // per sequence: first per-channel K block stored
+  int32_t kblkn[kMaxSeq];  // per sequence: number of such blocks (0: none)
 };
 static_assert(sizeof(QuantizeArgs) <= 4096, "QuantizeArgs must fit the kernel argument limit");
 
@@ -79,7 +82,7 @@ struct DecodeArgs {
   int32_t nx[kMaxSeq];      // per sequence
   int32_t nxcum[kMaxSeq + 1];  // per sequence: sum of nx over earlier sequences
   int32_t rotate_k;         // coded K rows are stored rotated: rotate q for them
-  int32_t pad_[1];          // the split kernels copy this block in 16-byte pieces
+  int32_t k_per_channel;    // coded K rows carry per-channel (scale, min) per block
 };
 static_assert(sizeof(DecodeArgs) % 16 == 0, "DecodeArgs is copied in 16-byte pieces");
 static_assert(sizeof(DecodeArgs) <= 4096, "DecodeArgs must fit the kernel argument limit");
@@ -114,8 +117,15 @@ __device__ inline void decode_block(const DecodeArgs& a, int b, int n_seq, int& 
 // [x * chunk, (x + 1) * chunk) and its waves split that evenly.  chunk == 0
 // (balanced): the len tokens form ceil(len / 32) steps dealt into
 // waves * nxs nearly equal wave units.
+//
+// phase (0..31) shifts the grid: ranges are cut from [0, len + phase) and then
+// moved down by phase (the first range loses phase tokens), so position p
+// starts a 32-token step when p + phase is a multiple of 32.  Per-channel K
+// uses phase = (32 - vis_begin % 32) % 32, which starts every step of the
+// coded span inside one g-token block.
 __host__ __device__ inline void wave_range(int x, int w, int nxs, int len, int chunk,
-                                           int waves, int& a, int& b) {
+                                           int waves, int& a, int& b, int phase = 0) {
+  const int n = len + phase;
   if (chunk > 0) {
     const int per = chunk / waves;
     a = x * chunk + w * per;
@@ -123,12 +133,14 @@ __host__ __device__ inline void wave_range(int x, int w, int nxs, int len, int c
     const int e = x * chunk + chunk;
     if (b > e) b = e;
   } else {
-    const int64_t nblk = (len + 31) / 32, U = int64_t(waves) * nxs, u = int64_t(x) * waves + w;
+    const int64_t nblk = (n + 31) / 32, U = int64_t(waves) * nxs, u = int64_t(x) * waves + w;
     a = int(32 * (u * nblk / U));
     b = int(32 * ((u + 1) * nblk / U));
   }
-  if (a > len) a = len;
-  if (b > len) b = len;
+  if (a > n) a = n;
+  if (b > n) b = n;
+  a = a < phase ? 0 : a - phase;
+  b = b < phase ? 0 : b - phase;
 }
 
 // Index of a split partial: (layer-local l, global seq s, head h, chunk x).
@@ -139,6 +151,10 @@ __host__ __device__ inline int64_t partial_index(int l, int s, int h, int x, int
 
 hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
                            hipStream_t stream);
+// Per-channel K blocks of a launch (k_per_channel): one workgroup per
+// (layer-head slot, sequence, block); max_blocks = the largest kblkn.
+hipError_t launch_quantize_kblocks(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
+                                   int max_blocks, hipStream_t stream);
 hipError_t launch_decode_simple(const DecodeArgs& a, int n_seq_launch, hipStream_t stream);
 // Matrix-core split kernel: needs (D / g) * G <= 16 (one 16-row MFMA tile of
 // (head, group) columns); writes the final output itself when max_chunks == 1.

@@ -223,6 +223,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   const bool visual = t >= vb && t < ve;
   uint8_t* vis = a.cache + uint64_t(a.base256[lh][X]) * 256u;
 
+  // Coded K rows of a per-channel cache are written by quantize_kblock_kernel.
+  if (visual && bits < 16 && X == 0 && a.k_per_channel) return;
   // Every lane of a row takes the same branch; groups never straddle rows.
   if (visual && bits < 16) {
     uint32_t meta;
@@ -273,7 +275,77 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   }
 }
 
+// Per-channel K (k_per_channel): one workgroup per (slot, sequence, block of
+// g coded tokens), one thread per channel d.  The channel's g values over the
+// block form one group, quantised with the same arithmetic as a per-token
+// group (the exact IEEE divide for every code); the thread writes the
+// channel's (scale, min) pair into the block's META row, and the codes go
+// through LDS so that every token row is packed and stored as whole words.
+template <int D>
+__global__ __launch_bounds__(D) void quantize_kblock_kernel(QuantizeArgs a) {
+  __shared__ uint8_t codes[128][D];  // [token in block][channel]
+  const int d = threadIdx.x;
+  const int lh = blockIdx.z, sl = blockIdx.y, j = blockIdx.x;
+  const int g = a.g, bits = a.bits[lh][0];
+  if (j >= a.kblkn[sl] || bits >= 16) return;  // workgroup-uniform (bf16 K: no blocks)
+  const int blk = a.kblk0[sl] + j;            // block within the sequence
+  const int t0 = a.vb[sl] + blk * g;          // its first position
+  const int r0 = t0 - a.tok0[sl];             // its first source row
+  const int glh = a.lh_off + lh;
+  const int l_local = glh / a.Hkv, h = glh % a.Hkv;
+  const int64_t src_row0 =
+      ((int64_t(l_local) * a.num_seqs_total + (a.seq_off + sl)) * a.Hkv + h) * a.n_tok + r0;
+  auto load = [&](int i) {
+    const int64_t e = (src_row0 + i) * D + d;
+    return a.src_bf16 ? bf16_float(static_cast<const uint16_t*>(a.k_src)[e])
+                      : static_cast<const float*>(a.k_src)[e];
+  };
+  float lo = load(0), hi = lo;
+  for (int i = 1; i < g; ++i) {
+    const float x = load(i);
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  const uint16_t mn16 = f16_round_down(lo);
+  const float mn = f16_float(mn16);
+  const float n = float((1 << bits) - 1);
+  const float range = hi - mn;
+  const bool live = range != 0.0f;
+  const uint16_t sc16 = live ? f16_round_up(range / n) : uint16_t(0);
+  const float sc = f16_float(sc16);
+  for (int i = 0; i < g; ++i) {
+    const float c = live ? __builtin_rintf((load(i) - mn) / sc) : 0.0f;
+    codes[i][d] = uint8_t(__builtin_amdgcn_fmed3f(c, 0.0f, n));
+  }
+  uint8_t* vis = a.cache + uint64_t(a.base256[lh][0]) * 256u;
+  const int64_t row0 = a.vrow0[sl] + int64_t(blk) * g;  // VIS row of t0 (a multiple of g)
+  uint8_t* meta = vis + meta_plane_offset(a.Rvis, D, bits) + (row0 / g) * int64_t(4 * D);
+  reinterpret_cast<uint32_t*>(meta)[d] = uint32_t(sc16) | (uint32_t(mn16) << 16);
+  __syncthreads();
+  // row i of the block: D * bits / 32 words, word k holds channels
+  // [k * 32 / bits, (k + 1) * 32 / bits), channel c at bit (c * bits) % 32
+  const int wpr = D * bits / 32, per = 32 / bits;
+  uint32_t* rows = reinterpret_cast<uint32_t*>(vis + row0 * int64_t(D * bits / 8));
+  for (int w = d; w < g * wpr; w += D) {
+    const int i = w / wpr, k = w % wpr;
+    uint32_t word = 0u;
+    for (int e = 0; e < per; ++e) word |= uint32_t(codes[i][k * per + e]) << (e * bits);
+    rows[w] = word;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_kblocks(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
+                                   int max_blocks, hipStream_t stream) {
+  if (max_blocks <= 0) return hipSuccess;
+  const dim3 grid(max_blocks, n_seq_launch, n_lh_launch);
+  if (a.D == 128)
+    hipLaunchKernelGGL(quantize_kblock_kernel<128>, grid, dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL(quantize_kblock_kernel<64>, grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
                            hipStream_t stream) {

@@ -44,7 +44,8 @@ class _Cfg(C.Structure):
                 ("head_dim", C.c_int32), ("group_size", C.c_int32),
                 ("capacity", C.POINTER(C.c_int32)), ("vis_begin", C.POINTER(C.c_int32)),
                 ("vis_end", C.POINTER(C.c_int32)), ("k_bits", C.POINTER(C.c_uint8)),
-                ("v_bits", C.POINTER(C.c_uint8)), ("rotate_k", C.c_int32)]
+                ("v_bits", C.POINTER(C.c_uint8)), ("rotate_k", C.c_int32),
+                ("k_per_channel", C.c_int32)]
 
 
 class _Info(C.Structure):
@@ -96,7 +97,7 @@ class Config:
 
     def __init__(self, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, group_size: int, capacity, vis_begin, vis_end, k_bits, v_bits,
-                 rotate_k: bool = False):
+                 rotate_k: bool = False, k_per_channel: bool = False):
         self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
         self.vis_begin = np.ascontiguousarray(vis_begin, dtype=np.int32)
         self.vis_end = np.ascontiguousarray(vis_end, dtype=np.int32)
@@ -106,19 +107,22 @@ class Config:
         self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
         self.head_dim, self.group_size = head_dim, group_size
         self.rotate_k = bool(rotate_k)
+        self.k_per_channel = bool(k_per_channel)
         self.c = _Cfg(num_layers, batch, num_q_heads, num_kv_heads, head_dim, group_size,
                       self.capacity.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_begin.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_end.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.k_bits.ctypes.data_as(C.POINTER(C.c_uint8)),
-                      self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)), int(self.rotate_k))
+                      self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)), int(self.rotate_k),
+                      int(self.k_per_channel))
 
     @classmethod
     def from_workload(cls, w) -> "Config":
         a = w.config_arrays()
         return cls(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                    w.group_size, a["capacity"], a["vis_begin"], a["vis_end"],
-                   a["k_bits"], a["v_bits"], getattr(w, "rotate_k", False))
+                   a["k_bits"], a["v_bits"], getattr(w, "rotate_k", False),
+                   getattr(w, "k_per_channel", False))
 
     @property
     def ref(self):

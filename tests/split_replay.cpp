@@ -15,6 +15,9 @@
 namespace kvq {
 static std::vector<DecodeArgs> g_mfma;
 hipError_t launch_quantize(const QuantizeArgs&, int, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_quantize_kblocks(const QuantizeArgs&, int, int, int, hipStream_t) {
+  return hipSuccess;
+}
 hipError_t launch_decode_simple(const DecodeArgs&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode_merge(const DecodeArgs&, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode_mfma(const DecodeArgs& a, int, int, hipStream_t) {
@@ -39,8 +42,10 @@ static void unit_of(const DecodeArgs& a, int b, int& slot, int& sl, int& x) {
 
 static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int g,
                     std::vector<int> cap, std::vector<int> vb, std::vector<int> ve,
-                    std::vector<uint8_t> kb, std::vector<uint8_t> vbits, int chunk) {
+                    std::vector<uint8_t> kb, std::vector<uint8_t> vbits, int chunk,
+                    int per_channel = 0) {
   kvq_config c{};
+  c.k_per_channel = per_channel;
   c.num_layers = L; c.batch = B; c.num_q_heads = Hq; c.num_kv_heads = Hkv;
   c.head_dim = D; c.group_size = g;
   c.capacity = cap.data(); c.vis_begin = vb.data(); c.vis_end = ve.data();
@@ -87,14 +92,16 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
         if (cv.empty()) cv.assign(len, 0);
         seen_px[key].insert(px);
         npieces[key] = pn;
+        const int vbeg = a.vb[sl], vend = a.ve[sl];  // vend: end of the coded span
+        const int phase = a.k_per_channel ? (32 - vbeg % 32) % 32 : 0;
         int wa, wb, ga, gb, gt;
         if (a.chunk > 0)
-          wave_range(u / kMfmaWaves, u % kMfmaWaves, ne / kMfmaWaves, len, a.chunk, kMfmaWaves, wa, wb);
+          wave_range(u / kMfmaWaves, u % kMfmaWaves, ne / kMfmaWaves, len, a.chunk, kMfmaWaves,
+                     wa, wb, phase);
         else
-          wave_range(u, 0, ne, len, 0, 1, wa, wb);
-        wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt);
-        wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb);
-        const int vbeg = a.vb[sl], vend = a.ve[sl];
+          wave_range(u, 0, ne, len, 0, 1, wa, wb, phase);
+        wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt, phase);
+        wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb, phase);
         for (int seg = 0; seg < 3; ++seg) {
           const bool vis = seg == 2;
           int x0, x1;
@@ -105,6 +112,12 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
           } else {
             x0 = seg == 0 ? wa : vis ? std::max(wa, vbeg) : std::max(wa, vend);
             x1 = seg == 0 ? std::min(wb, vbeg) : vis ? std::min(wb, vend) : wb;
+          }
+          // per-channel K: a visual segment's 32-token steps start on the
+          // block grid, so none straddles two blocks of g tokens
+          if (vis && a.k_per_channel && x0 < x1 && (x0 - vbeg) % 32) {
+            if (bad < 8) printf("%s: visual segment at %d off the step grid\n", name, x0 - vbeg);
+            ++bad;
           }
           for (int tk = x0; tk < x1; ++tk) cv[tk]++;
         }
@@ -161,6 +174,15 @@ int main() {
   for (int len : {1, 31, 33, 200})
     bad += run_case("short", 2, 2, 8, 2, 128, 64, {len, len}, {0, 0}, {len, len}, {4, 4, 4, 16},
                     {2, 2, 2, 16}, 0);
+  // per-channel K (coded spans in whole blocks, steps on the block grid)
+  for (int ch : {0, 256, 1024})
+    bad += run_case("pc 28x4 6288", 28, 1, 28, 4, 128, 64, {6288}, {14}, {6287},
+                    std::vector<uint8_t>(112, 4), std::vector<uint8_t>(112, 2), ch, 1);
+  bad += run_case("pc 4 x 32769", 1, 4, 32, 8, 128, 64, {32769, 32769, 32769, 32769},
+                  {64, 7, 100, 0}, {32768, 32000, 30000, 31999}, std::vector<uint8_t>(8, 4),
+                  std::vector<uint8_t>(8, 2), 0, 1);
+  bad += run_case("pc mixed", 2, 3, 8, 2, 64, 32, {400, 1, 970}, {3, 0, 10}, {350, 1, 970},
+                  {4, 8, 8, 2}, {2, 4, 8, 4}, 0, 1);
   printf(bad ? "FAIL\n" : "ok\n");
   return bad != 0;
 }

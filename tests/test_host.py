@@ -67,8 +67,10 @@ def _configs():
         ve = np.array([rng.integers(b, c + 1) for b, c in zip(vb, cap)])
         kb = rng.choice([2, 4, 8, 16], L_ * Hkv)
         vbits = rng.choice([2, 4, 8, 16], L_ * Hkv)
-        yield synth.Workload(f"rand{i}", L_, B, Hkv * 2, Hkv, D, g, list(cap), list(vb),
-                             list(ve), list(cap), kb.astype(np.uint8), vbits.astype(np.uint8))
+        w = synth.Workload(f"rand{i}", L_, B, Hkv * 2, Hkv, D, g, list(cap), list(vb),
+                           list(ve), list(cap), kb.astype(np.uint8), vbits.astype(np.uint8))
+        w.k_per_channel = bool(i % 2)  # per-channel K: coded spans in whole blocks
+        yield w
 
 
 def test_cache_bytes_matches_oracle(L, orc):
@@ -300,3 +302,33 @@ def test_binding_rejects_wrong_dtypes_and_sizes(L):
             kvq.kvq_quantize_ragged(cfg, cache, 0, 1, [0, 1], [0, 3], 8, kk, vv)
     with pytest.raises(ValueError, match="device tensor"):
         kvq.kvq_quantize(cfg, cache, 0, 1, [0, 1], 0, 8, k, k)
+
+
+def test_per_channel_validation(L):
+    """Per-channel K: a store that cuts a block of the coded span, rotation on
+    top, fixed chunks off the 256-token grid, coded K with bf16 V, and shapes
+    of the general kernel are refused before any launch."""
+    cfg = _cfg(capacity=[256], vis_begin=[16], vis_end=[250])  # coded [16, 240), g 32
+    pc = kvq.Config(**{**dict(num_layers=1, batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                              group_size=32, capacity=[256], vis_begin=[16], vis_end=[250],
+                              k_bits=[4], v_bits=[2]), "k_per_channel": True})
+    assert _quant(L, pc, t0=0, t1=40) == kvq.KVQ_ERR_SHAPE      # cuts [16, 48)
+    assert _quant(L, pc, t0=20, t1=48) == kvq.KVQ_ERR_SHAPE     # starts inside a block
+    assert _quant(L, pc, t0=16, t1=48, cache=None) == kvq.KVQ_ERR_NULL  # whole block: passes shape
+    assert _quant(L, pc, t0=240, t1=256, cache=None) == kvq.KVQ_ERR_NULL  # residual + text
+    info = kvq.kvq_cache_bytes(pc)
+    assert info["quantized_values"] == (240 - 16) * 64 * 2
+    assert _dec(L, pc, chunk=64)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    assert _dec(L, pc, chunk=256, ws=None)[0] == kvq.KVQ_OK
+    assert _dec(L, pc, ws=None)[0] == kvq.KVQ_OK
+    bf16v = kvq.Config(1, 1, 4, 1, 64, 32, [256], [16], [250], [4], [16], k_per_channel=True)
+    assert _dec(L, bf16v, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    rot = kvq.Config(1, 1, 4, 1, 64, 32, [256], [16], [250], [4], [2], rotate_k=True,
+                     k_per_channel=True)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_cache_bytes(rot)
+    assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
+    general = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
+                         k_per_channel=True)  # 28 (head, group) columns
+    assert _dec(L, general, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    del cfg
