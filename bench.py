@@ -317,6 +317,9 @@ def main():
         del refs, wsr
         extras["rotated_k_decode"] = rotated_decode(torch, kvq, w, args, dev, T, lens_d, q, out,
                                                     to_dev, dec_avg, alg)
+        if args.chunk == 0:
+            extras["per_channel_k_decode"] = per_channel_decode(torch, kvq, w, args, dev, T, lens_d,
+                                                                q, out, to_dev, dec_avg)
         extras["quantize_block"] = quantize_block(torch, kvq, synth, dev, stream, args)
         extras["copy_ceiling"] = copy_ceiling(torch, dev, stream)
         extras["read_stream_ceiling"] = read_stream_ceiling(torch, dev, args, alg, dec_avg)
@@ -394,6 +397,43 @@ def rotated_decode(torch, kvq, w, args, dev, T, lens_d, q, out, to_dev, dec_avg,
     return {"us": round(ms * 1e3, 2), "algorithmic_bytes": alg,
             "gbps": round(alg / (ms * 1e-3) / 1e9, 1),
             "vs_unrotated": round(ms / dec_avg, 3)}
+
+
+def per_channel_decode(torch, kvq, w, args, dev, T, lens_d, q, out, to_dev, dec_avg):
+    """The same workload with K grouped per channel over blocks of group_size
+    visual tokens (k_per_channel): the coded span shrinks to whole blocks and
+    the residual tail is bf16, so its algorithmic bytes are counted anew."""
+    import copy
+    pw = copy.deepcopy(w)
+    pw.k_per_channel = True
+    cfg = kvq.Config.from_workload(pw)
+    nbytes = kvq.kvq_cache_bytes(cfg)["total_bytes"]
+    R = max(2, math.ceil(args.replica_mb * 2 ** 20 / nbytes))
+    c0 = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    for l in range(pw.num_layers):
+        for s in range(pw.batch):
+            k = to_dev(pw.sources(l, [s], 0, T[s] + 1, "k")[None])
+            v = to_dev(pw.sources(l, [s], 0, T[s] + 1, "v")[None])
+            kvq.kvq_quantize(cfg, c0, l, 1, [s], 0, T[s] + 1, k, v)
+    caches = [c0] + [c0.clone() for _ in range(R - 1)]
+    ws = torch.zeros(kvq.workspace_bytes(cfg, pw.num_layers, args.chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def dec(i):
+        kvq.kvq_decode_attention(cfg, caches[i % R], 0, pw.num_layers, lens_d, q, out,
+                                 pw.sm_scale, args.chunk, ws)
+
+    for i in range(args.warmup):
+        dec(i)
+    ms = timed(torch, args, dec)
+    g = pw.group_size
+    coded = [pw.vis_begin[s] + (pw.vis_end[s] - pw.vis_begin[s]) // g * g for s in range(pw.batch)]
+    bw = copy.deepcopy(pw)
+    bw.vis_end = coded  # the residual window counts as bf16 rows
+    alg = algorithmic_bytes(bw, [t + 1 for t in T])
+    del caches, ws
+    return {"us": round(ms * 1e3, 2), "algorithmic_bytes": alg,
+            "gbps": round(alg / (ms * 1e-3) / 1e9, 1), "vs_per_token": round(ms / dec_avg, 3)}
 
 
 def _bf16_like(w):

@@ -41,7 +41,10 @@ class _Cfg(C.Structure):
                 ("capacity", C.POINTER(C.c_int32)), ("vis_begin", C.POINTER(C.c_int32)),
                 ("vis_end", C.POINTER(C.c_int32)), ("k_bits", C.POINTER(C.c_uint8)),
                 ("v_bits", C.POINTER(C.c_uint8)), ("rotate_k", C.c_int32),
-                ("k_per_channel", C.c_int32)]
+                ("k_per_channel", C.c_int32),
+                ("bf16_range_offsets", C.POINTER(C.c_int32)),
+                ("bf16_range_begin", C.POINTER(C.c_int32)),
+                ("bf16_range_end", C.POINTER(C.c_int32))]
 
 
 class _Info(C.Structure):
@@ -79,6 +82,7 @@ def lib():
         L.orc_row_of.argtypes = [C.POINTER(_Cfg), C.c_int, C.c_int, C.POINTER(C.c_int),
                                  C.POINTER(C.c_int64)]
         L.orc_coded_end.argtypes = [C.POINTER(_Cfg), C.c_int]
+        L.orc_is_coded.argtypes = [C.POINTER(_Cfg), C.c_int, C.c_int]
         L.orc_store_rows.argtypes = [C.POINTER(_Cfg), P, C.c_int, C.c_int, C.c_int,
                                      C.c_int, C.c_int, C.c_int, P]
         L.orc_load_row.argtypes = [C.POINTER(_Cfg), P, C.c_int, C.c_int, C.c_int,
@@ -110,19 +114,31 @@ class Config:
 
     def __init__(self, num_layers, batch, num_q_heads, num_kv_heads, head_dim,
                  group_size, capacity, vis_begin, vis_end, k_bits, v_bits, rotate_k=False,
-                 k_per_channel=False):
+                 k_per_channel=False, bf16_ranges=None):
+        """bf16_ranges: None, or one list of (begin, end) position pairs per
+        sequence (ranges inside the visual span stored bf16)."""
         self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
         self.vis_begin = np.ascontiguousarray(vis_begin, dtype=np.int32)
         self.vis_end = np.ascontiguousarray(vis_end, dtype=np.int32)
         self.k_bits = np.ascontiguousarray(k_bits, dtype=np.uint8)
         self.v_bits = np.ascontiguousarray(v_bits, dtype=np.uint8)
+        if bf16_ranges is not None:
+            offs = np.cumsum([0] + [len(r) for r in bf16_ranges]).astype(np.int32)
+            flat = [p for r in bf16_ranges for p in r]
+            self.rng_off = np.ascontiguousarray(offs)
+            self.rng_b = np.ascontiguousarray([p[0] for p in flat] or [0], dtype=np.int32)
+            self.rng_e = np.ascontiguousarray([p[1] for p in flat] or [0], dtype=np.int32)
+            ptrs = [a.ctypes.data_as(C.POINTER(C.c_int32))
+                    for a in (self.rng_off, self.rng_b, self.rng_e)]
+        else:
+            ptrs = [C.POINTER(C.c_int32)()] * 3
         self.c = _Cfg(num_layers, batch, num_q_heads, num_kv_heads, head_dim, group_size,
                       self.capacity.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_begin.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_end.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.k_bits.ctypes.data_as(C.POINTER(C.c_uint8)),
                       self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)), int(bool(rotate_k)),
-                      int(bool(k_per_channel)))
+                      int(bool(k_per_channel)), *ptrs)
 
     @classmethod
     def from_workload(cls, w) -> "Config":
@@ -130,7 +146,7 @@ class Config:
         return cls(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                    w.group_size, a["capacity"], a["vis_begin"], a["vis_end"],
                    a["k_bits"], a["v_bits"], getattr(w, "rotate_k", False),
-                   getattr(w, "k_per_channel", False))
+                   getattr(w, "k_per_channel", False), getattr(w, "bf16_ranges", None))
 
     @property
     def ref(self):
@@ -195,6 +211,10 @@ def plane_offsets(cfg: Config, layer: int, head: int, X: int):
 def coded_end(cfg: Config, seq: int) -> int:
     """End of the coded part of the visual span (see kvq_oracle.h)."""
     return int(lib().orc_coded_end(cfg.ref, seq))
+
+
+def is_coded(cfg: Config, seq: int, t: int) -> bool:
+    return bool(lib().orc_is_coded(cfg.ref, seq, t))
 
 
 def row_of(cfg: Config, seq: int, t: int):

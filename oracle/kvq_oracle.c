@@ -193,6 +193,21 @@ int orc_validate(const orc_config *c) {
   if (c->head_dim < 1 || c->group_size < 1 || c->head_dim % c->group_size) return 3;
   if (c->rotate_k && (c->head_dim & (c->head_dim - 1))) return 3; /* rotation: D = 2^k */
   if (c->rotate_k && c->k_per_channel) return 3; /* one grouping of rotated rows only */
+  if (c->bf16_range_offsets) {
+    const int32_t *o = c->bf16_range_offsets;
+    if (!c->bf16_range_begin || !c->bf16_range_end || o[0] != 0) return 5;
+    for (s = 0; s < c->batch; s++) {
+      int k, prev = c->vis_begin[s];
+      if (o[s + 1] < o[s]) return 5;
+      if (o[s + 1] > o[s] && c->k_per_channel) return 5; /* blocks must be contiguous */
+      for (k = o[s]; k < o[s + 1]; k++) {
+        if (c->bf16_range_begin[k] < prev || c->bf16_range_end[k] <= c->bf16_range_begin[k] ||
+            c->bf16_range_end[k] > c->vis_end[s])
+          return 5;
+        prev = c->bf16_range_end[k];
+      }
+    }
+  }
   for (i = 0; i < c->num_layers * c->num_kv_heads; i++) {
     if (!bits_ok(c->k_bits[i]) || !bits_ok(c->v_bits[i])) return 3;
     if ((c->head_dim * c->k_bits[i]) % 8 || (c->head_dim * c->v_bits[i]) % 8) return 3;
@@ -210,11 +225,29 @@ int orc_coded_end(const orc_config *c, int seq) {
   return c->k_per_channel ? vb + (ve - vb) / g * g : ve;
 }
 
+/* Coded positions of sequence seq before position t: those of
+ * [vis_begin, min(t, coded end)) minus the parts of its bf16 ranges there. */
+static int64_t coded_before(const orc_config *c, int seq, int t) {
+  int vb = c->vis_begin[seq], qe = orc_coded_end(c, seq), k;
+  int hi = t < qe ? t : qe;
+  int64_t n = hi > vb ? hi - vb : 0;
+  if (c->bf16_range_offsets)
+    for (k = c->bf16_range_offsets[seq]; k < c->bf16_range_offsets[seq + 1]; k++) {
+      int b = c->bf16_range_begin[k], e = c->bf16_range_end[k] < hi ? c->bf16_range_end[k] : hi;
+      if (e > b) n -= e - b;
+    }
+  return n;
+}
+
+int orc_is_coded(const orc_config *c, int seq, int t) {
+  return coded_before(c, seq, t + 1) > coded_before(c, seq, t);
+}
+
 static void row_totals(const orc_config *c, uint64_t *rvis, uint64_t *rtxt) {
   uint64_t v = 0, all = 0;
   int s;
   for (s = 0; s < c->batch; s++) {
-    v += (uint64_t)(orc_coded_end(c, s) - c->vis_begin[s]);
+    v += (uint64_t)coded_before(c, s, c->capacity[s]);
     all += (uint64_t)c->capacity[s];
   }
   *rvis = v;
@@ -286,22 +319,21 @@ int orc_plane_offsets(const orc_config *c, int layer, int head, int X,
 }
 
 int orc_row_of(const orc_config *c, int seq, int t, int *plane, int64_t *row) {
-  int64_t vbase = 0, tbase = 0;
-  int s, vb, ve;
+  int64_t vbase = 0, tbase = 0, nc;
+  int s;
   if (seq < 0 || seq >= c->batch || t < 0 || t >= c->capacity[seq]) return 1;
   for (s = 0; s < seq; s++) {
-    int nv = orc_coded_end(c, s) - c->vis_begin[s];
+    int64_t nv = coded_before(c, s, c->capacity[s]);
     vbase += nv;
     tbase += c->capacity[s] - nv;
   }
-  vb = c->vis_begin[seq];
-  ve = orc_coded_end(c, seq);
-  if (t >= vb && t < ve) {
+  nc = coded_before(c, seq, t);
+  if (orc_is_coded(c, seq, t)) {
     *plane = 0;
-    *row = vbase + (t - vb);
+    *row = vbase + nc;
   } else {
     *plane = 2;
-    *row = tbase + (t < vb ? t : t - (ve - vb));
+    *row = tbase + (t - nc);
   }
   return 0;
 }

@@ -45,6 +45,16 @@ typedef struct {
   int32_t k_per_channel; /* nonzero: K codes are grouped per channel over
                             blocks of group_size consecutive visual tokens
                             (see orc_store_rows); V stays per token */
+  /* Optional (NULL: none).  Ranges of positions inside a sequence's visual
+   * span that are stored bf16 like text: sequence s owns ranges
+   * [bf16_range_begin[k], bf16_range_end[k]) for k in
+   * [bf16_range_offsets[s], bf16_range_offsets[s + 1]), each non-empty,
+   * inside [vis_begin, vis_end), sorted and disjoint.  A one-token range
+   * protects that token; a range between two images splits the span into
+   * two visual spans.  Not combinable with k_per_channel. */
+  const int32_t *bf16_range_offsets; /* [batch + 1] */
+  const int32_t *bf16_range_begin;
+  const int32_t *bf16_range_end;
 } orc_config;
 
 typedef struct {
@@ -92,9 +102,14 @@ int orc_plane_offsets(const orc_config *c, int layer, int head, int X,
  * does not fill a block (the newest visual tokens, a residual window of
  * fewer than group_size tokens) is stored bf16 like text, for K and V.     */
 int orc_coded_end(const orc_config *c, int seq);
+/* Is position t of sequence s coded (a VIS row when its head's width is
+ * below 16)?  Coded: vis_begin <= t < orc_coded_end and t in no bf16 range. */
+int orc_is_coded(const orc_config *c, int seq, int t);
 /* Where the row of position t of sequence s lives: plane 0 = VIS, 2 = TXT;
- * row index within that plane.  A position is in the VIS plane when
- * vis_begin <= t < orc_coded_end. */
+ * row index within that plane.  Coded positions take VIS rows in order,
+ * sequence after sequence; every other position takes TXT rows in order:
+ * VIS row = (coded positions of earlier sequences) + (coded positions of
+ * this sequence before t), TXT row likewise over the other positions. */
 int orc_row_of(const orc_config *c, int seq, int t, int *plane, int64_t *row);
 
 /* ---- store / load ---------------------------------------------------------- */

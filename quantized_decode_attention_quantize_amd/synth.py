@@ -183,6 +183,9 @@ class Workload:
     protected: Optional[np.ndarray] = None  # flat (layer*Hkv + head) ids kept bf16
     rotate_k: bool = False  # coded K rows stored Walsh-Hadamard rotated
     k_per_channel: bool = False  # K codes grouped per channel over token blocks
+    # per sequence, (begin, end) ranges inside the visual span stored bf16
+    # (protected tokens, or text between two images); None: none
+    bf16_ranges: Optional[List[List[Tuple[int, int]]]] = None
 
     @property
     def group_ratio(self) -> int:

@@ -941,3 +941,114 @@ def test_per_channel_grouping_follows_channel_outliers(orc):
             errs.append(np.linalg.norm(rec - x) / np.linalg.norm(x))
         print(f"[per-channel] INT{bits}: per token {errs[0]:.4f}, per channel {errs[1]:.4f}")
         assert errs[1] < errs[0]
+
+
+# --------------------------------------------------------------------------
+# bf16 ranges inside the visual span: token-level protection and several
+# visual spans per sequence (nuiw.github.io "VLM_KV_Quantization" section 1:
+# protecting important tokens in FP16 is the policy the study set aside;
+# section 2: the prompt interleaves text and visual blocks).
+
+
+def _rng_cfg(orc, kbits=(4,), vbits=(2,), D=64, g=32):
+    # seq 0: text 0-1 | image 2-4 | protected 5 | image 6-8 | text 9-11 |
+    #        image 12-14 | question 15-19 ; seq 1: first token protected
+    return orc.Config(1, 2, 2, 1, D, g, [20, 10], [2, 0], [15, 10], list(kbits), list(vbits),
+                      bf16_ranges=[[(5, 6), (9, 12)], [(0, 1)]])
+
+
+def test_bf16_ranges_row_mapping_by_hand(orc):
+    cfg = _rng_cfg(orc)
+    coded0 = [2, 3, 4, 6, 7, 8, 12, 13, 14]
+    text0 = [0, 1, 5, 9, 10, 11, 15, 16, 17, 18, 19]
+    for i, t in enumerate(coded0):
+        assert orc.row_of(cfg, 0, t) == (0, i)
+    for i, t in enumerate(text0):
+        assert orc.row_of(cfg, 0, t) == (2, i)
+    # seq 1 continues both planes after seq 0 (9 VIS rows, 11 TXT rows)
+    assert orc.row_of(cfg, 1, 0) == (2, 11)
+    for t in range(1, 10):
+        assert orc.row_of(cfg, 1, t) == (0, 9 + t - 1)
+    assert [orc.is_coded(cfg, 0, t) for t in range(20)] == [t in coded0 for t in range(20)]
+    info = orc.cache_info(cfg)
+    assert info["quantized_values"] == (9 + 9) * 64 * 2
+    assert info["bf16_text_bytes"] == (11 + 1) * 128 * 2
+
+
+def test_bf16_ranges_store_exact_and_decode_matches_sdpa(orc):
+    """Protected and in-between positions come back as their bf16 sources;
+    decode over the mixed rows equals SDPA over rows rebuilt by the
+    definition (coded: per-token groups of the pinned quantiser; others:
+    bf16), with the coded set computed here from the ranges."""
+    cfg = _rng_cfg(orc, kbits=(2,), vbits=(4,))
+    rng = np.random.default_rng(23)
+    spans = {0: (2, 15, [(5, 6), (9, 12)]), 1: (0, 10, [(0, 1)])}
+    src = {}
+    cache = orc.new_cache(cfg)
+    for s, cap in ((0, 20), (1, 10)):
+        for X in (0, 1):
+            x = rng.standard_normal((cap, 64)).astype(np.float32)
+            src[(s, X)] = x
+            orc.store_rows(cfg, cache, 0, s, 0, X, 0, cap, x)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((1, 2, 2, 64)).astype(np.float32))
+    lens = np.array([20, 10], np.int32)
+    got = orc.decode_all(cfg, cache, 0, 1, lens, q, 0.125)
+    for s in (0, 1):
+        vb, ve, ranges = spans[s]
+        coded = [vb <= t < ve and not any(b <= t < e for b, e in ranges) for t in range(lens[s])]
+        rows = {}
+        for X, bits in ((0, 2), (1, 4)):
+            rows[X] = np.stack([
+                np.concatenate([_dequant(*orc.quantize_group(src[(s, X)][t, j:j + 32], bits))
+                                for j in (0, 32)]) if coded[t]
+                else torch.from_numpy(src[(s, X)][t]).to(torch.bfloat16).double().numpy()
+                for t in range(lens[s])])
+            for t in range(lens[s]):
+                assert np.array_equal(orc.load_row(cfg, cache, 0, s, 0, X, t), rows[X][t])
+        for i in (0, 1):
+            qh = synth.bf16_bits_to_f32(q[0, s, i]).astype(np.float64)
+            assert np.allclose(got[0, s, i], _attn_sdpa(qh, rows[0], rows[1], 0.125),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_bf16_ranges_covering_the_span_is_textbook_attention(orc):
+    """Ranges covering the whole visual span leave nothing coded: the decode
+    is plain SDPA on bf16-rounded sources and the scores equal those of an
+    all-bf16 cache (KL 0)."""
+    w = synth.tiny()
+    cfg = orc.Config(1, 1, 4, 1, 64, 32, [256], [16], [256], [4], [4],
+                     bf16_ranges=[[(16, 100), (100, 256)]])
+    assert orc.cache_info(cfg)["quantized_values"] == 0
+    cache = orc.new_cache(cfg)
+    k = w.k_rows(0, 0, 0, 0, 256)
+    v = w.v_rows(0, 0, 0, 0, 256)
+    orc.store_rows(cfg, cache, 0, 0, 0, 0, 0, 256, k)
+    orc.store_rows(cfg, cache, 0, 0, 0, 1, 0, 256, v)
+    K = torch.from_numpy(k).to(torch.bfloat16).double().numpy()
+    V = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    q = w.q_bits(0)
+    for h in range(4):
+        out, _, sc = orc.decode_one(cfg, cache, 0, 0, h, 256, q[0, h], w.sm_scale, want_scores=True)
+        qh = synth.bf16_bits_to_f32(q[0, h]).astype(np.float64)
+        assert np.allclose(out, _attn_sdpa(qh, K, V, w.sm_scale), rtol=1e-12, atol=1e-13)
+        assert orc.kl_logits(w.sm_scale * (K @ qh), sc) == pytest.approx(0.0, abs=1e-14)
+
+
+@pytest.mark.parametrize("ranges", [
+    [[(5, 5)], []],            # empty
+    [[(9, 12), (5, 6)], []],   # unsorted
+    [[(5, 10), (9, 12)], []],  # overlapping
+    [[(1, 3)], []],            # starts before the span
+    [[(14, 16)], []],          # ends past the span
+])
+def test_bf16_ranges_rejected(orc, ranges):
+    cfg = orc.Config(1, 2, 2, 1, 64, 32, [20, 10], [2, 0], [15, 10], [4], [2], bf16_ranges=ranges)
+    with pytest.raises(ValueError):
+        orc.cache_info(cfg)
+
+
+def test_bf16_ranges_not_with_per_channel(orc):
+    cfg = orc.Config(1, 1, 2, 1, 64, 32, [100], [2], [98], [4], [2], k_per_channel=True,
+                     bf16_ranges=[[(40, 41)]])
+    with pytest.raises(ValueError):
+        orc.cache_info(cfg)
