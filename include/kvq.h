@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 
 typedef enum {
   KVQ_OK = 0,
@@ -113,7 +113,28 @@ typedef struct {
                             /* before quantisation (see below); 0: none        */
   int32_t k_per_channel;    /* nonzero: K codes grouped per channel over token */
                             /* blocks, with a bf16 residual window (below)     */
+  /* Optional bf16 ranges inside the visual spans (NULL: none; see below). */
+  const int32_t *bf16_range_offsets; /* [B + 1]                                */
+  const int32_t *bf16_range_begin;   /* [bf16_range_offsets[B]]                */
+  const int32_t *bf16_range_end;     /* [bf16_range_offsets[B]]                */
 } kvq_config;
+
+/* bf16 ranges (bf16_range_offsets != NULL).  nuiw.github.io
+ * "VLM_KV_Quantization" section 1 names keeping important tokens at full
+ * precision as a policy outside its study, and section 2 lays the prompt out
+ * as text and visual blocks.  Sequence s may list ranges
+ * [bf16_range_begin[k], bf16_range_end[k]) for k in [bf16_range_offsets[s],
+ * bf16_range_offsets[s + 1]): non-empty, inside [vis_begin[s], vis_end[s]),
+ * sorted and disjoint (bf16_range_offsets[0] == 0, non-decreasing).  Their
+ * positions are stored bf16 exactly like text.  A one-token range protects
+ * that token (a sink or a selected token); a range between two images makes
+ * one sequence hold two visual spans.  The layout generalises by counting:
+ * a position is coded when it lies in the visual span and in no range;
+ * coded positions take VIS (and META) rows in order and every other
+ * position takes TXT rows in order, sequence after sequence.  A sequence
+ * may have at most 36 ranges.  Sequences with ranges are decoded with a
+ * static split.  Malformed ranges return KVQ_ERR_SHAPE; ranges together
+ * with k_per_channel, or more than 36 in one sequence, KVQ_ERR_UNSUPPORTED. */
 
 /* Per-channel K groups (k_per_channel != 0).  nuiw.github.io
  * "VLM_KV_Quantization" section 4: K is stored after RoPE, its error reaches

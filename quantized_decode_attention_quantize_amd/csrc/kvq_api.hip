@@ -48,7 +48,31 @@ kvq_status check_config(const kvq_config* c) {
   }
   if (total >= (int64_t(1) << 31)) return KVQ_ERR_UNSUPPORTED;  // row indices are 32-bit
   if (c->k_per_channel && c->rotate_k) return KVQ_ERR_UNSUPPORTED;
+  if (c->bf16_range_offsets) {
+    const int32_t* o = c->bf16_range_offsets;
+    if (!c->bf16_range_begin || !c->bf16_range_end) return KVQ_ERR_NULL;
+    if (o[0] != 0) return KVQ_ERR_SHAPE;
+    for (int s = 0; s < c->batch; ++s) {
+      if (o[s + 1] < o[s]) return KVQ_ERR_SHAPE;
+      int prev = c->vis_begin[s];
+      for (int k = o[s]; k < o[s + 1]; ++k) {
+        const int b = c->bf16_range_begin[k], e = c->bf16_range_end[k];
+        if (b < prev || e <= b || e > c->vis_end[s]) return KVQ_ERR_SHAPE;
+        prev = e;
+      }
+      if (o[s + 1] > o[s] && c->k_per_channel) return KVQ_ERR_UNSUPPORTED;
+      if (o[s + 1] - o[s] > kMaxRangesD) return KVQ_ERR_UNSUPPORTED;
+    }
+  }
   return KVQ_OK;
+}
+
+// bf16 ranges of sequence s: [first, last) indices into the range arrays.
+int ranges_first(const kvq_config* c, int s) {
+  return c->bf16_range_offsets ? c->bf16_range_offsets[s] : 0;
+}
+int ranges_count(const kvq_config* c, int s) {
+  return c->bf16_range_offsets ? c->bf16_range_offsets[s + 1] - c->bf16_range_offsets[s] : 0;
 }
 
 // End of the coded part of sequence s's visual span: all of it with per-token
@@ -57,6 +81,34 @@ kvq_status check_config(const kvq_config* c) {
 int coded_end(const kvq_config* c, int s) {
   const int vb = c->vis_begin[s], ve = c->vis_end[s], g = c->group_size;
   return c->k_per_channel ? vb + (ve - vb) / g * g : ve;
+}
+
+// Coded positions of sequence s: its coded span minus its bf16 ranges.
+int64_t coded_count(const kvq_config* c, int s) {
+  int64_t n = coded_end(c, s) - c->vis_begin[s];
+  for (int k = ranges_first(c, s); k < ranges_first(c, s) + ranges_count(c, s); ++k)
+    n -= c->bf16_range_end[k] - c->bf16_range_begin[k];
+  return n;
+}
+
+// Consecutive sequence groups [s0, s0 + n) of at most kMaxSeq sequences
+// whose bf16 ranges fit a launch's table of `max_ranges`.
+std::vector<std::pair<int, int>> sequence_groups(const kvq_config* c, const int32_t* ids,
+                                                 int count, int max_ranges) {
+  std::vector<std::pair<int, int>> out;
+  int s0 = 0;
+  while (s0 < count) {
+    int n = 0, nr = 0;
+    while (s0 + n < count && n < kMaxSeq) {
+      const int r = ranges_count(c, ids ? ids[s0 + n] : s0 + n);
+      if (n > 0 && nr + r > max_ranges) break;
+      nr += r;
+      ++n;
+    }
+    out.emplace_back(s0, n);
+    s0 += n;
+  }
+  return out;
 }
 
 // Plane geometry of a validated config.
@@ -72,7 +124,7 @@ struct Layout {
         D(c->head_dim), g(c->group_size), G(c->num_q_heads / c->num_kv_heads),
         vrow0(c->batch), trow0(c->batch), vis_off(size_t(c->num_layers) * c->num_kv_heads * 2) {
     for (int s = 0; s < B; ++s) {
-      const int64_t nv = coded_end(c, s) - c->vis_begin[s];
+      const int64_t nv = coded_count(c, s);
       vrow0[s] = Rvis;
       trow0[s] = Rtxt;
       Rvis += nv;
@@ -324,8 +376,8 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
   const int64_t wave_slots = int64_t(kMfmaWaves) * device_cus();
   constexpr int kMinWaveRows = 64;  // fewer rows per wave only add merge work
   int64_t max_pieces = 1;
-  for (int s0 = 0; s0 < B; s0 += kMaxSeq) {
-    const int ns = std::min(kMaxSeq, B - s0);
+  for (const auto& grp : sequence_groups(c, nullptr, B, kMaxRangesD)) {
+    const int s0 = grp.first, ns = grp.second;
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       std::vector<int> sel;
       for (int i = 0; i < nlh; ++i)
@@ -408,6 +460,7 @@ std::shared_ptr<const DecodePlan> cached_plan(const kvq_config* c, int layer_beg
                               c->group_size};
   key.reserve(key.size() + c->batch + size_t(nl) * Hkv);
   for (int s = 0; s < c->batch; ++s) key.push_back(c->capacity[s]);
+  for (int s = 0; s < c->batch; ++s) key.push_back(ranges_count(c, s));  // launch grouping
   for (int i = layer_begin * Hkv; i < (layer_begin + nl) * Hkv; ++i)
     key.push_back(c->k_bits[i] * 32 + c->v_bits[i]);
   std::lock_guard<std::mutex> lock(mu);
@@ -497,10 +550,11 @@ kvq_status quantize_rows(const kvq_config* cfg, void* cache, int32_t layer_begin
   if (lay.info.total_bytes / 256 >= (uint64_t(1) << 32)) return KVQ_ERR_UNSUPPORTED;
 
   const int nlh = num_layers * cfg->num_kv_heads;
+  const auto groups = sequence_groups(cfg, seq_ids, num_seqs, kMaxRangesQ);
   for (int lh0 = 0; lh0 < nlh; lh0 += kMaxLH) {
     const int nlh_l = std::min(kMaxLH, nlh - lh0);
-    for (int s0 = 0; s0 < num_seqs; s0 += kMaxSeq) {
-      const int ns_l = std::min(kMaxSeq, num_seqs - s0);
+    for (const auto& grp : groups) {
+      const int s0 = grp.first, ns_l = grp.second;
       QuantizeArgs a;
       std::memset(&a, 0, sizeof(a));
       a.cache = static_cast<uint8_t*>(cache);
@@ -528,6 +582,11 @@ kvq_status quantize_rows(const kvq_config* cfg, void* cache, int32_t layer_begin
       int max_blocks = 0;
       for (int i = 0; i < ns_l; ++i) {
         const int s = seq_ids[s0 + i];
+        a.rng_first[i + 1] = a.rng_first[i] + ranges_count(cfg, s);
+        for (int k = 0; k < ranges_count(cfg, s); ++k) {
+          a.rng_b[a.rng_first[i] + k] = cfg->bf16_range_begin[ranges_first(cfg, s) + k];
+          a.rng_e[a.rng_first[i] + k] = cfg->bf16_range_end[ranges_first(cfg, s) + k];
+        }
         a.vb[i] = cfg->vis_begin[s];
         a.ve[i] = coded_end(cfg, s);
         a.vrow0[i] = int32_t(lay.vrow0[s]);
@@ -603,8 +662,10 @@ static kvq_status decode_prologue(const kvq_config* cfg, int32_t layer_begin, in
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
   *use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
-  // the general kernel has no rotated-query or per-channel path
-  if ((cfg->rotate_k || cfg->k_per_channel) && !*use_mfma) return KVQ_ERR_UNSUPPORTED;
+  // the general kernel has no rotated-query, per-channel or bf16-range path
+  const bool ranges = cfg->bf16_range_offsets && cfg->bf16_range_offsets[cfg->batch] > 0;
+  if ((cfg->rotate_k || cfg->k_per_channel || ranges) && !*use_mfma)
+    return KVQ_ERR_UNSUPPORTED;
   if (cfg->k_per_channel) {
     // per-channel K runs on the staged path (coded K with coded V), and its
     // 32-token steps must fall on the block grid: fixed chunks in multiples
@@ -670,8 +731,12 @@ static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_
       a.cap[i] = cfg->capacity[s];
       a.vrow0[i] = int32_t(lay.vrow0[s]);
       a.trow0[i] = int32_t(lay.trow0[s]);
-      a.nx[i] = L.nx[i];
       a.nxcum[i + 1] = a.nxcum[i] + L.nx[i];
+      a.rng_first[i + 1] = uint8_t(a.rng_first[i] + ranges_count(cfg, s));
+      for (int k = 0; k < ranges_count(cfg, s); ++k) {
+        a.rng_b[a.rng_first[i] + k] = cfg->bf16_range_begin[ranges_first(cfg, s) + k];
+        a.rng_e[a.rng_first[i] + k] = cfg->bf16_range_end[ranges_first(cfg, s) + k];
+      }
     }
     a.n_lh = int(L.glh.size());
     for (int i = 0; i < a.n_lh; ++i) {

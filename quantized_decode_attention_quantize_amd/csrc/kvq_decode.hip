@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_simple_kernel(DecodeArgs a) {
   const int lh = a.lh_glob[slot];
   const int l_local = lh / a.Hkv, h = lh % a.Hkv;
   const int sl = blockIdx.z, s = a.seq_off + sl;
-  const int nxs = a.nx[sl];  // workgroups of this (layer, seq, head); chunk mode
+  const int nxs = a.nxcum[sl + 1] - a.nxcum[sl];  // workgroups of this (layer, seq, head); chunk mode
   if (int(blockIdx.x) >= nxs) return;
   const int cap = a.cap[sl];
   int len = a.seq_lens[s];

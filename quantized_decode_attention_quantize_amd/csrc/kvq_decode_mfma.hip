@@ -1312,7 +1312,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int bitsB = int(t.bits[sB][0]) | int(t.bits[sB][1]) << 8;
   const uint32_t kbaseA = t.base256[sA][0], kbaseB = t.base256[sB][0];
   const uint32_t vbaseA = t.base256[sA][1], vbaseB = t.base256[sB][1];
-  const int nxc = t.nxcum[lane], nxl = t.nx[lane];
+  const int nxc = t.nxcum[lane], nxl = t.nxcum[lane + 1] - nxc;  // nxcum has kMaxSeq + 1 entries
   const int vbl = t.vb[lane], vel = t.ve[lane], capl = t.cap[lane];
   const int vr0l = t.vrow0[lane], tr0l = t.trow0[lane], lenl = lens_lds[lane];
   const int per_mult = t.nxcum[n_seq];  // units of one slot with mult 1
@@ -1450,31 +1450,67 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const int64_t vrow0 = __builtin_amdgcn_readlane(vr0l, sl);
     const int64_t trow0 = __builtin_amdgcn_readlane(tr0l, sl);
     const bool quant_vis = !(KB == 16 && VB == 16) && kbits == KB && vbits == VB;
+    // bf16 ranges of this sequence inside its coded span (rows of the text
+    // plane); a sequence with ranges takes the static split
+    const int r_lo = __builtin_amdgcn_readfirstlane(int(t.rng_first[sl]));
+    const int nr = __builtin_amdgcn_readfirstlane(int(t.rng_first[sl + 1])) - r_lo;
+    int range_total = 0;  // positions of the span inside bf16 ranges
+#pragma clang loop unroll(disable)
+    for (int k = 0; k < nr; ++k) range_total += t.rng_e[r_lo + k] - t.rng_b[r_lo + k];
+    range_total = __builtin_amdgcn_readfirstlane(range_total);
     // In a balanced split the piece's visual rows (the union of its waves'
     // static ranges) are claimed step by step by its waves; text rows, and
-    // everything in the fixed chunk mode, follow the static split [wa, wb).
-    // The static text rows go first so the claimed part absorbs their
-    // imbalance.
-    const bool dyn = La.chunk == 0;
+    // everything in the fixed chunk mode or of a sequence with bf16 ranges,
+    // follow the static split [wa, wb).  The static text rows go first so
+    // the claimed part absorbs their imbalance.
+    const bool dyn = La.chunk == 0 && nr == 0;
     int ga, gb, gt;
     wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt, phase);
     wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb, phase);
     const Claim cl{&lds_claim[p_lo], pos - p_lo, p_hi - p_lo};
-    // segments: text prefix [0, vb), text suffix [ve, cap), visual [vb, ve);
-    // kept as a loop so each row path is emitted once
+    // segments: 0 text prefix [0, vb), 1 text suffix [ve, cap), then for
+    // j = 0 .. 2 nr: coded piece j / 2 (even j) or bf16 range (j - 1) / 2
+    // (odd j) of the span; rows are consecutive inside a segment.  Kept as a
+    // loop so each row path is emitted once.
+    int skipped = 0;  // range positions before the current piece or range
 #pragma clang loop unroll(disable)
-    for (int seg = 0; seg < 3; ++seg) {
-      const bool vis = seg == 2;
+    for (int seg = 0; seg < 3 + 2 * nr; ++seg) {
+      const bool vis = seg >= 2 && ((seg - 2) & 1) == 0;
+      int f0, f1;
+      int64_t frow;  // plane row of position f0
+      if (seg == 0) {
+        f0 = 0;
+        f1 = vb;
+        frow = trow0;
+      } else if (seg == 1) {  // text rows before it: vb + range_total
+        f0 = ve;
+        f1 = cap;
+        frow = trow0 + vb + range_total;
+      } else {
+        const int k = (seg - 2) >> 1;
+        if (vis) {
+          f0 = k == 0 ? vb : t.rng_e[r_lo + k - 1];
+          f1 = k < nr ? t.rng_b[r_lo + k] : ve;
+          frow = vrow0 + (f0 - vb) - skipped;
+        } else {
+          f0 = t.rng_b[r_lo + k];
+          f1 = t.rng_e[r_lo + k];
+          frow = trow0 + vb + skipped;
+          skipped += f1 - f0;
+        }
+      }
+      f0 = __builtin_amdgcn_readfirstlane(f0);
+      f1 = __builtin_amdgcn_readfirstlane(f1);
       int x0, x1;
       if (vis && dyn) {
-        x0 = max(ga, vb);
-        x1 = min(gb, ve);
+        x0 = max(ga, f0);
+        x1 = min(gb, f1);
       } else {
-        x0 = seg == 0 ? wa : vis ? max(wa, vb) : max(wa, ve);
-        x1 = seg == 0 ? min(wb, vb) : vis ? min(wb, ve) : wb;
+        x0 = max(wa, f0);
+        x1 = min(wb, f1);
       }
       if (x0 >= x1) continue;
-      const int64_t row0 = vis ? vrow0 + (x0 - vb) : trow0 + (seg == 0 ? x0 : x0 - (ve - vb));
+      const int64_t row0 = frow + (x0 - f0);
       const Claim use = vis && dyn ? cl : Claim{nullptr, 0, 1};
       if (vis && quant_vis) {
         run_segment<D, NG, KB, VB, PC>(c, st, x0, x1, row0, true, use, qreg, q_pending);

@@ -13,6 +13,8 @@ namespace kvq {
 constexpr int kMaxLH = 128;   // (layer, KV head) pairs per launch
 constexpr int kMaxSeq = 64;   // sequences per launch
 constexpr int kMaxGroupRatio = 16;  // Hq / Hkv supported by the decode kernels
+constexpr int kMaxRangesQ = 64;     // bf16 ranges per quantize launch
+constexpr int kMaxRangesD = 36;     // bf16 ranges per decode launch (and per sequence)
 
 // Width codes for the per-(layer, head, X) row formats.
 __host__ __device__ constexpr int vis_row_bytes(int D, int bits) {
@@ -49,6 +51,10 @@ struct QuantizeArgs {
   int32_t k_per_channel;  // K codes grouped per channel over g-token blocks
   int32_t kblk0[kMaxSeq];  // per sequence: first per-channel K block stored
   int32_t kblkn[kMaxSeq];  // per sequence: number of such blocks (0: none)
+  // bf16 ranges inside the visual spans: sequence i owns ranges
+  // [rng_first[i], rng_first[i + 1]) of this launch's table
+  int32_t rng_first[kMaxSeq + 1];
+  int32_t rng_b[kMaxRangesQ], rng_e[kMaxRangesQ];
 };
 static_assert(sizeof(QuantizeArgs) <= 4096, "QuantizeArgs must fit the kernel argument limit");
 
@@ -79,10 +85,16 @@ struct DecodeArgs {
   uint16_t mult[kMaxLH];    // per slot
   uint16_t mcum[kMaxLH + 1];  // per slot: sum of mult over earlier slots
   int32_t vb[kMaxSeq], ve[kMaxSeq], cap[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
-  int32_t nx[kMaxSeq];      // per sequence
-  int32_t nxcum[kMaxSeq + 1];  // per sequence: sum of nx over earlier sequences
+  // per sequence: units of one slot with mult 1 before it (sequence i has
+  // nx_i = nxcum[i + 1] - nxcum[i])
+  int32_t nxcum[kMaxSeq + 1];
   int32_t rotate_k;         // coded K rows are stored rotated: rotate q for them
   int32_t k_per_channel;    // coded K rows carry per-channel (scale, min) per block
+  // bf16 ranges inside the visual spans: sequence i owns ranges
+  // [rng_first[i], rng_first[i + 1]) of this launch's table
+  uint8_t rng_first[kMaxSeq + 1];
+  uint8_t pad_[3];
+  int32_t rng_b[kMaxRangesD], rng_e[kMaxRangesD];
 };
 static_assert(sizeof(DecodeArgs) % 16 == 0, "DecodeArgs is copied in 16-byte pieces");
 static_assert(sizeof(DecodeArgs) <= 4096, "DecodeArgs must fit the kernel argument limit");

@@ -220,7 +220,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
 
   const int bits = a.bits[lh][X];
   const int vb = a.vb[sl], ve = a.ve[sl];
-  const bool visual = t >= vb && t < ve;
+  // Position t is coded when it lies in the coded span and in none of the
+  // sequence's bf16 ranges.  nc = coded positions before t: coded positions
+  // take VIS rows in order, all others TXT rows in order.
+  bool visual = t >= vb && t < ve;
+  int nc = min(max(t, vb), ve) - vb;
+  for (int k = a.rng_first[sl]; k < a.rng_first[sl + 1]; ++k) {
+    const int b = a.rng_b[k], e = a.rng_e[k];
+    nc -= t >= e ? e - b : t > b ? t - b : 0;
+    visual = visual && !(t >= b && t < e);
+  }
   uint8_t* vis = a.cache + uint64_t(a.base256[lh][X]) * 256u;
 
   // Coded K rows of a per-channel cache are written by quantize_kblock_kernel.
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
     else if (a.g == 64) quantize_lane<64 / kE>(x, bits, packed, meta);
     else quantize_lane<128 / kE>(x, bits, packed, meta);
     if (!active) return;
-    const int64_t row = a.vrow0[sl] + (t - vb);
+    const int64_t row = a.vrow0[sl] + nc;
     uint8_t* rowp = vis + row * (D * bits / 8) + lane_in_row * (kE * bits / 8);
     // the lane's kE * bits / 32 words, in 16-byte pieces where they fill one
     const int words = kE * bits / 32;
@@ -257,10 +266,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
   } else {
     if (!active) return;
     uint8_t* rowp;
-    if (visual) {  // 16-bit (protected) head: visual row kept bf16 in VIS
-      rowp = vis + (a.vrow0[sl] + (t - vb)) * int64_t(2 * D);
+    if (visual) {  // 16-bit (protected) head: coded position kept bf16 in VIS
+      rowp = vis + (a.vrow0[sl] + nc) * int64_t(2 * D);
     } else {
-      const int64_t trow = a.trow0[sl] + (t < vb ? t : t - (ve - vb));
+      const int64_t trow = a.trow0[sl] + (t - nc);
       rowp = vis + txt_plane_offset(a.Rvis, D, a.g, bits) + trow * int64_t(2 * D);
     }
 #pragma unroll

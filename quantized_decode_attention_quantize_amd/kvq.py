@@ -45,7 +45,10 @@ class _Cfg(C.Structure):
                 ("capacity", C.POINTER(C.c_int32)), ("vis_begin", C.POINTER(C.c_int32)),
                 ("vis_end", C.POINTER(C.c_int32)), ("k_bits", C.POINTER(C.c_uint8)),
                 ("v_bits", C.POINTER(C.c_uint8)), ("rotate_k", C.c_int32),
-                ("k_per_channel", C.c_int32)]
+                ("k_per_channel", C.c_int32),
+                ("bf16_range_offsets", C.POINTER(C.c_int32)),
+                ("bf16_range_begin", C.POINTER(C.c_int32)),
+                ("bf16_range_end", C.POINTER(C.c_int32))]
 
 
 class _Info(C.Structure):
@@ -97,7 +100,9 @@ class Config:
 
     def __init__(self, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, group_size: int, capacity, vis_begin, vis_end, k_bits, v_bits,
-                 rotate_k: bool = False, k_per_channel: bool = False):
+                 rotate_k: bool = False, k_per_channel: bool = False, bf16_ranges=None):
+        """bf16_ranges: None, or per sequence a list of (begin, end) position
+        pairs inside its visual span whose rows are stored bf16."""
         self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
         self.vis_begin = np.ascontiguousarray(vis_begin, dtype=np.int32)
         self.vis_end = np.ascontiguousarray(vis_end, dtype=np.int32)
@@ -108,13 +113,27 @@ class Config:
         self.head_dim, self.group_size = head_dim, group_size
         self.rotate_k = bool(rotate_k)
         self.k_per_channel = bool(k_per_channel)
+        i32p = C.POINTER(C.c_int32)
+        self.bf16_ranges = bf16_ranges
+        if bf16_ranges is None:
+            rng = (i32p(), i32p(), i32p())
+        else:
+            if len(bf16_ranges) != batch:
+                raise ValueError(f"bf16_ranges needs one list per sequence ({batch})")
+            pairs = [(int(b), int(e)) for seq in bf16_ranges for (b, e) in seq]
+            self._rng_off = np.zeros(batch + 1, dtype=np.int32)
+            self._rng_off[1:] = np.cumsum([len(seq) for seq in bf16_ranges])
+            # one spare element so an empty table still has an address
+            self._rng_b = np.array([b for b, _ in pairs] + [0], dtype=np.int32)
+            self._rng_e = np.array([e for _, e in pairs] + [0], dtype=np.int32)
+            rng = tuple(x.ctypes.data_as(i32p) for x in (self._rng_off, self._rng_b, self._rng_e))
         self.c = _Cfg(num_layers, batch, num_q_heads, num_kv_heads, head_dim, group_size,
                       self.capacity.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_begin.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.vis_end.ctypes.data_as(C.POINTER(C.c_int32)),
                       self.k_bits.ctypes.data_as(C.POINTER(C.c_uint8)),
                       self.v_bits.ctypes.data_as(C.POINTER(C.c_uint8)), int(self.rotate_k),
-                      int(self.k_per_channel))
+                      int(self.k_per_channel), *rng)
 
     @classmethod
     def from_workload(cls, w) -> "Config":
@@ -122,7 +141,7 @@ class Config:
         return cls(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
                    w.group_size, a["capacity"], a["vis_begin"], a["vis_end"],
                    a["k_bits"], a["v_bits"], getattr(w, "rotate_k", False),
-                   getattr(w, "k_per_channel", False))
+                   getattr(w, "k_per_channel", False), getattr(w, "bf16_ranges", None))
 
     @property
     def ref(self):

@@ -50,6 +50,7 @@ TAG_APPEND_K = 7
 TAG_APPEND_V = 8
 TAG_BLOCK_K = 9
 TAG_BLOCK_V = 10
+TAG_TOKENS = 11
 
 
 def _mix64_int(z: int) -> int:
@@ -343,6 +344,33 @@ def visual_block(seed: int = 4, num_seqs: int = 8, n_vis: int = 6273) -> Workloa
                     [14] * num_seqs, [T] * num_seqs, [T] * num_seqs, kb, vb, seed=seed)
 
 
+def protected_tokens(seed: int, vb: int, ve: int, count: int) -> List[Tuple[int, int]]:
+    """Seeded one-token ranges: the span's first token (an attention sink)
+    and ``count - 1`` further distinct positions of [vb, ve)."""
+    if ve <= vb or count <= 0:
+        return []
+    picks = permutation_prefix(stream_key(seed, TAG_TOKENS, vb, ve, count), ve - vb - 1,
+                               min(count - 1, ve - vb - 1)) + vb + 1
+    return [(int(t), int(t) + 1) for t in sorted({vb, *picks.tolist()})]
+
+
+def two_images(seed: int = 5, tokens_protected: int = 8) -> Workload:
+    """LLaVA-OneVision-7B shaped layer whose prompt holds two images:
+    14 text + 3,136 visual + 32 text + 3,136 visual + 14 text tokens.  The
+    text between the images is a bf16 range of one visual span, and
+    ``tokens_protected`` seeded visual tokens (the first one a sink) are kept
+    bf16 too.  K INT4 / V INT2, group 64."""
+    n1 = n2 = 3136
+    vb, mid = 14, 14 + n1
+    ve = mid + 32 + n2
+    T = ve + 14
+    kb, vbits = _bits_table(1, 4, 4, 2)
+    singles = protected_tokens(seed, vb, ve, tokens_protected)
+    ranges = sorted([r for r in singles if not (mid <= r[0] < mid + 32)] + [(mid, mid + 32)])
+    return Workload("two_images", 1, 1, 28, 4, 128, 64, [T], [vb], [ve], [T], kb, vbits,
+                    seed=seed, bf16_ranges=[ranges])
+
+
 WORKLOADS = {
     "tiny": tiny,
     "llava_layer": llava_layer,
@@ -350,4 +378,5 @@ WORKLOADS = {
     "long_gqa": long_gqa,
     "ragged_serving": ragged_serving,
     "visual_block": visual_block,
+    "two_images": two_images,
 }

@@ -44,6 +44,17 @@ def as_f32(rows: np.ndarray) -> np.ndarray:
     return rows.astype(np.float32)
 
 
+def coded_count(w: synth.Workload, s: int) -> int:
+    """Positions of sequence s stored as codes: the visual span (whole
+    g-token blocks of it with per-channel K) minus its bf16 ranges."""
+    n = w.vis_end[s] - w.vis_begin[s]
+    if getattr(w, "k_per_channel", False):
+        n -= n % w.group_size
+    for b, e in (getattr(w, "bf16_ranges", None) or [[]] * w.batch)[s]:
+        n -= e - b
+    return int(n)
+
+
 class Pair:
     """The same workload stored by libkvq on the GPU and by the oracle."""
 
@@ -92,8 +103,9 @@ class Pair:
         seqs = range(w.batch) if seqs is None else seqs
         out = []
         vrow0, trow0, rv, rt = [], [], 0, 0
+        coded = [coded_count(w, s) for s in range(w.batch)]
         for s in range(w.batch):
-            nv = w.vis_end[s] - w.vis_begin[s]
+            nv = coded[s]
             vrow0.append(rv)
             trow0.append(rt)
             rv += nv
@@ -105,7 +117,7 @@ class Pair:
                     vis, meta, txt = oracle.plane_offsets(self.ocfg, l, h, X)
                     vrb = 2 * D if b == 16 else D * b // 8
                     for s in seqs:
-                        nv = w.vis_end[s] - w.vis_begin[s]
+                        nv = coded[s]
                         nt = w.capacity[s] - nv
                         if nv:
                             out.append((vis + vrow0[s] * vrb, vis + (vrow0[s] + nv) * vrb))

@@ -43,9 +43,40 @@ static void unit_of(const DecodeArgs& a, int b, int& slot, int& sl, int& x) {
 static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int g,
                     std::vector<int> cap, std::vector<int> vb, std::vector<int> ve,
                     std::vector<uint8_t> kb, std::vector<uint8_t> vbits, int chunk,
-                    int per_channel = 0) {
+                    int per_channel = 0,
+                    const std::vector<std::vector<std::pair<int, int>>>& ranges = {}) {
   kvq_config c{};
   c.k_per_channel = per_channel;
+  std::vector<int32_t> r_off(1, 0), r_b, r_e;
+  for (const auto& seq : ranges) {
+    for (const auto& r : seq) { r_b.push_back(r.first); r_e.push_back(r.second); }
+    r_off.push_back(int32_t(r_b.size()));
+  }
+  r_b.push_back(0); r_e.push_back(0);
+  if (!ranges.empty()) {
+    c.bf16_range_offsets = r_off.data(); c.bf16_range_begin = r_b.data();
+    c.bf16_range_end = r_e.data();
+  }
+  // rows of every position by counting: coded positions (in the coded span
+  // and no range) take VIS rows in order, the rest TXT rows, sequence after
+  // sequence; -1 marks a position of the other plane
+  std::vector<std::pair<std::vector<long>, std::vector<long>>> row_of(B);
+  {
+    long vr = 0, tr = 0;
+    for (int s = 0; s < B; ++s) {
+      int cend = ve[s];
+      if (per_channel) cend = vb[s] + (ve[s] - vb[s]) / g * g;
+      row_of[s].first.assign(cap[s], -1);
+      row_of[s].second.assign(cap[s], -1);
+      for (int t = 0; t < cap[s]; ++t) {
+        bool coded = t >= vb[s] && t < cend;
+        if (!ranges.empty())
+          for (const auto& r : ranges[s]) coded = coded && !(t >= r.first && t < r.second);
+        if (coded) row_of[s].first[t] = vr++;
+        else row_of[s].second[t] = tr++;
+      }
+    }
+  }
   c.num_layers = L; c.batch = B; c.num_q_heads = Hq; c.num_kv_heads = Hkv;
   c.head_dim = D; c.group_size = g;
   c.capacity = cap.data(); c.vis_begin = vb.data(); c.vis_end = ve.data();
@@ -77,7 +108,7 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
       for (int pos = 0; pos < kMfmaWaves && b8 + pos < total; ++pos) {
         int slot, sl, u;
         unit_of(a, b8 + pos, slot, sl, u);
-        const int ne = a.nx[sl] * int(a.mult[slot]), w0 = b8 + pos - u;
+        const int ne = (a.nxcum[sl + 1] - a.nxcum[sl]) * int(a.mult[slot]), w0 = b8 + pos - u;
         const int p_lo = std::max(w0, b8) - b8, p_hi = std::min(w0 + ne, b8 + kMfmaWaves) - b8;
         const int px = int(b) - w0 / kMfmaWaves;
         const int pn = (w0 + ne - 1) / kMfmaWaves - w0 / kMfmaWaves + 1;
@@ -102,22 +133,57 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
           wave_range(u, 0, ne, len, 0, 1, wa, wb, phase);
         wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt, phase);
         wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb, phase);
-        for (int seg = 0; seg < 3; ++seg) {
-          const bool vis = seg == 2;
-          int x0, x1;
-          if (vis && a.chunk == 0) {
-            if (pos != p_lo) continue;  // the piece's claimed range, once per piece
-            x0 = std::max(ga, vbeg);
-            x1 = std::min(gb, vend);
+        // the kernel's segments: text prefix, text suffix, then the coded
+        // pieces and bf16 ranges of the span in turn
+        const int r_lo = a.rng_first[sl], nr = a.rng_first[sl + 1] - r_lo;
+        int range_total = 0;
+        for (int k = 0; k < nr; ++k) range_total += a.rng_e[r_lo + k] - a.rng_b[r_lo + k];
+        const bool dyn = a.chunk == 0 && nr == 0;
+        int skipped = 0;
+        for (int seg = 0; seg < 3 + 2 * nr; ++seg) {
+          const bool vis = seg >= 2 && ((seg - 2) & 1) == 0;
+          int f0, f1;
+          long frow;
+          if (seg == 0) {
+            f0 = 0; f1 = vbeg; frow = a.trow0[sl];
+          } else if (seg == 1) {
+            f0 = vend; f1 = a.cap[sl]; frow = a.trow0[sl] + vbeg + range_total;
           } else {
-            x0 = seg == 0 ? wa : vis ? std::max(wa, vbeg) : std::max(wa, vend);
-            x1 = seg == 0 ? std::min(wb, vbeg) : vis ? std::min(wb, vend) : wb;
+            const int k = (seg - 2) >> 1;
+            if (vis) {
+              f0 = k == 0 ? vbeg : a.rng_e[r_lo + k - 1];
+              f1 = k < nr ? a.rng_b[r_lo + k] : vend;
+              frow = a.vrow0[sl] + (f0 - vbeg) - skipped;
+            } else {
+              f0 = a.rng_b[r_lo + k]; f1 = a.rng_e[r_lo + k];
+              frow = a.trow0[sl] + vbeg + skipped;
+              skipped += f1 - f0;
+            }
+          }
+          int x0, x1;
+          if (vis && dyn) {
+            if (pos != p_lo) continue;  // the piece's claimed range, once per piece
+            x0 = std::max(ga, f0);
+            x1 = std::min(gb, f1);
+          } else {
+            x0 = std::max(wa, f0);
+            x1 = std::min(wb, f1);
           }
           // per-channel K: a visual segment's 32-token steps start on the
           // block grid, so none straddles two blocks of g tokens
           if (vis && a.k_per_channel && x0 < x1 && (x0 - vbeg) % 32) {
             if (bad < 8) printf("%s: visual segment at %d off the step grid\n", name, x0 - vbeg);
             ++bad;
+          }
+          // every row against the layout's plain definition (by counting)
+          for (int tk = x0; tk < x1; ++tk) {
+            const long want = vis ? row_of[s].first[tk] : row_of[s].second[tk];
+            if (want < 0 || frow + (tk - f0) != want) {
+              if (bad < 8)
+                printf("%s: seq %d token %d (%s) row %ld, layout row %ld\n", name, s, tk,
+                       vis ? "coded" : "bf16", frow + (tk - f0), want);
+              ++bad;
+            }
           }
           for (int tk = x0; tk < x1; ++tk) cv[tk]++;
         }
@@ -183,6 +249,43 @@ int main() {
                   std::vector<uint8_t>(8, 2), 0, 1);
   bad += run_case("pc mixed", 2, 3, 8, 2, 64, 32, {400, 1, 970}, {3, 0, 10}, {350, 1, 970},
                   {4, 8, 8, 2}, {2, 4, 8, 4}, 0, 1);
+  // bf16 ranges inside the visual spans (static split for those sequences)
+  using R = std::vector<std::vector<std::pair<int, int>>>;
+  for (int ch : {0, 1024}) {
+    std::vector<uint8_t> kb(112, 4), vb(112, 2);
+    for (int i = 0; i < 14; ++i) kb[(i * 37) % 112] = vb[(i * 37) % 112] = 16;
+    bad += run_case("rng 28x4 6288", 28, 1, 28, 4, 128, 64, {6288}, {14}, {6287}, kb, vb, ch, 0,
+                    R{{{14, 15}, {600, 601}, {3000, 3100}, {6000, 6287}}});
+  }
+  {  // 36 one-token ranges in one sequence, none in the other two
+    std::vector<std::pair<int, int>> many;
+    for (int i = 0; i < 36; ++i) many.push_back({20 + 97 * i, 21 + 97 * i + (i % 3)});
+    for (int ch : {0, 256})
+      bad += run_case("rng 36", 2, 3, 32, 8, 128, 64, {4000, 3600, 129}, {10, 10, 0},
+                      {3990, 3600, 129}, std::vector<uint8_t>(16, 4), std::vector<uint8_t>(16, 2),
+                      ch, 0, R{{}, many, {}});
+  }
+  {  // 70 ragged sequences with 0-3 ranges each (several range tables)
+    std::vector<int> cap, vbg, ve;
+    R rng;
+    uint32_t x = 777;
+    for (int s = 0; s < 70; ++s) {
+      x = x * 1664525u + 1013904223u;
+      const int l = 512 + int(x % 8000u);
+      cap.push_back(l); vbg.push_back(5); ve.push_back(l - 3);
+      std::vector<std::pair<int, int>> r;
+      const int k = s % 4;
+      for (int i = 0; i < k; ++i) {
+        const int b = 5 + (l - 8) * i / k + 1;
+        r.push_back({b, std::min(b + 1 + int(x % 200u), l - 3)});
+      }
+      rng.push_back(r);
+    }
+    bad += run_case("rng 70 ragged", 1, 70, 28, 4, 128, 64, cap, vbg, ve,
+                    std::vector<uint8_t>(4, 4), std::vector<uint8_t>(4, 2), 0, 0, rng);
+  }
+  bad += run_case("rng mixed", 2, 3, 8, 2, 64, 32, {40, 1, 97}, {3, 0, 10}, {35, 1, 97},
+                  {4, 16, 8, 2}, {2, 16, 8, 4}, 0, 0, R{{{3, 4}, {30, 35}}, {}, {{10, 97}}});
   printf(bad ? "FAIL\n" : "ok\n");
   return bad != 0;
 }

@@ -70,7 +70,19 @@ def _configs():
         w = synth.Workload(f"rand{i}", L_, B, Hkv * 2, Hkv, D, g, list(cap), list(vb),
                            list(ve), list(cap), kb.astype(np.uint8), vbits.astype(np.uint8))
         w.k_per_channel = bool(i % 2)  # per-channel K: coded spans in whole blocks
+        if i % 4 == 2:  # bf16 ranges inside the visual spans
+            w.bf16_ranges = [_random_ranges(rng, int(b), int(e)) for b, e in zip(vb, ve)]
         yield w
+
+
+def _random_ranges(rng, vb, ve, most=5):
+    """Sorted, disjoint, non-empty ranges inside [vb, ve)."""
+    if ve - vb < 2:
+        return []
+    cuts = np.sort(rng.choice(np.arange(vb, ve + 1), size=min(2 * most, ve - vb + 1),
+                              replace=False))
+    out = [(int(cuts[j]), int(cuts[j + 1])) for j in range(0, len(cuts) - 1, 2)]
+    return out[:int(rng.integers(0, most + 1))]
 
 
 def test_cache_bytes_matches_oracle(L, orc):
@@ -332,3 +344,60 @@ def test_per_channel_validation(L):
                          k_per_channel=True)  # 28 (head, group) columns
     assert _dec(L, general, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
     del cfg
+
+
+def test_bf16_range_validation(L):
+    """bf16 ranges: malformed tables are shape errors, missing arrays null
+    errors, and per-channel K with ranges, more than 36 ranges in a
+    sequence, or ranges on a shape of the general kernel are refused."""
+    def cfg(ranges, **over):
+        base = dict(num_layers=1, batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64,
+                    group_size=32, capacity=[256, 300], vis_begin=[16, 0],
+                    vis_end=[250, 300], k_bits=[4], v_bits=[2], bf16_ranges=ranges)
+        base.update(over)
+        return kvq.Config(**base)
+
+    def status(c):
+        try:
+            kvq.kvq_cache_bytes(c)
+            return kvq.KVQ_OK
+        except kvq.KvqError as e:
+            return e.status
+
+    assert status(cfg([[(16, 17), (100, 250)], [(0, 300)]])) == kvq.KVQ_OK
+    assert status(cfg([[], []])) == kvq.KVQ_OK
+    assert status(cfg([[(15, 17)], []])) == kvq.KVQ_ERR_SHAPE     # starts before the span
+    assert status(cfg([[(16, 251)], []])) == kvq.KVQ_ERR_SHAPE    # ends after it
+    assert status(cfg([[(20, 20)], []])) == kvq.KVQ_ERR_SHAPE     # empty
+    assert status(cfg([[(30, 40), (20, 25)], []])) == kvq.KVQ_ERR_SHAPE  # unsorted
+    assert status(cfg([[(30, 40), (39, 45)], []])) == kvq.KVQ_ERR_SHAPE  # overlapping
+    assert status(cfg([[(17, 18)], []], k_per_channel=True)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert status(cfg([[], []], k_per_channel=True)) == kvq.KVQ_OK
+    many = [(20 + 4 * i, 22 + 4 * i) for i in range(37)]
+    assert status(cfg([many, []])) == kvq.KVQ_ERR_UNSUPPORTED
+    assert status(cfg([many[:36], many[:36]])) == kvq.KVQ_OK
+    c = cfg([[(16, 17)], []])
+    c.c.bf16_range_end = C.POINTER(C.c_int32)()
+    info = kvq._Info()
+    assert L.kvq_cache_bytes(c.ref, C.byref(info)) == kvq.KVQ_ERR_NULL
+    c = cfg([[(16, 17)], []])
+    c._rng_off[0] = 1
+    assert status(c) == kvq.KVQ_ERR_SHAPE
+    c = cfg([[(16, 17)], []])
+    c._rng_off[1] = 2  # offsets must not decrease
+    assert status(c) == kvq.KVQ_ERR_SHAPE
+    # storage: ranges move rows from the VIS plane to the TXT plane
+    plain = kvq.kvq_cache_bytes(cfg(None))
+    moved = kvq.kvq_cache_bytes(cfg([[(16, 17), (100, 250)], [(0, 300)]]))
+    assert plain["quantized_values"] - moved["quantized_values"] == (1 + 150 + 300) * 64 * 2
+    assert moved["bf16_text_bytes"] - plain["bf16_text_bytes"] == (1 + 150 + 300) * 64 * 2 * 2
+    # decode: the matrix-core kernel takes ranges, the general kernel does not
+    ok = cfg([[(16, 17), (100, 250)], []])
+    assert _dec(L, ok, ws=None)[0] == kvq.KVQ_OK
+    assert _dec(L, ok, chunk=64, ws=None)[0] == kvq.KVQ_OK
+    general = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
+                         bf16_ranges=[[(20, 30)]])  # 28 (head, group) columns
+    assert _dec(L, general, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    general_plain = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
+                               bf16_ranges=[[]])
+    assert _dec(L, general_plain, ws=None)[0] == kvq.KVQ_OK
