@@ -22,9 +22,8 @@ none); ``latent_offset`` writes it out one element at a time:
 * (layer, KV head, X) planes follow each other, X = 0 (K) then 1 (V), each
   ``align256(R * r * 2)`` bytes with R = the last row0 plus its capacity
   rounded up to 32;
-* K latents are row-major bf16: element (row, j) at ``(row * r + j) * 2``;
-* V latents are stored in tiles of 32 rows, latent-dimension-major inside a
-  tile: element (row, j) at ``((row // 32) * r + j) * 64 + (row % 32) * 2``.
+* K and V latents are row-major bf16: element (row, j) of a plane at
+  ``(row * r + j) * 2``.
 """
 from __future__ import annotations
 
@@ -66,9 +65,7 @@ def latent_offset(num_kv_heads: int, capacity: Sequence[int], rank: int, layer: 
     assert 0 <= t < capacity[seq] and 0 <= j < rank and X in (0, 1)
     plane = ((layer * num_kv_heads + head) * 2 + X) * plane_bytes(capacity, rank)
     row = row_bases(capacity)[seq] + t
-    if X == 0:
-        return plane + (row * rank + j) * 2
-    return plane + ((row // 32) * rank + j) * 64 + (row % 32) * 2
+    return plane + (row * rank + j) * 2
 
 
 def write_rows(cache: np.ndarray, num_kv_heads: int, capacity: Sequence[int], rank: int,

@@ -121,14 +121,15 @@ def test_layout_is_a_bijection_onto_disjoint_tiles():
                             assert o % 2 == 0 and 0 <= o and o + 2 <= total
                             assert o not in seen
                             seen.add(o)
-    # K: a row's r elements are contiguous; V: one latent dimension's 32
-    # rows of a tile are contiguous (64 bytes)
-    o0 = latent.latent_offset(Hkv, cap, r, 1, 1, 0, 1, 3, 0)
-    assert latent.latent_offset(Hkv, cap, r, 1, 1, 0, 1, 3, 7) == o0 + 14
-    assert latent.latent_offset(Hkv, cap, r, 1, 1, 0, 1, 4, 0) == o0 + 2 * r
-    v0 = latent.latent_offset(Hkv, cap, r, 0, 1, 1, 1, 0, 5)
-    assert latent.latent_offset(Hkv, cap, r, 0, 1, 1, 1, 31, 5) == v0 + 62
-    assert latent.latent_offset(Hkv, cap, r, 0, 1, 1, 1, 0, 6) == v0 + 64
+    # rows are r contiguous bf16 values, consecutive positions consecutive
+    # rows, and a sequence starts on a 32-row boundary of its plane
+    plane = total // (L * Hkv * 2)
+    for X in (0, 1):
+        o0 = latent.latent_offset(Hkv, cap, r, 1, 1, X, 1, 3, 0)
+        assert latent.latent_offset(Hkv, cap, r, 1, 1, X, 1, 3, 7) == o0 + 14
+        assert latent.latent_offset(Hkv, cap, r, 1, 1, X, 1, 4, 0) == o0 + 2 * r
+        assert latent.latent_offset(Hkv, cap, r, 1, 1, X, 2, 0, 0) == \
+            ((1 * Hkv + 1) * 2 + X) * plane + 96 * r * 2
 
 
 @pytest.mark.parametrize("bits,value", [(0x3F80, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -133),
