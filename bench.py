@@ -325,6 +325,7 @@ def main():
         extras["read_stream_ceiling"] = read_stream_ceiling(torch, dev, args, alg, dec_avg)
         if w.name != "long_gqa" and args.chunk == 0:
             extras["long_gqa_decode"] = long_context_decode(torch, kvq, args, dev)
+        extras["latent_decode"] = latent_decode(torch, kvq, synth, args, dev)
 
     cpu = None if args.no_cpu else cpu_baseline(w, lens, q_bits, alg)
     profiled = args.chunk == 0 and (w.name != "headguard_step" or args.protected == 14)
@@ -573,6 +574,55 @@ def long_context_decode(torch, kvq, args, dev):
     return {"workload": describe(w), "us": round(ms * 1e3, 2), "algorithmic_bytes": alg,
             "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
             "traffic_source": src, "cache_replicas": R}
+
+
+def latent_decode(torch, kvq, synth, args, dev):
+    """Decode over a per-head low-rank latent cache (rank 96) of the same
+    28-layer LLaVA-shaped step: latents stream from HBM, the query is
+    projected once per workgroup and B_V applied after the merge."""
+    w = synth.llava_latent()
+    cfg = kvq.LatentConfig(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           w.rank, w.capacity)
+    nbytes = kvq.kvq_latent_cache_bytes(cfg)
+    R = max(2, math.ceil(args.replica_mb * 2 ** 20 / nbytes))
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    c0 = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    T = w.capacity[0]
+    for l in range(w.num_layers):
+        kv = [to_dev(np.stack([w.latents(l, 0, h, X, 0, T) for h in range(w.num_kv_heads)])
+                     [None, None]) for X in (0, 1)]
+        kvq.kvq_latent_store(cfg, c0, l, 1, [0], 0, T, kv[0], kv[1])
+    torch.cuda.synchronize()
+    caches = [c0] + [c0.clone() for _ in range(R - 1)]
+    up = [to_dev(np.stack([np.stack([w.up(l, h, X) for h in range(w.num_kv_heads)])
+                           for l in range(w.num_layers)])) for X in (0, 1)]
+    q = to_dev(np.stack([w.q_bits(l) for l in range(w.num_layers)]))
+    out = torch.empty_like(q)
+    lens_d = torch.tensor(w.seq_lens, dtype=torch.int32, device=dev)
+    ws = torch.empty(kvq.latent_workspace_bytes(cfg, w.num_layers, 0), dtype=torch.uint8,
+                     device=dev)
+
+    def dec(i):
+        kvq.kvq_latent_decode(cfg, caches[i % R], 0, w.num_layers, lens_d, up[0], up[1], q, out,
+                              w.sm_scale, 0, ws)
+
+    for i in range(args.warmup):
+        dec(i)
+    ms = timed(torch, args, dec)
+    L, H, r, D = w.num_layers, w.num_kv_heads, w.rank, w.head_dim
+    alg = (2 * L * H * sum(w.seq_lens) * r * 2 + 2 * L * H * r * D * 2 +
+           2 * L * w.batch * w.num_q_heads * D * 2)
+    gbs = alg / (ms * 1e-3) / 1e9
+    del caches, ws
+    return {"workload": "28 layers x 4 KV heads (28 query heads, D=128), 6288 tokens, "
+                        "bf16 latents of rank 96 with per-head up-projections",
+            "us": round(ms * 1e3, 2), "algorithmic_bytes": alg, "gbps": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "cache_replicas": R,
+            "kernels": "latent_decode_kernel + latent_merge_kernel"}
 
 
 def cpu_model():

@@ -316,6 +316,93 @@ kvq_status kvq_decode_attention_noalloc(const kvq_config *cfg, const void *cache
                                         const int32_t *seq_lens, const void *q, void *out,
                                         float sm_scale, int32_t chunk_tokens, void *stream);
 
+/* ---- Low-rank latent cache --------------------------------------------
+ * gist.science 2604.02570 (WSVD), section 2-A: every attention head has its
+ * own low-rank factorisation, so the cache of one (layer, KV head) holds
+ * latent rows c_t of width r (the rank) instead of K/V rows of width D, and
+ * K_t = c^K_t B_K, V_t = c^V_t B_V with per-head r x D up-projections;
+ * section 2-D: K and V are reconstructed on chip inside flash decoding and
+ * never written to memory.  The latents come from the model (the down
+ * projection of the hidden state); this library stores and attends over
+ * them.
+ *
+ * Layout (bf16, little-endian): sequence s owns rows [row0_s, row0_s +
+ * capacity[s]) of every plane, row0_s = the sum of the earlier capacities
+ * each rounded up to 32.  For every layer l and KV head h, in that nesting
+ * order, a K plane then a V plane, each align256(R * rank * 2) bytes with R
+ * = row0 of a sequence past the last; element j of row t of a plane at
+ * byte (t * rank + j) * 2.  Padding rows and bytes are never read as data.
+ *
+ * Supported: head_dim in {64, 128}; rank in {32, 64, 96, 128} and <= head_dim;
+ * num_q_heads a multiple of num_kv_heads with a ratio <= 16; a plane below
+ * 2 GiB (KVQ_ERR_UNSUPPORTED otherwise). */
+typedef struct {
+  int32_t num_layers;       /* L                                                */
+  int32_t batch;            /* B                                                */
+  int32_t num_q_heads;      /* Hq                                               */
+  int32_t num_kv_heads;     /* Hkv                                              */
+  int32_t head_dim;         /* D                                                */
+  int32_t rank;             /* r                                                */
+  const int32_t *capacity;  /* HOST [B] rows reserved per sequence (>= 1)      */
+} kvq_latent_config;
+
+/* Bytes of the latent cache `cfg` describes (the layout above).
+ *   cfg    HOST; bytes HOST, written on success.
+ * Host only, pure, synchronous.  Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE,
+ * KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_latent_cache_bytes(const kvq_latent_config *cfg, uint64_t *bytes);
+
+/* Store latent rows of positions [tok_begin, tok_end) of the sequences
+ * seq_ids[0..num_seqs) for layers [layer_begin, layer_begin + num_layers)
+ * (the cached per-head latents of WSVD section 2-A), bit for bit.
+ *   cache      device, kvq_latent_cache_bytes bytes, 256-byte aligned
+ *   seq_ids    HOST [num_seqs], distinct, each in [0, batch)
+ *   k_latent,
+ *   v_latent   device bf16, 16-byte aligned, contiguous
+ *              [num_layers, num_seqs, Hkv, tok_end - tok_begin, rank]
+ * Enqueues on `stream` only.  Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (seq ids
+ * repeated, tok_end < tok_begin), KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN,
+ * KVQ_ERR_RANGE (layers, seq ids, positions outside [0, capacity)),
+ * KVQ_ERR_HIP.  An empty range is a no-op. */
+kvq_status kvq_latent_store(const kvq_latent_config *cfg, void *cache, int32_t layer_begin,
+                            int32_t num_layers, int32_t num_seqs, const int32_t *seq_ids,
+                            int32_t tok_begin, int32_t tok_end, const void *k_latent,
+                            const void *v_latent, void *stream);
+
+/* One decode step over the latent cache (WSVD section 2-D): for every layer
+ * l, sequence s and query head i, with h = floor(i * Hkv / Hq),
+ *   out[l,s,i,:] = softmax(sm_scale * K q) V   over positions [0, seq_lens[s])
+ * where K = C_K B_K and V = C_V B_V are the latents of (l, h) times its
+ * up-projections.  K and V are never formed: the query is projected once
+ * (q' = B_K q) and attends over the latents, and B_V is applied to the
+ * merged latent output (the same result up to rounding order).  Split-K over
+ * token chunks with a log-sum-exp merge, fp32 accumulation, bf16 output
+ * (nearest even).
+ *   cache      device, as written by kvq_latent_store (read only)
+ *   seq_lens   DEVICE int32 [batch], clamped into [1, capacity[s]]
+ *   up_k,
+ *   up_v       device bf16 [L, Hkv, rank, D] (all layers of the cache),
+ *              16-byte aligned: B_K and B_V of every (layer, KV head)
+ *   q, out     device bf16 [num_layers, batch, Hq, D], 16-byte aligned; out
+ *              must not alias any input or the workspace
+ *   chunk_tokens  0 = library choice (about four workgroups per compute unit
+ *              over the call), else a positive multiple of 32 = tokens per
+ *              workgroup.  Each chunk's summation order is fixed: repeated
+ *              calls give identical bytes.
+ *   workspace  device, 256-byte aligned, for the split partials; NULL = only
+ *              write the required size to *workspace_bytes.  Needs no
+ *              initialisation; calls that may overlap in time must use
+ *              distinct workspaces.
+ * Two kernel launches per 64 sequences, enqueued on `stream`.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (also more than
+ * 4096 chunks per sequence), KVQ_ERR_ALIGN, KVQ_ERR_RANGE, KVQ_ERR_WORKSPACE,
+ * KVQ_ERR_HIP. */
+kvq_status kvq_latent_decode(const kvq_latent_config *cfg, const void *cache,
+                             int32_t layer_begin, int32_t num_layers, const int32_t *seq_lens,
+                             const void *up_k, const void *up_v, const void *q, void *out,
+                             float sm_scale, int32_t chunk_tokens, void *workspace,
+                             size_t *workspace_bytes, void *stream);
+
 /* Static description of a status code (never NULL; unknown codes get a
  * generic string).  A utility of the ABI, not a step of the method. */
 const char *kvq_status_string(kvq_status s);

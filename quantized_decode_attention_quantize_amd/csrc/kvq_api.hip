@@ -172,6 +172,8 @@ int default_chunk(const kvq_config* c, int nl, int quantum, int64_t target) {
   return int(std::max<int64_t>(ch, quantum));
 }
 
+}  // namespace
+
 // Compute units of the current device (256 on MI355X); 256 when no device
 // can be queried (host-only use such as workspace size queries in tests).
 // The count is read once per device and cached.
@@ -188,6 +190,8 @@ int device_cus() {
   if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
+
+namespace {
 
 static_assert(sizeof(DecodeArgs) <= 4096, "decode kernel arguments exceed 4 KB");
 static_assert(sizeof(QuantizeArgs) <= 4096, "quantize kernel arguments exceed 4 KB");

@@ -161,6 +161,10 @@ __host__ __device__ inline int64_t partial_index(int l, int s, int h, int x, int
   return ((int64_t(l) * B + s) * Hkv + h) * max_chunks + x;
 }
 
+// Compute units of the current device, read once per device (256 when no
+// device can be queried).
+int device_cus();
+
 hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
                            hipStream_t stream);
 // Per-channel K blocks of a launch (k_per_channel): one workgroup per

@@ -1,0 +1,624 @@
+// kvq_latent.hip -- decode-step attention over a low-rank latent cache, and
+// the store of latent rows: kvq_latent_cache_bytes, kvq_latent_store and
+// kvq_latent_decode of include/kvq.h.
+//
+// gist.science 2604.02570 (WSVD), section 2-A: every attention head gets its
+// own low-rank factorisation, so one (layer, KV head) caches latent rows c_t
+// of width r instead of K/V rows of width D, with K_t = c^K_t B_K and
+// V_t = c^V_t B_V for per-head r x D up-projections; section 2-D: K and V
+// are reconstructed on chip inside flash decoding and never written back.
+//
+// The kernel never forms a K or V row: q . (c B_K) = (B_K q) . c and
+// sum_t p_t (c_t B_V) = (sum_t p_t c_t) B_V, so each workgroup projects its
+// query heads once on the matrix cores (q' = B_K q), attends over the
+// latents at width r, and the merge applies B_V to the combined latent
+// output.  It reads the same bytes as a row-by-row reconstruction and skips
+// its r x D product per token.  Precision: q' and the probabilities enter
+// the bf16 matrix cores as hi/lo bf16 pairs (about 16 significant bits),
+// every sum is fp32, the output is rounded to bf16 once.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+constexpr int kLWaves = 4;                // waves per decode workgroup
+constexpr int kLThreads = 64 * kLWaves;
+constexpr float kLLazy = 6.0f;            // p <= 2^6 between rescales
+constexpr int kLMaxChunks = 4096;         // partial slots per (layer, seq, head)
+
+struct LatentArgs {
+  const uint8_t* cache;
+  const int32_t* seq_lens;  // device [batch]
+  const uint16_t* q;        // bf16 [nl, B, Hq, D]
+  uint16_t* out;            // bf16 [nl, B, Hq, D]
+  const uint16_t* up_k;     // bf16 [L, Hkv, r, D]
+  const uint16_t* up_v;
+  float* ws_o;              // [entries][G][r] unnormalised latent outputs
+  float* ws_ml;             // [entries][G][2] (max in log2 units, sum)
+  float qscale;             // sm_scale * log2(e)
+  int64_t plane_bytes;
+  int Hkv, Hq, G, B;
+  int layer_begin, nl;
+  int chunk;                // tokens per decode workgroup (multiple of 32)
+  int max_chunks;
+  int seq_off, n_seq;       // sequences [seq_off, seq_off + n_seq) of this launch
+  int32_t row0[kMaxSeq];    // first plane row of each sequence
+  int32_t cap[kMaxSeq];
+  int32_t nxcum[kMaxSeq + 1];  // sequence i has nxcum[i + 1] - nxcum[i] chunks
+};
+static_assert(sizeof(LatentArgs) <= 4096, "LatentArgs must fit the kernel argument limit");
+
+struct LatentStoreArgs {
+  uint8_t* cache;
+  const uint16_t* src[2];   // bf16 [nl, S, Hkv, n, r] for K and V
+  int64_t plane_bytes;
+  int Hkv, n, S, seq_off, layer_begin, nl;
+  int32_t row0[kMaxSeq];    // plane row of the call's first position, per sequence
+};
+
+__device__ inline f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ inline float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+__device__ inline uint32_t bf16_bits(float x) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)x));  // nearest even
+}
+// hi/lo bf16 pair words of (x0, x1): hi = bf16(x), lo = bf16(x - hi).
+__device__ inline void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+  hi = h0 | (h1 << 16);
+  lo = bf16_bits(x0 - bf16_lo(h0)) | (bf16_bits(x1 - bf16_lo(h1)) << 16);
+}
+__device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+// Max over lanes {l, l^16, l^32, l^48}: the four row quarters of one column
+// of a 16 x 16 accumulator.
+__device__ inline float max_quarters(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ inline float sum_quarters(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// One 32-token step of one wave, as loaded: lane (n = lane % 16, j = lane /
+// 16) holds, for rows 16 tau + n, the j-th quarter of the K latent row (r/4
+// values, r/32 chunks of 8), and for the eight rows 16 (e / 4) + 4 j + e % 4
+// the n-th sixteenth of the V latent row (r/16 values).
+template <int R>
+struct LStep {
+  u32x4 k[2][R / 32];
+  uint32_t v[8][R / 32];
+};
+
+template <int R>
+__device__ inline void load_vpiece(Rsrc r, uint32_t off, uint32_t* out) {
+  if constexpr (R == 128) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    out[0] = x[0]; out[1] = x[1]; out[2] = x[2]; out[3] = x[3];
+  } else if constexpr (R == 96) {
+    const u32x3 x = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    out[0] = x[0]; out[1] = x[1]; out[2] = x[2];
+  } else if constexpr (R == 64) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    out[0] = x[0]; out[1] = x[1];
+  } else {
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+}
+
+// Loads the step whose first plane row is `row`, of which `rows` (1..32)
+// exist: rows past them re-read the last one (their scores are masked).
+template <int R>
+__device__ inline void load_lstep(Rsrc kr, Rsrc vr, int row, int rows, int n, int j,
+                                  LStep<R>& st) {
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const uint32_t off = uint32_t(row + min(16 * tau + n, rows - 1)) * (2 * R) + j * (R / 2);
+#pragma unroll
+    for (int c = 0; c < R / 32; ++c)
+      st.k[tau][c] = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 16 * c, 0, 0);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = 16 * (e >> 2) + 4 * j + (e & 3);
+    load_vpiece<R>(vr, uint32_t(row + min(t, rows - 1)) * (2 * R) + n * (R / 8), st.v[e]);
+  }
+}
+
+template <int R>
+struct LWave {
+  float m = -INFINITY;  // running max of this lane's column (log2 units)
+  float l = 0.0f;       // this lane's share of the column's sum
+  f32x4 o[R / 16];      // o[mb][i]: head 4 j + i, latent column n * R / 16 + mb
+};
+
+// q' . c, online softmax and p . c^V of one step of `rows` real rows.
+template <int R>
+__device__ inline void compute_lstep(LWave<R>& w, const LStep<R>& st, const u32x4 (&qhi)[R / 32],
+                                     const u32x4 (&qlo)[R / 32], int rows, int j) {
+  f32x4 acc[2];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    acc[tau] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < R / 32; ++c) {
+      acc[tau] = mfma_bf16(st.k[tau][c], qhi[c], acc[tau]);
+      acc[tau] = mfma_bf16(st.k[tau][c], qlo[c], acc[tau]);
+    }
+  }
+  // sc[e]: score of row 16 (e / 4) + 4 j + e % 4 for head n (log2 units)
+  float sc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sc[e] = acc[e >> 2][e & 3];
+    if (rows < 32 && 16 * (e >> 2) + 4 * j + (e & 3) >= rows) sc[e] = -INFINITY;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+  mx = max_quarters(mx);
+  const float mnew = fmaxf(w.m, mx);
+  if (__builtin_amdgcn_ballot_w64(mnew > w.m + kLLazy) != 0) {
+    const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);  // 0 on the first step
+    w.l *= alpha;
+    float ar[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+    for (int mb = 0; mb < R / 16; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w.o[mb][i] *= ar[i];
+    w.m = mnew;
+  }
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(sc[e] - w.m);
+    w.l += p[e];
+  }
+  // P as the A operand (rows = heads, k = the lane's eight rows), hi and lo
+  u32x4 pa, pb;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    uint32_t hi, lo;
+    split_pair(p[2 * e2], p[2 * e2 + 1], hi, lo);
+    pa[e2] = hi;
+    pb[e2] = lo;
+  }
+#pragma unroll
+  for (int mb = 0; mb < R / 16; ++mb) {
+    u32x4 b;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const uint32_t w0 = st.v[2 * e2][mb >> 1], w1 = st.v[2 * e2 + 1][mb >> 1];
+      b[e2] = (mb & 1) ? __builtin_amdgcn_perm(w1, w0, 0x07060302u)
+                       : __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+    }
+    w.o[mb] = mfma_bf16(pa, b, w.o[mb]);
+    w.o[mb] = mfma_bf16(pb, b, w.o[mb]);
+  }
+}
+
+// One workgroup: one chunk of one (layer, sequence, KV head); its four waves
+// take the chunk's 32-token steps in turn, then combine into one partial.
+template <int D, int R>
+__global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) {
+  __shared__ float q_lds[16][R + 4];
+  __shared__ float o_lds[kLWaves][16][R];
+  __shared__ float ml_lds[kLWaves][16][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, j = lane >> 4;
+
+  // workgroup -> (layer-local l, head h, sequence index i, chunk x)
+  const int per = a.nxcum[a.n_seq];
+  const int u = blockIdx.x;
+  const int lh = u / per;
+  const int rem = u - lh * per;
+  int lo = 0, hi = a.n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.nxcum[mid] <= rem) lo = mid; else hi = mid - 1;
+  }
+  const int i = lo, x = rem - a.nxcum[lo];
+  const int l = lh / a.Hkv, h = lh - l * a.Hkv, s = a.seq_off + i, G = a.G;
+  const int len = min(max(a.seq_lens[s], 1), a.cap[i]);
+  const int t0 = x * a.chunk, t1 = min(t0 + a.chunk, len);
+  const int64_t lhg = int64_t(a.layer_begin + l) * a.Hkv + h;
+  const uint8_t* kplane = a.cache + 2 * lhg * a.plane_bytes;
+  const Rsrc kr = make_rsrc(kplane, a.plane_bytes);
+  const Rsrc vr = make_rsrc(kplane + a.plane_bytes, a.plane_bytes);
+  const int row0 = a.row0[i];
+
+  // ---- q' = qscale * B_K q for the group's heads, on the matrix cores ----
+  // B operand: lane (n, j) holds q_n[32 sd + 8 j .. + 8] (zeros past G);
+  // A operand: B_K rows 16 jb + n.  Result lane (n, j), element ii: q'_n at
+  // latent index 16 jb + 4 j + ii.  The waves share the r/16 blocks.
+  {
+    u32x4 qop[D / 32];
+    const uint16_t* qrow = a.q + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G + n) * D;
+#pragma unroll
+    for (int sd = 0; sd < D / 32; ++sd)
+      qop[sd] = n < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * sd + 8 * j)
+                      : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jb = wave; jb < R / 16; jb += kLWaves) {
+      const uint16_t* bk = a.up_k + (lhg * R + 16 * jb + n) * D;
+      f32x4 c = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int sd = 0; sd < D / 32; ++sd)
+        c = mfma_bf16(*reinterpret_cast<const u32x4*>(bk + 32 * sd + 8 * j), qop[sd], c);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) q_lds[n][16 * jb + 4 * j + ii] = c[ii] * a.qscale;
+    }
+  }
+  __syncthreads();
+  // score B operand, chunk c: lane (n, j) holds q'_n[j r/4 + 8 c .. + 8]
+  u32x4 qhi[R / 32], qlo[R / 32];
+#pragma unroll
+  for (int c = 0; c < R / 32; ++c)
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int k = j * (R / 4) + 8 * c + 2 * e2;
+      uint32_t hw, lw;
+      split_pair(q_lds[n][k], q_lds[n][k + 1], hw, lw);
+      qhi[c][e2] = hw;
+      qlo[c][e2] = lw;
+    }
+
+  // ---- the wave's steps: k = wave, wave + 4, ... of the chunk ------------
+  LWave<R> w;
+#pragma unroll
+  for (int mb = 0; mb < R / 16; ++mb) w.o[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int nsteps = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
+  if (wave < nsteps) {
+    LStep<R> cur, nxt;
+    int k = wave;
+    load_lstep<R>(kr, vr, row0 + t0 + 32 * k, min(32, t1 - t0 - 32 * k), n, j, cur);
+    while (true) {
+      const int rows = min(32, t1 - t0 - 32 * k);
+      const int kn = k + kLWaves;
+      if (kn < nsteps) {
+        load_lstep<R>(kr, vr, row0 + t0 + 32 * kn, min(32, t1 - t0 - 32 * kn), n, j, nxt);
+        compute_lstep<R>(w, cur, qhi, qlo, rows, j);
+        cur = nxt;
+        k = kn;
+      } else {
+        compute_lstep<R>(w, cur, qhi, qlo, rows, j);
+        break;
+      }
+    }
+  }
+
+  // ---- combine the waves into the chunk's partial ------------------------
+  const float l_col = sum_quarters(w.l);
+#pragma unroll
+  for (int mb = 0; mb < R / 16; ++mb)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) o_lds[wave][4 * j + ii][n * (R / 16) + mb] = w.o[mb][ii];
+  if (j == 0) {
+    ml_lds[wave][n][0] = w.m;
+    ml_lds[wave][n][1] = l_col;
+  }
+  __syncthreads();
+  const int64_t p = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks + x;
+  for (int idx = threadIdx.x; idx < G * R; idx += kLThreads) {
+    const int hh = idx / R, jj = idx - hh * R;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kLWaves; ++v)
+      if (ml_lds[v][hh][1] > 0.0f) M = fmaxf(M, ml_lds[v][hh][0]);
+    float o = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kLWaves; ++v) {
+      const float lv = ml_lds[v][hh][1];
+      const float f = lv > 0.0f ? __builtin_amdgcn_exp2f(ml_lds[v][hh][0] - M) : 0.0f;
+      o = __builtin_fmaf(f, o_lds[v][hh][jj], o);
+      L = __builtin_fmaf(f, lv, L);
+    }
+    a.ws_o[(p * G + hh) * R + jj] = o;
+    if (jj == 0) {
+      a.ws_ml[(p * G + hh) * 2] = M;
+      a.ws_ml[(p * G + hh) * 2 + 1] = L;
+    }
+  }
+}
+
+// One workgroup per (layer, sequence, KV head): log-sum-exp merge of the
+// chunks' partials, then out = (merged latent output) B_V, rounded to bf16.
+template <int D, int R>
+__global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
+  __shared__ float ml[16][2];
+  __shared__ float ob[16][R];
+  const int G = a.G;
+  const int e = blockIdx.x;
+  const int h = e % a.Hkv, i = (e / a.Hkv) % a.n_seq, l = e / (a.Hkv * a.n_seq);
+  const int s = a.seq_off + i, nx = a.nxcum[i + 1] - a.nxcum[i];
+  const int64_t p0 = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks;
+  const int tid = threadIdx.x;
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int x = 0; x < nx; ++x) {
+      const float* m = a.ws_ml + ((p0 + x) * G + tid) * 2;
+      if (m[1] > 0.0f) M = fmaxf(M, m[0]);
+    }
+    float L = 0.0f;
+    for (int x = 0; x < nx; ++x) {
+      const float* m = a.ws_ml + ((p0 + x) * G + tid) * 2;
+      if (m[1] > 0.0f) L = __builtin_fmaf(m[1], __builtin_amdgcn_exp2f(m[0] - M), L);
+    }
+    ml[tid][0] = M;
+    ml[tid][1] = L;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * R; idx += 256) {
+    const int hh = idx / R, jj = idx - hh * R;
+    const float M = ml[hh][0];
+    float o = 0.0f;
+    for (int x = 0; x < nx; ++x) {
+      const float* m = a.ws_ml + ((p0 + x) * G + hh) * 2;
+      if (m[1] > 0.0f)
+        o = __builtin_fmaf(__builtin_amdgcn_exp2f(m[0] - M), a.ws_o[((p0 + x) * G + hh) * R + jj], o);
+    }
+    ob[hh][jj] = o / ml[hh][1];
+  }
+  __syncthreads();
+  const int64_t lhg = int64_t(a.layer_begin + l) * a.Hkv + h;
+  const uint16_t* bv = a.up_v + lhg * R * D;
+  uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int hh = idx / D, d = idx - hh * D;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int jj = 0; jj < R; ++jj) acc = __builtin_fmaf(ob[hh][jj], bf16_lo(bv[jj * D + d]), acc);
+    outp[int64_t(hh) * D + d] = uint16_t(bf16_bits(acc));
+  }
+}
+
+// Copies 16-byte pieces of latent rows into their planes.
+template <int R>
+__global__ __launch_bounds__(256) void latent_store_kernel(LatentStoreArgs a) {
+  constexpr int kPieces = R / 8;  // 16-byte pieces per row
+  const int piece = blockIdx.x * 256 + threadIdx.x;
+  const int t = piece / kPieces, c = piece - t * kPieces;
+  if (t >= a.n) return;
+  const int si = blockIdx.y;
+  const int z = blockIdx.z;  // (layer-local l, head h, X)
+  const int X = z & 1, lh = z >> 1, l = lh / a.Hkv, h = lh - l * a.Hkv;
+  const uint16_t* src =
+      a.src[X] + ((((int64_t(l) * a.S + a.seq_off + si) * a.Hkv + h) * a.n + t) * R + 8 * c);
+  const int64_t lhg = int64_t(a.layer_begin + l) * a.Hkv + h;
+  uint8_t* dst = a.cache + (2 * lhg + X) * a.plane_bytes + (int64_t(a.row0[si]) + t) * (2 * R) +
+                 16 * c;
+  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+}
+
+// ---- host side ---------------------------------------------------------
+
+bool rank_ok(int r, int D) { return (r == 32 || r == 64 || r == 96 || r == 128) && r <= D; }
+
+std::vector<int64_t> row_bases(const kvq_latent_config* c) {
+  std::vector<int64_t> b(size_t(c->batch) + 1, 0);
+  for (int s = 0; s < c->batch; ++s) b[s + 1] = b[s] + (int64_t(c->capacity[s]) + 31) / 32 * 32;
+  return b;
+}
+
+int64_t plane_bytes_of(const kvq_latent_config* c) {
+  return (row_bases(c).back() * c->rank * 2 + 255) / 256 * 256;
+}
+
+kvq_status check_latent(const kvq_latent_config* c) {
+  if (!c || !c->capacity) return KVQ_ERR_NULL;
+  if (c->num_layers < 1 || c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1)
+    return KVQ_ERR_SHAPE;
+  for (int s = 0; s < c->batch; ++s)
+    if (c->capacity[s] < 1) return KVQ_ERR_SHAPE;
+  if (c->num_q_heads % c->num_kv_heads) return KVQ_ERR_UNSUPPORTED;
+  if (c->num_q_heads / c->num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (!rank_ok(c->rank, c->head_dim)) return KVQ_ERR_UNSUPPORTED;
+  if (plane_bytes_of(c) > int64_t(0x7FFFFFFF)) return KVQ_ERR_UNSUPPORTED;  // 32-bit offsets
+  return KVQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Tokens per decode workgroup: about four workgroups per compute unit over
+// the whole call, in 128-token multiples (one step per wave at least).
+int latent_chunk(const kvq_latent_config* c, int num_layers, int chunk_tokens) {
+  if (chunk_tokens > 0) return chunk_tokens;
+  int64_t work = 0;
+  for (int s = 0; s < c->batch; ++s) work += c->capacity[s];
+  work *= int64_t(num_layers) * c->num_kv_heads;
+  const int64_t target = 4 * int64_t(device_cus());
+  int64_t ch = (work + target - 1) / target;
+  ch = (ch + 127) / 128 * 128;
+  return int(std::min<int64_t>(std::max<int64_t>(ch, 256), 1 << 20));
+}
+
+int max_chunks_of(const kvq_latent_config* c, int chunk) {
+  int m = 1;
+  for (int s = 0; s < c->batch; ++s) m = std::max(m, (c->capacity[s] + chunk - 1) / chunk);
+  return m;
+}
+
+template <int D, int R>
+hipError_t launch_latent(const LatentArgs& a, hipStream_t st) {
+  const int units = a.nl * a.Hkv * a.nxcum[a.n_seq];
+  hipLaunchKernelGGL((latent_decode_kernel<D, R>), dim3(units), dim3(kLThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((latent_merge_kernel<D, R>), dim3(a.nl * a.n_seq * a.Hkv), dim3(256), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_latent(int D, int R, const LatentArgs& a, hipStream_t st) {
+#define KVQ_LATENT_CASE(d, r) \
+  if (D == d && R == r) return launch_latent<d, r>(a, st);
+  KVQ_LATENT_CASE(64, 32)
+  KVQ_LATENT_CASE(64, 64)
+  KVQ_LATENT_CASE(128, 32)
+  KVQ_LATENT_CASE(128, 64)
+  KVQ_LATENT_CASE(128, 96)
+  KVQ_LATENT_CASE(128, 128)
+#undef KVQ_LATENT_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int R>
+hipError_t launch_latent_store(const LatentStoreArgs& a, int n_seq, hipStream_t st) {
+  const int pieces = a.n * (R / 8);
+  const dim3 grid((pieces + 255) / 256, n_seq, a.nl * a.Hkv * 2);
+  hipLaunchKernelGGL((latent_store_kernel<R>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" kvq_status kvq_latent_cache_bytes(const kvq_latent_config* cfg, uint64_t* bytes) {
+  if (!bytes) return KVQ_ERR_NULL;
+  const kvq_status st = check_latent(cfg);
+  if (st != KVQ_OK) return st;
+  *bytes = uint64_t(cfg->num_layers) * cfg->num_kv_heads * 2 * uint64_t(plane_bytes_of(cfg));
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_latent_store(const kvq_latent_config* cfg, void* cache,
+                                       int32_t layer_begin, int32_t num_layers,
+                                       int32_t num_seqs, const int32_t* seq_ids,
+                                       int32_t tok_begin, int32_t tok_end, const void* k_latent,
+                                       const void* v_latent, void* stream) {
+  kvq_status st = check_latent(cfg);
+  if (st != KVQ_OK) return st;
+  if (num_layers < 0 || num_seqs < 0 || tok_end < tok_begin) return KVQ_ERR_SHAPE;
+  if (num_layers == 0 || num_seqs == 0 || tok_end == tok_begin) return KVQ_OK;
+  if (!cache || !seq_ids || !k_latent || !v_latent) return KVQ_ERR_NULL;
+  if (!aligned(cache, 256) || !aligned(k_latent, 16) || !aligned(v_latent, 16))
+    return KVQ_ERR_ALIGN;
+  if (layer_begin < 0 || int64_t(layer_begin) + num_layers > cfg->num_layers) return KVQ_ERR_RANGE;
+  if (tok_begin < 0) return KVQ_ERR_RANGE;
+  std::vector<char> seen(size_t(cfg->batch), 0);
+  for (int i = 0; i < num_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (s < 0 || s >= cfg->batch) return KVQ_ERR_RANGE;
+    if (seen[s]) return KVQ_ERR_SHAPE;
+    seen[s] = 1;
+    if (tok_end > cfg->capacity[s]) return KVQ_ERR_RANGE;
+  }
+  const std::vector<int64_t> base = row_bases(cfg);
+  LatentStoreArgs a{};
+  a.cache = static_cast<uint8_t*>(cache);
+  a.src[0] = static_cast<const uint16_t*>(k_latent);
+  a.src[1] = static_cast<const uint16_t*>(v_latent);
+  a.plane_bytes = plane_bytes_of(cfg);
+  a.Hkv = cfg->num_kv_heads;
+  a.n = tok_end - tok_begin;
+  a.S = num_seqs;
+  a.layer_begin = layer_begin;
+  a.nl = num_layers;
+  if (int64_t(num_layers) * cfg->num_kv_heads * 2 > 65535) return KVQ_ERR_UNSUPPORTED;
+  for (int s0 = 0; s0 < num_seqs; s0 += kMaxSeq) {
+    const int ns = std::min(kMaxSeq, num_seqs - s0);
+    a.seq_off = s0;
+    for (int i = 0; i < ns; ++i) a.row0[i] = int32_t(base[seq_ids[s0 + i]] + tok_begin);
+    hipError_t e;
+    switch (cfg->rank) {
+      case 32: e = launch_latent_store<32>(a, ns, static_cast<hipStream_t>(stream)); break;
+      case 64: e = launch_latent_store<64>(a, ns, static_cast<hipStream_t>(stream)); break;
+      case 96: e = launch_latent_store<96>(a, ns, static_cast<hipStream_t>(stream)); break;
+      default: e = launch_latent_store<128>(a, ns, static_cast<hipStream_t>(stream)); break;
+    }
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}
+
+extern "C" kvq_status kvq_latent_decode(const kvq_latent_config* cfg, const void* cache,
+                                        int32_t layer_begin, int32_t num_layers,
+                                        const int32_t* seq_lens, const void* up_k,
+                                        const void* up_v, const void* q, void* out,
+                                        float sm_scale, int32_t chunk_tokens, void* workspace,
+                                        size_t* workspace_bytes, void* stream) {
+  kvq_status st = check_latent(cfg);
+  if (st != KVQ_OK) return st;
+  if (!workspace_bytes) return KVQ_ERR_NULL;
+  if (num_layers < 1) return KVQ_ERR_SHAPE;
+  if (layer_begin < 0 || int64_t(layer_begin) + num_layers > cfg->num_layers) return KVQ_ERR_RANGE;
+  if (chunk_tokens < 0 || chunk_tokens % 32) return KVQ_ERR_SHAPE;
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
+  const int D = cfg->head_dim, R = cfg->rank, Hkv = cfg->num_kv_heads;
+  const int G = cfg->num_q_heads / Hkv;
+  const int chunk = latent_chunk(cfg, num_layers, chunk_tokens);
+  const int max_chunks = max_chunks_of(cfg, chunk);
+  if (max_chunks > kLMaxChunks) return KVQ_ERR_UNSUPPORTED;
+  const int64_t entries = int64_t(num_layers) * cfg->batch * Hkv * max_chunks;
+  const int64_t o_bytes = (entries * G * R * 4 + 255) / 256 * 256;
+  const int64_t need = o_bytes + entries * G * 2 * 4;
+  if (!workspace) {
+    *workspace_bytes = size_t(need);
+    return KVQ_OK;
+  }
+  if (int64_t(*workspace_bytes) < need) return KVQ_ERR_WORKSPACE;
+  if (!cache || !seq_lens || !up_k || !up_v || !q || !out) return KVQ_ERR_NULL;
+  if (!aligned(cache, 256) || !aligned(workspace, 256) || !aligned(up_k, 16) ||
+      !aligned(up_v, 16) || !aligned(q, 16) || !aligned(out, 16))
+    return KVQ_ERR_ALIGN;
+  const std::vector<int64_t> base = row_bases(cfg);
+  LatentArgs a{};
+  a.cache = static_cast<const uint8_t*>(cache);
+  a.seq_lens = seq_lens;
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.up_k = static_cast<const uint16_t*>(up_k);
+  a.up_v = static_cast<const uint16_t*>(up_v);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  a.qscale = sm_scale * 1.4426950408889634f;
+  a.plane_bytes = plane_bytes_of(cfg);
+  a.Hkv = Hkv;
+  a.Hq = cfg->num_q_heads;
+  a.G = G;
+  a.B = cfg->batch;
+  a.layer_begin = layer_begin;
+  a.nl = num_layers;
+  a.chunk = chunk;
+  a.max_chunks = max_chunks;
+  for (int s0 = 0; s0 < cfg->batch; s0 += kMaxSeq) {
+    const int ns = std::min(kMaxSeq, cfg->batch - s0);
+    a.seq_off = s0;
+    a.n_seq = ns;
+    a.nxcum[0] = 0;
+    for (int i = 0; i < ns; ++i) {
+      a.row0[i] = int32_t(base[s0 + i]);
+      a.cap[i] = cfg->capacity[s0 + i];
+      a.nxcum[i + 1] = a.nxcum[i] + (a.cap[i] + chunk - 1) / chunk;
+    }
+    if (int64_t(num_layers) * Hkv * a.nxcum[ns] > int64_t(0x7FFFFFFF)) return KVQ_ERR_UNSUPPORTED;
+    if (dispatch_latent(D, R, a, static_cast<hipStream_t>(stream)) != hipSuccess)
+      return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}

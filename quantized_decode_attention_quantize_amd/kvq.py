@@ -29,7 +29,8 @@ KVQ_SRC_F32 = 0
 KVQ_SRC_BF16 = 1
 
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize", "kvq_quantize_ragged", "kvq_decode_attention",
-           "kvq_decode_attention_noalloc", "kvq_status_string")
+           "kvq_decode_attention_noalloc", "kvq_latent_cache_bytes", "kvq_latent_store",
+           "kvq_latent_decode", "kvq_status_string")
 
 
 class KvqError(RuntimeError):
@@ -49,6 +50,13 @@ class _Cfg(C.Structure):
                 ("bf16_range_offsets", C.POINTER(C.c_int32)),
                 ("bf16_range_begin", C.POINTER(C.c_int32)),
                 ("bf16_range_end", C.POINTER(C.c_int32))]
+
+
+class _LatentCfg(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("batch", C.c_int32),
+                ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("rank", C.c_int32),
+                ("capacity", C.POINTER(C.c_int32))]
 
 
 class _Info(C.Structure):
@@ -85,6 +93,14 @@ def lib(path: str = LIB_PATH):
         L.kvq_decode_attention_noalloc.restype = C.c_int
         L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, P,
                                                    P, P, C.c_float, C.c_int32, P]
+        L.kvq_latent_cache_bytes.restype = C.c_int
+        L.kvq_latent_cache_bytes.argtypes = [C.POINTER(_LatentCfg), C.POINTER(C.c_uint64)]
+        L.kvq_latent_store.restype = C.c_int
+        L.kvq_latent_store.argtypes = [C.POINTER(_LatentCfg), P, C.c_int32, C.c_int32, C.c_int32,
+                                       C.POINTER(C.c_int32), C.c_int32, C.c_int32, P, P, P]
+        L.kvq_latent_decode.restype = C.c_int
+        L.kvq_latent_decode.argtypes = [C.POINTER(_LatentCfg), P, C.c_int32, C.c_int32, P, P, P,
+                                        P, P, C.c_float, C.c_int32, P, C.POINTER(C.c_size_t), P]
         L.kvq_status_string.restype = C.c_char_p
         L.kvq_status_string.argtypes = [C.c_int]
         _lib = L
@@ -287,3 +303,89 @@ def kvq_decode_attention_noalloc(cfg: Config, cache, layer_begin: int, num_layer
                                               _dev_ptr(q, "q"), _dev_ptr(out, "out"),
                                               float(sm_scale), chunk_tokens, _stream(stream)),
            "kvq_decode_attention_noalloc")
+
+
+# ---- low-rank latent cache ------------------------------------------------
+
+class LatentConfig:
+    """A kvq_latent_config plus the host array it points into."""
+
+    def __init__(self, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, rank: int, capacity):
+        self.capacity = np.ascontiguousarray(capacity, dtype=np.int32)
+        self.num_layers, self.batch = num_layers, batch
+        self.num_q_heads, self.num_kv_heads = num_q_heads, num_kv_heads
+        self.head_dim, self.rank = head_dim, rank
+        self.c = _LatentCfg(num_layers, batch, num_q_heads, num_kv_heads, head_dim, rank,
+                            self.capacity.ctypes.data_as(C.POINTER(C.c_int32)))
+
+    @property
+    def ref(self):
+        return C.byref(self.c)
+
+
+def kvq_latent_cache_bytes(cfg: LatentConfig) -> int:
+    n = C.c_uint64(0)
+    _check(lib().kvq_latent_cache_bytes(cfg.ref, C.byref(n)), "kvq_latent_cache_bytes")
+    return int(n.value)
+
+
+def _check_bf16(t, name: str, shape) -> None:
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def kvq_latent_store(cfg: LatentConfig, cache, layer_begin: int, num_layers: int,
+                     seq_ids: Sequence[int], tok_begin: int, tok_end: int, k_latent, v_latent,
+                     stream=None) -> None:
+    """k_latent/v_latent: device bf16 [num_layers, len(seq_ids), Hkv, tok_end - tok_begin, r]."""
+    import torch
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+    if cache.dtype != torch.uint8 or cache.numel() < kvq_latent_cache_bytes(cfg):
+        raise ValueError("cache must be a uint8 tensor of kvq_latent_cache_bytes bytes")
+    want = (num_layers, len(ids), cfg.num_kv_heads, max(0, tok_end - tok_begin), cfg.rank)
+    _check_bf16(k_latent, "k_latent", want)
+    _check_bf16(v_latent, "v_latent", want)
+    _check(lib().kvq_latent_store(cfg.ref, _dev_ptr(cache, "cache"), layer_begin, num_layers,
+                                  len(ids), ids.ctypes.data_as(C.POINTER(C.c_int32)), tok_begin,
+                                  tok_end, _dev_ptr(k_latent, "k_latent"),
+                                  _dev_ptr(v_latent, "v_latent"), _stream(stream)),
+           "kvq_latent_store")
+
+
+def latent_workspace_bytes(cfg: LatentConfig, num_layers: int, chunk_tokens: int = 0) -> int:
+    n = C.c_size_t(0)
+    _check(lib().kvq_latent_decode(cfg.ref, None, 0, num_layers, None, None, None, None, None,
+                                   1.0, chunk_tokens, None, C.byref(n), None),
+           "kvq_latent_decode(size query)")
+    return int(n.value)
+
+
+def kvq_latent_decode(cfg: LatentConfig, cache, layer_begin: int, num_layers: int, seq_lens,
+                      up_k, up_v, q, out, sm_scale: float, chunk_tokens: int = 0,
+                      workspace=None, stream=None) -> None:
+    """up_k/up_v: device bf16 [L, Hkv, r, D]; q/out: device bf16 [num_layers, B, Hq, D];
+    seq_lens: device int32 [B]; workspace: device uint8 of latent_workspace_bytes(...)."""
+    import torch
+    if workspace is None:
+        raise ValueError("workspace tensor required (see latent_workspace_bytes)")
+    if cache.dtype != torch.uint8 or cache.numel() < kvq_latent_cache_bytes(cfg):
+        raise ValueError("cache must be a uint8 tensor of kvq_latent_cache_bytes bytes")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != cfg.batch:
+        raise ValueError(f"seq_lens must be int32 [{cfg.batch}]")
+    up = (cfg.num_layers, cfg.num_kv_heads, cfg.rank, cfg.head_dim)
+    _check_bf16(up_k, "up_k", up)
+    _check_bf16(up_v, "up_v", up)
+    io = (num_layers, cfg.batch, cfg.num_q_heads, cfg.head_dim)
+    _check_bf16(q, "q", io)
+    _check_bf16(out, "out", io)
+    n = C.c_size_t(_nbytes(workspace))
+    _check(lib().kvq_latent_decode(cfg.ref, _dev_ptr(cache, "cache"), layer_begin, num_layers,
+                                   _dev_ptr(seq_lens, "seq_lens"), _dev_ptr(up_k, "up_k"),
+                                   _dev_ptr(up_v, "up_v"), _dev_ptr(q, "q"),
+                                   _dev_ptr(out, "out"), float(sm_scale), chunk_tokens,
+                                   _dev_ptr(workspace, "workspace"), C.byref(n),
+                                   _stream(stream)), "kvq_latent_decode")

@@ -51,6 +51,8 @@ TAG_APPEND_V = 8
 TAG_BLOCK_K = 9
 TAG_BLOCK_V = 10
 TAG_TOKENS = 11
+TAG_LATENT = 12
+TAG_UP = 13
 
 
 def _mix64_int(z: int) -> int:
@@ -369,6 +371,65 @@ def two_images(seed: int = 5, tokens_protected: int = 8) -> Workload:
     ranges = sorted([r for r in singles if not (mid <= r[0] < mid + 32)] + [(mid, mid + 32)])
     return Workload("two_images", 1, 1, 28, 4, 128, 64, [T], [vb], [ve], [T], kb, vbits,
                     seed=seed, bf16_ranges=[ranges])
+
+
+@dataclass
+class LatentWorkload:
+    """Synthetic low-rank latent decode workload.
+
+    Per (layer, KV head): latent rows c^K_t, c^V_t of width ``rank`` ~ N(0, 1)
+    and up-projections B_K, B_V [rank, D] ~ N(0, 1/rank), so reconstructed
+    K and V rows have unit variance per element like the quantised
+    workloads' sources; queries N(0, 1).  Everything is bf16.
+    """
+
+    name: str
+    num_layers: int
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    rank: int
+    capacity: List[int]
+    seq_lens: List[int]
+    seed: int = 0
+
+    @property
+    def group_ratio(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def sm_scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.head_dim)))
+
+    def latents(self, layer: int, seq: int, head: int, X: int, t0: int, t1: int) -> np.ndarray:
+        """bf16 bits [t1 - t0, rank] of K (X = 0) or V (X = 1) latents."""
+        key = stream_key(self.seed, TAG_LATENT, layer, seq, head, X)
+        x = normal(key, t0 * self.rank, (t1 - t0) * self.rank).reshape(t1 - t0, self.rank)
+        return f32_to_bf16_bits(x.astype(np.float32))
+
+    def up(self, layer: int, head: int, X: int) -> np.ndarray:
+        """bf16 bits [rank, D] of B_K (X = 0) or B_V (X = 1)."""
+        key = stream_key(self.seed, TAG_UP, layer, head, X)
+        x = normal(key, 0, self.rank * self.head_dim).reshape(self.rank, self.head_dim)
+        return f32_to_bf16_bits((x / math.sqrt(self.rank)).astype(np.float32))
+
+    def q_bits(self, layer: int) -> np.ndarray:
+        key = stream_key(self.seed, TAG_Q, layer, 1)
+        n = self.batch * self.num_q_heads * self.head_dim
+        q = normal(key, 0, n).reshape(self.batch, self.num_q_heads, self.head_dim)
+        return f32_to_bf16_bits(q.astype(np.float32))
+
+
+def llava_latent(seed: int = 6, rank: int = 96, num_layers: int = 28) -> LatentWorkload:
+    """A LLaVA-OneVision-7B-shaped decode step over a per-head latent cache:
+    28 layers x 4 KV heads (28 query heads, D = 128), 6,288 cached tokens.
+    Rank 96: WSVD section 4 reports models keeping 70 % of their parameters
+    (rho1); one r x (E + D) factor pair of a 3584 x 128 head projection keeps
+    r * 3712 / (3584 * 128) of it, 78 % at r = 96, the smallest multiple of 32
+    at or above 70 %."""
+    T = 14 + 6273 + 1
+    return LatentWorkload("llava_latent", num_layers, 1, 28, 4, 128, rank, [T], [T], seed=seed)
 
 
 WORKLOADS = {

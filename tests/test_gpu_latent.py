@@ -1,0 +1,199 @@
+"""GPU parity of the low-rank latent decode (MI355X).
+
+The latent store must write exactly the bytes of the oracle's layout; the
+decode must match the oracle, which rebuilds every K and V row in float64
+from the latents and up-projections and then runs softmax attention, within
+the output tolerance (bf16 output vs the unrounded fp64 result), with the
+kernel's own error (beyond rounding the exact output to bf16) below 2e-4
+relative L2.  That budget follows from the arithmetic: the projected query
+and the probabilities enter the bf16 matrix cores as hi/lo pairs (relative
+error about 2^-17 each), every sum is fp32, so the kernel should add well
+under a tenth of the 1.7e-3 that rounding the exact output to bf16 costs.
+Every case prints its name before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import latent as olat
+from quantized_decode_attention_quantize_amd import kvq, synth
+
+from kvq_testlib import assert_close, bf16_to_f64, kernel_error
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvq.lib()
+    yield
+
+
+def _t():
+    import torch
+    return torch
+
+
+def _bits_dev(bits):
+    t = _t()
+    return t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(t.bfloat16).cuda()
+
+
+class LatentPair:
+    """A latent workload stored by libkvq and held by the oracle."""
+
+    def __init__(self, w: synth.LatentWorkload):
+        t = _t()
+        self.w = w
+        self.cfg = kvq.LatentConfig(w.num_layers, w.batch, w.num_q_heads, w.num_kv_heads,
+                                    w.head_dim, w.rank, w.capacity)
+        self.cache = t.zeros(kvq.kvq_latent_cache_bytes(self.cfg), dtype=t.uint8, device="cuda")
+        L, H = w.num_layers, w.num_kv_heads
+        self.up_bits = [np.stack([np.stack([w.up(l, h, X) for h in range(H)]) for l in range(L)])
+                        for X in (0, 1)]
+        self.up_dev = [_bits_dev(b) for b in self.up_bits]
+        self._lat = {}
+
+    def store(self, layers=None, seqs=None, t0=0, t1=None):
+        """One kvq_latent_store call per (layer, sequence)."""
+        w = self.w
+        for l in (range(w.num_layers) if layers is None else layers):
+            for s in (range(w.batch) if seqs is None else seqs):
+                e = w.capacity[s] if t1 is None else t1
+                kv = [np.stack([w.latents(l, s, h, X, t0, e) for h in range(w.num_kv_heads)])
+                      for X in (0, 1)]
+                kvq.kvq_latent_store(self.cfg, self.cache, l, 1, [s], t0, e,
+                                     _bits_dev(kv[0][None, None]), _bits_dev(kv[1][None, None]))
+
+    def decode(self, lens, layer_begin=0, num_layers=None, chunk=0):
+        t = _t()
+        w = self.w
+        nl = w.num_layers - layer_begin if num_layers is None else num_layers
+        qb = np.stack([w.q_bits(layer_begin + i) for i in range(nl)])
+        q = _bits_dev(qb)
+        out = t.empty_like(q)
+        ws = t.empty(kvq.latent_workspace_bytes(self.cfg, nl, chunk), dtype=t.uint8, device="cuda")
+        lens_d = t.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
+        kvq.kvq_latent_decode(self.cfg, self.cache, layer_begin, nl, lens_d, self.up_dev[0],
+                              self.up_dev[1], q, out, w.sm_scale, chunk, ws)
+        t.cuda.synchronize()
+        return bf16_to_f64(out), qb
+
+    def oracle(self, l, s, i, length, q_bits_row):
+        w = self.w
+        h = i // w.group_ratio
+        key = (l, s, h)
+        if key not in self._lat:
+            self._lat = {key: [olat.bf16_bits_to_f64(w.latents(l, s, h, X, 0, w.capacity[s]))
+                               for X in (0, 1)]}
+        ck, cv = self._lat[key]
+        return olat.decode_one(ck, cv, olat.bf16_bits_to_f64(self.up_bits[0][l, h]),
+                               olat.bf16_bits_to_f64(self.up_bits[1][l, h]),
+                               olat.bf16_bits_to_f64(q_bits_row), length, w.sm_scale)
+
+
+def _check(p, lens, layers=None, chunk=0, what="", budget=2e-4):
+    w = p.w
+    out, qb = p.decode(lens, chunk=chunk)
+    got, ref = [], []
+    for l in (range(w.num_layers) if layers is None else layers):
+        for s in range(w.batch):
+            for i in range(w.num_q_heads):
+                ref.append(p.oracle(l, s, i, lens[s], qb[l, s, i]))
+                got.append(out[l, s, i])
+    got, ref = np.array(got), np.array(ref)
+    assert_close(got, ref, what)
+    assert kernel_error(got, ref, what) <= budget
+    return out
+
+
+def test_latent_store_bitexact():
+    """Bytes of stores in pieces (ragged capacities, two layers, two heads)
+    equal the oracle's element-by-element layout."""
+    _say("latent store bytes")
+    w = synth.LatentWorkload("lat_store", 2, 3, 4, 2, 64, 32, [5, 40, 70], [5, 40, 70], seed=1)
+    p = LatentPair(w)
+    p.store(t0=0, t1=None, seqs=[0])
+    p.store(t0=0, t1=17, seqs=[1, 2])
+    p.store(t0=17, t1=40, seqs=[1, 2])
+    p.store(t0=40, t1=70, seqs=[2])
+    cache = p.cache.cpu().numpy()
+    ref = np.zeros_like(cache)
+    for l in range(2):
+        for h in range(2):
+            for X in (0, 1):
+                for s in range(3):
+                    olat.write_rows(ref, 2, w.capacity, 32, l, h, X, s, 0,
+                                    w.latents(l, s, h, X, 0, w.capacity[s]))
+    mask = np.zeros(cache.size, dtype=bool)
+    for l in range(2):
+        for h in range(2):
+            for X in (0, 1):
+                for s in range(3):
+                    for t in range(w.capacity[s]):
+                        o = olat.latent_offset(2, w.capacity, 32, l, h, X, s, t, 0)
+                        mask[o:o + 64] = True
+    assert int(np.count_nonzero(cache[mask] != ref[mask])) == 0
+    assert int(np.count_nonzero(cache[~mask])) == 0  # nothing written outside the rows
+
+
+def test_latent_decode_tiny():
+    _say("latent decode tiny (D 64, r 32, G 4)")
+    w = synth.LatentWorkload("lat_tiny", 1, 2, 4, 1, 64, 32, [300, 77], [300, 77], seed=2)
+    p = LatentPair(w)
+    p.store()
+    _check(p, [300, 77], what="latent tiny")
+    _check(p, [1, 33], what="latent tiny, short")
+
+
+@pytest.mark.parametrize("rank", [32, 64, 96, 128])
+def test_latent_decode_llava_layer_ranks(rank):
+    """One LLaVA-shaped layer (28/4 heads, D 128, 6,288 tokens), all heads."""
+    _say("latent decode llava layer, rank", rank)
+    p = LatentPair(synth.llava_latent(rank=rank, num_layers=1))
+    p.store()
+    _check(p, p.w.seq_lens, what=f"latent llava r{rank}")
+
+
+@pytest.mark.parametrize("chunk", [32, 256, 4096])
+def test_latent_decode_chunks_and_ragged(chunk):
+    """D 64, 16 query heads per KV head, ragged lengths below capacity,
+    fixed chunks from one step to whole sequences."""
+    _say("latent decode ragged, chunk", chunk)
+    w = synth.LatentWorkload("lat_rag", 2, 3, 32, 2, 64, 64, [1000, 64, 2500], [999, 1, 1777],
+                             seed=3)
+    p = LatentPair(w)
+    p.store()
+    _check(p, w.seq_lens, chunk=chunk, what=f"latent ragged chunk {chunk}")
+
+
+def test_latent_decode_many_sequences():
+    """70 sequences: two launches of the sequence table."""
+    _say("latent decode 70 sequences")
+    rng = np.random.default_rng(4)
+    caps = [int(x) for x in rng.integers(1, 300, 70)]
+    lens = [int(rng.integers(1, c + 1)) for c in caps]
+    w = synth.LatentWorkload("lat_many", 1, 70, 8, 2, 128, 64, caps, lens, seed=4)
+    p = LatentPair(w)
+    p.store()
+    _check(p, lens, what="latent 70 sequences")
+
+
+def test_latent_decode_full_step_sampled_and_deterministic():
+    """The 28-layer step at full size: three layers against the oracle, and
+    two calls give identical bytes."""
+    _say("latent decode 28-layer step, sampled layers")
+    p = LatentPair(synth.llava_latent())
+    p.store()
+    out = _check(p, p.w.seq_lens, layers=[0, 13, 27], what="latent step")
+    again, _ = p.decode(p.w.seq_lens)
+    assert np.array_equal(out, again)

@@ -401,3 +401,82 @@ def test_bf16_range_validation(L):
     general_plain = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
                                bf16_ranges=[[]])
     assert _dec(L, general_plain, ws=None)[0] == kvq.KVQ_OK
+
+
+def test_latent_cache_bytes_and_validation(L):
+    """Latent cache: sizes equal the oracle layout's, malformed configs and
+    calls are refused before any launch."""
+    from oracle import latent as olat
+
+    def cfg(**over):
+        base = dict(num_layers=2, batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    rank=96, capacity=[5, 33, 64])
+        base.update(over)
+        return kvq.LatentConfig(**base)
+
+    def status(c):
+        try:
+            kvq.kvq_latent_cache_bytes(c)
+            return kvq.KVQ_OK
+        except kvq.KvqError as e:
+            return e.status
+
+    for r, D in ((32, 64), (64, 64), (32, 128), (96, 128), (128, 128)):
+        c = cfg(rank=r, head_dim=D)
+        assert kvq.kvq_latent_cache_bytes(c) == olat.cache_bytes(2, 2, [5, 33, 64], r)
+    assert status(cfg(rank=48)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert status(cfg(rank=128, head_dim=64)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert status(cfg(head_dim=96)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert status(cfg(num_q_heads=7)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert status(cfg(num_q_heads=34)) == kvq.KVQ_ERR_UNSUPPORTED   # ratio 17
+    assert status(cfg(capacity=[5, 0, 64])) == kvq.KVQ_ERR_SHAPE
+    assert status(cfg(num_layers=0)) == kvq.KVQ_ERR_SHAPE
+    assert status(cfg(batch=1, capacity=[1 << 23], rank=128)) == kvq.KVQ_ERR_UNSUPPORTED
+    c = cfg()
+    assert L.kvq_latent_cache_bytes(c.ref, None) == kvq.KVQ_ERR_NULL
+    c.c.capacity = C.POINTER(C.c_int32)()
+    assert L.kvq_latent_cache_bytes(c.ref, C.byref(C.c_uint64())) == kvq.KVQ_ERR_NULL
+
+    c = cfg()
+    ids = np.array([1], dtype=np.int32)
+    ip = ids.ctypes.data_as(C.POINTER(C.c_int32))
+
+    def store(layer_begin=0, nl=1, t0=0, t1=8, cache=A256, k=A16, ids_p=ip, n=1):
+        return L.kvq_latent_store(c.ref, C.c_void_p(cache) if cache else None, layer_begin, nl,
+                                  n, ids_p, t0, t1, C.c_void_p(k) if k else None,
+                                  C.c_void_p(A16), None)
+    assert store(t1=34) == kvq.KVQ_ERR_RANGE      # past capacity 33
+    assert store(t0=-1) == kvq.KVQ_ERR_RANGE
+    assert store(layer_begin=1, nl=2) == kvq.KVQ_ERR_RANGE
+    assert store(cache=A256 + 16) == kvq.KVQ_ERR_ALIGN
+    assert store(k=A16 + 2) == kvq.KVQ_ERR_ALIGN
+    assert store(k=None) == kvq.KVQ_ERR_NULL
+    assert store(t0=8, t1=4) == kvq.KVQ_ERR_SHAPE
+    assert store(t0=3, t1=3) == kvq.KVQ_OK          # empty: no launch
+    two = np.array([1, 1], dtype=np.int32)
+    assert store(ids_p=two.ctypes.data_as(C.POINTER(C.c_int32)), n=2) == kvq.KVQ_ERR_SHAPE
+    bad = np.array([3], dtype=np.int32)
+    assert store(ids_p=bad.ctypes.data_as(C.POINTER(C.c_int32))) == kvq.KVQ_ERR_RANGE
+
+    def dec(layer_begin=0, nl=1, chunk=0, ws=A256 + 4096, ws_bytes=1 << 30, q=A16, scale=0.1):
+        n = C.c_size_t(ws_bytes)
+        st = L.kvq_latent_decode(c.ref, C.c_void_p(A256), layer_begin, nl, C.c_void_p(A16),
+                                 C.c_void_p(A16), C.c_void_p(A16), C.c_void_p(q) if q else None,
+                                 C.c_void_p(A16 + 4096), scale, chunk,
+                                 C.c_void_p(ws) if ws else None, C.byref(n), None)
+        return st, n.value
+    st, need = dec(ws=None)
+    assert st == kvq.KVQ_OK and need > 0
+    entries = 1 * 3 * 2 * 1  # one chunk per sequence at these capacities
+    assert need == -(-(entries * 4 * 96 * 4) // 256) * 256 + entries * 4 * 2 * 4
+    assert dec(ws_bytes=need - 1)[0] == kvq.KVQ_ERR_WORKSPACE
+    assert dec(layer_begin=2)[0] == kvq.KVQ_ERR_RANGE
+    assert dec(nl=0)[0] == kvq.KVQ_ERR_SHAPE
+    assert dec(chunk=48)[0] == kvq.KVQ_ERR_SHAPE
+    assert dec(scale=0.0)[0] == kvq.KVQ_ERR_SHAPE
+    assert dec(q=None)[0] == kvq.KVQ_ERR_NULL
+    assert dec(q=A16 + 4)[0] == kvq.KVQ_ERR_ALIGN
+    assert dec(ws=A256 + 64)[0] == kvq.KVQ_ERR_ALIGN
+    # 32-token chunks: the longest sequence (64 rows) has 2, so 2 slots per entry
+    assert dec(chunk=32, ws=None)[1] == -(-(1 * 3 * 2 * 2 * 4 * 96 * 4) // 256) * 256 + \
+        1 * 3 * 2 * 2 * 4 * 2 * 4
