@@ -385,7 +385,7 @@ kvq_status kvq_latent_store(const kvq_latent_config *cfg, void *cache, int32_t l
  *              16-byte aligned: B_K and B_V of every (layer, KV head)
  *   q, out     device bf16 [num_layers, batch, Hq, D], 16-byte aligned; out
  *              must not alias any input or the workspace
- *   chunk_tokens  0 = library choice (about four workgroups per compute unit
+ *   chunk_tokens  0 = library choice (about one workgroup per compute unit
  *              over the call), else a positive multiple of 32 = tokens per
  *              workgroup.  Each chunk's summation order is fixed: repeated
  *              calls give identical bytes.

@@ -40,6 +40,9 @@ constexpr int kLWaves = 4;                // waves per decode workgroup
 constexpr int kLThreads = 64 * kLWaves;
 constexpr float kLLazy = 6.0f;            // p <= 2^6 between rescales
 constexpr int kLMaxChunks = 4096;         // partial slots per (layer, seq, head)
+#ifndef KVQ_LAT_AHEAD
+#define KVQ_LAT_AHEAD 0  // ring of 1 + KVQ_LAT_AHEAD steps; 0: two buffers, copied
+#endif
 
 struct LatentArgs {
   const uint8_t* cache;
@@ -48,7 +51,7 @@ struct LatentArgs {
   uint16_t* out;            // bf16 [nl, B, Hq, D]
   const uint16_t* up_k;     // bf16 [L, Hkv, r, D]
   const uint16_t* up_v;
-  float* ws_o;              // [entries][G][r] unnormalised latent outputs
+  float* ws_o;              // [entries][G][D] unnormalised outputs (B_V applied)
   float* ws_ml;             // [entries][G][2] (max in log2 units, sum)
   float qscale;             // sm_scale * log2(e)
   int64_t plane_bytes;
@@ -223,9 +226,16 @@ __device__ inline void compute_lstep(LWave<R>& w, const LStep<R>& st, const u32x
 // take the chunk's 32-token steps in turn, then combine into one partial.
 template <int D, int R>
 __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) {
-  __shared__ float q_lds[16][R + 4];
-  __shared__ float o_lds[kLWaves][16][R];
+  constexpr int kParts = 256 / D;  // threads per output column in the projection
+  constexpr int kJ = R / kParts;   // latent indices per thread in the projection
+  constexpr int kBig = kLWaves * 16 * R > kParts * 16 * D ? kLWaves * 16 * R : kParts * 16 * D;
+  __shared__ float q_lds[16][R + 4];  // q', later the chunk's combined latent output
+  __shared__ float big[kBig];         // the waves' outputs, later projection sums
   __shared__ float ml_lds[kLWaves][16][2];
+  __shared__ float mlc[16][2];
+  __shared__ uint4 bv_lds[R * D / 8];  // B_V of this (layer, head), bf16
+  float(*o_lds)[16][R] = reinterpret_cast<float(*)[16][R]>(big);
+  float(*part)[16][D] = reinterpret_cast<float(*)[16][D]>(big);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, j = lane >> 4;
 
@@ -248,6 +258,17 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
   const Rsrc kr = make_rsrc(kplane, a.plane_bytes);
   const Rsrc vr = make_rsrc(kplane + a.plane_bytes, a.plane_bytes);
   const int row0 = a.row0[i];
+
+  // B_V goes to LDS now, its loads in flight with the query's
+  const int64_t lhg_v = int64_t(a.layer_begin + l) * a.Hkv + h;
+  {
+    const uint4* bvg = reinterpret_cast<const uint4*>(a.up_v + lhg_v * R * D);
+    uint4 t[R * D / 8 / kLThreads];
+#pragma unroll
+    for (int k = 0; k < R * D / 8 / kLThreads; ++k) t[k] = bvg[threadIdx.x + kLThreads * k];
+#pragma unroll
+    for (int k = 0; k < R * D / 8 / kLThreads; ++k) bv_lds[threadIdx.x + kLThreads * k] = t[k];
+  }
 
   // ---- q' = qscale * B_K q for the group's heads, on the matrix cores ----
   // B operand: lane (n, j) holds q_n[32 sd + 8 j .. + 8] (zeros past G);
@@ -290,26 +311,67 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
 #pragma unroll
   for (int mb = 0; mb < R / 16; ++mb) w.o[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int nsteps = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
+  // Steps in flight per wave: the current one plus KVQ_LAT_AHEAD loaded
+  // ahead, in a ring of buffers with static indices (the loop is unrolled
+  // over the ring).
+  auto rows_of = [&](int k) { return min(32, t1 - t0 - 32 * k); };
+  auto load = [&](int k, LStep<R>& b) {
+    if (k < nsteps) load_lstep<R>(kr, vr, row0 + t0 + 32 * k, rows_of(k), n, j, b);
+  };
+#if KVQ_LAT_AHEAD == 2
+  {
+    LStep<R> b0, b1, b2;
+    load(wave, b0);
+    load(wave + kLWaves, b1);
+    for (int k = wave; k < nsteps; k += 3 * kLWaves) {
+      load(k + 2 * kLWaves, b2);
+      compute_lstep<R>(w, b0, qhi, qlo, rows_of(k), j);
+      if (k + kLWaves >= nsteps) break;
+      load(k + 3 * kLWaves, b0);
+      compute_lstep<R>(w, b1, qhi, qlo, rows_of(k + kLWaves), j);
+      if (k + 2 * kLWaves >= nsteps) break;
+      load(k + 4 * kLWaves, b1);
+      compute_lstep<R>(w, b2, qhi, qlo, rows_of(k + 2 * kLWaves), j);
+    }
+  }
+#elif KVQ_LAT_AHEAD == 0
   if (wave < nsteps) {
     LStep<R> cur, nxt;
     int k = wave;
-    load_lstep<R>(kr, vr, row0 + t0 + 32 * k, min(32, t1 - t0 - 32 * k), n, j, cur);
+    load(k, cur);
     while (true) {
-      const int rows = min(32, t1 - t0 - 32 * k);
       const int kn = k + kLWaves;
       if (kn < nsteps) {
-        load_lstep<R>(kr, vr, row0 + t0 + 32 * kn, min(32, t1 - t0 - 32 * kn), n, j, nxt);
-        compute_lstep<R>(w, cur, qhi, qlo, rows, j);
+        load(kn, nxt);
+        compute_lstep<R>(w, cur, qhi, qlo, rows_of(k), j);
         cur = nxt;
         k = kn;
       } else {
-        compute_lstep<R>(w, cur, qhi, qlo, rows, j);
+        compute_lstep<R>(w, cur, qhi, qlo, rows_of(k), j);
         break;
       }
     }
   }
+#else
+  {
+    LStep<R> b0, b1;
+    load(wave, b0);
+    for (int k = wave; k < nsteps; k += 2 * kLWaves) {
+      load(k + kLWaves, b1);
+      compute_lstep<R>(w, b0, qhi, qlo, rows_of(k), j);
+      if (k + kLWaves >= nsteps) break;
+      load(k + 2 * kLWaves, b0);
+      compute_lstep<R>(w, b1, qhi, qlo, rows_of(k + kLWaves), j);
+    }
+  }
+#endif
 
-  // ---- combine the waves into the chunk's partial ------------------------
+  // ---- combine the waves, apply B_V, write the chunk's partial ----------
+  // The chunk's latent output is projected here, so partials (and the
+  // merge) are D wide; a call whose sequences each fit one chunk writes the
+  // final output directly and needs no merge.
+  const uint16_t* bv = reinterpret_cast<const uint16_t*>(bv_lds);
+  const int d = threadIdx.x % D, pt = threadIdx.x / D;
   const float l_col = sum_quarters(w.l);
 #pragma unroll
   for (int mb = 0; mb < R / 16; ++mb)
@@ -320,8 +382,7 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
     ml_lds[wave][n][1] = l_col;
   }
   __syncthreads();
-  const int64_t p = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks + x;
-  for (int idx = threadIdx.x; idx < G * R; idx += kLThreads) {
+  for (int idx = threadIdx.x; idx < 16 * R; idx += kLThreads) {
     const int hh = idx / R, jj = idx - hh * R;
     float M = -INFINITY;
 #pragma unroll
@@ -335,62 +396,115 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
       o = __builtin_fmaf(f, o_lds[v][hh][jj], o);
       L = __builtin_fmaf(f, lv, L);
     }
-    a.ws_o[(p * G + hh) * R + jj] = o;
+    q_lds[hh][jj] = hh < G ? o : 0.0f;
     if (jj == 0) {
-      a.ws_ml[(p * G + hh) * 2] = M;
-      a.ws_ml[(p * G + hh) * 2 + 1] = L;
+      mlc[hh][0] = M;
+      mlc[hh][1] = L;
+    }
+  }
+  __syncthreads();
+  float y[16];
+#pragma unroll
+  for (int hh = 0; hh < 16; ++hh) y[hh] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kJ; ++k)
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh)
+      y[hh] = __builtin_fmaf(q_lds[hh][pt + kParts * k], bf16_lo(bv[(pt + kParts * k) * D + d]),
+                             y[hh]);
+#pragma unroll
+  for (int hh = 0; hh < 16; ++hh) part[pt][hh][d] = y[hh];
+  __syncthreads();
+  const int64_t p = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks + x;
+  uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += kLThreads) {
+    const int hh = idx / D, dd = idx - hh * D;
+    float v = part[0][hh][dd];
+#pragma unroll
+    for (int k = 1; k < kParts; ++k) v += part[k][hh][dd];
+    if (a.max_chunks == 1) {
+      outp[int64_t(hh) * D + dd] = uint16_t(bf16_bits(v / mlc[hh][1]));
+    } else {
+      a.ws_o[(p * G + hh) * D + dd] = v;
+      if (dd == 0) {
+        a.ws_ml[(p * G + hh) * 2] = mlc[hh][0];
+        a.ws_ml[(p * G + hh) * 2 + 1] = mlc[hh][1];
+      }
     }
   }
 }
 
 // One workgroup per (layer, sequence, KV head): log-sum-exp merge of the
-// chunks' partials, then out = (merged latent output) B_V, rounded to bf16.
-template <int D, int R>
+// chunks' D-wide partials, rounded to bf16.  The merge is latency-bound, so
+// all global loads of a block of up to kMB chunks -- the (m, l) pairs and
+// the partial outputs -- are issued before the block's first barrier.
+constexpr int kMB = 8;  // chunks per merge block
+template <int D>
 __global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
-  __shared__ float ml[16][2];
-  __shared__ float ob[16][R];
+  constexpr int kE = 16 * D / 256;  // (head, column) elements per thread
+  __shared__ float2 mls[kMB][16];
+  __shared__ float fx[kMB][16];
+  __shared__ float scl[16];
+  __shared__ float Ls[16];
   const int G = a.G;
   const int e = blockIdx.x;
   const int h = e % a.Hkv, i = (e / a.Hkv) % a.n_seq, l = e / (a.Hkv * a.n_seq);
   const int s = a.seq_off + i, nx = a.nxcum[i + 1] - a.nxcum[i];
   const int64_t p0 = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks;
   const int tid = threadIdx.x;
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int x = 0; x < nx; ++x) {
-      const float* m = a.ws_ml + ((p0 + x) * G + tid) * 2;
-      if (m[1] > 0.0f) M = fmaxf(M, m[0]);
+  const float2* mlp = reinterpret_cast<const float2*>(a.ws_ml);
+  float acc[kE];
+#pragma unroll
+  for (int k = 0; k < kE; ++k) acc[k] = 0.0f;
+  float M = -INFINITY, L = 0.0f;  // running (max, sum) of head tid (threads < 16)
+  for (int xb = 0; xb < nx; xb += kMB) {
+    const int nb = min(kMB, nx - xb);
+    float ov[kMB][kE];
+#pragma unroll
+    for (int x = 0; x < kMB; ++x)
+#pragma unroll
+      for (int k = 0; k < kE; ++k) {
+        const int idx = tid + 256 * k, hh = idx / D;
+        ov[x][k] = x < nb && hh < G ? a.ws_o[(p0 + xb + x) * G * D + idx] : 0.0f;
+      }
+    if (tid < kMB * 16) {
+      const int x = tid >> 4, hh = tid & 15;
+      mls[x][hh] = x < nb && hh < G ? mlp[(p0 + xb + x) * G + hh] : make_float2(-INFINITY, 0.0f);
     }
-    float L = 0.0f;
-    for (int x = 0; x < nx; ++x) {
-      const float* m = a.ws_ml + ((p0 + x) * G + tid) * 2;
-      if (m[1] > 0.0f) L = __builtin_fmaf(m[1], __builtin_amdgcn_exp2f(m[0] - M), L);
+    __syncthreads();
+    if (tid < 16) {  // new running max; this block's weights relative to it
+      float Mn = M;
+      for (int x = 0; x < nb; ++x)
+        if (mls[x][tid].y > 0.0f) Mn = fmaxf(Mn, mls[x][tid].x);
+      const float sc = L > 0.0f ? __builtin_amdgcn_exp2f(M - Mn) : 0.0f;
+      L *= sc;
+      for (int x = 0; x < kMB; ++x) {
+        const float2 v = mls[x][tid];
+        const float f = x < nb && v.y > 0.0f ? __builtin_amdgcn_exp2f(v.x - Mn) : 0.0f;
+        fx[x][tid] = f;
+        L = __builtin_fmaf(f, v.y, L);
+      }
+      scl[tid] = sc;  // factor for the sums of earlier blocks
+      M = Mn;
     }
-    ml[tid][0] = M;
-    ml[tid][1] = L;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kE; ++k) {
+      const int hh = (tid + 256 * k) / D;
+      float o = acc[k] * scl[hh];
+#pragma unroll
+      for (int x = 0; x < kMB; ++x) o = __builtin_fmaf(fx[x][hh], ov[x][k], o);
+      acc[k] = o;
+    }
+    __syncthreads();  // fx and scl are rewritten by the next block
   }
+  if (tid < 16) Ls[tid] = L;
   __syncthreads();
-  for (int idx = tid; idx < G * R; idx += 256) {
-    const int hh = idx / R, jj = idx - hh * R;
-    const float M = ml[hh][0];
-    float o = 0.0f;
-    for (int x = 0; x < nx; ++x) {
-      const float* m = a.ws_ml + ((p0 + x) * G + hh) * 2;
-      if (m[1] > 0.0f)
-        o = __builtin_fmaf(__builtin_amdgcn_exp2f(m[0] - M), a.ws_o[((p0 + x) * G + hh) * R + jj], o);
-    }
-    ob[hh][jj] = o / ml[hh][1];
-  }
-  __syncthreads();
-  const int64_t lhg = int64_t(a.layer_begin + l) * a.Hkv + h;
-  const uint16_t* bv = a.up_v + lhg * R * D;
   uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int hh = idx / D, d = idx - hh * D;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int jj = 0; jj < R; ++jj) acc = __builtin_fmaf(ob[hh][jj], bf16_lo(bv[jj * D + d]), acc);
-    outp[int64_t(hh) * D + d] = uint16_t(bf16_bits(acc));
+#pragma unroll
+  for (int k = 0; k < kE; ++k) {
+    const int idx = tid + 256 * k, hh = idx / D;
+    if (hh < G) outp[idx] = uint16_t(bf16_bits(acc[k] / Ls[hh]));
   }
 }
 
@@ -442,17 +556,29 @@ kvq_status check_latent(const kvq_latent_config* c) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Tokens per decode workgroup: about four workgroups per compute unit over
-// the whole call, in 128-token multiples (one step per wave at least).
+// Tokens per decode workgroup: the shortest 128-token multiple (at least 256)
+// for which the call has at most one workgroup per compute unit.  Long
+// chunks measured fastest (the per-workgroup query projection and epilogue
+// are paid least often), and a count just above the unit count leaves some
+// units with two workgroups and the rest idle at the end.
 int latent_chunk(const kvq_latent_config* c, int num_layers, int chunk_tokens) {
   if (chunk_tokens > 0) return chunk_tokens;
   int64_t work = 0;
-  for (int s = 0; s < c->batch; ++s) work += c->capacity[s];
-  work *= int64_t(num_layers) * c->num_kv_heads;
-  const int64_t target = 4 * int64_t(device_cus());
-  int64_t ch = (work + target - 1) / target;
-  ch = (ch + 127) / 128 * 128;
-  return int(std::min<int64_t>(std::max<int64_t>(ch, 256), 1 << 20));
+  int longest = 1;
+  for (int s = 0; s < c->batch; ++s) {
+    work += c->capacity[s];
+    longest = std::max(longest, int(c->capacity[s]));
+  }
+  const int64_t lh = int64_t(num_layers) * c->num_kv_heads, units = device_cus();
+  int64_t ch = (work * lh + units - 1) / units;
+  ch = std::max<int64_t>((ch + 127) / 128 * 128, 256);
+  auto count = [&](int64_t chunk) {
+    int64_t n = 0;
+    for (int s = 0; s < c->batch; ++s) n += (c->capacity[s] + chunk - 1) / chunk;
+    return n * lh;
+  };
+  while (ch < longest && count(ch) > units) ch += 128;
+  return int(std::min<int64_t>(ch, 1 << 20));
 }
 
 int max_chunks_of(const kvq_latent_config* c, int chunk) {
@@ -466,9 +592,8 @@ hipError_t launch_latent(const LatentArgs& a, hipStream_t st) {
   const int units = a.nl * a.Hkv * a.nxcum[a.n_seq];
   hipLaunchKernelGGL((latent_decode_kernel<D, R>), dim3(units), dim3(kLThreads), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((latent_merge_kernel<D, R>), dim3(a.nl * a.n_seq * a.Hkv), dim3(256), 0, st,
-                     a);
+  if (e != hipSuccess || a.max_chunks == 1) return e;  // one chunk: written directly
+  hipLaunchKernelGGL((latent_merge_kernel<D>), dim3(a.nl * a.n_seq * a.Hkv), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -575,7 +700,7 @@ extern "C" kvq_status kvq_latent_decode(const kvq_latent_config* cfg, const void
   const int max_chunks = max_chunks_of(cfg, chunk);
   if (max_chunks > kLMaxChunks) return KVQ_ERR_UNSUPPORTED;
   const int64_t entries = int64_t(num_layers) * cfg->batch * Hkv * max_chunks;
-  const int64_t o_bytes = (entries * G * R * 4 + 255) / 256 * 256;
+  const int64_t o_bytes = (entries * G * D * 4 + 255) / 256 * 256;
   const int64_t need = o_bytes + entries * G * 2 * 4;
   if (!workspace) {
     *workspace_bytes = size_t(need);
