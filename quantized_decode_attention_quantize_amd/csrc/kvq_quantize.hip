@@ -174,50 +174,13 @@ __device__ inline void hadamard_row(float (&x)[kE], int lane_in_row) {
   for (int i = 0; i < kE; ++i) x[i] = x[i] * kScale;
 }
 
+// Stores one row's lane share: this lane's kE values x of position t (row
+// r of the call; inactive lanes past the call's rows only join the group
+// reductions).
 template <int D>
-__global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
-  constexpr int LPR = D / kE;            // lanes per row
-  constexpr int RPB = 256 / LPR;         // rows per block
-  const int lane_in_row = threadIdx.x % LPR;
-  const int row_in_block = threadIdx.x / LPR;
-  const int z = blockIdx.z;              // (lh, X)
-  const int lh = z >> 1, X = z & 1;
-  const int sl = blockIdx.y;             // sequence within this launch
-  const int r = blockIdx.x * RPB + row_in_block;  // token within [0, n_tok)
-  const bool active = r < a.n_tok;
-  const int rr = active ? r : a.n_tok - 1;  // keep inactive lanes in bounds
-  const int t = a.tok0[sl] + rr;
-
-  // source element offset: [nl, num_seqs, Hkv, n_tok, D]
-  const int glh = a.lh_off + lh;         // layer-local * Hkv + head
-  const int l_local = glh / a.Hkv, h = glh % a.Hkv;
-  const int64_t src_row =
-      ((int64_t(l_local) * a.num_seqs_total + (a.seq_off + sl)) * a.Hkv + h) * a.n_tok + rr;
-  const void* src = X ? a.v_src : a.k_src;
-  float x[kE];
-  if (a.src_bf16) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) +
-                                                    src_row * D + lane_in_row * kE);
-#pragma unroll
-    for (int k = 0; k < kE / 8; ++k) {
-      const uint4 v = p[k];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[8 * k + 2 * i] = __builtin_bit_cast(float, w[i] << 16);
-        x[8 * k + 2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) +
-                                                      src_row * D + lane_in_row * kE);
-#pragma unroll
-    for (int k = 0; k < kE / 4; ++k) {
-      const float4 u = p[k];
-      x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
-    }
-  }
-
+__device__ __forceinline__ void quantize_row(const QuantizeArgs& a, float (&x)[kE], int t,
+                                             bool active, int lane_in_row, int sl, int lh,
+                                             int X) {
   const int bits = a.bits[lh][X];
   const int vb = a.vb[sl], ve = a.ve[sl];
   // Position t is coded when it lies in the coded span and in none of the
@@ -282,6 +245,54 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
       reinterpret_cast<uint4*>(rowp + lane_in_row * (2 * kE))[k] = o;
     }
   }
+}
+
+// One row per D/kE lanes, 256 / (D/kE) rows per workgroup.  Instances per
+// source dtype: the bf16 one holds half the source registers of the fp32
+// one, which keeps more waves resident (the kernel is bound by how many rows
+// are in flight, not by its arithmetic).
+template <int D, bool BF16>  // BF16: bf16 sources (else fp32)
+__global__ __launch_bounds__(256) void quantize_kernel(QuantizeArgs a) {
+  constexpr int LPR = D / kE;            // lanes per row
+  constexpr int RPB = 256 / LPR;         // rows per workgroup
+  const int lane_in_row = threadIdx.x % LPR;
+  const int row_in_block = threadIdx.x / LPR;
+  const int z = blockIdx.z;              // (lh, X)
+  const int lh = z >> 1, X = z & 1;
+  const int sl = blockIdx.y;             // sequence within this launch
+  const int r = blockIdx.x * RPB + row_in_block;  // row within [0, n_tok)
+  const bool active = r < a.n_tok;
+  const int rr = active ? r : a.n_tok - 1;  // keep inactive lanes in bounds
+  // source element offset: [nl, num_seqs, Hkv, n_tok, D]
+  const int glh = a.lh_off + lh;         // layer-local * Hkv + head
+  const int l_local = glh / a.Hkv, h = glh % a.Hkv;
+  const int64_t src_row =
+      ((int64_t(l_local) * a.num_seqs_total + (a.seq_off + sl)) * a.Hkv + h) * a.n_tok + rr;
+  const void* src = X ? a.v_src : a.k_src;
+  float x[kE];
+  if constexpr (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) +
+                                                    src_row * D + lane_in_row * kE);
+#pragma unroll
+    for (int k = 0; k < kE / 8; ++k) {
+      const uint4 v = p[k];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * k + 2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        x[8 * k + 2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) +
+                                                      src_row * D + lane_in_row * kE);
+#pragma unroll
+    for (int k = 0; k < kE / 4; ++k) {
+      const float4 u = p[k];
+      x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
+    }
+  }
+  quantize_row<D>(a, x, a.tok0[sl] + rr, active, lane_in_row, sl, lh, X);
 }
 
 // Per-channel K (k_per_channel): one workgroup per (slot, sequence, block of
@@ -360,10 +371,14 @@ hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_lau
                            hipStream_t stream) {
   const int rpb = 256 / (a.D / kE);  // rows per block
   dim3 grid((a.n_tok + rpb - 1) / rpb, n_seq_launch, n_lh_launch * 2);
-  if (a.D == 128)
-    hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, stream, a);
+  if (a.D == 128 && a.src_bf16)
+    hipLaunchKernelGGL((quantize_kernel<128, true>), grid, dim3(256), 0, stream, a);
+  else if (a.D == 128)
+    hipLaunchKernelGGL((quantize_kernel<128, false>), grid, dim3(256), 0, stream, a);
+  else if (a.src_bf16)
+    hipLaunchKernelGGL((quantize_kernel<64, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((quantize_kernel<64, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
