@@ -249,6 +249,12 @@ int main() {
                   std::vector<uint8_t>(8, 2), 0, 1);
   bad += run_case("pc mixed", 2, 3, 8, 2, 64, 32, {400, 1, 970}, {3, 0, 10}, {350, 1, 970},
                   {4, 8, 8, 2}, {2, 4, 8, 4}, 0, 1);
+  // one layer (a small call: library-chosen 1024-token chunks), plain and
+  // per-channel
+  bad += run_case("1x4 6288", 1, 1, 28, 4, 128, 64, {6288}, {14}, {6287},
+                  std::vector<uint8_t>(4, 4), std::vector<uint8_t>(4, 2), 0);
+  bad += run_case("pc 1x4 6288", 1, 1, 28, 4, 128, 64, {6288}, {14}, {6287},
+                  std::vector<uint8_t>(4, 4), std::vector<uint8_t>(4, 2), 0, 1);
   // bf16 ranges inside the visual spans (static split for those sequences)
   using R = std::vector<std::vector<std::pair<int, int>>>;
   for (int ch : {0, 1024}) {
