@@ -5,6 +5,8 @@ from __future__ import annotations
 
 from typing import Iterable, List, Optional, Sequence
 
+import os
+
 import numpy as np
 
 import oracle
@@ -156,6 +158,15 @@ class Pair:
         out, _ = oracle.decode_one(self.ocfg, self.ocache, layer, seq, qhead, length,
                                    q_bits_row, self.w.sm_scale)
         return out
+
+    def oracle_decode_many(self, jobs):
+        """oracle_decode over (layer, seq, qhead, length, q_bits_row) jobs on a
+        pool of host threads (the C oracle runs without the interpreter lock),
+        results in job order."""
+        from concurrent.futures import ThreadPoolExecutor
+        workers = max(1, min(16, os.cpu_count() or 1))
+        with ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(lambda j: self.oracle_decode(*j), jobs))
 
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
