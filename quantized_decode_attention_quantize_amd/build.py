@@ -15,8 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip",
-           "kvq_latent.hip"]
+SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode_mfma.hip", "kvq_latent.hip"]
 # The benchmark's read-only HBM stream kernel: a library of its own, so
 # libkvq's exports stay exactly the ABI of include/kvq.h.
 BENCH_LIB = os.path.join(HERE, "libkvqbench.so")

@@ -161,17 +161,6 @@ int bits_of(const kvq_config* c, int l, int h, int X) {
   return X ? c->v_bits[l * c->num_kv_heads + h] : c->k_bits[l * c->num_kv_heads + h];
 }
 
-// Library choice of the split chunk: aim for about `target` workgroups over
-// the whole call, in multiples of `quantum` tokens.
-int default_chunk(const kvq_config* c, int nl, int quantum, int64_t target) {
-  int64_t rows = 0;
-  for (int s = 0; s < c->batch; ++s) rows += c->capacity[s];
-  const int64_t work = rows * nl * c->num_kv_heads;
-  int64_t ch = (work + target - 1) / target;
-  ch = ((ch + quantum - 1) / quantum) * quantum;
-  return int(std::max<int64_t>(ch, quantum));
-}
-
 }  // namespace
 
 // Compute units of the current device (256 on MI355X); 256 when no device
@@ -198,19 +187,19 @@ static_assert(sizeof(QuantizeArgs) <= 4096, "quantize kernel arguments exceed 4 
 
 // One kernel launch of a decode call: up to kMaxLH (layer, head) slots of
 // one visual format over up to kMaxSeq sequences.  Work is laid out in units
-// (waves of the matrix-core kernel, workgroups of the general one): slot i
-// and sequence s get mult[i] * nx[s] consecutive units, slot-major.
+// (waves): slot i and sequence s get mult[i] * nx[s] consecutive units,
+// slot-major.
 struct LaunchPlan {
-  int key;                  // matrix-core format key kb * 32 + vb; -1: general kernel
+  int key;                  // format key kb * 32 + vb
   int s0, ns;               // sequences [s0, s0 + ns) of the call
   std::vector<int> glh;     // per slot: layer-local * Hkv + head
   std::vector<int> mult;    // per slot
   std::vector<int> nx;      // per sequence of the launch
-  bool merge_after;         // general kernel: merge partials after this launch
 };
 
 struct DecodePlan {
   int chunk;                // tokens per split; 0 = balanced split
+  int nsub, gsub;           // query-head subgroups of every launch, heads in each (<=)
   std::vector<LaunchPlan> launches;
   int max_chunks;           // partial slots per (layer, seq, head)
   int64_t entries;
@@ -327,22 +316,24 @@ void balance_launch(const std::vector<double>& cost, const std::vector<double>& 
 // per workgroup.
 int64_t pieces(int64_t w0, int64_t n, int per) { return (w0 + n - 1) / per - w0 / per + 1; }
 
-// Split planning.  With chunk_tokens > 0 (or on the general kernel) every
-// (layer, seq, head) is cut into fixed token chunks, one workgroup each.
-// Otherwise (matrix-core kernel) each launch spreads its work over all the
-// device's wave slots (8 waves per CU, two per SIMD) with the balanced split
-// above; a workgroup may then hold waves of several (layer, seq, head)
-// entries.
+// Split planning.  With chunk_tokens > 0 every (layer, seq, head) is cut into
+// fixed token chunks, one workgroup each.  Otherwise each launch spreads its
+// work over all the device's wave slots (8 waves per CU, two per SIMD) with
+// the balanced split above; a workgroup may then hold waves of several
+// (layer, seq, head) entries.  A KV head whose query heads need more than
+// one 16-column tile ((D / g) * G > 16) is decoded in nsub launches, one per
+// subgroup of its query heads: each reads the K/V rows again, which still
+// runs far ahead of any vector-ALU path.
 constexpr int kSmallCallChunk = 1024;  // tokens per workgroup for small calls (see below)
 
-DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_tokens,
-                       bool use_mfma) {
+DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_tokens) {
   DecodePlan p;
   const int B = c->batch, Hkv = c->num_kv_heads, D = c->head_dim, g = c->group_size;
   const int nlh = nl * Hkv;
-  p.chunk = chunk_tokens > 0 || !use_mfma
-                ? (chunk_tokens > 0 ? chunk_tokens : default_chunk(c, nl, 256, 1024))
-                : 0;
+  const int Gfull = c->num_q_heads / Hkv;
+  p.nsub = mfma_subgroups(D, g, Gfull);
+  p.gsub = (Gfull + p.nsub - 1) / p.nsub;
+  p.chunk = chunk_tokens > 0 ? chunk_tokens : 0;
   // A small call (fewer rows than one 32-token step per wave slot, e.g. one
   // layer of a 6K-token sequence) is bound by latency, not bandwidth: fixed
   // 1024-token chunks (static, 4 steps per wave, few partials) beat spreading
@@ -375,7 +366,6 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
     if (fkey[i] != 16 * 32 + 16 && std::find(groups.begin(), groups.end(), fkey[i]) == groups.end())
       groups.push_back(fkey[i]);
   if (groups.empty()) groups.push_back(16 * 32 + 16);
-  if (!use_mfma) groups.assign(1, -1);  // the general kernel takes every format
 
   const int64_t wave_slots = int64_t(kMfmaWaves) * device_cus();
   constexpr int kMinWaveRows = 64;  // fewer rows per wave only add merge work
@@ -393,11 +383,10 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
         L.s0 = s0;
         L.ns = ns;
         L.glh.assign(sel.begin() + k0, sel.begin() + std::min(sel.size(), k0 + kMaxLH));
-        L.merge_after = false;
         const int S = int(L.glh.size());
         if (p.chunk > 0) {
           // fixed chunks: one workgroup (8 waves on the matrix-core kernel) each
-          L.mult.assign(S, use_mfma ? kMfmaWaves : 1);
+          L.mult.assign(S, kMfmaWaves);
           L.nx.resize(ns);
           for (int i = 0; i < ns; ++i) L.nx[i] = (c->capacity[s0 + i] + p.chunk - 1) / p.chunk;
         } else {
@@ -416,7 +405,7 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
           balance_launch(cost, cap, waves, L.mult, L.nx);
         }
         // partials per (layer, seq, head): workgroups its unit range touches
-        const int per = use_mfma ? kMfmaWaves : 1;
+        const int per = kMfmaWaves;
         int64_t xs = 0, mc = 0;
         for (int v : L.nx) xs += v;
         for (int i = 0; i < S; ++i) {
@@ -431,11 +420,9 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
         p.launches.push_back(std::move(L));
       }
     }
-    // the general kernel leaves split partials for a separate merge
-    if (!use_mfma) p.launches.back().merge_after = true;
   }
   p.max_chunks = int(max_pieces);
-  const int G = c->num_q_heads / c->num_kv_heads;
+  const int G = p.gsub;  // partials hold one subgroup's heads at a time
   p.entries = int64_t(nl) * B * Hkv * p.max_chunks;
   // The arrival counters come first and are sized by the cache configuration
   // (every layer, sequence and KV head), not by this call: every call on one
@@ -454,12 +441,12 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
 // last few plans are kept, keyed by everything plan_decode reads: the layer
 // count of the cache sizes the arrival counters, so it is part of the key.
 std::shared_ptr<const DecodePlan> cached_plan(const kvq_config* c, int layer_begin, int nl,
-                                              int chunk_tokens, bool use_mfma) {
+                                              int chunk_tokens) {
   constexpr size_t kKeep = 4;
   static std::mutex mu;
   static std::vector<std::pair<std::vector<int32_t>, std::shared_ptr<const DecodePlan>>> kept;
   const int Hkv = c->num_kv_heads;
-  std::vector<int32_t> key = {layer_begin, nl, chunk_tokens, int32_t(use_mfma), device_cus(),
+  std::vector<int32_t> key = {layer_begin, nl, chunk_tokens, device_cus(),
                               c->num_layers, c->batch, c->num_q_heads, Hkv, c->head_dim,
                               c->group_size};
   key.reserve(key.size() + c->batch + size_t(nl) * Hkv);
@@ -474,7 +461,7 @@ std::shared_ptr<const DecodePlan> cached_plan(const kvq_config* c, int layer_beg
       return kept.front().second;
     }
   auto plan = std::make_shared<const DecodePlan>(
-      plan_decode(c, layer_begin, nl, chunk_tokens, use_mfma));
+      plan_decode(c, layer_begin, nl, chunk_tokens));
   kept.insert(kept.begin(), {std::move(key), plan});
   if (kept.size() > kKeep) kept.pop_back();
   return plan;
@@ -654,10 +641,9 @@ struct WsRegions {
 };
 
 // Checks shared by both decode entry points; on success *plan holds the call's
-// split plan and *use_mfma the kernel family.
+// split plan.
 static kvq_status decode_prologue(const kvq_config* cfg, int32_t layer_begin, int32_t num_layers,
-                           int32_t chunk_tokens, std::shared_ptr<const DecodePlan>* plan,
-                           bool* use_mfma) {
+                           int32_t chunk_tokens, std::shared_ptr<const DecodePlan>* plan) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if (num_layers < 1) return KVQ_ERR_SHAPE;
@@ -665,11 +651,7 @@ static kvq_status decode_prologue(const kvq_config* cfg, int32_t layer_begin, in
   if (chunk_tokens < 0 || chunk_tokens % 32) return KVQ_ERR_SHAPE;
   const int G = cfg->num_q_heads / cfg->num_kv_heads;
   if (G > kMaxGroupRatio) return KVQ_ERR_UNSUPPORTED;
-  *use_mfma = mfma_supported(cfg->head_dim, cfg->group_size, G);
-  // the general kernel has no rotated-query, per-channel or bf16-range path
-  const bool ranges = cfg->bf16_range_offsets && cfg->bf16_range_offsets[cfg->batch] > 0;
-  if ((cfg->rotate_k || cfg->k_per_channel || ranges) && !*use_mfma)
-    return KVQ_ERR_UNSUPPORTED;
+  if (mfma_subgroups(cfg->head_dim, cfg->group_size, G) < 1) return KVQ_ERR_UNSUPPORTED;
   if (cfg->k_per_channel) {
     // per-channel K runs on the staged path (coded K with coded V), and its
     // 32-token steps must fall on the block grid: fixed chunks in multiples
@@ -678,14 +660,14 @@ static kvq_status decode_prologue(const kvq_config* cfg, int32_t layer_begin, in
     for (int i = layer_begin * cfg->num_kv_heads; i < (layer_begin + num_layers) * cfg->num_kv_heads; ++i)
       if (cfg->k_bits[i] < 16 && cfg->v_bits[i] == 16) return KVQ_ERR_UNSUPPORTED;
   }
-  *plan = cached_plan(cfg, layer_begin, num_layers, chunk_tokens, *use_mfma);
+  *plan = cached_plan(cfg, layer_begin, num_layers, chunk_tokens);
   return KVQ_OK;
 }
 
 // Launches of one validated decode call over workspace regions `wr`.
 static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_t layer_begin,
                          int32_t num_layers, const int32_t* seq_lens, const void* q, void* out,
-                         float sm_scale, const DecodePlan& plan, bool use_mfma, WsRegions wr,
+                         float sm_scale, const DecodePlan& plan, WsRegions wr,
                          void* stream) {
   if (!cache || !seq_lens || !q || !out) return KVQ_ERR_NULL;
   if (!aligned(cache, 256) || !aligned(q, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
@@ -703,13 +685,17 @@ static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_
     if (xs * ms >= (int64_t(1) << 31) || ms > 0xFFFF) return KVQ_ERR_UNSUPPORTED;
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  // every launch once per query-head subgroup (stream order keeps a
+  // subgroup's use of the workspace after the previous one's)
+  for (int sg = 0; sg < plan.nsub; ++sg)
   for (const LaunchPlan& L : plan.launches) {
+    const int g0 = sg * plan.gsub;  // first query head of the subgroup
     DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
     a.cache = static_cast<const uint8_t*>(cache);
     a.seq_lens = seq_lens;
-    a.q = static_cast<const uint16_t*>(q);
-    a.out = static_cast<uint16_t*>(out);
+    a.q = static_cast<const uint16_t*>(q) + int64_t(g0) * cfg->head_dim;
+    a.out = static_cast<uint16_t*>(out) + int64_t(g0) * cfg->head_dim;
     a.ws_arrive = reinterpret_cast<int32_t*>(wr.arrive);
     a.ws_o = reinterpret_cast<float*>(wr.rest);
     a.ws_ml = reinterpret_cast<float*>(wr.rest + plan.o_bytes);
@@ -718,7 +704,8 @@ static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_
     a.Rvis = lay.Rvis;
     a.D = lay.D;
     a.g = lay.g;
-    a.G = G;
+    a.G = std::min(plan.gsub, G - g0);
+    a.g_stride = uint8_t(G);
     a.Hkv = Hkv;
     a.Hq = cfg->num_q_heads;
     a.B = cfg->batch;
@@ -754,14 +741,7 @@ static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_
       a.mult[i] = uint16_t(L.mult[i]);
       a.mcum[i + 1] = uint16_t(a.mcum[i] + a.mult[i]);
     }
-    const hipError_t e = use_mfma ? launch_decode_mfma(a, L.key / 32, L.key % 32, hs)
-                                  : launch_decode_simple(a, L.ns, hs);
-    if (e != hipSuccess) return KVQ_ERR_HIP;
-    // the general kernel leaves split partials for a separate merge; the
-    // matrix-core kernel merges them itself
-    if (L.merge_after && plan.max_chunks > 1 &&
-        launch_decode_merge(a, num_layers, L.ns, hs) != hipSuccess)
-      return KVQ_ERR_HIP;
+    if (launch_decode_mfma(a, L.key / 32, L.key % 32, hs) != hipSuccess) return KVQ_ERR_HIP;
   }
   return KVQ_OK;
 }
@@ -774,8 +754,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
                                            void* stream) {
   try {
     std::shared_ptr<const DecodePlan> plan;
-    bool use_mfma = false;
-    kvq_status st = decode_prologue(cfg, layer_begin, num_layers, chunk_tokens, &plan, &use_mfma);
+    kvq_status st = decode_prologue(cfg, layer_begin, num_layers, chunk_tokens, &plan);
     if (st != KVQ_OK) return st;
     if (!workspace_bytes) return KVQ_ERR_NULL;
     if (!workspace) {
@@ -787,7 +766,7 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
     if (!aligned(workspace, 256)) return KVQ_ERR_ALIGN;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     return decode_launch(cfg, cache, layer_begin, num_layers, seq_lens, q, out, sm_scale, *plan,
-                         use_mfma, WsRegions{ws, ws + plan->arrive_bytes}, stream);
+                         WsRegions{ws, ws + plan->arrive_bytes}, stream);
   } catch (...) {
     return KVQ_ERR_INTERNAL;
   }
@@ -841,8 +820,7 @@ extern "C" kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const 
                                                    int32_t chunk_tokens, void* stream) {
   try {
     std::shared_ptr<const DecodePlan> plan;
-    bool use_mfma = false;
-    kvq_status st = decode_prologue(cfg, layer_begin, num_layers, chunk_tokens, &plan, &use_mfma);
+    kvq_status st = decode_prologue(cfg, layer_begin, num_layers, chunk_tokens, &plan);
     if (st != KVQ_OK) return st;
     if (!cache || !seq_lens || !q || !out) return KVQ_ERR_NULL;
     // counters of this cache shape, then the call's partials, must fit
@@ -854,7 +832,7 @@ extern "C" kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const 
     st = scratch_for_device(static_cast<hipStream_t>(stream), &base);
     if (st != KVQ_OK) return st;
     return decode_launch(cfg, cache, layer_begin, num_layers, seq_lens, q, out, sm_scale, *plan,
-                         use_mfma, WsRegions{base, base + kScratchCounterBytes}, stream);
+                         WsRegions{base, base + kScratchCounterBytes}, stream);
   } catch (...) {
     return KVQ_ERR_INTERNAL;
   }

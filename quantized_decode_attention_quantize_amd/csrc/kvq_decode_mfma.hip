@@ -1,14 +1,18 @@
 // kvq_decode_mfma.hip -- split-K decode attention on the CDNA4 matrix cores.
 //
-// Same contract as the general split kernel (kvq_decode.hip): one workgroup
-// per token chunk of one (layer, sequence, KV head); stored rows are
-// reconstructed on chip and never written back (gist.science 2604.02570,
+// Work is split over waves of (layer, sequence, KV head) token ranges; stored
+// rows are reconstructed on chip and never written back (gist.science 2604.02570,
 // section 2-D: reconstruction fused into flash decoding); K/V widths per
 // head and the Visual/Text split follow nuiw.github.io "VLM_KV_Quantization"
 // (sections 1-2) and the HeadGuard briefing (bf16 protected heads).
 //
 // Work of one wave: 32 tokens per step, all contractions on
 // v_mfma_f32_16x16x32_{f16,bf16} (wave64, 16x16 tile, K = 32):
+//
+// A launch decodes a subgroup of G query heads of every KV head (a KV head
+// with more than one tile of (head, group) columns takes several launches,
+// each reading its rows again); q and out stride by all of the KV head's
+// query heads (Gs).
 //
 //   q.k   S^T[token][c] = sum_k A[token][k] B[k][c] over two 16-token tiles.
 //         A = stored K row data of the tile, B = Q' (built once per segment).
@@ -985,7 +989,7 @@ struct Launch {
   int32_t* ws_arrive;
   int64_t Rvis;
   float qscale;
-  int G, Hkv, Hq, B, chunk, max_chunks, seq_off, n_lh, n_seq, rotate_k, k_per_channel;
+  int G, Gs, Hkv, Hq, B, chunk, max_chunks, seq_off, n_lh, n_seq, rotate_k, k_per_channel;
 };
 // A device pointer read from LDS, made wave-uniform and marked as a global
 // (not generic) address, so accesses through it compile to global or buffer
@@ -1014,6 +1018,7 @@ __device__ inline Launch launch_scalars(const DecodeArgs& t) {
                    uint32_t(uniform_int(int(uint32_t(rv)))));
   L.qscale = __builtin_bit_cast(float, uniform_int(__builtin_bit_cast(int, t.qscale)));
   L.G = uniform_int(t.G);
+  L.Gs = uniform_int(int(t.g_stride));
   L.Hkv = uniform_int(t.Hkv);
   L.Hq = uniform_int(t.Hq);
   L.B = uniform_int(t.B);
@@ -1038,7 +1043,7 @@ __device__ void merge_entry(const Launch& a, uint8_t* big_lds, int l_local, int 
                             int nxs) {
   const int G = a.G;
   const int64_t entry = (int64_t(l_local) * a.B + s) * a.Hkv + h;
-  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * a.Gs) * D;
   // Merge in LDS: the (m, l) pairs of all partials come in with the first
   // batch of partial rows and become weights w[cx][j] = l 2^(m - M_j) (0 for
   // a partial without tokens); the partial rows (normalised, o / l) stream
@@ -1215,7 +1220,7 @@ __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int
         buf[t][cx] = __builtin_amdgcn_raw_buffer_load_b128(
             ro, uint32_t(cx * G * D + 4 * v) * 4u, 0, kCoherent);
   }
-  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * a.Gs) * D;
 #pragma unroll
   for (int t = 0; t < kWmT; ++t) {
     const int v = v_lo + lane + 64 * t;
@@ -1394,7 +1399,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   u32x4 qreg[D / 32];
   {
     const int qh = (lane & 15) < G * NG ? (lane & 15) / NG : 0;
-    const uint16_t* qp = La.q + ((int64_t(l_local) * La.B + s) * La.Hq + int64_t(h) * G + qh) * D +
+    const uint16_t* qp = La.q + ((int64_t(l_local) * La.B + s) * La.Hq + int64_t(h) * La.Gs + qh) * D +
                          (lane >> 4) * (D / 4);
 #pragma unroll
     for (int k = 0; k < D / 32; ++k)
@@ -1569,7 +1574,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const int ppx = __builtin_amdgcn_readfirstlane(winfo[wl][5]);
     const int ppn = __builtin_amdgcn_readfirstlane(winfo[wl][6]);
     const int64_t pidx = partial_index(pl, ps, ph, ppx, La.B, La.Hkv, La.max_chunks);
-    uint16_t* outp = La.out + ((int64_t(pl) * La.B + ps) * La.Hq + int64_t(ph) * G) * D;
+    uint16_t* outp = La.out + ((int64_t(pl) * La.B + ps) * La.Hq + int64_t(ph) * La.Gs) * D;
     // four consecutive outputs per thread (one head, one group: D and g are
     // multiples of 4): 16-byte LDS reads and one 16-byte store
     const Rsrc rpo = make_rsrc(La.ws_o + pidx * GD, int64_t(GD) * 4);
@@ -1685,6 +1690,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 #if !defined(KVQ_MFMA_PART) || KVQ_MFMA_PART == 0
 bool mfma_supported(int D, int g, int G) {
   return (D == 64 || D == 128) && G * (D / g) <= 16;
+}
+int mfma_subgroups(int D, int g, int G) {
+  if (!(D == 64 || D == 128) || g < 32 || D % g) return 0;
+  return (G * (D / g) + 15) / 16;
 }
 #endif
 

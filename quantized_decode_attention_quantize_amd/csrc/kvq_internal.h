@@ -79,9 +79,9 @@ struct DecodeArgs {
   uint16_t lh_glob[kMaxLH];  // grid.y slot -> layer_local * Hkv + head
   uint32_t base256[kMaxLH][2];  // per slot: VIS plane offset / 256 of K and V
   uint8_t bits[kMaxLH][2];
-  // Work units (waves of the matrix-core kernel, workgroups of the general
-  // one): slot i and sequence s get mult[i] * nx[s] consecutive units,
-  // slot-major, so unit u of the launch decodes with two searches.
+  // Work units (waves): slot i and sequence s get mult[i] * nx[s]
+  // consecutive units, slot-major, so unit u of the launch decodes with two
+  // searches.
   uint16_t mult[kMaxLH];    // per slot
   uint16_t mcum[kMaxLH + 1];  // per slot: sum of mult over earlier slots
   int32_t vb[kMaxSeq], ve[kMaxSeq], cap[kMaxSeq], vrow0[kMaxSeq], trow0[kMaxSeq];
@@ -93,7 +93,9 @@ struct DecodeArgs {
   // bf16 ranges inside the visual spans: sequence i owns ranges
   // [rng_first[i], rng_first[i + 1]) of this launch's table
   uint8_t rng_first[kMaxSeq + 1];
-  uint8_t pad_[3];
+  uint8_t g_stride;         // query heads per KV head in q / out (G counts this
+                            // launch's subgroup of them; q and out point at its first)
+  uint8_t pad_[2];
   int32_t rng_b[kMaxRangesD], rng_e[kMaxRangesD];
 };
 static_assert(sizeof(DecodeArgs) % 16 == 0, "DecodeArgs is copied in 16-byte pieces");
@@ -171,10 +173,13 @@ hipError_t launch_quantize(const QuantizeArgs& a, int n_lh_launch, int n_seq_lau
 // (layer-head slot, sequence, block); max_blocks = the largest kblkn.
 hipError_t launch_quantize_kblocks(const QuantizeArgs& a, int n_lh_launch, int n_seq_launch,
                                    int max_blocks, hipStream_t stream);
-hipError_t launch_decode_simple(const DecodeArgs& a, int n_seq_launch, hipStream_t stream);
-// Matrix-core split kernel: needs (D / g) * G <= 16 (one 16-row MFMA tile of
-// (head, group) columns); writes the final output itself when max_chunks == 1.
+// Matrix-core split kernel: one 16-row MFMA tile of (head, group) columns,
+// i.e. (D / g) * G <= 16 query heads of each KV head per launch; writes the
+// final output itself when max_chunks == 1.
 bool mfma_supported(int D, int g, int G);
+// Launches (query-head subgroups) a call with G query heads per KV head
+// needs, each of at most ceil(G / n) heads: ceil(G * (D / g) / 16).
+int mfma_subgroups(int D, int g, int G);
 // kb, vb: the visual widths every non-bf16 (layer, head) pair of the launch has.
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
 hipError_t launch_decode_mfma_128_1(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
@@ -182,9 +187,6 @@ hipError_t launch_decode_mfma_128_2(const DecodeArgs& a, int kb, int vb, hipStre
 hipError_t launch_decode_mfma_128_4(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
 hipError_t launch_decode_mfma_64_1(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
 hipError_t launch_decode_mfma_64_2(const DecodeArgs& a, int kb, int vb, hipStream_t stream);
-hipError_t launch_decode_merge(const DecodeArgs& a, int nl, int n_seq_launch,
-                               hipStream_t stream);
 constexpr int kMfmaWaves = 8;      // waves per workgroup of the matrix-core kernel
-constexpr int kSimpleWaves = 4;    // waves per workgroup of the general kernel
 
 }  // namespace kvq

@@ -18,13 +18,15 @@ hipError_t launch_quantize(const QuantizeArgs&, int, int, hipStream_t) { return 
 hipError_t launch_quantize_kblocks(const QuantizeArgs&, int, int, int, hipStream_t) {
   return hipSuccess;
 }
-hipError_t launch_decode_simple(const DecodeArgs&, int, hipStream_t) { return hipSuccess; }
-hipError_t launch_decode_merge(const DecodeArgs&, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode_mfma(const DecodeArgs& a, int, int, hipStream_t) {
   g_mfma.push_back(a);
   return hipSuccess;
 }
 bool mfma_supported(int D, int g, int G) { return (D == 64 || D == 128) && G * (D / g) <= 16; }
+int mfma_subgroups(int D, int g, int G) {
+  if (!(D == 64 || D == 128) || g < 32 || D % g) return 0;
+  return (G * (D / g) + 15) / 16;
+}
 }  // namespace kvq
 using namespace kvq;
 
@@ -99,6 +101,7 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
   std::map<long, std::vector<int>> cov;
   std::map<long, std::set<int>> seen_px;
   std::map<long, int> npieces;
+  std::map<long, std::set<long>> heads_seen;  // per entry: its subgroups (first head, count)
   long waves = 0;
   for (const DecodeArgs& a : g_mfma) {
     const long total = long(a.nxcum[a.n_seq]) * a.mcum[a.n_lh];
@@ -118,7 +121,16 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
         }
         const int lh = a.lh_glob[slot], l = lh / Hkv, h = lh % Hkv, s = a.seq_off + sl;
         const int len = a.cap[sl];  // seq_lens = capacity
-        const long key = (long(l) * B + s) * Hkv + h;
+        // query-head subgroup of this launch: q points at its first head
+        const long g0 = long(reinterpret_cast<const char*>(a.q) - reinterpret_cast<const char*>(0x2000)) /
+                        (2 * D);
+        const long key = ((g0 * L + l) * B + s) * Hkv + h;
+        if (a.g_stride != Hq / Hkv || (g0 % a.G != 0 && g0 + a.G != Hq / Hkv)) {
+          if (bad < 8) printf("%s: subgroup at head %ld of %d heads, stride %d\n", name, g0, a.G,
+                              a.g_stride);
+          ++bad;
+        }
+        heads_seen[(long(l) * B + s) * Hkv + h].insert(g0 * 100 + a.G);
         std::vector<int>& cv = cov[key];
         if (cv.empty()) cv.assign(len, 0);
         seen_px[key].insert(px);
@@ -202,8 +214,18 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
       ++bad;
     }
   }
-  if (!g_mfma.empty() && long(cov.size()) != long(L) * B * Hkv) {
-    printf("%s: %zu entries covered of %d\n", name, cov.size(), L * B * Hkv);
+  // every query head of every entry in exactly one subgroup
+  for (auto& kv : heads_seen) {
+    int covered = 0;
+    for (long x : kv.second) covered += int(x % 100);
+    if (covered != Hq / Hkv) {
+      if (bad < 8) printf("%s: entry %ld has %d of %d query heads\n", name, kv.first, covered, Hq / Hkv);
+      ++bad;
+    }
+  }
+  const long nsub = heads_seen.empty() ? 1 : long(heads_seen.begin()->second.size());
+  if (!g_mfma.empty() && long(cov.size()) != long(L) * B * Hkv * nsub) {
+    printf("%s: %zu entries covered of %ld\n", name, cov.size(), long(L) * B * Hkv * nsub);
     ++bad;
   }
   printf("%-16s chunk %5d launches %zu waves %ld workspace %zu %s\n", name, chunk, g_mfma.size(),
@@ -255,6 +277,11 @@ int main() {
                   std::vector<uint8_t>(4, 4), std::vector<uint8_t>(4, 2), 0);
   bad += run_case("pc 1x4 6288", 1, 1, 28, 4, 128, 64, {6288}, {14}, {6287},
                   std::vector<uint8_t>(4, 4), std::vector<uint8_t>(4, 2), 0, 1);
+  // more than one 16-column tile per KV head: query-head subgroups
+  bad += run_case("sub 28/4 g32", 2, 2, 28, 4, 128, 32, {700, 300}, {14, 0}, {690, 300},
+                  std::vector<uint8_t>(8, 4), std::vector<uint8_t>(8, 2), 0);
+  bad += run_case("sub 16/1 g32", 1, 1, 16, 1, 128, 32, {6288}, {14}, {6287},
+                  std::vector<uint8_t>(1, 4), std::vector<uint8_t>(1, 2), 256);
   // bf16 ranges inside the visual spans (static split for those sequences)
   using R = std::vector<std::vector<std::pair<int, int>>>;
   for (int ch : {0, 1024}) {

@@ -191,10 +191,10 @@ def test_decode_mixed_formats_and_d64():
         _check_decode(p, [300, 101], what=f"D{D} g{g} k{kb} v{vb}")
 
 
-@pytest.mark.parametrize("hq,hkv,g", [(28, 4, 32), (16, 1, 64), (8, 8, 128)])
+@pytest.mark.parametrize("hq,hkv,g", [(28, 4, 32), (16, 1, 64), (16, 1, 32), (8, 8, 128)])
 def test_decode_general_kernel_shapes(hq, hkv, g):
-    """(head, group) columns beyond one 16-wide tile go to the general kernel;
-    G = 1 (no GQA) goes to the matrix-core kernel."""
+    """(head, group) columns beyond one 16-wide tile (28, 32 and 64 here)
+    decode in two or four query-head subgroups; G = 1 (no GQA) in one launch."""
     _say("decode heads/group", hq, hkv, g)
     kb = np.full(hkv, 4, np.uint8)
     vb = np.full(hkv, 2, np.uint8)

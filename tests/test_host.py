@@ -217,17 +217,24 @@ def test_decode_workspace_query(L):
     assert st == kvq.KVQ_OK and n > 0
 
 
-def test_decode_rotation_needs_the_matrix_core_kernel(L):
-    """The general kernel (more than 16 (head, group) columns) has no rotated
-    query path: a rotated cache of that shape is refused before any launch."""
-    # G = 7 query heads per KV head, 4 groups per row: 28 columns
-    cfg = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4)
-    assert _dec(L, cfg, ws=None)[0] == kvq.KVQ_OK
-    rot = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4, rotate_k=True)
-    assert _dec(L, rot, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
-    rot_ok = kvq.Config(1, 1, 28, 4, 128, 64, [256], [16], [256], [4] * 4, [2] * 4,
-                        rotate_k=True)
-    assert _dec(L, rot_ok, ws=None)[0] == kvq.KVQ_OK
+def test_decode_query_head_subgroups(L):
+    """More than 16 (head, group) columns per KV head: the decode runs in
+    query-head subgroups (launches of at most 16 columns), so every feature
+    is available and the workspace holds one subgroup's partials."""
+    # G = 7 query heads per KV head, 4 groups per row: 28 columns, two subgroups
+    # of 4 and 3 heads
+    wide = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4)
+    narrow = kvq.Config(1, 1, 16, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4)  # 16
+    st, n_wide = _dec(L, wide, ws=None, chunk=64)
+    st2, n_narrow = _dec(L, narrow, ws=None, chunk=64)
+    assert st == st2 == kvq.KVQ_OK and n_wide == n_narrow
+    for extra in (dict(rotate_k=True), dict(k_per_channel=True),
+                  dict(bf16_ranges=[[(20, 30)]])):
+        c = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4, **extra)
+        assert _dec(L, c, ws=None)[0] == kvq.KVQ_OK, extra
+    # 16 query heads per KV head at g = 32: 64 columns, four subgroups
+    g16 = kvq.Config(1, 1, 16, 1, 128, 32, [256], [16], [256], [4], [2])
+    assert _dec(L, g16, ws=None)[0] == kvq.KVQ_OK
 
 
 def test_decode_validation(L):
@@ -318,8 +325,8 @@ def test_binding_rejects_wrong_dtypes_and_sizes(L):
 
 def test_per_channel_validation(L):
     """Per-channel K: a store that cuts a block of the coded span, rotation on
-    top, fixed chunks off the 256-token grid, coded K with bf16 V, and shapes
-    of the general kernel are refused before any launch."""
+    top, fixed chunks off the 256-token grid and coded K with bf16 V are
+    refused before any launch; shapes of several query-head subgroups run."""
     cfg = _cfg(capacity=[256], vis_begin=[16], vis_end=[250])  # coded [16, 240), g 32
     pc = kvq.Config(**{**dict(num_layers=1, batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64,
                               group_size=32, capacity=[256], vis_begin=[16], vis_end=[250],
@@ -340,16 +347,16 @@ def test_per_channel_validation(L):
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_cache_bytes(rot)
     assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
-    general = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
-                         k_per_channel=True)  # 28 (head, group) columns
-    assert _dec(L, general, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    wide = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
+                      k_per_channel=True)  # 28 (head, group) columns: two subgroups
+    assert _dec(L, wide, ws=None)[0] == kvq.KVQ_OK
     del cfg
 
 
 def test_bf16_range_validation(L):
     """bf16 ranges: malformed tables are shape errors, missing arrays null
-    errors, and per-channel K with ranges, more than 36 ranges in a
-    sequence, or ranges on a shape of the general kernel are refused."""
+    errors, and per-channel K with ranges or more than 36 ranges in a
+    sequence are refused."""
     def cfg(ranges, **over):
         base = dict(num_layers=1, batch=2, num_q_heads=4, num_kv_heads=1, head_dim=64,
                     group_size=32, capacity=[256, 300], vis_begin=[16, 0],
@@ -391,16 +398,10 @@ def test_bf16_range_validation(L):
     moved = kvq.kvq_cache_bytes(cfg([[(16, 17), (100, 250)], [(0, 300)]]))
     assert plain["quantized_values"] - moved["quantized_values"] == (1 + 150 + 300) * 64 * 2
     assert moved["bf16_text_bytes"] - plain["bf16_text_bytes"] == (1 + 150 + 300) * 64 * 2 * 2
-    # decode: the matrix-core kernel takes ranges, the general kernel does not
+    # decode takes ranges in the balanced split and in fixed chunks
     ok = cfg([[(16, 17), (100, 250)], []])
     assert _dec(L, ok, ws=None)[0] == kvq.KVQ_OK
     assert _dec(L, ok, chunk=64, ws=None)[0] == kvq.KVQ_OK
-    general = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
-                         bf16_ranges=[[(20, 30)]])  # 28 (head, group) columns
-    assert _dec(L, general, ws=None)[0] == kvq.KVQ_ERR_UNSUPPORTED
-    general_plain = kvq.Config(1, 1, 28, 4, 128, 32, [256], [16], [256], [4] * 4, [2] * 4,
-                               bf16_ranges=[[]])
-    assert _dec(L, general_plain, ws=None)[0] == kvq.KVQ_OK
 
 
 def test_latent_cache_bytes_and_validation(L):
