@@ -151,9 +151,9 @@ typedef struct {
  * min) pairs are META row r / g, which holds D pairs, pair d for channel d.
  * The plane sizes are the same as with per-token groups.  kvq_quantize must
  * store whole blocks: a call whose positions cut a block of the coded span
- * apart returns KVQ_ERR_SHAPE.  Not combinable with rotate_k, and decoding
- * needs the matrix-core kernel's shapes (Hq / Hkv * D / g <= 16); otherwise
- * KVQ_ERR_UNSUPPORTED. */
+ * apart returns KVQ_ERR_SHAPE.  Not combinable with rotate_k; the decode
+ * takes fixed chunks only in multiples of 256 tokens and no (layer, head)
+ * with coded K but bf16 V (KVQ_ERR_UNSUPPORTED otherwise). */
 
 /* K rotation (rotate_k != 0).  gist.science 2604.02570 (WSVD, section 2-C)
  * rotates vectors ahead of quantisation to remove per-channel outliers; the
@@ -251,6 +251,9 @@ kvq_status kvq_quantize_ragged(const kvq_config *cfg, void *cache, int32_t layer
  * of KV head floor(i * Hkv / Hq), with K^, V^ the stored rows reconstructed
  * on chip (codes * scale + min, or bf16).  Split-K over token chunks with a
  * log-sum-exp merge; fp32 accumulation; out rounded to bf16 (nearest even).
+ * A KV head whose Hq / Hkv query heads times D / g groups exceed 16 columns
+ * is decoded in ceil(Hq / Hkv * (D / g) / 16) launches, one per subgroup of
+ * its query heads, each reading the head's rows again.
  *
  *   cache      device, as written by kvq_quantize (read only)
  *   seq_lens   DEVICE int32 [batch], 1 <= seq_lens[s] <= capacity[s]
