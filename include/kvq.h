@@ -379,7 +379,8 @@ kvq_status kvq_latent_store(const kvq_latent_config *cfg, void *cache, int32_t l
  * up-projections.  K and V are never formed: the query is projected once
  * (q' = B_K q) and attends over the latents, and B_V is applied to the
  * merged latent output (the same result up to rounding order).  Split-K over
- * token chunks with a log-sum-exp merge, fp32 accumulation, bf16 output
+ * token chunks with a log-sum-exp merge, done by the last workgroup of a
+ * (layer, sequence, KV head) to finish; fp32 accumulation, bf16 output
  * (nearest even).
  *   cache      device, as written by kvq_latent_store (read only)
  *   seq_lens   DEVICE int32 [batch], clamped into [1, capacity[s]]
@@ -392,11 +393,13 @@ kvq_status kvq_latent_store(const kvq_latent_config *cfg, void *cache, int32_t l
  *              over the call), else a positive multiple of 32 = tokens per
  *              workgroup.  Each chunk's summation order is fixed: repeated
  *              calls give identical bytes.
- *   workspace  device, 256-byte aligned, for the split partials; NULL = only
- *              write the required size to *workspace_bytes.  Needs no
- *              initialisation; calls that may overlap in time must use
- *              distinct workspaces.
- * Two kernel launches per 64 sequences, enqueued on `stream`.
+ *   workspace  device, 256-byte aligned: arrival counters for every (layer,
+ *              sequence, KV head) of the cache, then the split partials;
+ *              NULL = only write the required size to *workspace_bytes.
+ *              Must be zero-filled before its first use; every call leaves
+ *              the counters at zero again.  Calls that may overlap in time
+ *              must use distinct workspaces.
+ * One kernel launch per 64 sequences, enqueued on `stream`.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (also more than
  * 4096 chunks per sequence), KVQ_ERR_ALIGN, KVQ_ERR_RANGE, KVQ_ERR_WORKSPACE,
  * KVQ_ERR_HIP. */

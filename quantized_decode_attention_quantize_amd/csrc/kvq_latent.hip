@@ -53,6 +53,7 @@ struct LatentArgs {
   const uint16_t* up_v;
   float* ws_o;              // [entries][G][D] unnormalised outputs (B_V applied)
   float* ws_ml;             // [entries][G][2] (max in log2 units, sum)
+  int32_t* ws_arrive;       // [cache layers][B][Hkv] arrival counters, zero between calls
   float qscale;             // sm_scale * log2(e)
   int64_t plane_bytes;
   int Hkv, Hq, G, B;
@@ -220,6 +221,89 @@ __device__ inline void compute_lstep(LWave<R>& w, const LStep<R>& st, const u32x
     w.o[mb] = mfma_bf16(pa, b, w.o[mb]);
     w.o[mb] = mfma_bf16(pb, b, w.o[mb]);
   }
+}
+
+// Loads past this XCD's caches: partials written by workgroups on other
+// XCDs (with write-through stores) are read from memory.
+__device__ inline float ld_sys(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Log-sum-exp merge of one (layer, sequence, KV head)'s nx chunk partials
+// (D wide, B_V already applied) into its bf16 output, by the whole
+// workgroup.  Latency-bound: all loads of a block of up to kMB chunks -- the
+// (m, l) pairs and the partial outputs -- are issued before the block's
+// first barrier.  kMB * kE = 32 values in flight per thread, so the merge
+// needs no more registers than the decode loop before it.
+template <int D>
+__device__ void merge_latent_entry(const LatentArgs& a, int l, int s, int h, int nx) {
+  constexpr int kE = 16 * D / 256;  // (head, column) elements per thread
+  constexpr int kMB = 32 / kE;      // chunks per merge block: 8 at D = 64, 4 at D = 128
+  __shared__ float2 mls[kMB][16];
+  __shared__ float fx[kMB][16];
+  __shared__ float scl[16];
+  __shared__ float Ls[16];
+  const int G = a.G;
+  const int64_t p0 = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks;
+  const int tid = threadIdx.x;
+  float acc[kE];
+#pragma unroll
+  for (int k = 0; k < kE; ++k) acc[k] = 0.0f;
+  float M = -INFINITY, L = 0.0f;  // running (max, sum) of head tid (threads < 16)
+  for (int xb = 0; xb < nx; xb += kMB) {
+    const int nb = min(kMB, nx - xb);
+    float ov[kMB][kE];
+#pragma unroll
+    for (int x = 0; x < kMB; ++x)
+#pragma unroll
+      for (int k = 0; k < kE; ++k) {
+        const int idx = tid + 256 * k, hh = idx / D;
+        ov[x][k] = x < nb && hh < G ? ld_sys(a.ws_o + (p0 + xb + x) * G * D + idx) : 0.0f;
+      }
+    if (tid < kMB * 16) {
+      const int x = tid >> 4, hh = tid & 15;
+      const float* m = a.ws_ml + ((p0 + xb + x) * G + hh) * 2;
+      mls[x][hh] = x < nb && hh < G ? make_float2(ld_sys(m), ld_sys(m + 1))
+                                    : make_float2(-INFINITY, 0.0f);
+    }
+    __syncthreads();
+    if (tid < 16) {  // new running max; this block's weights relative to it
+      float Mn = M;
+      for (int x = 0; x < nb; ++x)
+        if (mls[x][tid].y > 0.0f) Mn = fmaxf(Mn, mls[x][tid].x);
+      const float sc = L > 0.0f ? __builtin_amdgcn_exp2f(M - Mn) : 0.0f;
+      L *= sc;
+      for (int x = 0; x < kMB; ++x) {
+        const float2 v = mls[x][tid];
+        const float f = x < nb && v.y > 0.0f ? __builtin_amdgcn_exp2f(v.x - Mn) : 0.0f;
+        fx[x][tid] = f;
+        L = __builtin_fmaf(f, v.y, L);
+      }
+      scl[tid] = sc;  // factor for the sums of earlier blocks
+      M = Mn;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kE; ++k) {
+      const int hh = (tid + 256 * k) / D;
+      float o = acc[k] * scl[hh];
+#pragma unroll
+      for (int x = 0; x < kMB; ++x) o = __builtin_fmaf(fx[x][hh], ov[x][k], o);
+      acc[k] = o;
+    }
+    __syncthreads();  // fx and scl are rewritten by the next block
+  }
+  if (tid < 16) Ls[tid] = L;
+  __syncthreads();
+  uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
+#pragma unroll
+  for (int k = 0; k < kE; ++k) {
+    const int idx = tid + 256 * k, hh = idx / D;
+    if (hh < G) outp[idx] = uint16_t(bf16_bits(acc[k] / Ls[hh]));
+  }
+  if (tid == 0)
+    __hip_atomic_store(&a.ws_arrive[(int64_t(a.layer_begin + l) * a.B + s) * a.Hkv + h], 0,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // One workgroup: one chunk of one (layer, sequence, KV head); its four waves
@@ -416,96 +500,38 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
   for (int hh = 0; hh < 16; ++hh) part[pt][hh][d] = y[hh];
   __syncthreads();
   const int64_t p = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks + x;
+  const int nx = a.nxcum[i + 1] - a.nxcum[i];
   uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
   for (int idx = threadIdx.x; idx < G * D; idx += kLThreads) {
     const int hh = idx / D, dd = idx - hh * D;
     float v = part[0][hh][dd];
 #pragma unroll
     for (int k = 1; k < kParts; ++k) v += part[k][hh][dd];
-    if (a.max_chunks == 1) {
+    if (nx == 1) {  // the whole sequence in this chunk: the output itself
       outp[int64_t(hh) * D + dd] = uint16_t(bf16_bits(v / mlc[hh][1]));
     } else {
-      a.ws_o[(p * G + hh) * D + dd] = v;
+      // write-through stores: the merging workgroup may sit on another XCD
+      __hip_atomic_store(&a.ws_o[(p * G + hh) * D + dd], v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
       if (dd == 0) {
-        a.ws_ml[(p * G + hh) * 2] = mlc[hh][0];
-        a.ws_ml[(p * G + hh) * 2 + 1] = mlc[hh][1];
+        __hip_atomic_store(&a.ws_ml[(p * G + hh) * 2], mlc[hh][0], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&a.ws_ml[(p * G + hh) * 2 + 1], mlc[hh][1], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
-}
-
-// One workgroup per (layer, sequence, KV head): log-sum-exp merge of the
-// chunks' D-wide partials, rounded to bf16.  The merge is latency-bound, so
-// all global loads of a block of up to kMB chunks -- the (m, l) pairs and
-// the partial outputs -- are issued before the block's first barrier.
-constexpr int kMB = 8;  // chunks per merge block
-template <int D>
-__global__ __launch_bounds__(256) void latent_merge_kernel(LatentArgs a) {
-  constexpr int kE = 16 * D / 256;  // (head, column) elements per thread
-  __shared__ float2 mls[kMB][16];
-  __shared__ float fx[kMB][16];
-  __shared__ float scl[16];
-  __shared__ float Ls[16];
-  const int G = a.G;
-  const int e = blockIdx.x;
-  const int h = e % a.Hkv, i = (e / a.Hkv) % a.n_seq, l = e / (a.Hkv * a.n_seq);
-  const int s = a.seq_off + i, nx = a.nxcum[i + 1] - a.nxcum[i];
-  const int64_t p0 = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks;
-  const int tid = threadIdx.x;
-  const float2* mlp = reinterpret_cast<const float2*>(a.ws_ml);
-  float acc[kE];
-#pragma unroll
-  for (int k = 0; k < kE; ++k) acc[k] = 0.0f;
-  float M = -INFINITY, L = 0.0f;  // running (max, sum) of head tid (threads < 16)
-  for (int xb = 0; xb < nx; xb += kMB) {
-    const int nb = min(kMB, nx - xb);
-    float ov[kMB][kE];
-#pragma unroll
-    for (int x = 0; x < kMB; ++x)
-#pragma unroll
-      for (int k = 0; k < kE; ++k) {
-        const int idx = tid + 256 * k, hh = idx / D;
-        ov[x][k] = x < nb && hh < G ? a.ws_o[(p0 + xb + x) * G * D + idx] : 0.0f;
-      }
-    if (tid < kMB * 16) {
-      const int x = tid >> 4, hh = tid & 15;
-      mls[x][hh] = x < nb && hh < G ? mlp[(p0 + xb + x) * G + hh] : make_float2(-INFINITY, 0.0f);
-    }
-    __syncthreads();
-    if (tid < 16) {  // new running max; this block's weights relative to it
-      float Mn = M;
-      for (int x = 0; x < nb; ++x)
-        if (mls[x][tid].y > 0.0f) Mn = fmaxf(Mn, mls[x][tid].x);
-      const float sc = L > 0.0f ? __builtin_amdgcn_exp2f(M - Mn) : 0.0f;
-      L *= sc;
-      for (int x = 0; x < kMB; ++x) {
-        const float2 v = mls[x][tid];
-        const float f = x < nb && v.y > 0.0f ? __builtin_amdgcn_exp2f(v.x - Mn) : 0.0f;
-        fx[x][tid] = f;
-        L = __builtin_fmaf(f, v.y, L);
-      }
-      scl[tid] = sc;  // factor for the sums of earlier blocks
-      M = Mn;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kE; ++k) {
-      const int hh = (tid + 256 * k) / D;
-      float o = acc[k] * scl[hh];
-#pragma unroll
-      for (int x = 0; x < kMB; ++x) o = __builtin_fmaf(fx[x][hh], ov[x][k], o);
-      acc[k] = o;
-    }
-    __syncthreads();  // fx and scl are rewritten by the next block
-  }
-  if (tid < 16) Ls[tid] = L;
+  if (nx == 1) return;
+  // The workgroup counts its chunk in once its partial has reached memory;
+  // the one that completes the count merges the entry (no second launch).
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
   __syncthreads();
-  uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-#pragma unroll
-  for (int k = 0; k < kE; ++k) {
-    const int idx = tid + 256 * k, hh = idx / D;
-    if (hh < G) outp[idx] = uint16_t(bf16_bits(acc[k] / Ls[hh]));
-  }
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(&a.ws_arrive[(int64_t(a.layer_begin + l) * a.B + s) * a.Hkv + h],
+                                  1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == nx - 1;
+  __syncthreads();
+  if (last) merge_latent_entry<D>(a, l, s, h, nx);
 }
 
 // Copies 16-byte pieces of latent rows into their planes.
@@ -591,9 +617,6 @@ template <int D, int R>
 hipError_t launch_latent(const LatentArgs& a, hipStream_t st) {
   const int units = a.nl * a.Hkv * a.nxcum[a.n_seq];
   hipLaunchKernelGGL((latent_decode_kernel<D, R>), dim3(units), dim3(kLThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_chunks == 1) return e;  // one chunk: written directly
-  hipLaunchKernelGGL((latent_merge_kernel<D>), dim3(a.nl * a.n_seq * a.Hkv), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -700,8 +723,11 @@ extern "C" kvq_status kvq_latent_decode(const kvq_latent_config* cfg, const void
   const int max_chunks = max_chunks_of(cfg, chunk);
   if (max_chunks > kLMaxChunks) return KVQ_ERR_UNSUPPORTED;
   const int64_t entries = int64_t(num_layers) * cfg->batch * Hkv * max_chunks;
+  // arrival counters first, sized by the cache (every layer, sequence and KV
+  // head), so calls of any layer range find them at the same offsets
+  const int64_t arrive_bytes = (int64_t(cfg->num_layers) * cfg->batch * Hkv * 4 + 255) / 256 * 256;
   const int64_t o_bytes = (entries * G * D * 4 + 255) / 256 * 256;
-  const int64_t need = o_bytes + entries * G * 2 * 4;
+  const int64_t need = arrive_bytes + o_bytes + entries * G * 2 * 4;
   if (!workspace) {
     *workspace_bytes = size_t(need);
     return KVQ_OK;
@@ -719,8 +745,9 @@ extern "C" kvq_status kvq_latent_decode(const kvq_latent_config* cfg, const void
   a.out = static_cast<uint16_t*>(out);
   a.up_k = static_cast<const uint16_t*>(up_k);
   a.up_v = static_cast<const uint16_t*>(up_v);
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + o_bytes);
+  a.ws_arrive = static_cast<int32_t*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + arrive_bytes);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + arrive_bytes + o_bytes);
   a.qscale = sm_scale * 1.4426950408889634f;
   a.plane_bytes = plane_bytes_of(cfg);
   a.Hkv = Hkv;

@@ -368,7 +368,8 @@ def kvq_latent_decode(cfg: LatentConfig, cache, layer_begin: int, num_layers: in
                       up_k, up_v, q, out, sm_scale: float, chunk_tokens: int = 0,
                       workspace=None, stream=None) -> None:
     """up_k/up_v: device bf16 [L, Hkv, r, D]; q/out: device bf16 [num_layers, B, Hq, D];
-    seq_lens: device int32 [B]; workspace: device uint8 of latent_workspace_bytes(...)."""
+    seq_lens: device int32 [B]; workspace: device uint8 of latent_workspace_bytes(...),
+    zero-filled before its first use (the calls leave it reusable)."""
     import torch
     if workspace is None:
         raise ValueError("workspace tensor required (see latent_workspace_bytes)")

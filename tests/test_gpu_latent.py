@@ -74,14 +74,17 @@ class LatentPair:
                 kvq.kvq_latent_store(self.cfg, self.cache, l, 1, [s], t0, e,
                                      _bits_dev(kv[0][None, None]), _bits_dev(kv[1][None, None]))
 
-    def decode(self, lens, layer_begin=0, num_layers=None, chunk=0):
+    def decode(self, lens, layer_begin=0, num_layers=None, chunk=0, ws=None):
+        """ws: a workspace to reuse; None = a fresh zero-filled one."""
         t = _t()
         w = self.w
         nl = w.num_layers - layer_begin if num_layers is None else num_layers
         qb = np.stack([w.q_bits(layer_begin + i) for i in range(nl)])
         q = _bits_dev(qb)
         out = t.empty_like(q)
-        ws = t.empty(kvq.latent_workspace_bytes(self.cfg, nl, chunk), dtype=t.uint8, device="cuda")
+        if ws is None:
+            ws = t.zeros(kvq.latent_workspace_bytes(self.cfg, nl, chunk), dtype=t.uint8,
+                         device="cuda")
         lens_d = t.tensor(np.asarray(lens, dtype=np.int32), device="cuda")
         kvq.kvq_latent_decode(self.cfg, self.cache, layer_begin, nl, lens_d, self.up_dev[0],
                               self.up_dev[1], q, out, w.sm_scale, chunk, ws)
@@ -197,3 +200,27 @@ def test_latent_decode_full_step_sampled_and_deterministic():
     out = _check(p, p.w.seq_lens, layers=[0, 13, 27], what="latent step")
     again, _ = p.decode(p.w.seq_lens)
     assert np.array_equal(out, again)
+
+
+def test_latent_workspace_reused_across_calls():
+    """One workspace, zero-filled once, serves calls of different layer
+    ranges, chunk sizes and lengths: each gives the bytes a fresh workspace
+    gives, and the arrival counters are back at zero after every call."""
+    t = _t()
+    _say("latent decode, one workspace over several calls")
+    p = LatentPair(synth.llava_latent())
+    p.store()
+    w = p.w
+    ragged = [max(1, n // 3) for n in w.seq_lens]
+    calls = [(w.seq_lens, 0, None, 0), (w.seq_lens, 13, 2, 256), (ragged, 0, 3, 32),
+             (w.seq_lens, 27, 1, 0), (w.seq_lens, 0, None, 0)]
+    size = max(kvq.latent_workspace_bytes(p.cfg, w.num_layers - lb if nl is None else nl, ch)
+               for _, lb, nl, ch in calls)
+    ws = t.zeros(size, dtype=t.uint8, device="cuda")
+    counters = w.num_layers * w.batch * w.num_kv_heads * 4
+    for lens, lb, nl, ch in calls:
+        _say("  layers from", lb, "count", nl, "chunk", ch)
+        got, _ = p.decode(lens, layer_begin=lb, num_layers=nl, chunk=ch, ws=ws)
+        ref, _ = p.decode(lens, layer_begin=lb, num_layers=nl, chunk=ch)
+        assert np.array_equal(got, ref)
+        assert int(t.count_nonzero(ws[:counters]).item()) == 0

@@ -469,7 +469,8 @@ def test_latent_cache_bytes_and_validation(L):
     st, need = dec(ws=None)
     assert st == kvq.KVQ_OK and need > 0
     entries = 1 * 3 * 2 * 1  # one chunk per sequence at these capacities
-    assert need == -(-(entries * 4 * 128 * 4) // 256) * 256 + entries * 4 * 2 * 4
+    counters = 256           # 2 layers * 3 sequences * 2 KV heads int32, padded to 256 B
+    assert need == counters + -(-(entries * 4 * 128 * 4) // 256) * 256 + entries * 4 * 2 * 4
     assert dec(ws_bytes=need - 1)[0] == kvq.KVQ_ERR_WORKSPACE
     assert dec(layer_begin=2)[0] == kvq.KVQ_ERR_RANGE
     assert dec(nl=0)[0] == kvq.KVQ_ERR_SHAPE
@@ -479,5 +480,5 @@ def test_latent_cache_bytes_and_validation(L):
     assert dec(q=A16 + 4)[0] == kvq.KVQ_ERR_ALIGN
     assert dec(ws=A256 + 64)[0] == kvq.KVQ_ERR_ALIGN
     # 32-token chunks: the longest sequence (64 rows) has 2, so 2 slots per entry
-    assert dec(chunk=32, ws=None)[1] == -(-(1 * 3 * 2 * 2 * 4 * 128 * 4) // 256) * 256 + \
-        1 * 3 * 2 * 2 * 4 * 2 * 4
+    assert dec(chunk=32, ws=None)[1] == counters + \
+        -(-(1 * 3 * 2 * 2 * 4 * 128 * 4) // 256) * 256 + 1 * 3 * 2 * 2 * 4 * 2 * 4
