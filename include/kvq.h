@@ -390,8 +390,10 @@ kvq_status kvq_latent_store(const kvq_latent_config *cfg, void *cache, int32_t l
  *   q, out     device bf16 [num_layers, batch, Hq, D], 16-byte aligned; out
  *              must not alias any input or the workspace
  *   chunk_tokens  0 = library choice (about one workgroup per compute unit
- *              over the call), else a positive multiple of 32 = tokens per
- *              workgroup.  Each chunk's summation order is fixed: repeated
+ *              over the call; its waves take the chunk's steps as they
+ *              finish, so the summation order, hence the output's last bits,
+ *              can differ between calls), else a positive multiple of 32 =
+ *              tokens per workgroup, steps assigned statically: repeated
  *              calls give identical bytes.
  *   workspace  device, 256-byte aligned: arrival counters for every (layer,
  *              sequence, KV head) of the cache, then the split partials;

@@ -36,13 +36,13 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
-constexpr int kLWaves = 4;                // waves per decode workgroup
-constexpr int kLThreads = 64 * kLWaves;
+// Waves per decode workgroup: eight for narrow latents (a step is few
+// bytes, so more waves keep more of them in flight), four for wide ones
+// (more waves would cost registers the loop needs and a longer combine).
+template <int R>
+constexpr int lat_waves() { return R <= 64 ? 8 : 4; }
 constexpr float kLLazy = 6.0f;            // p <= 2^6 between rescales
 constexpr int kLMaxChunks = 4096;         // partial slots per (layer, seq, head)
-#ifndef KVQ_LAT_AHEAD
-#define KVQ_LAT_AHEAD 0  // ring of 1 + KVQ_LAT_AHEAD steps; 0: two buffers, copied
-#endif
 
 struct LatentArgs {
   const uint8_t* cache;
@@ -59,6 +59,7 @@ struct LatentArgs {
   int Hkv, Hq, G, B;
   int layer_begin, nl;
   int chunk;                // tokens per decode workgroup (multiple of 32)
+  int claim_steps;          // 1: waves claim their steps (library-chosen chunks)
   int max_chunks;
   int seq_off, n_seq;       // sequences [seq_off, seq_off + n_seq) of this launch
   int32_t row0[kMaxSeq];    // first plane row of each sequence
@@ -235,10 +236,11 @@ __device__ inline float ld_sys(const float* p) {
 // (m, l) pairs and the partial outputs -- are issued before the block's
 // first barrier.  kMB * kE = 32 values in flight per thread, so the merge
 // needs no more registers than the decode loop before it.
-template <int D>
+template <int D, int kLThreads>
 __device__ void merge_latent_entry(const LatentArgs& a, int l, int s, int h, int nx) {
-  constexpr int kE = 16 * D / 256;  // (head, column) elements per thread
-  constexpr int kMB = 32 / kE;      // chunks per merge block: 8 at D = 64, 4 at D = 128
+  constexpr int kE = 16 * D / kLThreads;  // (head, column) elements per thread
+  constexpr int kMB = 32 / kE;      // chunks per merge block
+  static_assert(kE >= 1 && kMB * 16 <= kLThreads, "merge block shape");
   __shared__ float2 mls[kMB][16];
   __shared__ float fx[kMB][16];
   __shared__ float scl[16];
@@ -257,7 +259,7 @@ __device__ void merge_latent_entry(const LatentArgs& a, int l, int s, int h, int
     for (int x = 0; x < kMB; ++x)
 #pragma unroll
       for (int k = 0; k < kE; ++k) {
-        const int idx = tid + 256 * k, hh = idx / D;
+        const int idx = tid + kLThreads * k, hh = idx / D;
         ov[x][k] = x < nb && hh < G ? ld_sys(a.ws_o + (p0 + xb + x) * G * D + idx) : 0.0f;
       }
     if (tid < kMB * 16) {
@@ -285,7 +287,7 @@ __device__ void merge_latent_entry(const LatentArgs& a, int l, int s, int h, int
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kE; ++k) {
-      const int hh = (tid + 256 * k) / D;
+      const int hh = (tid + kLThreads * k) / D;
       float o = acc[k] * scl[hh];
 #pragma unroll
       for (int x = 0; x < kMB; ++x) o = __builtin_fmaf(fx[x][hh], ov[x][k], o);
@@ -298,7 +300,7 @@ __device__ void merge_latent_entry(const LatentArgs& a, int l, int s, int h, int
   uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
 #pragma unroll
   for (int k = 0; k < kE; ++k) {
-    const int idx = tid + 256 * k, hh = idx / D;
+    const int idx = tid + kLThreads * k, hh = idx / D;
     if (hh < G) outp[idx] = uint16_t(bf16_bits(acc[k] / Ls[hh]));
   }
   if (tid == 0)
@@ -306,20 +308,17 @@ __device__ void merge_latent_entry(const LatentArgs& a, int l, int s, int h, int
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// One workgroup: one chunk of one (layer, sequence, KV head); its four waves
-// take the chunk's 32-token steps in turn, then combine into one partial.
+// One workgroup: one chunk of one (layer, sequence, KV head); its waves take
+// the chunk's 32-token steps, then combine into one partial.
 template <int D, int R>
-__global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) {
-  constexpr int kParts = 256 / D;  // threads per output column in the projection
-  constexpr int kJ = R / kParts;   // latent indices per thread in the projection
-  constexpr int kBig = kLWaves * 16 * R > kParts * 16 * D ? kLWaves * 16 * R : kParts * 16 * D;
-  __shared__ float q_lds[16][R + 4];  // q', later the chunk's combined latent output
-  __shared__ float big[kBig];         // the waves' outputs, later projection sums
+__global__ __launch_bounds__(64 * lat_waves<R>()) void latent_decode_kernel(LatentArgs a) {
+  constexpr int kLWaves = lat_waves<R>();
+  constexpr int kLThreads = 64 * kLWaves;
+  __shared__ float q_lds[16][R + 4];  // q'
+  __shared__ float o_lds[kLWaves][16][R];  // the waves' latent outputs
   __shared__ float ml_lds[kLWaves][16][2];
-  __shared__ float mlc[16][2];
   __shared__ uint4 bv_lds[R * D / 8];  // B_V of this (layer, head), bf16
-  float(*o_lds)[16][R] = reinterpret_cast<float(*)[16][R]>(big);
-  float(*part)[16][D] = reinterpret_cast<float(*)[16][D]>(big);
+  __shared__ int claim;                // the chunk's next unclaimed step
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, j = lane >> 4;
 
@@ -342,16 +341,29 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
   const Rsrc kr = make_rsrc(kplane, a.plane_bytes);
   const Rsrc vr = make_rsrc(kplane + a.plane_bytes, a.plane_bytes);
   const int row0 = a.row0[i];
+  const int nsteps = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
+  auto rows_of = [&](int k) { return min(32, t1 - t0 - 32 * k); };
+  auto load = [&](int k, LStep<R>& b) {
+    if (k < nsteps) load_lstep<R>(kr, vr, row0 + t0 + 32 * k, rows_of(k), n, j, b);
+  };
+  // The wave's first step is loaded first: its memory latency overlaps the
+  // query projection below, which does not depend on it.
+  LStep<R> cur, nxt;
+  load(wave, cur);
 
   // B_V goes to LDS now, its loads in flight with the query's
-  const int64_t lhg_v = int64_t(a.layer_begin + l) * a.Hkv + h;
   {
-    const uint4* bvg = reinterpret_cast<const uint4*>(a.up_v + lhg_v * R * D);
-    uint4 t[R * D / 8 / kLThreads];
+    const uint4* bvg = reinterpret_cast<const uint4*>(a.up_v + lhg * R * D);
+    if constexpr (R * D / 8 >= kLThreads) {
+      static_assert(R * D / 8 % kLThreads == 0, "B_V staging shape");
+      uint4 t[R * D / 8 / kLThreads];
 #pragma unroll
-    for (int k = 0; k < R * D / 8 / kLThreads; ++k) t[k] = bvg[threadIdx.x + kLThreads * k];
+      for (int k = 0; k < R * D / 8 / kLThreads; ++k) t[k] = bvg[threadIdx.x + kLThreads * k];
 #pragma unroll
-    for (int k = 0; k < R * D / 8 / kLThreads; ++k) bv_lds[threadIdx.x + kLThreads * k] = t[k];
+      for (int k = 0; k < R * D / 8 / kLThreads; ++k) bv_lds[threadIdx.x + kLThreads * k] = t[k];
+    } else if (threadIdx.x < R * D / 8) {
+      bv_lds[threadIdx.x] = bvg[threadIdx.x];
+    }
   }
 
   // ---- q' = qscale * B_K q for the group's heads, on the matrix cores ----
@@ -376,6 +388,7 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
       for (int ii = 0; ii < 4; ++ii) q_lds[n][16 * jb + 4 * j + ii] = c[ii] * a.qscale;
     }
   }
+  if (threadIdx.x == 0) claim = kLWaves;
   __syncthreads();
   // score B operand, chunk c: lane (n, j) holds q'_n[j r/4 + 8 c .. + 8]
   u32x4 qhi[R / 32], qlo[R / 32];
@@ -390,72 +403,33 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
       qlo[c][e2] = lw;
     }
 
-  // ---- the wave's steps: k = wave, wave + 4, ... of the chunk ------------
+  // ---- the wave's steps ---------------------------------------------------
+  // Wave v starts on step v.  With library-chosen chunks later steps are
+  // claimed from an LDS counter, so waves that issue later (two share a
+  // SIMD) take fewer; fixed chunks take steps v, v + kLWaves, ... (a fixed
+  // summation order).  One step is computed while the next one loads.
   LWave<R> w;
 #pragma unroll
   for (int mb = 0; mb < R / 16; ++mb) w.o[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int nsteps = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
-  // Steps in flight per wave: the current one plus KVQ_LAT_AHEAD loaded
-  // ahead, in a ring of buffers with static indices (the loop is unrolled
-  // over the ring).
-  auto rows_of = [&](int k) { return min(32, t1 - t0 - 32 * k); };
-  auto load = [&](int k, LStep<R>& b) {
-    if (k < nsteps) load_lstep<R>(kr, vr, row0 + t0 + 32 * k, rows_of(k), n, j, b);
-  };
-#if KVQ_LAT_AHEAD == 2
-  {
-    LStep<R> b0, b1, b2;
-    load(wave, b0);
-    load(wave + kLWaves, b1);
-    for (int k = wave; k < nsteps; k += 3 * kLWaves) {
-      load(k + 2 * kLWaves, b2);
-      compute_lstep<R>(w, b0, qhi, qlo, rows_of(k), j);
-      if (k + kLWaves >= nsteps) break;
-      load(k + 3 * kLWaves, b0);
-      compute_lstep<R>(w, b1, qhi, qlo, rows_of(k + kLWaves), j);
-      if (k + 2 * kLWaves >= nsteps) break;
-      load(k + 4 * kLWaves, b1);
-      compute_lstep<R>(w, b2, qhi, qlo, rows_of(k + 2 * kLWaves), j);
+  for (int k = wave; k < nsteps;) {
+    int kn = k + kLWaves;
+    if (a.claim_steps) {
+      if (lane == 0)
+        kn = __hip_atomic_fetch_add(&claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      kn = __builtin_amdgcn_readfirstlane(kn);
     }
+    const bool more = kn < nsteps;
+    if (more) load(kn, nxt);
+    compute_lstep<R>(w, cur, qhi, qlo, rows_of(k), j);
+    if (!more) break;
+    cur = nxt;
+    k = kn;
   }
-#elif KVQ_LAT_AHEAD == 0
-  if (wave < nsteps) {
-    LStep<R> cur, nxt;
-    int k = wave;
-    load(k, cur);
-    while (true) {
-      const int kn = k + kLWaves;
-      if (kn < nsteps) {
-        load(kn, nxt);
-        compute_lstep<R>(w, cur, qhi, qlo, rows_of(k), j);
-        cur = nxt;
-        k = kn;
-      } else {
-        compute_lstep<R>(w, cur, qhi, qlo, rows_of(k), j);
-        break;
-      }
-    }
-  }
-#else
-  {
-    LStep<R> b0, b1;
-    load(wave, b0);
-    for (int k = wave; k < nsteps; k += 2 * kLWaves) {
-      load(k + kLWaves, b1);
-      compute_lstep<R>(w, b0, qhi, qlo, rows_of(k), j);
-      if (k + kLWaves >= nsteps) break;
-      load(k + 2 * kLWaves, b0);
-      compute_lstep<R>(w, b1, qhi, qlo, rows_of(k + kLWaves), j);
-    }
-  }
-#endif
 
   // ---- combine the waves, apply B_V, write the chunk's partial ----------
   // The chunk's latent output is projected here, so partials (and the
-  // merge) are D wide; a call whose sequences each fit one chunk writes the
-  // final output directly and needs no merge.
-  const uint16_t* bv = reinterpret_cast<const uint16_t*>(bv_lds);
-  const int d = threadIdx.x % D, pt = threadIdx.x / D;
+  // merge) are D wide; a sequence that fits one chunk gets its final output
+  // directly and needs no merge.
   const float l_col = sum_quarters(w.l);
 #pragma unroll
   for (int mb = 0; mb < R / 16; ++mb)
@@ -466,60 +440,86 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
     ml_lds[wave][n][1] = l_col;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * R; idx += kLThreads) {
-    const int hh = idx / R, jj = idx - hh * R;
-    float M = -INFINITY;
+  // Every wave combines the waves' outputs itself, straight into the A
+  // operand of the projection below: lane (n, j) weighs the waves' sums of
+  // head n (weights 0 for waves without rows) and gathers O[n][32 c + 8 j ..
+  // + 8].  (M, L) of head n end up in every lane of column n.
+  float fw[kLWaves];
+  float M = -INFINITY, L = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kLWaves; ++v)
-      if (ml_lds[v][hh][1] > 0.0f) M = fmaxf(M, ml_lds[v][hh][0]);
-    float o = 0.0f, L = 0.0f;
-#pragma unroll
-    for (int v = 0; v < kLWaves; ++v) {
-      const float lv = ml_lds[v][hh][1];
-      const float f = lv > 0.0f ? __builtin_amdgcn_exp2f(ml_lds[v][hh][0] - M) : 0.0f;
-      o = __builtin_fmaf(f, o_lds[v][hh][jj], o);
-      L = __builtin_fmaf(f, lv, L);
-    }
-    q_lds[hh][jj] = hh < G ? o : 0.0f;
-    if (jj == 0) {
-      mlc[hh][0] = M;
-      mlc[hh][1] = L;
-    }
+  for (int v = 0; v < kLWaves; ++v) {
+    const float mv = ml_lds[v][n][0], lv = ml_lds[v][n][1];
+    M = lv > 0.0f ? fmaxf(M, mv) : M;
+    fw[v] = mv;
   }
-  __syncthreads();
-  float y[16];
 #pragma unroll
-  for (int hh = 0; hh < 16; ++hh) y[hh] = 0.0f;
-#pragma unroll
-  for (int k = 0; k < kJ; ++k)
-#pragma unroll
-    for (int hh = 0; hh < 16; ++hh)
-      y[hh] = __builtin_fmaf(q_lds[hh][pt + kParts * k], bf16_lo(bv[(pt + kParts * k) * D + d]),
-                             y[hh]);
-#pragma unroll
-  for (int hh = 0; hh < 16; ++hh) part[pt][hh][d] = y[hh];
-  __syncthreads();
+  for (int v = 0; v < kLWaves; ++v) {
+    const float lv = ml_lds[v][n][1];
+    fw[v] = lv > 0.0f ? __builtin_amdgcn_exp2f(fw[v] - M) : 0.0f;
+    L = __builtin_fmaf(fw[v], lv, L);
+  }
+  // y = O B_V on the matrix cores, O (16 heads x r, rows past G zero) as a
+  // hi/lo bf16 pair.  A: lane (n, j) holds O[n][32 c + 8 j .. + 8]; B: lane
+  // (n, j) holds B_V[32 c + 8 j + e][16 nb + n] for e = 0..7; the result
+  // lane (n, j) holds y[4 j + ii][16 nb + n].  Waves take the D/16 column
+  // blocks nb in turn.
   const int64_t p = ((int64_t(l) * a.B + s) * a.Hkv + h) * a.max_chunks + x;
   const int nx = a.nxcum[i + 1] - a.nxcum[i];
   uint16_t* outp = a.out + ((int64_t(l) * a.B + s) * a.Hq + int64_t(h) * G) * D;
-  for (int idx = threadIdx.x; idx < G * D; idx += kLThreads) {
-    const int hh = idx / D, dd = idx - hh * D;
-    float v = part[0][hh][dd];
+  const uint16_t* bv = reinterpret_cast<const uint16_t*>(bv_lds);
+  u32x4 ohi[R / 32], olo[R / 32];
 #pragma unroll
-    for (int k = 1; k < kParts; ++k) v += part[k][hh][dd];
-    if (nx == 1) {  // the whole sequence in this chunk: the output itself
-      outp[int64_t(hh) * D + dd] = uint16_t(bf16_bits(v / mlc[hh][1]));
-    } else {
-      // write-through stores: the merging workgroup may sit on another XCD
-      __hip_atomic_store(&a.ws_o[(p * G + hh) * D + dd], v, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
-      if (dd == 0) {
-        __hip_atomic_store(&a.ws_ml[(p * G + hh) * 2], mlc[hh][0], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
-        __hip_atomic_store(&a.ws_ml[(p * G + hh) * 2 + 1], mlc[hh][1], __ATOMIC_RELAXED,
+  for (int c = 0; c < R / 32; ++c) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kLWaves; ++v)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(fw[v], o_lds[v][n][32 * c + 8 * j + e], o[e]);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      uint32_t hw, lw;
+      split_pair(n < G ? o[2 * e2] : 0.0f, n < G ? o[2 * e2 + 1] : 0.0f, hw, lw);
+      ohi[c][e2] = hw;
+      olo[c][e2] = lw;
+    }
+  }
+  // L of the four heads of this lane's result rows
+  float lr[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) lr[ii] = __shfl(L, 4 * j + ii);
+  for (int nb = wave; nb < D / 16; nb += kLWaves) {
+    const int dd = 16 * nb + n;
+    f32x4 y = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < R / 32; ++c) {
+      u32x4 b;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int k = 32 * c + 8 * j + 2 * e2;
+        b[e2] = uint32_t(bv[k * D + dd]) | uint32_t(bv[(k + 1) * D + dd]) << 16;
+      }
+      y = mfma_bf16(ohi[c], b, y);
+      y = mfma_bf16(olo[c], b, y);
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int hh = 4 * j + ii;
+      if (hh >= G) continue;
+      if (nx == 1) {  // the whole sequence in this chunk: the output itself
+        outp[int64_t(hh) * D + dd] = uint16_t(bf16_bits(y[ii] / lr[ii]));
+      } else {
+        // write-through stores: the merging workgroup may sit on another XCD
+        __hip_atomic_store(&a.ws_o[(p * G + hh) * D + dd], y[ii], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
+  }
+  if (nx > 1 && threadIdx.x < G) {  // wave 0, lanes (n < G, j = 0)
+    __hip_atomic_store(&a.ws_ml[(p * G + n) * 2], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&a.ws_ml[(p * G + n) * 2 + 1], L, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
   }
   if (nx == 1) return;
   // The workgroup counts its chunk in once its partial has reached memory;
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kLThreads) void latent_decode_kernel(LatentArgs a) 
     last = __hip_atomic_fetch_add(&a.ws_arrive[(int64_t(a.layer_begin + l) * a.B + s) * a.Hkv + h],
                                   1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == nx - 1;
   __syncthreads();
-  if (last) merge_latent_entry<D>(a, l, s, h, nx);
+  if (last) merge_latent_entry<D, kLThreads>(a, l, s, h, nx);
 }
 
 // Copies 16-byte pieces of latent rows into their planes.
@@ -616,7 +616,8 @@ int max_chunks_of(const kvq_latent_config* c, int chunk) {
 template <int D, int R>
 hipError_t launch_latent(const LatentArgs& a, hipStream_t st) {
   const int units = a.nl * a.Hkv * a.nxcum[a.n_seq];
-  hipLaunchKernelGGL((latent_decode_kernel<D, R>), dim3(units), dim3(kLThreads), 0, st, a);
+  hipLaunchKernelGGL((latent_decode_kernel<D, R>), dim3(units), dim3(64 * lat_waves<R>()), 0, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -757,6 +758,7 @@ extern "C" kvq_status kvq_latent_decode(const kvq_latent_config* cfg, const void
   a.layer_begin = layer_begin;
   a.nl = num_layers;
   a.chunk = chunk;
+  a.claim_steps = chunk_tokens == 0;
   a.max_chunks = max_chunks;
   for (int s0 = 0; s0 < cfg->batch; s0 += kMaxSeq) {
     const int ns = std::min(kMaxSeq, cfg->batch - s0);

@@ -192,20 +192,23 @@ def test_latent_decode_many_sequences():
 
 
 def test_latent_decode_full_step_sampled_and_deterministic():
-    """The 28-layer step at full size: three layers against the oracle, and
-    two calls give identical bytes."""
+    """The 28-layer step at full size: three layers against the oracle; with
+    fixed chunks (static steps) two calls give identical bytes."""
     _say("latent decode 28-layer step, sampled layers")
     p = LatentPair(synth.llava_latent())
     p.store()
-    out = _check(p, p.w.seq_lens, layers=[0, 13, 27], what="latent step")
-    again, _ = p.decode(p.w.seq_lens)
+    _check(p, p.w.seq_lens, layers=[0, 13, 27], what="latent step")
+    out, _ = p.decode(p.w.seq_lens, chunk=1024)
+    again, _ = p.decode(p.w.seq_lens, chunk=1024)
     assert np.array_equal(out, again)
 
 
 def test_latent_workspace_reused_across_calls():
     """One workspace, zero-filled once, serves calls of different layer
-    ranges, chunk sizes and lengths: each gives the bytes a fresh workspace
-    gives, and the arrival counters are back at zero after every call."""
+    ranges, chunk sizes and lengths: each gives what a fresh workspace gives
+    (the same bytes with fixed chunks; with library-chosen chunks, whose
+    waves claim steps as they go, within a unit in the last place of bf16
+    or, where sums cancel, 1e-4 of the largest output), and the arrival counters are back at zero after every call."""
     t = _t()
     _say("latent decode, one workspace over several calls")
     p = LatentPair(synth.llava_latent())
@@ -222,5 +225,9 @@ def test_latent_workspace_reused_across_calls():
         _say("  layers from", lb, "count", nl, "chunk", ch)
         got, _ = p.decode(lens, layer_begin=lb, num_layers=nl, chunk=ch, ws=ws)
         ref, _ = p.decode(lens, layer_begin=lb, num_layers=nl, chunk=ch)
-        assert np.array_equal(got, ref)
+        if ch:
+            assert np.array_equal(got, ref)
+        else:
+            # relative to each element, and absolute where sums cancel
+            np.testing.assert_allclose(got, ref, rtol=2.0 ** -7, atol=1e-4 * np.abs(ref).max())
         assert int(t.count_nonzero(ws[:counters]).item()) == 0
