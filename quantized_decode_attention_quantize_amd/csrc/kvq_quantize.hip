@@ -55,16 +55,33 @@ __device__ inline float bf16_float(uint16_t b) {
   return __builtin_bit_cast(float, uint32_t(b) << 16);
 }
 
-template <int LANES>  // butterfly over aligned groups of LANES lanes
+// Value of another lane of the same row of 16 (DPP moves; every source lane
+// exists): lane l ^ 1, lane l ^ 2, and lane 7 - l of each group of eight.
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+__device__ inline float lane_xor1(float v) { return dpp_mov<0xB1>(v); }     // quad_perm 1,0,3,2
+__device__ inline float lane_xor2(float v) { return dpp_mov<0x4E>(v); }     // quad_perm 2,3,0,1
+__device__ inline float lane_mirror8(float v) { return dpp_mov<0x141>(v); }  // row_half_mirror
+
+// Minimum / maximum over aligned groups of LANES (2, 4 or 8) lanes: pairs,
+// then quads, then each quad with the mirrored one of its group of eight.
+template <int LANES>
 __device__ inline float group_min(float v) {
-#pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  static_assert(LANES == 2 || LANES == 4 || LANES == 8, "group lanes");
+  v = fminf(v, lane_xor1(v));
+  if constexpr (LANES >= 4) v = fminf(v, lane_xor2(v));
+  if constexpr (LANES == 8) v = fminf(v, lane_mirror8(v));
   return v;
 }
 template <int LANES>
 __device__ inline float group_max(float v) {
-#pragma unroll
-  for (int o = 1; o < LANES; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  static_assert(LANES == 2 || LANES == 4 || LANES == 8, "group lanes");
+  v = fmaxf(v, lane_xor1(v));
+  if constexpr (LANES >= 4) v = fmaxf(v, lane_xor2(v));
+  if constexpr (LANES == 8) v = fmaxf(v, lane_mirror8(v));
   return v;
 }
 
@@ -81,13 +98,19 @@ constexpr int kE = 16;
 // to meta.
 constexpr int kWords = kE / 4;  // 32-bit words of an 8-bit lane chunk
 
-// Rounded quotients c clamped to [0, n], B bits each, packed little-endian.
+// Rounded quotients c, B bits each, packed little-endian.  Every c is an
+// integer in [0, 2^B - 1] (d >= 0 and d / sc <= 2^B - 1 for values inside
+// the binary16 range), so the codes of one byte combine exactly in binary32
+// (c0 + 2^B c1 + ...) and v_cvt_pk_u8_f32 places the byte.
 template <int B>
-__device__ inline void pack_codes(const float (&c)[kE], float n, uint32_t (&packed)[kWords]) {
+__device__ inline void pack_codes(const float (&c)[kE], uint32_t (&packed)[kWords]) {
+  constexpr int kPer = 8 / B;  // codes per byte
 #pragma unroll
-  for (int i = 0; i < kE; ++i) {
-    const uint32_t code = uint32_t(__builtin_amdgcn_fmed3f(c[i], 0.0f, n));
-    packed[(i * B) / 32] |= code << ((i * B) % 32);
+  for (int byte = 0; byte < kE / kPer; ++byte) {
+    float v = c[kPer * byte + kPer - 1];
+#pragma unroll
+    for (int k = kPer - 2; k >= 0; --k) v = __builtin_fmaf(v, float(1 << B), c[kPer * byte + k]);
+    packed[byte / 4] = __builtin_amdgcn_cvt_pk_u8_f32(v, byte % 4, packed[byte / 4]);
   }
 }
 
@@ -137,9 +160,9 @@ __device__ inline void quantize_lane(const float (&x)[kE], int bits, uint32_t (&
   if (live) {
     // the width is the same for the whole workgroup: one branch, and each
     // code's word and shift are constants
-    if (bits == 2) pack_codes<2>(c, n, packed);
-    else if (bits == 4) pack_codes<4>(c, n, packed);
-    else pack_codes<8>(c, n, packed);
+    if (bits == 2) pack_codes<2>(c, packed);
+    else if (bits == 4) pack_codes<4>(c, packed);
+    else pack_codes<8>(c, packed);
   }
   meta = uint32_t(sc16) | (uint32_t(mn16) << 16);
 }
