@@ -570,10 +570,24 @@ def long_context_decode(torch, kvq, args, dev):
     alg = algorithmic_bytes(w, lens)
     gbs = alg / (ms * 1e-3) / 1e9
     traffic, src = counted_traffic(w.name)
+    # fixed splits: about S chunks per (sequence, KV head), S = 16, 32, 64
+    sweep = {}
+    for S in (16, 32, 64):
+        chunk = 32 * math.ceil(max(lens) / (32 * S))
+        wss = torch.zeros(kvq.workspace_bytes(cfg, 1, chunk), dtype=torch.uint8, device=dev)
+
+        def dec_s(i, chunk=chunk, wss=wss):
+            kvq.kvq_decode_attention(cfg, caches[i % R], 0, 1, lens_d, q, out, w.sm_scale, chunk,
+                                     wss)
+
+        for i in range(args.warmup):
+            dec_s(i)
+        sweep[str(S)] = {"chunk_tokens": chunk, "us": round(timed(torch, args, dec_s) * 1e3, 2)}
+        del wss
     del caches, ws
     return {"workload": describe(w), "us": round(ms * 1e3, 2), "algorithmic_bytes": alg,
             "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "traffic_source": src, "cache_replicas": R}
+            "traffic_source": src, "cache_replicas": R, "fixed_split_sweep": sweep}
 
 
 def latent_decode(torch, kvq, synth, args, dev):
