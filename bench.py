@@ -1,10 +1,14 @@
 """Decode-step benchmark of libkvq on one MI355X.
 
-One step = the hot path of one decode step over a whole model:
-  1. kvq_quantize stores the new token's K/V for every layer (one launch,
-     positions [T, T+1): a generated token, so a bf16 row), then
-  2. kvq_decode_attention attends over [0, T+1) for every layer, KV head and
-     query head (split-K over token chunks + log-sum-exp merge).
+One step = the hot path of one decode step over a whole model, in one
+launch of kvq_decode_attention_append:
+  1. the new token's K/V rows are stored for every layer and KV head
+     (position T: a generated token, so a bf16 text row), by the wave that
+     attends that position, then
+  2. the launch attends over [0, T+1) for every layer, KV head and query head
+     (split-K over token chunks + log-sum-exp merge).
+The same step with the append as a launch of its own (kvq_quantize, then
+kvq_decode_attention) is reported among the extras.
 The cache is rotated over several replicas (>= 2 GB in total) so each step
 reads HBM, not the 256 MB Infinity Cache: at 2 GB even the bf16 rows of the
 protected heads alone (about 40 % of a step's bytes) span far more than that
@@ -17,7 +21,8 @@ attention launch, timed with HIP events on the stream it runs on.
 bounded sample of the same workload, scaled to one step.  Extras: the bf16
 reference decode, the long-context (32K) decode, a read-only stream kernel
 as the practical HBM ceiling, a device copy, the quantize block, rotated K,
-and the layer-by-layer launch pattern.
+per-channel K, the latent decode, the two-launch step and the layer-by-layer
+launch pattern.
 """
 from __future__ import annotations
 
@@ -259,6 +264,12 @@ def main():
     same_T = len(set(T)) == 1
 
     def step(i):
+        # the appended token (position T[s], a text row) is stored by the
+        # decode launch itself, by the wave that attends it
+        kvq.kvq_decode_attention_append(cfg, caches[i % R], 0, w.num_layers, lens_d, k_new,
+                                        v_new, q, out, w.sm_scale, args.chunk, ws)
+
+    def step_separate(i):
         c = caches[i % R]
         if same_T:
             kvq.kvq_quantize(cfg, c, 0, w.num_layers, seq_ids, T[0], T[0] + 1, k_new, v_new)
@@ -286,6 +297,13 @@ def main():
         f"{dec_gbs:.0f} GB/s")
 
     extras = {}
+    if not args.no_extras:
+        # the same step with the append as a launch of its own (kvq_quantize
+        # or kvq_quantize_ragged, then kvq_decode_attention)
+        sep_ms = timed(torch, args, step_separate)
+        extras["separate_append_step"] = {
+            "us": round(sep_ms * 1e3, 2), "launches": 2,
+            "gbps": round(step_bytes / (sep_ms * 1e-3) / 1e9, 1)}
     if not args.no_extras and w.num_layers > 1:
         # the same step as a layer-by-layer serving loop issues it: one
         # decode launch per layer, back to back

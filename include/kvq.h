@@ -292,6 +292,37 @@ kvq_status kvq_decode_attention(const kvq_config *cfg, const void *cache,
                                 float sm_scale, int32_t chunk_tokens, void *workspace,
                                 size_t *workspace_bytes, void *stream);
 
+/* The decode-time append and kvq_decode_attention in one launch: for every
+ * layer l of the call, sequence s and KV head h, the token at position
+ * seq_lens[s] - 1 (after clamping) is stored from k_new / v_new exactly as
+ * kvq_quantize_ragged stores it, and then attended like every other
+ * position.  nuiw.github.io "VLM_KV_Quantization" section 1: each generated
+ * token joins the cache in full precision and is attended at the step that
+ * produced it; section 2: it is a text position, so its rows are bf16.
+ * The workgroup that attends the position writes its rows first (write-
+ * through stores, completed before its own loads), so nothing else orders
+ * the store and the read, and the append costs no launch of its own.
+ *
+ *   cache      device, as for kvq_decode_attention; written at the appended
+ *              rows only
+ *   k_new,
+ *   v_new      device, 16-byte aligned, contiguous [num_layers, batch,
+ *              num_kv_heads, D] of float32 (KVQ_SRC_F32) or bf16
+ *              (KVQ_SRC_BF16): the rows of position seq_lens[s] - 1
+ * The appended position must be a text position of its sequence: before
+ * vis_begin, at or after the coded span's end, or inside a bf16 range.  A
+ * position the cache stores coded (or bf16 in a protected head's visual rows)
+ * is not written, and the call then attends whatever the cache held there.
+ * Other arguments, the workspace contract and errors as kvq_decode_attention
+ * (KVQ_ERR_NULL also for k_new / v_new, KVQ_ERR_ALIGN for their alignment,
+ * KVQ_ERR_UNSUPPORTED for another src_dtype). */
+kvq_status kvq_decode_attention_append(const kvq_config *cfg, void *cache, int32_t layer_begin,
+                                       int32_t num_layers, const int32_t *seq_lens,
+                                       const void *k_new, const void *v_new,
+                                       kvq_src_dtype src_dtype, const void *q, void *out,
+                                       float sm_scale, int32_t chunk_tokens, void *workspace,
+                                       size_t *workspace_bytes, void *stream);
+
 /* kvq_decode_attention without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, semantics and kernels as

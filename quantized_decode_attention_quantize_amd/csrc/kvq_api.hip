@@ -665,10 +665,17 @@ static kvq_status decode_prologue(const kvq_config* cfg, int32_t layer_begin, in
 }
 
 // Launches of one validated decode call over workspace regions `wr`.
+// Sources of a decode-time append (kvq_decode_attention_append); mode 0: none.
+struct AppendSrc {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int mode = 0;  // 1 bf16, 2 fp32
+};
+
 static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_t layer_begin,
                          int32_t num_layers, const int32_t* seq_lens, const void* q, void* out,
                          float sm_scale, const DecodePlan& plan, WsRegions wr,
-                         void* stream) {
+                         void* stream, AppendSrc app = AppendSrc()) {
   if (!cache || !seq_lens || !q || !out) return KVQ_ERR_NULL;
   if (!aligned(cache, 256) || !aligned(q, 16) || !aligned(out, 16) || !aligned(seq_lens, 4))
     return KVQ_ERR_ALIGN;
@@ -713,6 +720,9 @@ static kvq_status decode_launch(const kvq_config* cfg, const void* cache, int32_
     a.rotate_k = cfg->rotate_k != 0;
     a.k_per_channel = cfg->k_per_channel != 0;
     a.max_chunks = plan.max_chunks;
+    a.app_mode = uint8_t(app.mode);
+    a.app_k = app.k;
+    a.app_v = app.v;
     a.seq_off = L.s0;
     a.n_seq = L.ns;
     for (int i = 0; i < L.ns; ++i) {
@@ -767,6 +777,37 @@ extern "C" kvq_status kvq_decode_attention(const kvq_config* cfg, const void* ca
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     return decode_launch(cfg, cache, layer_begin, num_layers, seq_lens, q, out, sm_scale, *plan,
                          WsRegions{ws, ws + plan->arrive_bytes}, stream);
+  } catch (...) {
+    return KVQ_ERR_INTERNAL;
+  }
+}
+
+extern "C" kvq_status kvq_decode_attention_append(
+    const kvq_config* cfg, void* cache, int32_t layer_begin, int32_t num_layers,
+    const int32_t* seq_lens, const void* k_new, const void* v_new, kvq_src_dtype src_dtype,
+    const void* q, void* out, float sm_scale, int32_t chunk_tokens, void* workspace,
+    size_t* workspace_bytes, void* stream) {
+  try {
+    std::shared_ptr<const DecodePlan> plan;
+    kvq_status st = decode_prologue(cfg, layer_begin, num_layers, chunk_tokens, &plan);
+    if (st != KVQ_OK) return st;
+    if (!workspace_bytes) return KVQ_ERR_NULL;
+    if (!workspace) {
+      *workspace_bytes = plan->total;
+      return KVQ_OK;
+    }
+    if (!cache || !seq_lens || !q || !out || !k_new || !v_new) return KVQ_ERR_NULL;
+    if (src_dtype != KVQ_SRC_BF16 && src_dtype != KVQ_SRC_F32) return KVQ_ERR_UNSUPPORTED;
+    if (*workspace_bytes < plan->total) return KVQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256) || !aligned(k_new, 16) || !aligned(v_new, 16))
+      return KVQ_ERR_ALIGN;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    AppendSrc app;
+    app.k = k_new;
+    app.v = v_new;
+    app.mode = src_dtype == KVQ_SRC_BF16 ? 1 : 2;
+    return decode_launch(cfg, cache, layer_begin, num_layers, seq_lens, q, out, sm_scale, *plan,
+                         WsRegions{ws, ws + plan->arrive_bytes}, stream, app);
   } catch (...) {
     return KVQ_ERR_INTERNAL;
   }

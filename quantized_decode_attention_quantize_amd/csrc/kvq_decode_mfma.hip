@@ -1005,6 +1005,35 @@ __device__ inline T* uniform_ptr(T* p) {
   return (T*)((__attribute__((address_space(1))) T*)(hi << 32 | lo));
 }
 __device__ inline int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Decode-time append (kvq_decode_attention_append): stores the bf16 row of
+// one text position, plane row `row` of the K and V planes, from the call's
+// sources, then waits until the stores are complete, so the wave's loads of
+// that row, which follow, read it.  The stores are write-through (system
+// scope).  Lanes [0, D/2) take two elements each.
+template <int D>
+__device__ void append_row(const DecodeArgs& t, const uint8_t* kplane, const uint8_t* vplane,
+                           int64_t row, int64_t src, int lane) {
+  const int mode = __builtin_amdgcn_readfirstlane(int(t.app_mode));
+  if (lane < D / 2) {
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+      const uint8_t* sp = uniform_ptr(static_cast<const uint8_t*>(X ? t.app_v : t.app_k));
+      uint32_t w;
+      if (mode == 1) {
+        w = reinterpret_cast<const uint32_t*>(sp + src * 2)[lane];
+      } else {
+        const float2 f = reinterpret_cast<const float2*>(sp + src * 4)[lane];
+        w = pack_bf16(f.x, f.y);  // nearest even, as the quantizer stores bf16 rows
+      }
+      uint32_t* dst =
+          reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(X ? vplane : kplane) + row * (2 * D));
+      __hip_atomic_store(dst + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);      // the row's stores are complete
+  __asm__ volatile("" ::: "memory");  // and the compiler keeps the loads after them
+}
 __device__ inline Launch launch_scalars(const DecodeArgs& t) {
   Launch L;
   L.cache = uniform_ptr(t.cache);
@@ -1520,6 +1549,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       if (vis && quant_vis) {
         run_segment<D, NG, KB, VB, PC>(c, st, x0, x1, row0, true, use, qreg, q_pending);
       } else {  // text rows, or bf16 visual rows of a protected head
+        // decode-time append: the wave whose static rows hold the last
+        // attended position stores that position's row first (text
+        // positions: the prefix, the suffix and bf16 ranges)
+        if (t.app_mode != 0 && !vis && x0 <= len - 1 && len - 1 < x1)
+          append_row<D>(t, c.ktxt, c.vtxt, row0 + (len - 1 - x0),
+                        ((int64_t(l_local) * La.B + s) * La.Hkv + h) * D, lane);
         run_segment<D, NG, 16, 16>(c, st, x0, x1, row0, vis, use, qreg, q_pending);
       }
     }

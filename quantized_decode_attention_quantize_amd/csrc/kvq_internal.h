@@ -95,8 +95,13 @@ struct DecodeArgs {
   uint8_t rng_first[kMaxSeq + 1];
   uint8_t g_stride;         // query heads per KV head in q / out (G counts this
                             // launch's subgroup of them; q and out point at its first)
-  uint8_t pad_[2];
+  uint8_t app_mode;         // decode-time append: 0 none, 1 bf16 sources, 2 fp32 sources
+  uint8_t pad_;
   int32_t rng_b[kMaxRangesD], rng_e[kMaxRangesD];
+  // append sources [nl, B, Hkv, D]: the row of position seq_lens[s] - 1 of
+  // each (layer, seq, KV head), stored before it is attended
+  const void* app_k;
+  const void* app_v;
 };
 static_assert(sizeof(DecodeArgs) % 16 == 0, "DecodeArgs is copied in 16-byte pieces");
 static_assert(sizeof(DecodeArgs) <= 4096, "DecodeArgs must fit the kernel argument limit");

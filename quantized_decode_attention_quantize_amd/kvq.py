@@ -29,7 +29,8 @@ KVQ_SRC_F32 = 0
 KVQ_SRC_BF16 = 1
 
 EXPORTS = ("kvq_cache_bytes", "kvq_quantize", "kvq_quantize_ragged", "kvq_decode_attention",
-           "kvq_decode_attention_noalloc", "kvq_latent_cache_bytes", "kvq_latent_store",
+           "kvq_decode_attention_append", "kvq_decode_attention_noalloc",
+           "kvq_latent_cache_bytes", "kvq_latent_store",
            "kvq_latent_decode", "kvq_status_string")
 
 
@@ -93,6 +94,10 @@ def lib(path: str = LIB_PATH):
         L.kvq_decode_attention_noalloc.restype = C.c_int
         L.kvq_decode_attention_noalloc.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, P,
                                                    P, P, C.c_float, C.c_int32, P]
+        L.kvq_decode_attention_append.restype = C.c_int
+        L.kvq_decode_attention_append.argtypes = [C.POINTER(_Cfg), P, C.c_int32, C.c_int32, P,
+                                                  P, P, C.c_int, P, P, C.c_float, C.c_int32,
+                                                  P, C.POINTER(C.c_size_t), P]
         L.kvq_latent_cache_bytes.restype = C.c_int
         L.kvq_latent_cache_bytes.argtypes = [C.POINTER(_LatentCfg), C.POINTER(C.c_uint64)]
         L.kvq_latent_store.restype = C.c_int
@@ -289,6 +294,28 @@ def kvq_decode_attention(cfg: Config, cache, layer_begin: int, num_layers: int, 
                                       _dev_ptr(q, "q"), _dev_ptr(out, "out"), float(sm_scale),
                                       chunk_tokens, _dev_ptr(workspace, "workspace"),
                                       C.byref(n), _stream(stream)), "kvq_decode_attention")
+
+
+def kvq_decode_attention_append(cfg: Config, cache, layer_begin: int, num_layers: int, seq_lens,
+                                k_new, v_new, q, out, sm_scale: float, chunk_tokens: int = 0,
+                                workspace=None, stream=None) -> None:
+    """Stores the token at position seq_lens[s] - 1 of every (layer, sequence, KV
+    head) from k_new / v_new (device float32 or bfloat16 [num_layers, batch, Hkv,
+    D]; a text position), then decodes as kvq_decode_attention, in one launch."""
+    if workspace is None:
+        raise ValueError("workspace tensor required (see workspace_bytes)")
+    _check_decode_args(cfg, cache, num_layers, seq_lens, q, out)
+    dt = _check_sources(cfg, k_new.reshape(num_layers, cfg.batch, cfg.num_kv_heads, 1,
+                                           cfg.head_dim),
+                        v_new.reshape(num_layers, cfg.batch, cfg.num_kv_heads, 1, cfg.head_dim),
+                        num_layers, cfg.batch, 1)
+    n = C.c_size_t(_nbytes(workspace))
+    _check(lib().kvq_decode_attention_append(
+        cfg.ref, _dev_ptr(cache, "cache"), layer_begin, num_layers,
+        _dev_ptr(seq_lens, "seq_lens"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"), dt,
+        _dev_ptr(q, "q"), _dev_ptr(out, "out"), float(sm_scale), chunk_tokens,
+        _dev_ptr(workspace, "workspace"), C.byref(n), _stream(stream)),
+        "kvq_decode_attention_append")
 
 
 def kvq_decode_attention_noalloc(cfg: Config, cache, layer_begin: int, num_layers: int,

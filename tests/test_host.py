@@ -261,6 +261,33 @@ def test_decode_validation(L):
                                   C.byref(n), None) == kvq.KVQ_ERR_NULL
 
 
+def test_decode_append_validation(L):
+    """kvq_decode_attention_append: the size query equals the decode's, and
+    the append sources are checked (null, alignment, dtype) before any
+    launch."""
+    cfg = _cfg()
+
+    def app(k=A16 + 8192, v=A16 + 12288, dt=kvq.KVQ_SRC_BF16, ws=A256 + 4096, chunk=64,
+            ws_bytes=1 << 30, layer_begin=0):
+        n = C.c_size_t(ws_bytes)
+        st = L.kvq_decode_attention_append(
+            cfg.ref, C.c_void_p(A256), layer_begin, 1, C.c_void_p(A16),
+            C.c_void_p(k) if k else None, C.c_void_p(v) if v else None, dt, C.c_void_p(A16),
+            C.c_void_p(A16 + 4096), 0.125, chunk, C.c_void_p(ws) if ws else None, C.byref(n),
+            None)
+        return st, n.value
+    st, n = app(ws=None)
+    assert st == kvq.KVQ_OK and n == kvq.workspace_bytes(cfg, 1, 64)
+    assert app(k=None)[0] == kvq.KVQ_ERR_NULL
+    assert app(v=None)[0] == kvq.KVQ_ERR_NULL
+    assert app(k=A16 + 8)[0] == kvq.KVQ_ERR_ALIGN
+    assert app(v=A16 + 4)[0] == kvq.KVQ_ERR_ALIGN
+    assert app(dt=7)[0] == kvq.KVQ_ERR_UNSUPPORTED
+    assert app(ws_bytes=n - 1)[0] == kvq.KVQ_ERR_WORKSPACE
+    assert app(layer_begin=1)[0] == kvq.KVQ_ERR_RANGE
+    assert app(chunk=48)[0] == kvq.KVQ_ERR_SHAPE
+
+
 def _headguard_like(num_layers):
     return kvq.Config(num_layers, 1, 28, 4, 128, 64, [6288], [14], [6287], [4] * 4 * num_layers,
                       [2] * 4 * num_layers)
