@@ -117,14 +117,20 @@ CASES = [
                                          [800, 400], [4, 2], [4, 4]), [150, 350]),
     ("two query-head subgroups", lambda: _wl("app_sub", 2, 1, 28, 4, 128, 32, [14], [1100],
                                              [1200], [4] * 8, [2] * 8), [1150]),
+    ("rotated K", lambda: _wl("app_rot", 2, 1, 8, 2, 128, 64, [14], [1000], [1100], [4] * 4,
+                              [2] * 4, rotate_k=True), [1010]),
+    ("per-channel K", lambda: _wl("app_pc", 1, 2, 8, 2, 128, 64, [14, 30], [1038, 700],
+                                  [1100, 800], [4, 2], [4, 4], k_per_channel=True), [1038, 720]),
 ]
 
 
 @pytest.mark.parametrize("name,make,pos", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("chunk", [64, 0])
 def test_fused_append_matches_separate_and_oracle(name, make, pos, chunk):
-    _say("fused append:", name, "chunk", chunk)
     w = make()
+    if chunk and w.k_per_channel:
+        chunk = 256  # per-channel K takes fixed chunks in multiples of 256 tokens
+    _say("fused append:", name, "chunk", chunk)
     fused, sep, got_f, got_s = _run(w, pos, chunk)
     assert np.array_equal(fused, sep)  # the whole cache, padding included
     if chunk:
