@@ -219,3 +219,47 @@ def test_fused_append_headguard_step_sampled():
     got = np.array([outs[0][l, 0, i] for l in layers for i in range(w.num_q_heads)])
     assert_close(got, ref, "28-layer step, fused append")
     assert kernel_error(got, ref, "28-layer step, fused append") <= 8e-4
+
+
+def test_fused_append_layer_range_and_70_sequences():
+    """A call over layers [1, 3) of a 3-layer cache with 70 sequences (two
+    launches of the sequence table): every appended row lands where
+    kvq_quantize_ragged puts it, and the outputs agree at fixed chunks."""
+    import torch
+    _say("fused append: layers 1..2 of 3, 70 sequences")
+    B = 70
+    rng = np.random.default_rng(11)
+    caps = [int(c) for c in rng.integers(96, 400, B)]
+    vbs = [int(rng.integers(0, 20)) for _ in range(B)]
+    ves = [vb + int(rng.integers(0, c // 2)) for vb, c in zip(vbs, caps)]
+    w = _wl("app_many", 3, B, 8, 2, 64, 32, vbs, ves, caps, [4, 2, 8, 4, 2, 2], [2, 4, 4, 8, 4, 2])
+    pos = [int(rng.integers(ve, c)) for ve, c in zip(ves, caps)]
+    p = Pair(w)
+    for s in range(B):
+        p.store(seqs=[s], t0=0, t1=pos[s], oracle_too=False)
+    lb, nl = 1, 2
+    kn = np.stack([np.stack([w.sources(l, [s], pos[s], pos[s] + 1, "k")[0, :, 0]
+                             for s in range(B)]) for l in range(lb, lb + nl)])
+    vn = np.stack([np.stack([w.sources(l, [s], pos[s], pos[s] + 1, "v")[0, :, 0]
+                             for s in range(B)]) for l in range(lb, lb + nl)])
+    kd, vd = to_device_src(kn), to_device_src(vn)
+    lens_d = torch.tensor([x + 1 for x in pos], dtype=torch.int32, device="cuda")
+    q = bf16_device(np.stack([w.q_bits(l) for l in range(lb, lb + nl)]))
+    outs, caches = [], []
+    for fused in (True, False):
+        c = p.cache.clone()
+        out = torch.empty_like(q)
+        ws = torch.zeros(kvq.workspace_bytes(p.cfg, nl, 64), dtype=torch.uint8, device="cuda")
+        if fused:
+            kvq.kvq_decode_attention_append(p.cfg, c, lb, nl, lens_d, kd, vd, q, out, w.sm_scale,
+                                            64, ws)
+        else:
+            kvq.kvq_quantize_ragged(p.cfg, c, lb, nl, list(range(B)), pos, 1, kd[:, :, :, None],
+                                    vd[:, :, :, None])
+            kvq.kvq_decode_attention(p.cfg, c, lb, nl, lens_d, q, out, w.sm_scale, 64, ws)
+        torch.cuda.synchronize()
+        outs.append(out)
+        caches.append(c)
+    assert torch.equal(caches[0], caches[1])
+    assert torch.equal(outs[0], outs[1])
+    assert not torch.equal(caches[0], p.cache)  # rows were appended
