@@ -102,6 +102,10 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
   std::map<long, std::set<int>> seen_px;
   std::map<long, int> npieces;
   std::map<long, std::set<long>> heads_seen;  // per entry: its subgroups (first head, count)
+  // per entry: waves that would store the appended row (kvq_decode_attention_append),
+  // and whether the last position is stored as a text row
+  std::map<long, int> app_owners;
+  std::map<long, bool> app_text;
   long waves = 0;
   for (const DecodeArgs& a : g_mfma) {
     const long total = long(a.nxcum[a.n_seq]) * a.mcum[a.n_lh];
@@ -198,7 +202,10 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
             }
           }
           for (int tk = x0; tk < x1; ++tk) cv[tk]++;
+          // the append's owner: the kernel's test on the same segment range
+          if (!vis && x0 <= len - 1 && len - 1 < x1) app_owners[key]++;
         }
+        app_text[key] = row_of[s].second[len - 1] >= 0;
       }
     }
   }
@@ -211,6 +218,16 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
     if (int(seen_px[kv.first].size()) != npieces[kv.first]) {
       printf("%s: entry %ld has %zu of %d pieces\n", name, kv.first, seen_px[kv.first].size(),
              npieces[kv.first]);
+      ++bad;
+    }
+  }
+  // the appended position (seq_lens - 1): exactly one wave of each entry and
+  // subgroup stores it when it is a text row, none otherwise
+  for (auto& kv : app_text) {
+    const int want = kv.second ? 1 : 0, got = app_owners.count(kv.first) ? app_owners[kv.first] : 0;
+    if (got != want) {
+      if (bad < 8) printf("%s: entry %ld appended row owned by %d waves, want %d\n", name, kv.first,
+                          got, want);
       ++bad;
     }
   }
