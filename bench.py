@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the bf16 reference, quantize block and copy measurements")
+    ap.add_argument("--k-per-channel", action="store_true",
+                    help="cache with K grouped per channel over token blocks (chunk 0 or a "
+                         "multiple of 256)")
     ap.add_argument("--protected", type=int, default=14,
                     help="HeadGuard protected (bf16) heads of the 28-layer step")
     ap.add_argument("--eager", action="store_true",
@@ -102,8 +105,14 @@ def stored_row_bytes(w, l, h, X, t, s):
 
 
 def algorithmic_bytes(w, lens):
-    """Stored K/V bytes every attended position costs, plus q and out."""
+    """Stored K/V bytes every attended position costs, plus q and out.  With
+    per-channel K the coded span is its whole blocks of group_size tokens;
+    the residual tail is stored, and counted, as bf16 rows."""
     D, g = w.head_dim, w.group_size
+    vis_end = list(w.vis_end)
+    if getattr(w, "k_per_channel", False):
+        vis_end = [w.vis_begin[s] + (w.vis_end[s] - w.vis_begin[s]) // g * g
+                   for s in range(w.batch)]
     total = 0
     for l in range(w.num_layers):
         for h in range(w.num_kv_heads):
@@ -111,7 +120,7 @@ def algorithmic_bytes(w, lens):
                 b = int((w.v_bits if X else w.k_bits)[l * w.num_kv_heads + h])
                 for s in range(w.batch):
                     n = lens[s]
-                    nv = max(0, min(n, w.vis_end[s]) - w.vis_begin[s])
+                    nv = max(0, min(n, vis_end[s]) - w.vis_begin[s])
                     nt = n - nv
                     vis_row = (D * b // 8 + (D // g) * 4) if b < 16 else 2 * D
                     total += nv * vis_row + nt * 2 * D
@@ -204,6 +213,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     w = workload(args.workload, args.protected)
+    w.k_per_channel = args.k_per_channel
     T = [c - 1 for c in w.capacity]          # history length before the step
     lens = [t + 1 for t in T]                # attended after appending
     cfg = kvq.Config.from_workload(w)
@@ -333,9 +343,10 @@ def main():
             "gbps": round(ref_alg / (r_ms * 1e-3) / 1e9, 1),
             "speedup_of_quantized": round(r_ms / dec_avg, 3)}
         del refs, wsr
-        extras["rotated_k_decode"] = rotated_decode(torch, kvq, w, args, dev, T, lens_d, q, out,
-                                                    to_dev, dec_avg, alg)
-        if args.chunk == 0:
+        if not args.k_per_channel:  # rotation and per-channel K do not combine
+            extras["rotated_k_decode"] = rotated_decode(torch, kvq, w, args, dev, T, lens_d, q,
+                                                        out, to_dev, dec_avg, alg)
+        if args.chunk == 0 and not args.k_per_channel:
             extras["per_channel_k_decode"] = per_channel_decode(torch, kvq, w, args, dev, T, lens_d,
                                                                 q, out, to_dev, dec_avg)
         extras["quantize_block"] = quantize_block(torch, kvq, synth, dev, stream, args)
@@ -346,7 +357,8 @@ def main():
         extras["latent_decode"] = latent_decode(torch, kvq, synth, args, dev)
 
     cpu = None if args.no_cpu else cpu_baseline(w, lens, q_bits, alg)
-    profiled = args.chunk == 0 and (w.name != "headguard_step" or args.protected == 14)
+    profiled = (args.chunk == 0 and not args.k_per_channel and
+                (w.name != "headguard_step" or args.protected == 14))
     traffic, traffic_src = counted_traffic(w.name) if profiled else (None, None)
 
     line = {
@@ -364,7 +376,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f16/bf16 MFMA operands, fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": describe(w), "name": w.name, "layers": w.num_layers,
+        "config": {"workload": describe(w) + ("; K grouped per channel over blocks of the group "
+                                              "size" if args.k_per_channel else ""),
+                   "name": w.name, "layers": w.num_layers,
                    "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "group": w.group_size, "tokens": lens,
                    "cache_replicas": R, "chunk_tokens": args.chunk,

@@ -210,6 +210,8 @@ struct DecodePlan {
 // kernel: the bytes its visual row moves plus a fixed share for the per-row
 // arithmetic (waves of INT4/INT2 and of bf16 heads at D = 128 running side by
 // side take about 1 : 3.5 per row, which this reproduces).
+constexpr double kPerChannelCost = 1.8;  // per-channel coded rows vs per-token, measured
+
 double row_cost(int D, int g, int kb, int vb) {
   double bytes = vis_row_bytes(D, kb) + vis_row_bytes(D, vb);
   if (kb < 16) bytes += (D / g) * 4;
@@ -394,7 +396,11 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
           double rows = 0.0;
           for (int i = 0; i < S; ++i) {
             const int l = layer_begin + L.glh[i] / Hkv, h = L.glh[i] % Hkv;
-            cost[i] = row_cost(D, g, bits_of(c, l, h, 0), bits_of(c, l, h, 1));
+            const int kb = bits_of(c, l, h, 0);
+            cost[i] = row_cost(D, g, kb, bits_of(c, l, h, 1));
+            // coded per-channel K takes a second MFMA per k-step and a META
+            // stage per block: its steps measured 1.8x the per-token ones
+            if (c->k_per_channel && kb < 16) cost[i] *= kPerChannelCost;
           }
           for (int i = 0; i < ns; ++i) {
             cap[i] = c->capacity[s0 + i];
@@ -448,7 +454,7 @@ std::shared_ptr<const DecodePlan> cached_plan(const kvq_config* c, int layer_beg
   const int Hkv = c->num_kv_heads;
   std::vector<int32_t> key = {layer_begin, nl, chunk_tokens, device_cus(),
                               c->num_layers, c->batch, c->num_q_heads, Hkv, c->head_dim,
-                              c->group_size};
+                              c->group_size, c->k_per_channel != 0};
   key.reserve(key.size() + c->batch + size_t(nl) * Hkv);
   for (int s = 0; s < c->batch; ++s) key.push_back(c->capacity[s]);
   for (int s = 0; s < c->batch; ++s) key.push_back(ranges_count(c, s));  // launch grouping
