@@ -370,12 +370,16 @@ template <int D, int NG, int KB>
 __device__ inline float build_q_pc(const Ctx& c, const uint32_t* pairs, u32x4 (&qop)[D / 32],
                                    u32x4 (&qlo)[D / 32]) {
   constexpr int g = D / NG;
-  const int gj = c.n % NG;
-  const bool live = c.n < c.G * NG;
   const int c0 = c.jq * (D / 4);
+  // A lane's quarter [c0, c0 + D/4) lies inside one group (g is a multiple
+  // of D/4), so whether the lane's column (head, group) owns its channels is
+  // one test per lane; a lane that does not works on a zero query.
+  const bool in = c.n < c.G * NG && c0 / g == c.n % NG;
   float mt = 0.0f;
   // k-steps 2i and 2i + 1 cover quarter offsets [16 i, 16 i + 16): read
-  // those 16 query values and (scale, min) pairs, then fill both k-steps
+  // those 16 query values and (scale, min) pairs, then fill both k-steps.
+  // The products read the binary16 scale and min straight from the pair
+  // words (mixed-precision fmas, one rounding each); q * 16 / w is exact.
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
     uint32_t qw[8], sm[16];
@@ -384,6 +388,8 @@ __device__ inline float build_q_pc(const Ctx& c, const uint32_t* pairs, u32x4 (&
       const u32x4 w = c.qq[2 * i + k];
       qw[4 * k] = w[0]; qw[4 * k + 1] = w[1]; qw[4 * k + 2] = w[2]; qw[4 * k + 3] = w[3];
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qw[k] = in ? qw[k] : 0u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint4 w4 = reinterpret_cast<const uint4*>(pairs + c0 + 16 * i)[k];
@@ -399,14 +405,15 @@ __device__ inline float build_q_pc(const Ctx& c, const uint32_t* pairs, u32x4 (&
         for (int hf = 0; hf < 2; ++hf) {
           const int off = kslot_off<D, KB>(s, 2 * e2 + hf), o16 = off - 16 * i;
           const float w = kslot_w<D, KB>(s, 2 * e2 + hf);
-          const bool in = live && (c0 + off) / g == gj;
           const float q = bf16f((qw[o16 >> 1] >> (16 * (o16 & 1))) & 0xFFFFu);
-          mt += in ? q * f16hi(sm[o16]) : 0.0f;
-          v2[hf] = in ? q * f16lo(sm[o16]) * (16.0f / w) : 0.0f;  // w: power of two
+          mt = __builtin_fmaf(q, f16hi(sm[o16]), mt);
+          v2[hf] = __builtin_fmaf(q * (16.0f / w), f16lo(sm[o16]), 0.0f);  // w: power of two
         }
-        qop[s][e2] = pack_f16(v2[0], v2[1]);
+        const uint32_t hi = pack_f16(v2[0], v2[1]);
+        qop[s][e2] = hi;
         // the remainders are exact in fp32 (v minus its binary16 rounding)
-        qlo[s][e2] = pack_f16(v2[0] - f16lo(qop[s][e2]), v2[1] - f16hi(qop[s][e2]));
+        qlo[s][e2] = pack_f16(__builtin_fmaf(f16lo(hi), -1.0f, v2[0]),
+                              __builtin_fmaf(f16hi(hi), -1.0f, v2[1]));
       }
     }
   }
