@@ -351,20 +351,6 @@ __global__ __launch_bounds__(64 * lat_waves<R>()) void latent_decode_kernel(Late
   LStep<R> cur, nxt;
   load(wave, cur);
 
-  // B_V goes to LDS now, its loads in flight with the query's
-  {
-    const uint4* bvg = reinterpret_cast<const uint4*>(a.up_v + lhg * R * D);
-    if constexpr (R * D / 8 >= kLThreads) {
-      static_assert(R * D / 8 % kLThreads == 0, "B_V staging shape");
-      uint4 t[R * D / 8 / kLThreads];
-#pragma unroll
-      for (int k = 0; k < R * D / 8 / kLThreads; ++k) t[k] = bvg[threadIdx.x + kLThreads * k];
-#pragma unroll
-      for (int k = 0; k < R * D / 8 / kLThreads; ++k) bv_lds[threadIdx.x + kLThreads * k] = t[k];
-    } else if (threadIdx.x < R * D / 8) {
-      bv_lds[threadIdx.x] = bvg[threadIdx.x];
-    }
-  }
 
   // ---- q' = qscale * B_K q for the group's heads, on the matrix cores ----
   // B operand: lane (n, j) holds q_n[32 sd + 8 j .. + 8] (zeros past G);
@@ -390,6 +376,17 @@ __global__ __launch_bounds__(64 * lat_waves<R>()) void latent_decode_kernel(Late
   }
   if (threadIdx.x == 0) claim = kLWaves;
   __syncthreads();
+  // B_V loads go out after the projection (which waits for its own loads)
+  // and land during the loop; they reach LDS after it
+  constexpr int kBV = (R * D / 8 + kLThreads - 1) / kLThreads;
+  uint4 bvt[kBV];
+  {
+    const uint4* bvg = reinterpret_cast<const uint4*>(a.up_v + lhg * R * D);
+#pragma unroll
+    for (int k = 0; k < kBV; ++k)
+      if (R * D / 8 % kLThreads == 0 || threadIdx.x + kLThreads * k < R * D / 8)
+        bvt[k] = bvg[threadIdx.x + kLThreads * k];
+  }
   // score B operand, chunk c: lane (n, j) holds q'_n[j r/4 + 8 c .. + 8]
   u32x4 qhi[R / 32], qlo[R / 32];
 #pragma unroll
@@ -426,6 +423,10 @@ __global__ __launch_bounds__(64 * lat_waves<R>()) void latent_decode_kernel(Late
     k = kn;
   }
 
+#pragma unroll
+  for (int k = 0; k < kBV; ++k)
+    if (R * D / 8 % kLThreads == 0 || threadIdx.x + kLThreads * k < R * D / 8)
+      bv_lds[threadIdx.x + kLThreads * k] = bvt[k];
   // ---- combine the waves, apply B_V, write the chunk's partial ----------
   // The chunk's latent output is projected here, so partials (and the
   // merge) are D wide; a sequence that fits one chunk gets its final output
