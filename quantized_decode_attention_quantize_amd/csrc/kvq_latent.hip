@@ -351,7 +351,6 @@ __global__ __launch_bounds__(64 * lat_waves<R>()) void latent_decode_kernel(Late
   LStep<R> cur, nxt;
   load(wave, cur);
 
-
   // ---- q' = qscale * B_K q for the group's heads, on the matrix cores ----
   // B operand: lane (n, j) holds q_n[32 sd + 8 j .. + 8] (zeros past G);
   // A operand: B_K rows 16 jb + n.  Result lane (n, j), element ii: q'_n at
