@@ -673,6 +673,11 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 // Cache-policy operand of buffer loads: sc0 | sc1, i.e. system-coherent (the
 // load is served past this XCD's caches).
 constexpr int kCoherent = 1 | 16;
+// Cache rows are read once per call: the non-temporal bit (nt) lets them
+// stream through the caches without evicting what is reused -- the code of
+// the tail paths, the argument block, query rows -- so the combine and merge
+// at the end of a launch start warm (0.7-1 us per 28-layer step).
+constexpr int kStream = 2;
 __device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            int(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
@@ -683,16 +688,16 @@ __device__ inline void buf_load(Rsrc r, uint32_t voff, uint32_t soff, uint32_t* 
   if constexpr (NBYTES >= 16) {
 #pragma unroll
     for (int i = 0; i < NBYTES / 16; ++i) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, kStream);
       out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
     }
   } else if constexpr (NBYTES == 8) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStream);
     out[0] = v[0]; out[1] = v[1];
   } else if constexpr (NBYTES == 4) {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream);
   } else {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream);
   }
 }
 
@@ -717,7 +722,7 @@ __device__ inline void tile_load(Rsrc r, uint32_t soff, int rows, int lane, uint
     for (int i = 0; i < P / 16; ++i) {
       const uint32_t off = uint32_t(i * 64 + lane) * 16u;
       const uint32_t row = min(off / R, uint32_t(rows - 1)), col = off % R;
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, row * R + col, soff, 0);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, row * R + col, soff, kStream);
       out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
     }
   } else {
