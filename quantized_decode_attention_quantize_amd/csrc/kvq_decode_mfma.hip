@@ -1606,14 +1606,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   // without tokens), and L = sum l_w f_w.  Each thread forms the weights of
   // its own row from the (m, l) pairs, so one barrier separates the waves'
   // writes from the combine.  Head j's value at d lives in row
-  // c = j * NG + (d / g).
-  // pieces of this workgroup, by their lowest waves
+  // c = j * NG + (d / g).  The pieces are combined side by side: wave w
+  // takes piece w % np (np pieces, by their lowest waves) and slice w / np of
+  // its G * D / 4 vectors, so a workgroup holding two pieces spends one pass,
+  // not two.
   const unsigned lead = __builtin_amdgcn_readfirstlane(lead_lds);
   const bool any_split = __builtin_amdgcn_readfirstlane(split_lds) != 0u;
   const int GD = G * D;
-#pragma clang loop unroll(disable)
-  for (unsigned rest = lead; rest != 0u; rest &= rest - 1u) {
+  if (lead != 0u) {
+    const int np = __popc(lead);
+    const int kk = wave % np;
+    unsigned rest = lead;
+    for (int i = 0; i < kk; ++i) rest &= rest - 1u;
     const int wl = __builtin_ctz(rest);
+    const int slice = wave / np, nslices = (kWaves - kk + np - 1) / np;
     const unsigned pm = __builtin_amdgcn_readfirstlane(winfo[wl][0]);
     const int pl = __builtin_amdgcn_readfirstlane(winfo[wl][2]);
     const int ps = __builtin_amdgcn_readfirstlane(winfo[wl][3]);
@@ -1625,7 +1631,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // four consecutive outputs per thread (one head, one group: D and g are
     // multiples of 4): 16-byte LDS reads and one 16-byte store
     const Rsrc rpo = make_rsrc(La.ws_o + pidx * GD, int64_t(GD) * 4);
-    for (int i4 = threadIdx.x; i4 < GD / 4; i4 += kThreads) {
+    for (int i4 = slice * 64 + lane; i4 < GD / 4; i4 += nslices * 64) {
       const int i = 4 * i4;
       const int j = i / D, d = i % D, cr = j * NG + d / g;
       float2 ml[kWaves];  // all read up front: the selects below stay branch-free
