@@ -1505,11 +1505,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     for (int k = 0; k < nr; ++k) range_total += t.rng_e[r_lo + k] - t.rng_b[r_lo + k];
     range_total = __builtin_amdgcn_readfirstlane(range_total);
     // In a balanced split the piece's visual rows (the union of its waves'
-    // static ranges) are claimed step by step by its waves; text rows, and
-    // everything in the fixed chunk mode or of a sequence with bf16 ranges,
-    // follow the static split [wa, wb).  The static text rows go first so
-    // the claimed part absorbs their imbalance.
+    // static ranges) are claimed step by step by its waves, and the entry's
+    // text rows all go to one unit of its largest piece (text_unit), first,
+    // so the claimed part absorbs them; in the fixed chunk mode and for a
+    // sequence with bf16 ranges every row follows the static split [wa, wb).
     const bool dyn = La.chunk == 0 && nr == 0;
+    const bool txt_mine = u == text_unit(w0, ne, kWaves);
     int ga, gb, gt;
     wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt, phase);
     wave_range(p_hi - 1 + b8 - w0, 0, ne, len, 0, 1, gt, gb, phase);
@@ -1551,6 +1552,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       if (vis && dyn) {
         x0 = max(ga, f0);
         x1 = min(gb, f1);
+      } else if (dyn) {  // text prefix or suffix: the attended part, on one unit
+        x0 = txt_mine ? min(f0, len) : 0;
+        x1 = txt_mine ? min(f1, len) : 0;
       } else {
         x0 = max(wa, f0);
         x1 = min(wb, f1);

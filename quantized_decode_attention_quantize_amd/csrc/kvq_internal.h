@@ -162,6 +162,20 @@ __host__ __device__ inline void wave_range(int x, int w, int nxs, int len, int c
   b = b < phase ? 0 : b - phase;
 }
 
+// The unit of an entry (units [w0, w0 + ne) of a launch, `waves` units per
+// workgroup) that takes all of the entry's text rows in the balanced split:
+// the first unit of its largest piece -- the first full workgroup, else the
+// larger of its two pieces -- so that the piece's claimed visual steps absorb
+// the text steps and the decode-time append, which a piece of one or two
+// waves cannot.
+__host__ __device__ inline int text_unit(int w0, int ne, int waves) {
+  const int room = waves - w0 % waves;
+  const int n1 = ne < room ? ne : room;  // units in the entry's first piece
+  if (n1 == ne || n1 == waves) return 0;
+  if (ne - n1 >= waves) return n1;        // the entry's next workgroup is full
+  return n1 >= ne - n1 ? 0 : n1;
+}
+
 // Index of a split partial: (layer-local l, global seq s, head h, chunk x).
 __host__ __device__ inline int64_t partial_index(int l, int s, int h, int x, int B, int Hkv,
                                                  int max_chunks) {

@@ -181,6 +181,10 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
             if (pos != p_lo) continue;  // the piece's claimed range, once per piece
             x0 = std::max(ga, f0);
             x1 = std::min(gb, f1);
+          } else if (dyn) {  // text rows: all on the entry's text unit
+            const bool mine = u == text_unit(w0, ne, kMfmaWaves);
+            x0 = mine ? std::min(f0, len) : 0;
+            x1 = mine ? std::min(f1, len) : 0;
           } else {
             x0 = std::max(wa, f0);
             x1 = std::min(wb, f1);
