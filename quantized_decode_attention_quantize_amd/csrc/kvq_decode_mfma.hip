@@ -1638,9 +1638,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     for (int i4 = slice * 64 + lane; i4 < GD / 4; i4 += nslices * 64) {
       const int i = 4 * i4;
       const int j = i / D, d = i % D, cr = j * NG + d / g;
-      float2 ml[kWaves];  // all read up front: the selects below stay branch-free
+      // every LDS read up front (one round trip); the selects below stay
+      // branch-free
+      float2 ml[kWaves];
+      f32x4 ov[kWaves];
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) ml[v] = *reinterpret_cast<const float2*>(ml_lds[v][cr]);
+      for (int v = 0; v < kWaves; ++v) {
+        ml[v] = *reinterpret_cast<const float2*>(ml_lds[v][cr]);
+        ov[v] = *reinterpret_cast<const f32x4*>(&o_all[v][cr][d]);
+      }
       float M = -INFINITY;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v)
@@ -1652,7 +1658,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         const float f = (((pm >> v) & 1u) != 0u && ml[v].y > 0.0f)
                             ? __builtin_amdgcn_exp2f(ml[v].x - M) : 0.0f;
         L += ml[v].y * f;
-        acc += *reinterpret_cast<const f32x4*>(&o_all[v][cr][d]) * f;
+        acc += ov[v] * f;
       }
       const float rl = L > 0.0f ? __builtin_amdgcn_rcpf(L) : 0.0f;  // 0: no token here
       const f32x4 o = acc * rl;
