@@ -49,6 +49,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Eight waves per workgroup and one workgroup per CU: two waves per SIMD,
 // both of the same workgroup, so the LDS claim counter below can even out the
@@ -1223,13 +1224,14 @@ __device__ void merge_entry(const Launch& a, uint8_t* big_lds, int l_local, int 
 // entry's G * D outputs, so several merges run side by side with no
 // workgroup barrier and no LDS.  A lane holds one 16-byte vector of outputs
 // per t < kWmT and reads that vector of each of the entry's nxs partials
-// (plus one (m, l) pair per lane), all loads issued before the first use.
-// Entries whose partials do not fit that (nxs > kWmX, nxs * G > 64, or more
-// than kWmT vectors per lane) go through merge_entry instead.
+// together with the (m, l) pair of the vector's head in each partial, all
+// loads issued before the first use: one memory round trip and no
+// cross-lane traffic.  Entries whose partials do not fit that (nxs > kWmX or
+// more than kWmT vectors per lane) go through merge_entry instead.
 constexpr int kWmX = 8, kWmT = 2;
 __device__ inline bool wave_merge_fits(int nxs, int G, int D, int waves) {
   const int per_wave = (G * D / 4 + waves - 1) / waves;  // 16-byte vectors per wave
-  return nxs <= kWmX && nxs * G <= 64 && per_wave <= 64 * kWmT;
+  return nxs <= kWmX && per_wave <= 64 * kWmT;
 }
 template <int D>
 __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int nxs,
@@ -1240,55 +1242,55 @@ __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int
   const int nv = G * D / 4;
   const int per_wave = (nv + waves - 1) / waves;
   const int v_lo = slice * per_wave, v_hi = min(nv, v_lo + per_wave);
+  const int nt = min(kWmT, (v_hi - v_lo + 63) / 64);  // vector slots this wave uses
   const Rsrc ro = make_rsrc(a.ws_o + p0 * G * D, int64_t(nxs) * G * D * 4);
   const Rsrc rm = make_rsrc(a.ws_ml + p0 * G * 2, int64_t(nxs) * G * 8);
-  // every load first: this lane's (m, l) pair (lane = cx * G + j) and its
-  // vectors of every partial
-  float mlm = 0.0f, mll = 0.0f;
-  if (lane < nxs * G) {
-    mlm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                        rm, uint32_t(lane) * 8u, 0, kCoherent));
-    mll = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                        rm, uint32_t(lane) * 8u + 4u, 0, kCoherent));
-  }
   u32x4 buf[kWmT][kWmX];
-#pragma unroll
-  for (int t = 0; t < kWmT; ++t) {
-    const int v = v_lo + lane + 64 * t;
-#pragma unroll
-    for (int cx = 0; cx < kWmX; ++cx)
-      if (v < v_hi && cx < nxs)
-        buf[t][cx] = __builtin_amdgcn_raw_buffer_load_b128(
-            ro, uint32_t(cx * G * D + 4 * v) * 4u, 0, kCoherent);
-  }
-  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * a.Gs) * D;
+  u32x2 mlv[kWmT][kWmX];
 #pragma unroll
   for (int t = 0; t < kWmT; ++t) {
     const int v = v_lo + lane + 64 * t;
     const int j = min(4 * v / D, G - 1);  // head of this vector (clamped for idle lanes)
-    // weights l 2^(m - M_j) of the partials of head j (0 for one without tokens)
-    float mj[kWmX], lj[kWmX];
-    float M = -INFINITY;
 #pragma unroll
-    for (int cx = 0; cx < kWmX; ++cx) {
-      mj[cx] = __shfl(mlm, cx * G + j);
-      lj[cx] = __shfl(mll, cx * G + j);
-      if (cx < nxs && lj[cx] > 0.0f) M = fmaxf(M, mj[cx]);
-    }
-    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float wsum = 0.0f;
-#pragma unroll
-    for (int cx = 0; cx < kWmX; ++cx) {
-      if (cx < nxs && lj[cx] > 0.0f && v < v_hi) {
-        const float w = lj[cx] * __builtin_amdgcn_exp2f(mj[cx] - M);
-        wsum += w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)  // (the element as a value: bit_cast of a vector
-                                      // element reference reads element 0)
-          acc[e] += __builtin_bit_cast(float, uint32_t(buf[t][cx][e])) * w;
+    for (int cx = 0; cx < kWmX; ++cx)
+      if (t < nt && v < v_hi && cx < nxs) {
+        buf[t][cx] = __builtin_amdgcn_raw_buffer_load_b128(
+            ro, uint32_t(cx * G * D + 4 * v) * 4u, 0, kCoherent);
+        mlv[t][cx] = __builtin_amdgcn_raw_buffer_load_b64(rm, uint32_t(cx * G + j) * 8u, 0,
+                                                          kCoherent);
       }
-    }
+  }
+  uint16_t* outp = a.out + ((int64_t(l_local) * a.B + s) * a.Hq + int64_t(h) * a.Gs) * D;
+#pragma unroll
+  for (int t = 0; t < kWmT; ++t) {
+    if (t >= nt) break;
+    const int v = v_lo + lane + 64 * t;
     if (v < v_hi) {
+      // weights l 2^(m - M) of the partials of this vector's head (0 for
+      // one without tokens)
+      float mj[kWmX], lj[kWmX];
+      float M = -INFINITY;
+#pragma unroll
+      for (int cx = 0; cx < kWmX; ++cx) {
+        // (each element as a value: bit_cast of a vector element reference
+        // reads element 0)
+        mj[cx] = cx < nxs ? __builtin_bit_cast(float, uint32_t(mlv[t][cx][0])) : 0.0f;
+        lj[cx] = cx < nxs ? __builtin_bit_cast(float, uint32_t(mlv[t][cx][1])) : 0.0f;
+        if (lj[cx] > 0.0f) M = fmaxf(M, mj[cx]);
+      }
+      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      float wsum = 0.0f;
+#pragma unroll
+      for (int cx = 0; cx < kWmX; ++cx) {
+        if (lj[cx] > 0.0f) {
+          const float w = lj[cx] * __builtin_amdgcn_exp2f(mj[cx] - M);
+          wsum += w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)  // (the element as a value: bit_cast of a vector
+                                        // element reference reads element 0)
+            acc[e] += __builtin_bit_cast(float, uint32_t(buf[t][cx][e])) * w;
+        }
+      }
       const float r = __builtin_amdgcn_rcpf(wsum);
       uint2 o;
       o.x = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)(acc[0] * r))) |
