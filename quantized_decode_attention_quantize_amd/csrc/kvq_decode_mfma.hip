@@ -1228,12 +1228,15 @@ __device__ void merge_entry(const Launch& a, uint8_t* big_lds, int l_local, int 
 // loads issued before the first use: one memory round trip and no
 // cross-lane traffic.  Entries whose partials do not fit that (nxs > kWmX or
 // more than kWmT vectors per lane) go through merge_entry instead.
-constexpr int kWmX = 8, kWmT = 2;
+// Two instances: up to 8 partials (the common case) and up to 16 (a
+// costly pair split finer in a small call); the wider one's guarded loads
+// and loops cost about 0.5 us on entries the narrow one fits.
+constexpr int kWmX = 16, kWmT = 2;
 __device__ inline bool wave_merge_fits(int nxs, int G, int D, int waves) {
   const int per_wave = (G * D / 4 + waves - 1) / waves;  // 16-byte vectors per wave
   return nxs <= kWmX && per_wave <= 64 * kWmT;
 }
-template <int D>
+template <int D, int kX>
 __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int nxs,
                                  int slice, int waves, int lane) {
   const int G = a.G;
@@ -1245,14 +1248,14 @@ __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int
   const int nt = min(kWmT, (v_hi - v_lo + 63) / 64);  // vector slots this wave uses
   const Rsrc ro = make_rsrc(a.ws_o + p0 * G * D, int64_t(nxs) * G * D * 4);
   const Rsrc rm = make_rsrc(a.ws_ml + p0 * G * 2, int64_t(nxs) * G * 8);
-  u32x4 buf[kWmT][kWmX];
-  u32x2 mlv[kWmT][kWmX];
+  u32x4 buf[kWmT][kX];
+  u32x2 mlv[kWmT][kX];
 #pragma unroll
   for (int t = 0; t < kWmT; ++t) {
     const int v = v_lo + lane + 64 * t;
     const int j = min(4 * v / D, G - 1);  // head of this vector (clamped for idle lanes)
 #pragma unroll
-    for (int cx = 0; cx < kWmX; ++cx)
+    for (int cx = 0; cx < kX; ++cx)
       if (t < nt && v < v_hi && cx < nxs) {
         buf[t][cx] = __builtin_amdgcn_raw_buffer_load_b128(
             ro, uint32_t(cx * G * D + 4 * v) * 4u, 0, kCoherent);
@@ -1268,10 +1271,10 @@ __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int
     if (v < v_hi) {
       // weights l 2^(m - M) of the partials of this vector's head (0 for
       // one without tokens)
-      float mj[kWmX], lj[kWmX];
+      float mj[kX], lj[kX];
       float M = -INFINITY;
 #pragma unroll
-      for (int cx = 0; cx < kWmX; ++cx) {
+      for (int cx = 0; cx < kX; ++cx) {
         // (each element as a value: bit_cast of a vector element reference
         // reads element 0)
         mj[cx] = cx < nxs ? __builtin_bit_cast(float, uint32_t(mlv[t][cx][0])) : 0.0f;
@@ -1281,7 +1284,7 @@ __device__ void merge_entry_wave(const Launch& a, int l_local, int s, int h, int
       f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       float wsum = 0.0f;
 #pragma unroll
-      for (int cx = 0; cx < kWmX; ++cx) {
+      for (int cx = 0; cx < kX; ++cx) {
         if (lj[cx] > 0.0f) {
           const float w = lj[cx] * __builtin_amdgcn_exp2f(mj[cx] - M);
           wsum += w;
@@ -1490,8 +1493,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // multiples of 32 from vis_begin (each then lies inside one block)
     const int phase = kpc ? (32 - vb % 32) % 32 : 0;
     int wa, wb;
+    // fixed chunks: a slot with mult = f * kWaves units per chunk of the
+    // sequence grid takes f chunks of La.chunk / f tokens
     if (La.chunk > 0)
-      wave_range(u / kWaves, u % kWaves, ne / kWaves, len, La.chunk, kWaves, wa, wb, phase);
+      wave_range(u / kWaves, u % kWaves, ne / kWaves, len,
+                 La.chunk * kWaves / pick(mA, mB, slot), kWaves, wa, wb, phase);
     else
       wave_range(u, 0, ne, len, 0, 1, wa, wb, phase);
     const int ve = __builtin_amdgcn_readlane(vel, sl);
@@ -1727,11 +1733,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       unsigned rest = done;
       for (int i = 0; i < kk; ++i) rest &= rest - 1u;
       const int w = __builtin_ctz(rest);
-      merge_entry_wave<D>(La, __builtin_amdgcn_readfirstlane(winfo[w][2]),
-                          __builtin_amdgcn_readfirstlane(winfo[w][3]),
-                          __builtin_amdgcn_readfirstlane(winfo[w][4]),
-                          __builtin_amdgcn_readfirstlane(winfo[w][6]), wave / m,
-                          (kWaves - kk + m - 1) / m, lane);
+      const int el = __builtin_amdgcn_readfirstlane(winfo[w][2]);
+      const int es = __builtin_amdgcn_readfirstlane(winfo[w][3]);
+      const int eh = __builtin_amdgcn_readfirstlane(winfo[w][4]);
+      const int en = __builtin_amdgcn_readfirstlane(winfo[w][6]);
+      if (en <= 8)
+        merge_entry_wave<D, 8>(La, el, es, eh, en, wave / m, (kWaves - kk + m - 1) / m, lane);
+      else
+        merge_entry_wave<D, kWmX>(La, el, es, eh, en, wave / m, (kWaves - kk + m - 1) / m, lane);
       return;
     }
   }

@@ -205,12 +205,12 @@ def test_decode_general_kernel_shapes(hq, hkv, g):
     _check_decode(p, [700], what=f"Hq{hq} Hkv{hkv} g{g}")
 
 
-@pytest.mark.parametrize("chunk", [128, 256])
+@pytest.mark.parametrize("chunk", [64, 128, 256])
 def test_decode_wide_group_wave_merge(chunk):
     """G = 16 query heads on one KV head with g = D (16 columns, one launch),
-    split into 6 or 3 fixed chunks: the wave-parallel merge of an entry with
-    more than 64 (partial, head) pairs, each lane reading its own head's
-    (m, l) pairs."""
+    split into 11, 6 or 3 fixed chunks: both instances of the wave-parallel
+    merge (up to 8 and up to 16 partials) on an entry with more than 64
+    (partial, head) pairs, each lane reading its own head's (m, l) pairs."""
     _say("decode G 16 wave merge, chunk", chunk)
     w = synth.Workload("wide16", 1, 1, 16, 1, 128, 128, [700], [14], [700], [700],
                        np.full(1, 4, np.uint8), np.full(1, 2, np.uint8), seed=41)
