@@ -268,10 +268,8 @@ kvq_status kvq_quantize_ragged(const kvq_config *cfg, void *cache, int32_t layer
  *              cost, so that all waves of the call fit the device at once, and
  *              hands its steps to those waves as they finish (the summation
  *              order, hence the output's last bits, can differ between
- *              calls); a smaller call (latency-bound) takes fixed 1024-token
- *              chunks, 512 for a (layer, KV head) whose rows cost at least
- *              twice the cheapest in its launch (a protected bf16 head).
- *              Otherwise a positive multiple of 32 = tokens per
+ *              calls); a smaller call (latency-bound) takes fixed 512-token
+ *              chunks.  Otherwise a positive multiple of 32 = tokens per
  *              split-K workgroup.  Fixed chunks are assigned statically:
  *              repeated calls give identical bytes.
  *   workspace  device scratch for split partials and the merge's arrival

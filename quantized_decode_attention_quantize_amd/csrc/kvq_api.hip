@@ -326,11 +326,7 @@ int64_t pieces(int64_t w0, int64_t n, int per) { return (w0 + n - 1) / per - w0 
 // one 16-column tile ((D / g) * G > 16) is decoded in nsub launches, one per
 // subgroup of its query heads: each reads the K/V rows again, which still
 // runs far ahead of any vector-ALU path.
-constexpr int kSmallCallChunk = 1024;  // tokens per workgroup for small calls (see below)
-// Finest split of a costly pair in a small call: a protected (bf16) pair of
-// a 6,288-token layer then has 14 partials, which the wave-parallel merge
-// still takes (one-layer launches 17.9 -> 16.3 us on the HeadGuard step).
-constexpr int kSmallSplit = 2;
+constexpr int kSmallCallChunk = 512;  // tokens per workgroup for small calls (see below)
 
 DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_tokens) {
   DecodePlan p;
@@ -342,8 +338,10 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
   p.chunk = chunk_tokens > 0 ? chunk_tokens : 0;
   // A small call (fewer rows than one 32-token step per wave slot, e.g. one
   // layer of a 6K-token sequence) is bound by latency, not bandwidth: fixed
-  // 1024-token chunks (static, 4 steps per wave, few partials) beat spreading
-  // it over every wave slot (one 6,287-token layer: 16.9 against 20.3 us).
+  // 512-token chunks (static, 2 steps per wave, at most 16 partials for a
+  // 6K-token sequence, which the wave-parallel merge takes) beat spreading
+  // it over every wave slot, and 1024-token ones (one-layer launches of the
+  // 28-layer HeadGuard step: 15.45 against 17.8 us).
   if (p.chunk == 0) {
     int64_t rows = 0;
     for (int s = 0; s < B; ++s) rows += int64_t(c->capacity[s]) * nlh;
@@ -393,24 +391,6 @@ DecodePlan plan_decode(const kvq_config* c, int layer_begin, int nl, int chunk_t
         if (p.chunk > 0) {
           // fixed chunks: one workgroup (8 waves on the matrix-core kernel) each
           L.mult.assign(S, kMfmaWaves);
-          if (chunk_tokens == 0) {
-            // a small call chosen here: a pair whose rows cost f times the
-            // launch's cheapest (f a power of two, at most kSmallSplit) takes
-            // f chunks of 1/f the tokens, so its workgroups carry about the
-            // same bytes as the others'
-            std::vector<double> cost(S);
-            double cmin = 1e30;
-            for (int i = 0; i < S; ++i) {
-              const int l = layer_begin + L.glh[i] / Hkv, h = L.glh[i] % Hkv;
-              cost[i] = row_cost(D, g, bits_of(c, l, h, 0), bits_of(c, l, h, 1));
-              cmin = std::min(cmin, cost[i]);
-            }
-            for (int i = 0; i < S; ++i) {
-              int f = 1;
-              while (2 * f <= kSmallSplit && 2 * f <= cost[i] / cmin) f *= 2;
-              L.mult[i] = kMfmaWaves * f;
-            }
-          }
           L.nx.resize(ns);
           for (int i = 0; i < ns; ++i) L.nx[i] = (c->capacity[s0 + i] + p.chunk - 1) / p.chunk;
         } else {

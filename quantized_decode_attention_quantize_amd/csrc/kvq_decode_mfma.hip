@@ -1228,9 +1228,9 @@ __device__ void merge_entry(const Launch& a, uint8_t* big_lds, int l_local, int 
 // loads issued before the first use: one memory round trip and no
 // cross-lane traffic.  Entries whose partials do not fit that (nxs > kWmX or
 // more than kWmT vectors per lane) go through merge_entry instead.
-// Two instances: up to 8 partials (the common case) and up to 16 (a
-// costly pair split finer in a small call); the wider one's guarded loads
-// and loops cost about 0.5 us on entries the narrow one fits.
+// Two instances: up to 8 partials (the common case) and up to 16 (a small
+// call's 512-token chunks of a 6K-token sequence); the wider one's guarded
+// loads and loops cost about 0.5 us on entries the narrow one fits.
 constexpr int kWmX = 16, kWmT = 2;
 __device__ inline bool wave_merge_fits(int nxs, int G, int D, int waves) {
   const int per_wave = (G * D / 4 + waves - 1) / waves;  // 16-byte vectors per wave
@@ -1493,11 +1493,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // multiples of 32 from vis_begin (each then lies inside one block)
     const int phase = kpc ? (32 - vb % 32) % 32 : 0;
     int wa, wb;
-    // fixed chunks: a slot with mult = f * kWaves units per chunk of the
-    // sequence grid takes f chunks of La.chunk / f tokens
     if (La.chunk > 0)
-      wave_range(u / kWaves, u % kWaves, ne / kWaves, len,
-                 La.chunk * kWaves / pick(mA, mB, slot), kWaves, wa, wb, phase);
+      wave_range(u / kWaves, u % kWaves, ne / kWaves, len, La.chunk, kWaves, wa, wb, phase);
     else
       wave_range(u, 0, ne, len, 0, 1, wa, wb, phase);
     const int ve = __builtin_amdgcn_readlane(vel, sl);

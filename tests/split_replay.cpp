@@ -143,8 +143,8 @@ static int run_case(const char* name, int L, int B, int Hq, int Hkv, int D, int 
         const int phase = a.k_per_channel ? (32 - vbeg % 32) % 32 : 0;
         int wa, wb, ga, gb, gt;
         if (a.chunk > 0)
-          wave_range(u / kMfmaWaves, u % kMfmaWaves, ne / kMfmaWaves, len,
-                     a.chunk * kMfmaWaves / int(a.mult[slot]), kMfmaWaves, wa, wb, phase);
+          wave_range(u / kMfmaWaves, u % kMfmaWaves, ne / kMfmaWaves, len, a.chunk, kMfmaWaves,
+                     wa, wb, phase);
         else
           wave_range(u, 0, ne, len, 0, 1, wa, wb, phase);
         wave_range(p_lo + b8 - w0, 0, ne, len, 0, 1, ga, gt, phase);
