@@ -677,28 +677,34 @@ constexpr int kCoherent = 1 | 16;
 // Cache rows are read once per call: the non-temporal bit (nt) lets them
 // stream through the caches without evicting what is reused -- the code of
 // the tail paths, the argument block, query rows -- so the combine and merge
-// at the end of a launch start warm (0.7-1 us per 28-layer step).
+// at the end of a launch start warm (0.7-1 us per 28-layer step).  Only
+// loads whose instruction covers whole lines take it: a line that several
+// instructions read in parts is gone before the later ones arrive (64-byte
+// lane pieces of 128-byte INT8 K rows: 100 -> 124 us on a 64-sequence batch).
 constexpr int kStream = 2;
 __device__ inline Rsrc make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            int(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
                                            0x00020000);
 }
+// A lane's NBYTES at voff; callers lay the lanes' pieces end to end, so one
+// instruction covers whole lines only when a piece is one load.
 template <int NBYTES>
 __device__ inline void buf_load(Rsrc r, uint32_t voff, uint32_t soff, uint32_t* out) {
+  constexpr int kAux = NBYTES <= 16 ? kStream : 0;
   if constexpr (NBYTES >= 16) {
 #pragma unroll
     for (int i = 0; i < NBYTES / 16; ++i) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, kStream);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, kAux);
       out[4 * i] = v[0]; out[4 * i + 1] = v[1]; out[4 * i + 2] = v[2]; out[4 * i + 3] = v[3];
     }
   } else if constexpr (NBYTES == 8) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStream);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kAux);
     out[0] = v[0]; out[1] = v[1];
   } else if constexpr (NBYTES == 4) {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kAux);
   } else {
-    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStream);
+    out[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kAux);
   }
 }
 
